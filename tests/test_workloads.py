@@ -1,0 +1,70 @@
+"""The seeded input generator: determinism, table validity and poison placement (no GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_418_amd import workloads as wl
+
+
+def _check_tables(w):
+    B = w.block_size
+    used = []
+    for s in range(w.num_seqs):
+        nb = -(-int(w.seq_lens[s]) // B)
+        row = w.block_tables[s, :nb]
+        assert len(set(row.tolist())) == nb, "a block repeats inside one table"
+        assert np.all(w.block_tables[s, nb:] == w.poison_block)
+        assert np.all((row >= 0) & (row < w.num_blocks)) and w.poison_block not in row
+        used.append(row[w.shared_prefix_blocks:])
+    own = np.concatenate(used)
+    assert len(np.unique(own)) == own.size, "private blocks are shared across tables"
+    if w.shared_prefix_blocks:
+        assert np.all(w.block_tables[:, :w.shared_prefix_blocks] == w.block_tables[0, :w.shared_prefix_blocks])
+
+
+def _check_poison(w):
+    B = w.block_size
+    cov = np.zeros((w.num_blocks, B), bool)
+    for s in range(w.num_seqs):
+        cached = int(w.seq_lens[s] - w.q_lens[s])
+        for j in range(cached):
+            cov[w.block_tables[s, j // B], j % B] = True
+    if w.kv_dtype == "fp8":
+        bad = (w.k_cache == wl.FP8_NAN_CODE).all(-1).all(-1).numpy()
+    else:
+        bad = torch.isnan(w.k_cache).all(-1).all(-1).numpy()
+        assert not torch.isnan(w.k_cache[torch.from_numpy(cov)]).any()
+    assert np.array_equal(bad, ~cov)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_decode", "llama3_8b_decode_bf16", "prefix_shared_fp8_decode"])
+def test_named_workloads_are_valid(name):
+    w = wl.NAMED[name]()
+    _check_tables(w)
+    _check_poison(w)
+    assert w.query.shape == (w.num_tokens, w.num_q_heads, w.head_dim)
+    assert w.new_k.shape == (w.num_tokens, w.num_kv_heads, w.head_dim)
+
+
+def test_mixed_step_layout():
+    w = wl.mixed_step_bf16()
+    assert w.num_tokens == 1072 and w.num_seqs == 50
+    assert list(w.query_start_loc[:3]) == [0, 1, 2] and list(w.query_start_loc[-3:]) == [48, 560, 1072]
+    assert list(w.seq_lens[-2:]) == [512, 2048]
+    _check_tables(w)
+    assert wl.prefill_flops(w) == 4 * 32 * 128 * (131328 + 917760)
+
+
+def test_generation_is_deterministic():
+    a = wl.random_case(3, num_seqs=4, chunk_range=(1, 5), q_dtype="bf16", kv_dtype="bf16")
+    b = wl.random_case(3, num_seqs=4, chunk_range=(1, 5), q_dtype="bf16", kv_dtype="bf16")
+    assert np.array_equal(a.block_tables, b.block_tables)
+    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+    assert torch.equal(a.query.view(torch.int16), b.query.view(torch.int16))
+
+
+def test_random_cases_cover_ragged_shapes():
+    w = wl.random_case(9, num_seqs=6, ctx_range=(1, 70), chunk_range=(1, 30))
+    _check_tables(w)
+    _check_poison(w)
+    assert np.all(w.q_lens >= 1) and np.all(w.seq_lens >= w.q_lens)
