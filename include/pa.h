@@ -1,0 +1,205 @@
+/*
+ * pa.h -- C ABI of the paged-KV attention library for AMD MI355X (gfx950).
+ *
+ * The operations follow the statement of the problem on three pages about
+ * vLLM:
+ *   [A] "vLLM 架构概述" (blog.chen3feng.top/vllm-analysis), §2 (the block pool
+ *       and per-request int32 block tables: a table lookup plus address
+ *       arithmetic inside the kernel) and §3 (the kernel layer: a paged
+ *       attention kernel and the reshape_and_cache KV write);
+ *   [B] "vLLM：从 KV Cache 到高吞吐推理服务" (liujiyu20000308.github.io/vllm),
+ *       tutorial 3 (logical block, physical block, offset, slot, slot
+ *       mapping), tutorial 1 (MHA/GQA/MQA head sharing), tutorial 6 (FP8 E4M3
+ *       KV with a scale), tutorial 7 (tiling, online softmax, LSE);
+ *   [C] reading note on "Inside vLLM" (kb.wilsonhandbook.online), core point
+ *       1 (16-token blocks) and core point 2 (decode and chunked prefill in
+ *       one step, flattened into one super-sequence, each sequence masked to
+ *       its own tokens).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pool layout: key_cache and value_cache are two separate device arrays,
+ *    each [num_blocks][block_size][num_kv_heads][head_dim], row-major.
+ *  - block_tables: device int32 [num_seqs][bt_stride]; entry j of row s is the
+ *    physical block holding positions j*block_size .. j*block_size+block_size-1
+ *    of sequence s.  Only the first ceil(seq_len/block_size) entries are read.
+ *  - seq_lens[s]: tokens of sequence s INCLUDING the new tokens of this step
+ *    (they must have been written into the pool first).
+ *  - query_start_loc: device int32 [num_seqs+1], prefix sums of the new-token
+ *    counts; the new tokens of all sequences form one flattened array of
+ *    num_tokens = query_start_loc[num_seqs] rows.  Sequence s has
+ *    q_len = query_start_loc[s+1]-query_start_loc[s] >= 1 new rows at
+ *    positions seq_len-q_len .. seq_len-1; row i attends to positions
+ *    0 .. seq_len-q_len+i of its own sequence (causal, bottom-right aligned).
+ *  - GQA: q head h reads kv head h / (num_q_heads / num_kv_heads).
+ *  - Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
+ *    num_kv_heads; bf16/fp8 paths need num_q_heads/num_kv_heads <= 16.
+ *  - dtypes: PA_F32, PA_BF16 for activations and pools; PA_FP8_E4M3 pools
+ *    hold OCP E4M3FN codes (bias 7, max 448, no infinities).  The output has
+ *    the query's dtype; fp32 accumulation throughout; bf16 results are rounded
+ *    to nearest even.
+ *  - All pointers not marked "host" are device pointers owned by the caller.
+ *    The library keeps no pointer after a call returns and allocates no
+ *    device memory; scratch space comes from the caller's workspace.
+ *  - stream is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; nothing synchronises.
+ *  - Errors: a non-zero pa_status_t.  Argument errors are found on the host
+ *    before anything is enqueued and leave device memory untouched.
+ *    pa_last_error() returns a thread-local message for the last failure.
+ *    The contents of device arrays are trusted, except that block ids are
+ *    clamped to [0, num_blocks) and positions past max_seq_len are not read;
+ *    setting the environment variable PA_VALIDATE=1 makes every call copy the
+ *    metadata to the host (a synchronising step) and reject inconsistent
+ *    contents with PA_ERR_SHAPE.
+ *  - Thread safety: calls are independent; calls on different streams may run
+ *    concurrently as long as they do not share output or workspace memory.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* inconsistent sizes or metadata */
+  PA_ERR_DTYPE = 3,       /* dtype not valid for this entry point */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  PA_ERR_UNSUPPORTED = 5, /* valid but not implemented (e.g. head_dim 96) */
+  PA_ERR_HIP = 6          /* the HIP runtime reported an error */
+} pa_status_t;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype_t;
+
+/* ABI version (PA_ABI_VERSION of the built library). */
+int pa_abi_version(void);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status_t status);
+
+/* Thread-local message describing the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_slot_mapping -- where each new token's K/V goes.  [B] tutorial 3, [A] §2.
+ * For new row i of sequence s (position p = seq_lens[s] - q_len_s + i):
+ *   slot_mapping[query_start_loc[s] + i] =
+ *       block_tables[s][p / block_size] * block_size + p % block_size.
+ * slot_mapping: device int32 [query_start_loc[num_seqs]] (output).
+ * Bit-exact integer work.
+ */
+pa_status_t pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int32_t bt_stride,
+                            const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                            int32_t num_tokens, int32_t block_size, void* stream);
+
+/*
+ * pa_reshape_and_cache -- write new K/V into the pool through slot_mapping.  [A] §3, [B] tutorial 3.
+ * For t < num_tokens with slot = slot_mapping[t] >= 0:
+ *   key_cache[slot / block_size][slot % block_size][h][:] = key[t*key_tok_stride + h*head_dim + :]
+ * (same for value).  Negative slots are skipped; duplicate slots within one
+ * call are undefined.  key/value: [num_tokens][.. token stride in elements ..]
+ * with heads contiguous inside a token (so K and V may be slices of a fused
+ * QKV output).  dtype: PA_F32 or PA_BF16 for inputs and pools alike; a plain
+ * copy, bit-exact.  Slots >= num_blocks*block_size are skipped.
+ */
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t key_tok_stride,
+                                 int64_t value_tok_stride, void* key_cache, void* value_cache,
+                                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 pa_dtype_t dtype, void* stream);
+
+/*
+ * pa_reshape_and_cache_fp8 -- the same scatter into fp8 pools.  [B] tutorial 6.
+ * Stored code = E4M3FN(fl32(x / scale)) with x the fp32 value of the input
+ * element, one correctly rounded fp32 division, round to nearest even,
+ * finite overflow and infinity saturating to +-448, NaN kept as NaN (0x7F
+ * with the input's sign).  k_scale, v_scale: positive per-tensor scales.
+ * src_dtype: PA_F32 or PA_BF16.  key_cache/value_cache: uint8 codes.
+ */
+pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t key_tok_stride,
+                                     int64_t value_tok_stride, uint8_t* key_cache, uint8_t* value_cache,
+                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     pa_dtype_t src_dtype, float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- scratch pa_decode / pa_decode_fp8 need.
+ * The context of each sequence is split into partitions of partition_size
+ * tokens (0 = 512); partial results per partition are merged with the
+ * log-sum-exp rule ([B] tutorial 7).  Returns 0 when max_seq_len fits one
+ * partition (no scratch needed), and 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t partition_size);
+
+/*
+ * pa_decode -- paged attention for one new token per sequence.  [A] §2-§3,
+ * [B] tutorials 1, 3 and 7, [C] core point 2.
+ * out[s][h][:] = sum_j softmax_j(scale * q[s][h] . K_j) V_j over positions
+ * j = 0 .. seq_lens[s]-1, K_j/V_j read through block_tables.
+ * query/out: [num_seqs][num_q_heads][head_dim], dtype; pools: dtype.
+ * dtype: PA_F32 or PA_BF16.  max_seq_len: host bound on every seq_lens[s]
+ * (sizes the grid; ceil(max_seq_len/block_size) <= bt_stride).
+ * partition_size: multiple of 64, 0 = 512.  workspace: at least
+ * pa_decode_workspace_bytes(...) bytes of device memory (may be NULL when
+ * that is 0), 256-byte aligned.
+ */
+pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                      pa_dtype_t dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over E4M3FN pools.  [B] tutorial 6.
+ * K_j = decode(code) * k_scale, V_j = decode(code) * v_scale (exact values);
+ * q_dtype (= out dtype): PA_BF16 or PA_F32 (fp32 queries are rounded to
+ * bf16 for the matrix cores).  Other arguments as pa_decode.
+ */
+pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                          const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                          pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t partition_size,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_varlen_workspace_bytes -- scratch pa_prefill_varlen needs for
+ * this batch.  query_start_loc_host / seq_lens_host: host copies of the
+ * metadata (num_seqs+1 and num_seqs entries).  Returns 0 on invalid input.
+ */
+size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                         int32_t num_seqs, int32_t num_q_heads, int32_t head_dim);
+
+/*
+ * pa_prefill_varlen -- causal paged attention over a flattened batch of any
+ * mix of decode rows and chunked-prefill chunks.  [C] core point 2, [A] §2,
+ * [B] tutorials 5 (chunked prefill) and 7.
+ * For row t of sequence s (new row i, c = seq_lens[s]-q_len cached tokens):
+ * out[t][h][:] = sum_{j <= c+i} softmax_j(scale * q[t][h] . K_j) V_j.
+ * query/out: [num_tokens][num_q_heads][head_dim]; dtype PA_BF16 (PA_F32 is
+ * accepted for batches whose q_len are all 1).  The host copies of
+ * query_start_loc and seq_lens plan the work (the control plane is on the
+ * CPU) and must equal the device arrays.
+ */
+pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                              const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                              const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, float scale, pa_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,10 @@
+"""Paged-KV attention for AMD MI355X (gfx950).
+
+The compute path is the HIP library libpa.so (C ABI in include/pa.h); the
+functions re-exported here are its ctypes binding and take GPU torch tensors.
+``workloads`` holds the seeded synthetic inputs.
+"""
+from ._binding import (  # noqa: F401
+    PA_BF16, PA_F32, PA_FP8_E4M3, PAError, abi_version, header_symbols, load, pa_decode, pa_decode_fp8,
+    pa_decode_workspace_bytes, pa_prefill_varlen, pa_prefill_varlen_workspace_bytes, pa_reshape_and_cache,
+    pa_reshape_and_cache_fp8, pa_slot_mapping)

@@ -1,0 +1,489 @@
+// C ABI of the paged-KV attention library: argument checks, launch geometry,
+// workspace layout and error reporting.  Declarations and the meaning of
+// every argument are in include/pa.h.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status_t fail(pa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status_t ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+pa_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool validate_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("PA_VALIDATE");
+    return v && v[0] && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+template <typename T>
+bool copy_to_host(std::vector<T>& dst, const T* src, size_t n) {
+  dst.resize(n);
+  if (n == 0) return true;
+  return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+struct PartLayout {
+  size_t o_bytes, m_bytes, total;
+};
+
+PartLayout part_layout(int64_t rows, int64_t heads, int64_t parts, int64_t head_dim) {
+  PartLayout L;
+  L.o_bytes = align_up((size_t)(rows * heads * parts * head_dim) * sizeof(float));
+  L.m_bytes = align_up((size_t)(rows * heads * parts) * sizeof(float));
+  L.total = L.o_bytes + 2 * L.m_bytes;
+  return L;
+}
+
+// Checks of device metadata under PA_VALIDATE=1 (copies to the host, synchronising).
+pa_status_t validate_tables(const int32_t* block_tables, int bt_stride, const int32_t* seq_lens,
+                            const int32_t* qsl, int num_seqs, int num_blocks, int max_seq_len, int block_size) {
+  std::vector<int32_t> sl, q, bt;
+  if (!copy_to_host(sl, seq_lens, num_seqs) || !copy_to_host(bt, block_tables, (size_t)num_seqs * bt_stride))
+    return fail(PA_ERR_HIP, "PA_VALIDATE: metadata copy failed");
+  if (qsl && !copy_to_host(q, qsl, num_seqs + 1)) return fail(PA_ERR_HIP, "PA_VALIDATE: metadata copy failed");
+  if (qsl && q[0] != 0) return fail(PA_ERR_SHAPE, "PA_VALIDATE: query_start_loc[0] = %d, expected 0", q[0]);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = qsl ? q[s + 1] - q[s] : 1;
+    if (q_len < 1) return fail(PA_ERR_SHAPE, "PA_VALIDATE: sequence %d has q_len %d", s, q_len);
+    if (sl[s] < q_len || sl[s] > max_seq_len)
+      return fail(PA_ERR_SHAPE, "PA_VALIDATE: seq_lens[%d] = %d outside [%d, %d]", s, sl[s], q_len, max_seq_len);
+    const int nb = ceil_div(sl[s], block_size);
+    if (nb > bt_stride) return fail(PA_ERR_SHAPE, "PA_VALIDATE: sequence %d needs %d blocks > bt_stride", s, nb);
+    for (int j = 0; j < nb; ++j) {
+      const int b = bt[(size_t)s * bt_stride + j];
+      if (b < 0 || b >= num_blocks)
+        return fail(PA_ERR_SHAPE, "PA_VALIDATE: block_tables[%d][%d] = %d out of [0, %d)", s, j, b, num_blocks);
+    }
+  }
+  return PA_OK;
+}
+
+pa_status_t validate_slots(const int32_t* slots, int num_tokens, int64_t num_slots) {
+  std::vector<int32_t> sm;
+  if (!copy_to_host(sm, slots, num_tokens)) return fail(PA_ERR_HIP, "PA_VALIDATE: slot copy failed");
+  std::vector<int32_t> seen;
+  for (int t = 0; t < num_tokens; ++t) {
+    if (sm[t] < 0) continue;
+    if (sm[t] >= num_slots) return fail(PA_ERR_SHAPE, "PA_VALIDATE: slot_mapping[%d] = %d >= %lld", t, sm[t],
+                                        (long long)num_slots);
+    seen.push_back(sm[t]);
+  }
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+    return fail(PA_ERR_SHAPE, "PA_VALIDATE: duplicate slots in slot_mapping");
+  return PA_OK;
+}
+
+pa_status_t check_attention_shape(int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  int bt_stride) {
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads,
+                num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (block_size != pa::kBlockSize) return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+  if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks %d < 1", num_blocks);
+  if (bt_stride < 1) return fail(PA_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
+  return PA_OK;
+}
+
+int resolve_partition(int partition_size) { return partition_size == 0 ? 512 : partition_size; }
+
+// Shared by pa_decode / pa_decode_fp8 / the decode rows of pa_prefill_varlen.
+pa_status_t run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, const int32_t* qsl,
+                       int32_t num_seqs, int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
+                       int q_f32, float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const int ps = resolve_partition(partition_size);
+  const int n_parts = ceil_div(max_seq_len, ps);
+  pa::DecodeParams p{};
+  p.out = out;
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.qsl = qsl;
+  p.bt_stride = bt_stride;
+  p.num_seqs = num_seqs;
+  p.num_rows = num_rows;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.max_seq_len = max_seq_len;
+  p.part_size = ps;
+  p.n_parts_max = n_parts;
+  p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
+  p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
+  p.q_f32 = q_f32;
+  if (n_parts > 1) {
+    const PartLayout lay = part_layout(num_seqs, num_q_heads, n_parts, head_dim);
+    auto* base = static_cast<unsigned char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(base);
+    p.part_m = reinterpret_cast<float*>(base + lay.o_bytes);
+    p.part_l = reinterpret_cast<float*>(base + lay.o_bytes + lay.m_bytes);
+  }
+  (void)workspace_bytes;
+  (void)block_size;
+  return hip_status(pa::launch_decode(p, kv_kind, head_dim, stream), "decode launch");
+}
+
+pa_status_t check_decode_args(const void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                              int32_t partition_size, void* workspace, size_t workspace_bytes) {
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, bt_stride);
+  if (st != PA_OK) return st;
+  if (max_seq_len < 1) return fail(PA_ERR_SHAPE, "max_seq_len %d < 1", max_seq_len);
+  if (ceil_div(max_seq_len, block_size) > bt_stride)
+    return fail(PA_ERR_SHAPE, "max_seq_len %d needs %d table columns > bt_stride %d", max_seq_len,
+                ceil_div(max_seq_len, block_size), bt_stride);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+  if (partition_size < 0 || partition_size % 64)
+    return fail(PA_ERR_SHAPE, "partition_size %d must be 0 or a positive multiple of 64", partition_size);
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(pa_status_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_SHAPE: return "inconsistent shape or metadata";
+    case PA_ERR_DTYPE: return "unsupported dtype for this call";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status_t pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int32_t bt_stride,
+                            const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                            int32_t num_tokens, int32_t block_size, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_SHAPE, "negative num_seqs or num_tokens");
+  if (num_seqs == 0) return ok();
+  if (!slot_mapping || !block_tables || !seq_lens || !query_start_loc)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size %d < 1", block_size);
+  if (bt_stride < 1) return fail(PA_ERR_SHAPE, "bt_stride %d < 1", bt_stride);
+  if (validate_enabled()) {
+    std::vector<int32_t> q;
+    if (!copy_to_host(q, query_start_loc, num_seqs + 1)) return fail(PA_ERR_HIP, "PA_VALIDATE: copy failed");
+    if (q[num_seqs] != num_tokens)
+      return fail(PA_ERR_SHAPE, "PA_VALIDATE: query_start_loc[num_seqs] = %d != num_tokens %d", q[num_seqs],
+                  num_tokens);
+    pa_status_t st = validate_tables(block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, INT32_MAX,
+                                     bt_stride * block_size, block_size);
+    if (st != PA_OK) return st;
+  }
+  return hip_status(pa::launch_slot_mapping(slot_mapping, block_tables, bt_stride, seq_lens, query_start_loc,
+                                            num_seqs, num_tokens, block_size, static_cast<hipStream_t>(stream)),
+                    "slot_mapping launch");
+}
+
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t key_tok_stride,
+                                 int64_t value_tok_stride, void* key_cache, void* value_cache,
+                                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype_t dtype,
+                                 void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+  if (num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PA_ERR_SHAPE, "non-positive num_kv_heads/head_dim/block_size/num_blocks");
+  if (key_tok_stride < (int64_t)num_kv_heads * head_dim || value_tok_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "token stride smaller than num_kv_heads * head_dim");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_SHAPE, "pool has more than 2^31 slots");
+  if (validate_enabled()) {
+    pa_status_t st = validate_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size);
+    if (st != PA_OK) return st;
+  }
+  const int elem = dtype == PA_F32 ? 4 : 2;
+  return hip_status(pa::launch_reshape_and_cache(key, value, key_tok_stride, value_tok_stride, key_cache, value_cache,
+                                                 slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
+                                                 num_blocks, elem, static_cast<hipStream_t>(stream)),
+                    "reshape_and_cache launch");
+}
+
+pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t key_tok_stride,
+                                     int64_t value_tok_stride, uint8_t* key_cache, uint8_t* value_cache,
+                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype_t src_dtype,
+                                     float k_scale, float v_scale, void* stream) {
+  if (src_dtype != PA_F32 && src_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "src_dtype must be PA_F32 or PA_BF16");
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+  if (num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PA_ERR_SHAPE, "non-positive num_kv_heads/head_dim/block_size/num_blocks");
+  if (key_tok_stride < (int64_t)num_kv_heads * head_dim || value_tok_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "token stride smaller than num_kv_heads * head_dim");
+  if ((num_kv_heads * head_dim) % 8) return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * head_dim must be a multiple of 8");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_SHAPE, "pool has more than 2^31 slots");
+  if (validate_enabled()) {
+    pa_status_t st = validate_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size);
+    if (st != PA_OK) return st;
+  }
+  return hip_status(pa::launch_reshape_and_cache_fp8(key, value, key_tok_stride, value_tok_stride, key_cache,
+                                                     value_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                                     block_size, num_blocks, src_dtype == PA_F32, k_scale, v_scale,
+                                                     static_cast<hipStream_t>(stream)),
+                    "reshape_and_cache_fp8 launch");
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                                 int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_seq_len < 1 || partition_size < 0 ||
+      partition_size % 64)
+    return 0;
+  const int ps = resolve_partition(partition_size);
+  const int n_parts = ceil_div(max_seq_len, ps);
+  if (n_parts <= 1 || num_seqs == 0) return 0;
+  return part_layout(num_seqs, num_q_heads, n_parts, head_dim).total;
+}
+
+pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     partition_size, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (dtype == PA_BF16 && num_q_heads / num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  const int kind = dtype == PA_F32 ? pa::kF32 : pa::kBF16;
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, kind,
+                    dtype == PA_F32, 1.f, 1.f, partition_size, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream));
+}
+
+pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                          const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t q_dtype, float k_scale,
+                          float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     partition_size, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "fp8 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, pa::kFP8,
+                    q_dtype == PA_F32, k_scale, v_scale, partition_size, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+struct VarlenPlan {
+  int max_decode_len = 0;        // longest sequence with q_len == 1 (0: none)
+  bool any_decode = false;
+  std::vector<uint32_t> items;   // prefill work items, longest first
+};
+
+pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_tokens, int bt_stride,
+                        VarlenPlan& plan) {
+  if (qsl[0] != 0) return fail(PA_ERR_SHAPE, "query_start_loc_host[0] = %d, expected 0", qsl[0]);
+  struct Item {
+    int64_t cost;
+    uint32_t code;
+  };
+  std::vector<Item> items;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = qsl[s + 1] - qsl[s];
+    if (q_len < 1) return fail(PA_ERR_SHAPE, "sequence %d has q_len %d < 1", s, q_len);
+    if (sl[s] < q_len) return fail(PA_ERR_SHAPE, "seq_lens[%d] = %d < q_len %d", s, sl[s], q_len);
+    if (ceil_div(sl[s], pa::kBlockSize) > bt_stride)
+      return fail(PA_ERR_SHAPE, "sequence %d needs more than bt_stride = %d table columns", s, bt_stride);
+    if (q_len == 1) {
+      plan.any_decode = true;
+      plan.max_decode_len = std::max(plan.max_decode_len, (int)sl[s]);
+      continue;
+    }
+    const int tiles = ceil_div(q_len, pa::kPrefillRows);
+    if (s >= (1 << 20) || tiles > 4096) return fail(PA_ERR_UNSUPPORTED, "batch too large for the prefill planner");
+    const int c = sl[s] - q_len;
+    for (int t = 0; t < tiles; ++t) {
+      const int r_end = std::min(q_len, (t + 1) * pa::kPrefillRows);
+      items.push_back({(int64_t)(c + r_end), ((uint32_t)s << 12) | (uint32_t)t});
+    }
+  }
+  if (qsl[num_seqs] != num_tokens)
+    return fail(PA_ERR_SHAPE, "query_start_loc_host[num_seqs] = %d != num_tokens %d", qsl[num_seqs], num_tokens);
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+  plan.items.reserve(items.size());
+  for (const Item& it : items) plan.items.push_back(it.code);
+  return PA_OK;
+}
+
+}  // namespace
+
+size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                         int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || head_dim < 1) return 0;
+  int max_dec = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = query_start_loc_host[s + 1] - query_start_loc_host[s];
+    if (q_len == 1) max_dec = std::max(max_dec, (int)seq_lens_host[s]);
+  }
+  if (max_dec == 0) return 0;
+  return pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_dec, 0);
+}
+
+pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                              const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                              const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, float scale, pa_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_BF16 (or PA_F32 for decode rows)");
+  if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_SHAPE, "negative num_seqs or num_tokens");
+  if (num_seqs == 0) return num_tokens == 0 ? ok() : fail(PA_ERR_SHAPE, "num_tokens > 0 with no sequences");
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc ||
+      !seq_lens_host || !query_start_loc_host)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, bt_stride);
+  if (st != PA_OK) return st;
+  if (num_q_heads / num_kv_heads > pa::kMaxGroup && dtype == PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "up to %d q heads per kv head", pa::kMaxGroup);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+  VarlenPlan plan;
+  st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride, plan);
+  if (st != PA_OK) return st;
+  if (dtype == PA_F32 && !plan.items.empty())
+    return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
+  const size_t need = pa_prefill_varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads,
+                                                        head_dim);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (validate_enabled()) {
+    std::vector<int32_t> q, sl;
+    if (!copy_to_host(q, query_start_loc, num_seqs + 1) || !copy_to_host(sl, seq_lens, num_seqs))
+      return fail(PA_ERR_HIP, "PA_VALIDATE: metadata copy failed");
+    for (int s = 0; s <= num_seqs; ++s)
+      if (q[s] != query_start_loc_host[s]) return fail(PA_ERR_SHAPE, "PA_VALIDATE: host/device query_start_loc differ");
+    for (int s = 0; s < num_seqs; ++s)
+      if (sl[s] != seq_lens_host[s]) return fail(PA_ERR_SHAPE, "PA_VALIDATE: host/device seq_lens differ");
+    int max_len = 1;
+    for (int s = 0; s < num_seqs; ++s) max_len = std::max(max_len, (int)seq_lens_host[s]);
+    st = validate_tables(block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, num_blocks, max_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (plan.any_decode) {
+    st = run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
+                    num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, plan.max_decode_len, scale,
+                    dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype == PA_F32, 1.f, 1.f, 0, workspace, workspace_bytes,
+                    hs);
+    if (st != PA_OK) return st;
+  }
+  for (size_t i0 = 0; i0 < plan.items.size(); i0 += pa::kMaxPrefillItems) {
+    pa::PrefillParams p{};
+    p.out = out;
+    p.query = query;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.qsl = query_start_loc;
+    p.bt_stride = bt_stride;
+    p.num_tokens = num_tokens;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    const size_t n = std::min(plan.items.size() - i0, (size_t)pa::kMaxPrefillItems);
+    p.n_items = (int)n;
+    std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint32_t));
+    st = hip_status(pa::launch_prefill(p, head_dim, hs), "prefill launch");
+    if (st != PA_OK) return st;
+  }
+  return ok();
+}
+
+}  // extern "C"

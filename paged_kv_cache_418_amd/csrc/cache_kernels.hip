@@ -1,0 +1,144 @@
+// Slot mapping and the KV write for gfx950.
+//
+// Slot mapping (page "vLLM：从 KV Cache 到高吞吐推理服务", tutorial 3; page
+// "vLLM 架构概述" §2): new row i of sequence s sits at position
+// p = seq_len - q_len + i; its slot is block_tables[s][p / B] * B + p % B.
+// KV write (page "vLLM 架构概述" §3, the reshape_and_cache kernel): copy the
+// new token's K and V rows of every kv head to cache[slot / B][slot % B].
+// fp8 pools (tutorial 6: FP8 E4M3 KV with a scale) store the E4M3 code of
+// x / scale.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+__global__ void __launch_bounds__(256) slot_mapping_kernel(int32_t* slots, const int32_t* block_tables,
+                                                           int bt_stride, const int32_t* seq_lens,
+                                                           const int32_t* qsl, int num_tokens, int block_size) {
+  const int s = blockIdx.x;
+  const int q0 = qsl[s], q_len = qsl[s + 1] - q0;
+  const int cached = seq_lens[s] - q_len;
+  const int* bt = block_tables + (size_t)s * bt_stride;
+  for (int i = threadIdx.x; i < q_len; i += blockDim.x) {
+    if (q0 + i < 0 || q0 + i >= num_tokens) continue;
+    const int pos = cached + i;
+    const int logical = pos / block_size;
+    int slot = -1;
+    if (pos >= 0 && logical < bt_stride) slot = bt[logical] * block_size + (pos - logical * block_size);
+    slots[q0 + i] = slot;
+  }
+}
+
+// One work-group per token; threads copy VEC-byte chunks of all kv heads.
+template <typename VecT>
+__global__ void __launch_bounds__(256) reshape_kernel(const uint8_t* key, const uint8_t* value, int64_t key_stride_b,
+                                                      int64_t value_stride_b, uint8_t* key_cache, uint8_t* value_cache,
+                                                      const int32_t* slots, int row_bytes, int num_slots) {
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int n = row_bytes / (int)sizeof(VecT);
+  const VecT* ks = reinterpret_cast<const VecT*>(key + (int64_t)t * key_stride_b);
+  const VecT* vs = reinterpret_cast<const VecT*>(value + (int64_t)t * value_stride_b);
+  VecT* kd = reinterpret_cast<VecT*>(key_cache + (int64_t)slot * row_bytes);
+  VecT* vd = reinterpret_cast<VecT*>(value_cache + (int64_t)slot * row_bytes);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+// fp8: each thread quantises 8 consecutive elements (one 8-byte store).
+template <bool SRC_F32>
+__global__ void __launch_bounds__(256) reshape_fp8_kernel(const void* key, const void* value, int64_t key_stride,
+                                                          int64_t value_stride, uint8_t* key_cache,
+                                                          uint8_t* value_cache, const int32_t* slots, int row_elems,
+                                                          int num_slots, float k_scale, float v_scale) {
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  for (int c = threadIdx.x; c < row_elems / 8; c += blockDim.x) {
+    float xk[8], xv[8];
+    if constexpr (SRC_F32) {
+      const float* ks = reinterpret_cast<const float*>(key) + (int64_t)t * key_stride + c * 8;
+      const float* vs = reinterpret_cast<const float*>(value) + (int64_t)t * value_stride + c * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xk[j] = ks[j];
+        xv[j] = vs[j];
+      }
+    } else {
+      const uint16_t* ks = reinterpret_cast<const uint16_t*>(key) + (int64_t)t * key_stride + c * 8;
+      const uint16_t* vs = reinterpret_cast<const uint16_t*>(value) + (int64_t)t * value_stride + c * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xk[j] = bf16_to_f32(ks[j]);
+        xv[j] = bf16_to_f32(vs[j]);
+      }
+    }
+    uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kw[j >> 2] |= (uint32_t)f32_to_e4m3(__fdiv_rn(xk[j], k_scale)) << (8 * (j & 3));
+      vw[j >> 2] |= (uint32_t)f32_to_e4m3(__fdiv_rn(xv[j], v_scale)) << (8 * (j & 3));
+    }
+    *reinterpret_cast<u32x2*>(key_cache + (int64_t)slot * row_elems + c * 8) = u32x2{kw[0], kw[1]};
+    *reinterpret_cast<u32x2*>(value_cache + (int64_t)slot * row_elems + c * 8) = u32x2{vw[0], vw[1]};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int bt_stride,
+                               const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
+                               int block_size, hipStream_t stream) {
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(64), 0, stream, slot_mapping, block_tables, bt_stride,
+                     seq_lens, qsl, num_tokens, block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t key_stride, int64_t value_stride,
+                                    void* key_cache, void* value_cache, const int32_t* slots, int num_tokens,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks, int elem_bytes,
+                                    hipStream_t stream) {
+  const int row_bytes = num_kv_heads * head_dim * elem_bytes;  // one token of one pool
+  const int64_t ksb = key_stride * elem_bytes, vsb = value_stride * elem_bytes;
+  const int num_slots = num_blocks * block_size;
+  const uintptr_t align = (uintptr_t)key | (uintptr_t)value | (uintptr_t)key_cache | (uintptr_t)value_cache |
+                          (uintptr_t)ksb | (uintptr_t)vsb | (uintptr_t)row_bytes;
+  const int threads = 128;
+  const auto* k8 = reinterpret_cast<const uint8_t*>(key);
+  const auto* v8 = reinterpret_cast<const uint8_t*>(value);
+  auto* kc8 = reinterpret_cast<uint8_t*>(key_cache);
+  auto* vc8 = reinterpret_cast<uint8_t*>(value_cache);
+  if ((align & 15u) == 0)
+    hipLaunchKernelGGL(reshape_kernel<u32x4>, dim3(num_tokens), dim3(threads), 0, stream, k8, v8, ksb, vsb, kc8, vc8,
+                       slots, row_bytes, num_slots);
+  else if ((align & 3u) == 0)
+    hipLaunchKernelGGL(reshape_kernel<uint32_t>, dim3(num_tokens), dim3(threads), 0, stream, k8, v8, ksb, vsb, kc8,
+                       vc8, slots, row_bytes, num_slots);
+  else
+    hipLaunchKernelGGL(reshape_kernel<uint16_t>, dim3(num_tokens), dim3(threads), 0, stream, k8, v8, ksb, vsb, kc8,
+                       vc8, slots, row_bytes, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int64_t key_stride,
+                                        int64_t value_stride, uint8_t* key_cache, uint8_t* value_cache,
+                                        const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
+                                        int block_size, int num_blocks, int src_f32, float k_scale,
+                                        float v_scale, hipStream_t stream) {
+  const int row_elems = num_kv_heads * head_dim;
+  const int num_slots = num_blocks * block_size;
+  if (src_f32)
+    hipLaunchKernelGGL(reshape_fp8_kernel<true>, dim3(num_tokens), dim3(128), 0, stream, key, value, key_stride,
+                       value_stride, key_cache, value_cache, slots, row_elems, num_slots, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(reshape_fp8_kernel<false>, dim3(num_tokens), dim3(128), 0, stream, key, value, key_stride,
+                       value_stride, key_cache, value_cache, slots, row_elems, num_slots, k_scale, v_scale);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,85 @@
+// Internal launch parameters shared by the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockSize = 16;      // tokens per physical block
+constexpr int kDecodeWaves = 4;     // waves per decode work-group
+constexpr int kMaxGroup = 16;       // q heads per kv head handled by one MFMA column set
+constexpr int kPrefillRows = 128;   // query rows per prefill work-group (4 waves x 32)
+constexpr int kPrefillKeys = 64;    // keys per LDS tile in prefill
+constexpr int kMaxPrefillItems = 640;
+
+enum Dtype { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+// One decode launch: grid (n_parts_max, num_kv_heads, num_seqs).
+struct DecodeParams {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;        // optional: rows of a flattened batch; sequences with q_len != 1 are skipped
+  float* part_o;             // [num_seqs][Hq][n_parts_max][D] partial outputs (unnormalised)
+  float* part_m;             // [num_seqs][Hq][n_parts_max] running max (log2 units)
+  float* part_l;             // [num_seqs][Hq][n_parts_max] sum of weights
+  int bt_stride;
+  int num_seqs;
+  int num_rows;              // rows of query/out (num_seqs, or the flattened token count)
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                 // num_q_heads / num_kv_heads
+  int num_blocks;
+  int max_seq_len;
+  int part_size;             // tokens per partition (multiple of 64)
+  int n_parts_max;
+  float scale_log2;          // softmax scale * log2(e) (* k_scale for fp8 pools)
+  float v_scale;             // 1, or the fp8 value scale
+  int q_f32;                 // query / output are fp32 (else bf16)
+};
+
+struct PrefillParams {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int bt_stride;
+  int num_tokens;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int num_blocks;
+  float scale_log2;
+  int n_items;
+  // work items: (sequence << 12) | query tile; ordered longest first
+  uint32_t items[kMaxPrefillItems];
+};
+
+hipError_t launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int bt_stride,
+                               const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
+                               int block_size, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t key_stride, int64_t value_stride,
+                                    void* key_cache, void* value_cache, const int32_t* slots, int num_tokens,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks, int elem_bytes,
+                                    hipStream_t stream);
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int64_t key_stride,
+                                        int64_t value_stride, uint8_t* key_cache, uint8_t* value_cache,
+                                        const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
+                                        int block_size, int num_blocks, int src_f32, float k_scale,
+                                        float v_scale, hipStream_t stream);
+
+// kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel)
+hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace pa

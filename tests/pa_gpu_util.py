@@ -1,0 +1,62 @@
+"""Helpers shared by the GPU parity tests: move a workload to the device and run
+the HIP path through the C-ABI binding."""
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_418_amd as pk
+
+TOL = {"f32": 2e-3, "bf16": 1.5e-2, "fp8": 6e-2}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class DevWorkload:
+    """Device copies of a workload's arrays (pools as written before the step)."""
+
+    def __init__(self, w, dev="cuda"):
+        self.w = w
+        self.k_cache = w.k_cache.to(dev)
+        self.v_cache = w.v_cache.to(dev)
+        self.block_tables = torch.from_numpy(w.block_tables).to(dev)
+        self.seq_lens = torch.from_numpy(w.seq_lens).to(dev)
+        self.qsl = torch.from_numpy(w.query_start_loc).to(dev)
+        self.query = w.query.to(dev)
+        self.new_k = w.new_k.to(dev)
+        self.new_v = w.new_v.to(dev)
+
+    def write_new_tokens(self):
+        w = self.w
+        slots = pk.pa_slot_mapping(self.block_tables, self.seq_lens, self.qsl, w.num_tokens, w.block_size)
+        if w.kv_dtype == "fp8":
+            pk.pa_reshape_and_cache_fp8(self.new_k, self.new_v, self.k_cache, self.v_cache, slots, w.k_scale,
+                                        w.v_scale)
+        else:
+            pk.pa_reshape_and_cache(self.new_k, self.new_v, self.k_cache, self.v_cache, slots)
+        return slots
+
+    def max_seq_len(self):
+        return int(self.w.seq_lens.max())
+
+    def decode(self, partition_size=0, out=None):
+        w = self.w
+        if w.kv_dtype == "fp8":
+            return pk.pa_decode_fp8(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
+                                    w.k_scale, w.v_scale, self.max_seq_len(), partition_size, out=out)
+        return pk.pa_decode(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
+                            self.max_seq_len(), partition_size, out=out)
+
+    def prefill(self, out=None):
+        w = self.w
+        return pk.pa_prefill_varlen(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                    self.qsl, w.seq_lens, w.query_start_loc, w.scale, out=out)
+
+
+def max_err(got: torch.Tensor, ref: np.ndarray) -> float:
+    g = got.detach().float().cpu().double().numpy()
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
