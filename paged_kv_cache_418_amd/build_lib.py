@@ -24,6 +24,8 @@ CFLAGS = [
     "-Wno-unused-function", "-Wno-unused-variable",
     # packed fp32 instructions stay off on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs (the softmax rescales them every tile)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

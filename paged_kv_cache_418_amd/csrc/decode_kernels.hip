@@ -11,17 +11,14 @@
 // the log-sum-exp rule (tutorial 7: the LSE statistic).
 //
 // Work decomposition (designed for CDNA4, not taken from the pages): one
-// work-group of 4 waves per (partition, kv head, sequence).  The q heads that
-// share the kv head (GQA, tutorial 1) are the 16 columns of the matrix-core
-// tiles, so the K/V of a block are read once for all of them:
-//   S^T[token][g] = K[token][:] . Q[g][:]   v_mfma_f32_16x16x32_bf16, K from HBM
-//   O^T[d][g]    += V^T[d][token] P^T[token][g]   v_mfma_f32_16x16x16_bf16
-// The score layout of the first product is exactly the operand layout the
-// second one needs for P, so probabilities never leave registers; V is
-// transposed through a per-wave LDS tile.  Each wave streams its share of
-// the partition's 16-token blocks with the next block's loads in flight.
-// Masked positions (the partly filled last block) are removed by selection,
-// never by multiplying with zero, so NaN in unused pool slots cannot leak.
+// wave per (partition, kv head, sequence).  The q heads that share the kv
+// head (GQA, tutorial 1) are the 16 columns of the matrix-core tiles, so the
+// K/V of a block are read once for all of them.  Each 16-lane quarter of the
+// wave loads one whole token row of the block (coalesced 16-byte loads for
+// bf16 at head size 128); K goes through a small swizzled LDS tile to reach
+// the matrix-core operand layout, V is used from registers.  Masked positions
+// (the partly filled last block) are removed by selection, never by
+// multiplying with zero, so NaN in unused pool slots cannot leak.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -29,50 +26,78 @@ namespace pa {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <int D>
+// Per-lane geometry of one 16-token block for head size D.  A wave reads a
+// block's rows for one kv head with each 16-lane quarter covering one whole
+// token row (coalesced): lane (a = lane / 16, c = lane % 16) holds the VEC
+// consecutive elements c*VEC .. c*VEC+VEC-1 of token rows a, a+4, a+8, a+12.
+template <int D, bool FP8>
 struct DecodeShape {
-  static constexpr int kKSteps = D / 32;   // 16x16x32 MFMAs per score tile
-  static constexpr int kOTiles = D / 16;   // 16-wide d tiles of the output
-  static constexpr int kLaneD = D / 4;     // elements of one token row held by one lane
-  static constexpr int kVRow = D * 2 + 16;  // bytes per token row of the LDS V tile (padded, 16-aligned)
-  static constexpr int kStage = kDecodeWaves * 16 * kVRow;
+  static constexpr int kVec = D / 16;                 // elements of one row per lane
+  static constexpr int kWords = kVec / 2;             // bf16 dwords of one row slice
+  static constexpr int kLoadBytes = kVec * (FP8 ? 1 : 2);
+  static constexpr int kKSteps = D / 32;              // 16x16x32 MFMAs per score tile
+  static constexpr int kRowBytes = D * 2;             // bf16 bytes of one token row in LDS
+  static constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per LDS row
+  static constexpr int kLdsBytes = 16 * kRowBytes;    // one K block per wave
 };
 
-// Raw bytes of one lane's slice of a K or V token row: kLaneD elements.
-template <int D, bool FP8>
-struct RowSlice {
-  static constexpr int kBytes = FP8 ? D / 4 : D / 2;
-  static constexpr int kVecs = kBytes / 16;
-  u32x4 v[kVecs];
+template <int N>
+struct RawVec;
+template <>
+struct RawVec<16> {
+  u32x4 v;
+};
+template <>
+struct RawVec<8> {
+  u32x2 v;
+};
+template <>
+struct RawVec<4> {
+  uint32_t v;
 };
 
+// The raw bytes of one lane's slices of the four rows it owns, for K and V.
 template <int D, bool FP8>
-__device__ __forceinline__ void load_slice(RowSlice<D, FP8>& r, const uint8_t* p) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int i = 0; i < RowSlice<D, FP8>::kVecs; ++i) r.v[i] = q[i];
+struct BlockRegs {
+  using Sh = DecodeShape<D, FP8>;
+  RawVec<Sh::kLoadBytes> k[4], v[4];
+};
+
+template <int N>
+__device__ __forceinline__ void load_raw(RawVec<N>& r, const uint8_t* p) {
+  if constexpr (N == 16) r.v = *reinterpret_cast<const u32x4*>(p);
+  else if constexpr (N == 8) r.v = *reinterpret_cast<const u32x2*>(p);
+  else r.v = *reinterpret_cast<const uint32_t*>(p);
 }
 
-// Slice -> bf16 words: kLaneD/2 dwords, element order preserved.
+// Raw slice -> bf16 dwords (element order kept).  E4M3 codes are exact in bf16.
 template <int D, bool FP8>
-__device__ __forceinline__ void slice_to_bf16(const RowSlice<D, FP8>& r, uint32_t (&w)[D / 8]) {
+__device__ __forceinline__ void raw_to_words(const RawVec<DecodeShape<D, FP8>::kLoadBytes>& r,
+                                             uint32_t (&w)[DecodeShape<D, FP8>::kWords]) {
+  constexpr int W = DecodeShape<D, FP8>::kWords;
   if constexpr (FP8) {
+    uint32_t b[W / 2];
+    if constexpr (W == 4) {
+      b[0] = r.v.x;
+      b[1] = r.v.y;
+    } else {
+      b[0] = r.v;
+    }
 #pragma unroll
-    for (int i = 0; i < RowSlice<D, FP8>::kVecs; ++i) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        u32x2 b = e4m3x4_to_bf16x4(r.v[i][k]);
-        w[i * 8 + k * 2] = b.x;
-        w[i * 8 + k * 2 + 1] = b.y;
-      }
+    for (int i = 0; i < W / 2; ++i) {
+      const u32x2 t = e4m3x4_to_bf16x4(b[i]);
+      w[2 * i] = t.x;
+      w[2 * i + 1] = t.y;
     }
   } else {
-#pragma unroll
-    for (int i = 0; i < RowSlice<D, FP8>::kVecs; ++i) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) w[i * 4 + k] = r.v[i][k];
+    if constexpr (W == 4) {
+      w[0] = r.v.x;
+      w[1] = r.v.y;
+      w[2] = r.v.z;
+      w[3] = r.v.w;
+    } else {
+      w[0] = r.v.x;
+      w[1] = r.v.y;
     }
   }
 }
@@ -82,17 +107,45 @@ __device__ __forceinline__ bf16x8 words_to_bf16x8(uint32_t a, uint32_t b, uint32
   return __builtin_bit_cast(bf16x8, t);
 }
 
+// max / sum over the four lanes l, l^16, l^32, l^48 (the four row groups of a wave)
+__device__ __forceinline__ float max_across_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const uint32_t v = __float_as_uint(x);
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
+__device__ __forceinline__ float sum_across_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  const uint32_t v = __float_as_uint(x);
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
+// One wave per (partition, kv head, sequence).  Per 16-token block:
+//   S[tok][g] = K[tok][:] . Q[g][:]     v_mfma_f32_16x16x32_bf16, K through a swizzled LDS tile
+//   O^T[d][g] += V^T[d][tok] P^T[tok][g] v_mfma_f32_16x16x16_bf16, V straight from registers
+// The K tile rows are read in the order sigma(m) = m/4 + 4*(m%4), so score
+// element r of lane (a, g) belongs to token a + 4r: exactly the four tokens
+// whose V slices the same lane loaded.  P therefore never leaves its lane,
+// and the V^T operand of MFMA j (d = VEC*m + j) is two byte permutes of the
+// lane's own V words.  Two blocks are in flight while one is computed.
 template <int D, bool FP8>
-__global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeParams p) {
-  using Sh = DecodeShape<D>;
-  extern __shared__ __align__(16) unsigned char smem[];
+__global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
+  using Sh = DecodeShape<D, FP8>;
+  constexpr int VEC = Sh::kVec, W = Sh::kWords;
+  __shared__ __align__(16) unsigned char k_lds[Sh::kLdsBytes];
 
   const int s = blockIdx.z, kvh = blockIdx.y, part = blockIdx.x;
   int row = s;
   if (p.qsl) {
-    const int a = p.qsl[s], b = p.qsl[s + 1];
-    if (b - a != 1) return;
-    row = a;
+    const int qa = p.qsl[s], qb = p.qsl[s + 1];
+    if (qb - qa != 1) return;
+    row = qa;
   }
   if (row >= p.num_rows) return;
   const int L = min(p.seq_lens[s], p.max_seq_len);
@@ -102,200 +155,206 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeParams p) {
   const int tok1 = min(L, tok0 + p.part_size);
   const int nblk = (tok1 - tok0 + 15) >> 4;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane & 15, grp = lane >> 4;
+  const int lane = threadIdx.x;
+  const int a = lane >> 4, c = lane & 15;  // row group / column within the row group
   const int G = p.group;
 
-  // Q^T operand: lane holds q[head g][grp*D/4 + kk*8 + j]; the same d order is
-  // used for K, so the dot products are unchanged.
+  // Q^T operand of MFMA kk: lane (a, g = c) holds q[g][8*(a + 4*kk) .. +7]
   bf16x8 qf[Sh::kKSteps];
   {
-    uint32_t qw[D / 8];
+    const int g = c;
     if (g < G) {
-      const size_t qoff = ((size_t)row * p.num_q_heads + kvh * G + g) * D + grp * Sh::kLaneD;
-      if (p.q_f32) {
-        const float* qp = reinterpret_cast<const float*>(p.query) + qoff;
+      const size_t qoff = ((size_t)row * p.num_q_heads + kvh * G + g) * D;
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) qw[i] = pack_bf16x2(qp[2 * i], qp[2 * i + 1]);
-      } else {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.query) + qoff);
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-          const u32x4 t = qp[i];
-          qw[4 * i] = t.x;
-          qw[4 * i + 1] = t.y;
-          qw[4 * i + 2] = t.z;
-          qw[4 * i + 3] = t.w;
+      for (int kk = 0; kk < Sh::kKSteps; ++kk) {
+        const int d0 = 8 * (a + 4 * kk);
+        u32x4 t;
+        if (p.q_f32) {
+          const float* qp = reinterpret_cast<const float*>(p.query) + qoff + d0;
+          t = u32x4{pack_bf16x2(qp[0], qp[1]), pack_bf16x2(qp[2], qp[3]), pack_bf16x2(qp[4], qp[5]),
+                    pack_bf16x2(qp[6], qp[7])};
+        } else {
+          t = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.query) + qoff + d0);
         }
+        qf[kk] = __builtin_bit_cast(bf16x8, t);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) qw[i] = 0u;
+      for (int kk = 0; kk < Sh::kKSteps; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-#pragma unroll
-    for (int kk = 0; kk < Sh::kKSteps; ++kk)
-      qf[kk] = words_to_bf16x8(qw[4 * kk], qw[4 * kk + 1], qw[4 * kk + 2], qw[4 * kk + 3]);
   }
 
   float m = -INFINITY, l = 0.f;
-  f32x4 acc[Sh::kOTiles];
+  f32x4 acc[VEC];
 #pragma unroll
-  for (int n = 0; n < Sh::kOTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < VEC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + (tok0 >> 4);
-  unsigned char* vstage = smem + wave * 16 * Sh::kVRow;
-  const int tl = lane & 15;  // token row this lane loads
   constexpr int kElem = FP8 ? 1 : 2;
+  const size_t row_stride = (size_t)p.num_kv_heads * D * kElem;  // bytes between token rows of a block
+  const size_t block_bytes = row_stride * 16;
+  // byte offsets of this lane's four rows inside a block (a block of one pool is < 4 GB)
+  uint32_t roff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    roff[i] = (uint32_t)((a + 4 * i) * row_stride) + (uint32_t)(kvh * D * kElem) + (uint32_t)(c * Sh::kLoadBytes);
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
-  const size_t lane_off = (size_t)(grp * Sh::kLaneD) * kElem;
-  const size_t row_stride = (size_t)p.num_kv_heads * D * kElem;  // bytes between tokens of a block
-  const size_t head_off = (size_t)kvh * D * kElem;
+  // Physical block ids of the partition, 64 at a time in one VGPR (lane i holds block
+  // win0 + i); a wave-uniform block id is then one v_readlane away.
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + (tok0 >> 4);
+  int win0 = 0;
+  int bt_win = lane < nblk ? bt[lane] : 0;
 
-  auto slice_addr = [&](const uint8_t* base, int b) {
-    int phys = bt[b];
+  // Loads of block b of the partition.  Indices past the end re-read the last
+  // block (cache-resident, no HBM traffic) so that the loop is branch-free and
+  // the order of outstanding loads never depends on the data.
+  auto issue = [&](BlockRegs<D, FP8>& r, int b) {
+    b = min(b, nblk - 1);
+    if (b >= win0 + 64) {
+      win0 += 64;
+      bt_win = win0 + lane < nblk ? bt[win0 + lane] : 0;
+    }
+    int phys = __builtin_amdgcn_readlane(bt_win, b - win0);
     phys = min(max(phys, 0), p.num_blocks - 1);
-    return base + ((size_t)phys * 16 + tl) * row_stride + head_off + lane_off;
+    const uint8_t* kb = kbase + (size_t)phys * block_bytes;  // wave-uniform
+    const uint8_t* vb = vbase + (size_t)phys * block_bytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_raw(r.k[i], kb + roff[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_raw(r.v[i], vb + roff[i]);
   };
 
-  RowSlice<D, FP8> kcur, vcur, knext, vnext;
-  int b = wave;
-  if (b < nblk) {
-    load_slice(kcur, slice_addr(kbase, b));
-    load_slice(vcur, slice_addr(vbase, b));
-  }
-  for (; b < nblk; b += kDecodeWaves) {
-    const int bn = b + kDecodeWaves;
-    if (bn < nblk) {
-      load_slice(knext, slice_addr(kbase, bn));
-      load_slice(vnext, slice_addr(vbase, bn));
-    }
+  // LDS addresses: K row t, logical 16-byte chunk x lives at chunk x ^ (t % kChunks)
+  unsigned char* const kl = k_lds;
+  const int m_row = (c >> 2) + 4 * (c & 3);  // sigma(c): the token row this lane feeds into the MFMA
+
+  auto compute = [&](BlockRegs<D, FP8>& r, int b, BlockRegs<D, FP8>& refill, int b_refill) {
     const int blk_tok = tok0 + b * 16;
-
-    // V slice -> LDS (zero rows past the sequence end)
-    {
-      uint32_t vw[D / 8];
-      slice_to_bf16(vcur, vw);
-      const bool live = blk_tok + tl < L;
-      u32x4* dst = reinterpret_cast<u32x4*>(vstage + tl * Sh::kVRow + grp * Sh::kLaneD * 2);
+    const bool partial = blk_tok + 16 > tok1;
+    // K slices -> LDS (bf16, swizzled)
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        u32x4 t = {vw[4 * i], vw[4 * i + 1], vw[4 * i + 2], vw[4 * i + 3]};
-        if (!live) t = u32x4{0u, 0u, 0u, 0u};
-        dst[i] = t;
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w[W];
+      raw_to_words<D, FP8>(r.k[i], w);
+      const int t = a + 4 * i;
+      const int byte = c * VEC * 2;
+      unsigned char* dst = kl + t * Sh::kRowBytes + (((byte >> 4) ^ (t % Sh::kChunks)) << 4) + (byte & 15);
+      if constexpr (W == 4)
+        *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+      else
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    }
+    // V slices -> bf16 words, rows past the sequence end zeroed (never multiplied: NaN-safe)
+    uint32_t vw[4][W];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      raw_to_words<D, FP8>(r.v[i], vw[i]);
+      if (partial && blk_tok + a + 4 * i >= tok1) {
+#pragma unroll
+        for (int x = 0; x < W; ++x) vw[i][x] = 0u;
       }
     }
-
-    // scores S^T[token 4*grp+i][head g]
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    {
-      uint32_t kw[D / 8];
-      slice_to_bf16(kcur, kw);
 #pragma unroll
-      for (int kk = 0; kk < Sh::kKSteps; ++kk) {
-        bf16x8 a = words_to_bf16x8(kw[4 * kk], kw[4 * kk + 1], kw[4 * kk + 2], kw[4 * kk + 3]);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc, 0, 0, 0);
-      }
+    for (int kk = 0; kk < Sh::kKSteps; ++kk) {
+      const int x = a + 4 * kk;
+      const u32x4 kw =
+          *reinterpret_cast<const u32x4*>(kl + m_row * Sh::kRowBytes + ((x ^ (m_row % Sh::kChunks)) << 4));
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[kk], sacc, 0, 0, 0);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+    // online softmax over the block: element r of this lane is token a + 4r of head g = c
     float z[4];
     float bmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool live = blk_tok + grp * 4 + i < L;
+      const bool live = blk_tok + a + 4 * i < tok1;
       z[i] = live ? sacc[i] * p.scale_log2 : -INFINITY;
       bmax = fmaxf(bmax, z[i]);
     }
-    bmax = fmaxf(bmax, shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+    bmax = max_across_rows(bmax);
     const float mnew = fmaxf(m, bmax);
     const float alpha = fast_exp2(m - mnew);
     float pr[4];
-    float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[i] = fast_exp2(z[i] - mnew);
-      psum += pr[i];
-    }
-    l = l * alpha + psum;
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(z[i] - mnew);
+    l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = mnew;
-#pragma unroll
-    for (int n = 0; n < Sh::kOTiles; ++n) acc[n] *= alpha;
-
     i16x4 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pb[i] = (short)f32_to_bf16(pr[i]);
-
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    const uint16_t* vs = reinterpret_cast<const uint16_t*>(vstage);
-#pragma unroll
-    for (int n = 0; n < Sh::kOTiles; ++n) {
-      i16x4 va;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) va[j] = (short)vs[(grp * 4 + j) * (Sh::kVRow / 2) + n * 16 + g];
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[n], 0, 0, 0);
+    {
+      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+      pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-
-    kcur = knext;
-    vcur = vnext;
-  }
-
-  // the four lanes of a head hold partial sums over different tokens
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-
-  // combine the waves of the work-group
-  __syncthreads();
-  float* sm_m = reinterpret_cast<float*>(smem);
-  float* sm_l = sm_m + kDecodeWaves * 16;
-  float* sm_o = sm_l + kDecodeWaves * 16;  // [wave][g < G][D]
-  if (grp == 0) {
-    sm_m[wave * 16 + g] = m;
-    sm_l[wave * 16 + g] = l;
-  }
-  __syncthreads();
-  float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_m[w * 16 + g]);
-  const float f = fast_exp2(m - M);
-  if (g < G) {
-#pragma unroll
-    for (int n = 0; n < Sh::kOTiles; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[(wave * G + g) * D + n * 16 + grp * 4 + r] = acc[n][r] * f;
-  }
-  __syncthreads();
-
-  const bool single = n_parts == 1;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int gg = idx / D, d = idx - gg * D;
-    float Mg = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) Mg = fmaxf(Mg, sm_m[w * 16 + gg]);
-    float Lg = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      Lg += sm_l[w * 16 + gg] * fast_exp2(sm_m[w * 16 + gg] - Mg);
-      o += sm_o[(w * G + gg) * D + d];
+    for (int j = 0; j < VEC; ++j) {
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(vw[1][j >> 1], vw[0][j >> 1], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(vw[3][j >> 1], vw[2][j >> 1], sel);
+      const i16x4 va = __builtin_bit_cast(i16x4, u32x2{lo, hi});
+      acc[j] *= alpha;
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[j], 0, 0, 0);
     }
-    const int h = kvh * G + gg;
-    if (single) {
-      const float val = o * p.v_scale / Lg;
-      const size_t oi = ((size_t)row * p.num_q_heads + h) * D + d;
-      if (p.q_f32)
-        reinterpret_cast<float*>(p.out)[oi] = val;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(val);
+    // this block's registers are consumed: refill them with a later block
+    issue(refill, b_refill);
+  };
+
+  // Blocks alternate between two register sets; a missing odd block is a
+  // fully masked copy of the last one (no effect on m, l or the output).
+  BlockRegs<D, FP8> ra, rb;
+  issue(ra, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(rb, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int b = 0; b < nblk; b += 2) {
+    compute(ra, b, ra, b + 2);
+    compute(rb, b + 1, rb, b + 3);
+  }
+
+  // the four row groups hold partial sums over different tokens of the same head
+  l = sum_across_rows(l);
+
+  const int g = c;
+  if (g >= G) return;
+  const int h = kvh * G + g;
+  // lane (a, g) holds O[g][VEC*(4a + r) + j] in acc[j][r]: 4*VEC consecutive d
+  const int d0 = 4 * VEC * a;
+  if (n_parts == 1) {
+    const float inv = p.v_scale / l;
+    const size_t oi = ((size_t)row * p.num_q_heads + h) * D + d0;
+    if (p.q_f32) {
+      float* op = reinterpret_cast<float*>(p.out) + oi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < VEC; j += 4)
+          *reinterpret_cast<f32x4*>(op + VEC * r + j) =
+              f32x4{acc[j][r] * inv, acc[j + 1][r] * inv, acc[j + 2][r] * inv, acc[j + 3][r] * inv};
     } else {
-      const size_t pi = ((size_t)s * p.num_q_heads + h) * p.n_parts_max + part;
-      p.part_o[pi * D + d] = o;
-      if (d == 0) {
-        p.part_m[pi] = Mg;
-        p.part_l[pi] = Lg;
-      }
+      uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + oi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < VEC; j += 4)
+          *reinterpret_cast<u32x2*>(op + VEC * r + j) =
+              u32x2{pack_bf16x2(acc[j][r] * inv, acc[j + 1][r] * inv), pack_bf16x2(acc[j + 2][r] * inv, acc[j + 3][r] * inv)};
+    }
+  } else {
+    const size_t pi = ((size_t)s * p.num_q_heads + h) * p.n_parts_max + part;
+    float* po = p.part_o + pi * D + d0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < VEC; j += 4)
+        *reinterpret_cast<f32x4*>(po + VEC * r + j) = f32x4{acc[j][r], acc[j + 1][r], acc[j + 2][r], acc[j + 3][r]};
+    if (a == 0) {
+      p.part_m[pi] = m;
+      p.part_l[pi] = l;
     }
   }
 }
@@ -450,17 +509,15 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
 
 template <int D>
 hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
-  const dim3 grid(p.n_parts_max, kv == kF32 ? p.num_q_heads : p.num_kv_heads, p.num_seqs);
   if (kv == kF32) {
+    const dim3 grid(p.n_parts_max, p.num_q_heads, p.num_seqs);
     hipLaunchKernelGGL(decode_f32_kernel<D>, grid, dim3(64), 0, stream, p);
   } else {
-    using Sh = DecodeShape<D>;
-    const size_t merge_bytes = (size_t)(2 * kDecodeWaves * 16 + kDecodeWaves * p.group * D) * sizeof(float);
-    const size_t lds = merge_bytes > (size_t)Sh::kStage ? merge_bytes : (size_t)Sh::kStage;
+    const dim3 grid(p.n_parts_max, p.num_kv_heads, p.num_seqs);
     if (kv == kFP8)
-      hipLaunchKernelGGL((decode_mfma_kernel<D, true>), grid, dim3(256), lds, stream, p);
+      hipLaunchKernelGGL((decode_mfma_kernel<D, true>), grid, dim3(64), 0, stream, p);
     else
-      hipLaunchKernelGGL((decode_mfma_kernel<D, false>), grid, dim3(256), lds, stream, p);
+      hipLaunchKernelGGL((decode_mfma_kernel<D, false>), grid, dim3(64), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_parts_max <= 1) return e;
