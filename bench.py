@@ -56,9 +56,10 @@ class Step:
         self.out = torch.empty_like(self.q)
         self.max_len = int(w.seq_lens.max())
         if w.is_decode:
-            nb = pk.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, self.max_len, 0)
+            nb = pk.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, self.max_len, 0)
         else:
-            nb = pk.pa_prefill_varlen_workspace_bytes(w.query_start_loc, w.seq_lens, w.num_q_heads, w.head_dim)
+            nb = pk.pa_prefill_varlen_workspace_bytes(w.query_start_loc, w.seq_lens, w.num_q_heads, w.num_kv_heads,
+                                                      w.head_dim)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         self.i = 0
         for kc, vc in self.pools:  # the new tokens' slots hold their K/V before any timed call

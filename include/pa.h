@@ -131,13 +131,18 @@ pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t
 
 /*
  * pa_decode_workspace_bytes -- scratch pa_decode / pa_decode_fp8 need.
- * The context of each sequence is split into partitions of partition_size
- * tokens (0 = 512); partial results per partition are merged with the
- * log-sum-exp rule ([B] tutorial 7).  Returns 0 when max_seq_len fits one
- * partition (no scratch needed), and 0 for invalid arguments.
+ * The blocks of all sequences, laid end to end, are cut into num_splits
+ * equal shares per kv head (0 = automatic: about two waves per SIMD of the
+ * current device, PA_DECODE_WAVES_PER_SIMD overrides the two); a sequence
+ * split across shares gets partial results that are merged with the
+ * log-sum-exp rule ([B] tutorial 7).  The count is capped at
+ * num_seqs * ceil(max_seq_len / 16).  Returns 0 when a single share is used
+ * (no scratch needed), and 0 for invalid arguments.  The size depends on
+ * num_seqs, num_q_heads, head_dim and the share count, not on the contents
+ * of seq_lens.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_seq_len, int32_t partition_size);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t num_splits);
 
 /*
  * pa_decode -- paged attention for one new token per sequence.  [A] §2-§3,
@@ -146,16 +151,19 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * j = 0 .. seq_lens[s]-1, K_j/V_j read through block_tables.
  * query/out: [num_seqs][num_q_heads][head_dim], dtype; pools: dtype.
  * dtype: PA_F32 or PA_BF16.  max_seq_len: host bound on every seq_lens[s]
- * (sizes the grid; ceil(max_seq_len/block_size) <= bt_stride).
- * partition_size: multiple of 64, 0 = 512.  workspace: at least
- * pa_decode_workspace_bytes(...) bytes of device memory (may be NULL when
- * that is 0), 256-byte aligned.
+ * (longer sequences are cut to it; ceil(max_seq_len/block_size) <=
+ * bt_stride).  num_splits: see pa_decode_workspace_bytes (0 = automatic).
+ * workspace: at least pa_decode_workspace_bytes(...) bytes of device memory
+ * (may be NULL when that is 0), 256-byte aligned; its contents need no
+ * initialisation.  The result of a sequence does not depend on where its
+ * blocks sit in the pool; it may differ in the last bits between split
+ * counts (a different summation order).
  */
 pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                       const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
-                      pa_dtype_t dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      pa_dtype_t dtype, int32_t num_splits, void* workspace, size_t workspace_bytes,
                       void* stream);
 
 /*
@@ -168,7 +176,7 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
                           const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
-                          pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t partition_size,
+                          pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -177,7 +185,8 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
  * metadata (num_seqs+1 and num_seqs entries).  Returns 0 on invalid input.
  */
 size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
-                                         int32_t num_seqs, int32_t num_q_heads, int32_t head_dim);
+                                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim);
 
 /*
  * pa_prefill_varlen -- causal paged attention over a flattened batch of any

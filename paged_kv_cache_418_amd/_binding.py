@@ -60,12 +60,12 @@ def load() -> ctypes.CDLL:
                                      ctypes.c_int),
             "pa_reshape_and_cache_fp8": ([P, P, i64, i64, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, f32, f32,
                                           P], ctypes.c_int),
-            "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+            "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
             "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32, P, sz,
                            P], ctypes.c_int),
             "pa_decode_fp8": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, f32, f32,
                                i32, P, sz, P], ctypes.c_int),
-            "pa_prefill_varlen_workspace_bytes": ([P, P, i32, i32, i32], sz),
+            "pa_prefill_varlen_workspace_bytes": ([P, P, i32, i32, i32, i32], sz),
             "pa_prefill_varlen": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                    ctypes.c_int, P, sz, P], ctypes.c_int),
         }
@@ -156,48 +156,50 @@ def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k
         float(k_scale), float(v_scale), _stream()))
 
 
-def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
-                              partition_size: int = 0) -> int:
-    return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size))
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_seq_len: int,
+                              num_splits: int = 0) -> int:
+    return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                num_splits))
 
 
 def pa_decode(query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
-              partition_size: int = 0, out=None, workspace=None):
+              num_splits: int = 0, out=None, workspace=None):
     """One new token per sequence: query [S, Hq, D] -> out [S, Hq, D] (fp32 or bf16 pools)."""
     lib = load()
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
-    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, D, max_seq_len, partition_size), query.device, workspace)
+    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, num_splits), query.device, workspace)
     _check("pa_decode", lib.pa_decode(
         _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
         _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
         _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(key_cache),
-        partition_size, None if ws is None else ws.data_ptr(), wsb, _stream()))
+        num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
 
 
 def pa_decode_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: float, k_scale: float,
-                  v_scale: float, max_seq_len: int, partition_size: int = 0, out=None, workspace=None):
+                  v_scale: float, max_seq_len: int, num_splits: int = 0, out=None, workspace=None):
     """pa_decode over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
     lib = load()
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
-    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, D, max_seq_len, partition_size), query.device, workspace)
+    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, num_splits), query.device, workspace)
     _check("pa_decode_fp8", lib.pa_decode_fp8(
         _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
         _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
         _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(query),
-        float(k_scale), float(v_scale), partition_size, None if ws is None else ws.data_ptr(), wsb, _stream()))
+        float(k_scale), float(v_scale), num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
 
 
-def pa_prefill_varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_q_heads: int, head_dim: int) -> int:
+def pa_prefill_varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_q_heads: int, num_kv_heads: int,
+                                      head_dim: int) -> int:
     q = _i32_host(query_start_loc_host)
     s = _i32_host(seq_lens_host)
     return int(load().pa_prefill_varlen_workspace_bytes(q.data_ptr(), s.data_ptr(), s.numel(), num_q_heads,
-                                                        head_dim))
+                                                        num_kv_heads, head_dim))
 
 
 def pa_prefill_varlen(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, seq_lens_host,
@@ -209,7 +211,7 @@ def pa_prefill_varlen(query, key_cache, value_cache, block_tables, seq_lens, que
     qh = _i32_host(query_start_loc_host)
     sh = _i32_host(seq_lens_host)
     out = torch.empty_like(query) if out is None else out
-    need = int(lib.pa_prefill_varlen_workspace_bytes(qh.data_ptr(), sh.data_ptr(), sh.numel(), Hq, D))
+    need = int(lib.pa_prefill_varlen_workspace_bytes(qh.data_ptr(), sh.data_ptr(), sh.numel(), Hq, Hkv, D))
     ws, wsb = _workspace(need, query.device, workspace)
     _check("pa_prefill_varlen", lib.pa_prefill_varlen(
         _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),

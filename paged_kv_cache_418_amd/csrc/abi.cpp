@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -60,16 +61,53 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-struct PartLayout {
-  size_t o_bytes, m_bytes, total;
+// Decode scratch: partial results of sequence pieces (ids share + sequence),
+// then the first/last share of every sequence.
+struct DecodeLayout {
+  size_t o_bytes, m_bytes, idx_bytes, total;
 };
 
-PartLayout part_layout(int64_t rows, int64_t heads, int64_t parts, int64_t head_dim) {
-  PartLayout L;
-  L.o_bytes = align_up((size_t)(rows * heads * parts * head_dim) * sizeof(float));
-  L.m_bytes = align_up((size_t)(rows * heads * parts) * sizeof(float));
-  L.total = L.o_bytes + 2 * L.m_bytes;
+DecodeLayout decode_layout(int64_t num_seqs, int64_t heads, int64_t n_splits, int64_t head_dim) {
+  const int64_t pieces = n_splits + num_seqs;
+  DecodeLayout L;
+  L.o_bytes = align_up((size_t)(pieces * heads * head_dim) * sizeof(float));
+  L.m_bytes = align_up((size_t)(pieces * heads) * sizeof(float));
+  L.idx_bytes = align_up((size_t)num_seqs * sizeof(int32_t));
+  L.total = L.o_bytes + 2 * L.m_bytes + 2 * L.idx_bytes;
   return L;
+}
+
+// Compute units of the current device (cached per device; 256 when no device is visible).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Decode waves per SIMD the automatic split aims at (PA_DECODE_WAVES_PER_SIMD, default 2).
+int decode_waves_per_simd() {
+  static const int w = [] {
+    const char* v = std::getenv("PA_DECODE_WAVES_PER_SIMD");
+    const int x = v ? std::atoi(v) : 0;
+    return x >= 1 && x <= 16 ? x : 2;
+  }();
+  return w;
+}
+
+// Shares the decode work of each kv head is cut into: num_splits if positive,
+// else enough waves to give every SIMD of the device decode_waves_per_simd()
+// of them; never more than the blocks there can be.
+int resolve_splits(int num_splits, int num_seqs, int num_kv_heads, int max_seq_len) {
+  const int64_t max_blocks = (int64_t)num_seqs * ((max_seq_len + 15) / 16);
+  int64_t w = num_splits > 0 ? num_splits
+                             : (int64_t)decode_waves_per_simd() * 4 * device_cu_count() / std::max(1, num_kv_heads);
+  w = std::min<int64_t>(std::max<int64_t>(w, 1), std::max<int64_t>(max_blocks, 1));
+  return (int)std::min<int64_t>(w, 1 << 20);
 }
 
 // Checks of device metadata under PA_VALIDATE=1 (copies to the host, synchronising).
@@ -124,17 +162,14 @@ pa_status_t check_attention_shape(int num_q_heads, int num_kv_heads, int head_di
   return PA_OK;
 }
 
-int resolve_partition(int partition_size) { return partition_size == 0 ? 512 : partition_size; }
-
 // Shared by pa_decode / pa_decode_fp8 / the decode rows of pa_prefill_varlen.
 pa_status_t run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                        const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, const int32_t* qsl,
                        int32_t num_seqs, int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
-                       int q_f32, float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                       int q_f32, float k_scale, float v_scale, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  const int ps = resolve_partition(partition_size);
-  const int n_parts = ceil_div(max_seq_len, ps);
+  const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, max_seq_len);
   pa::DecodeParams p{};
   p.out = out;
   p.query = query;
@@ -151,17 +186,18 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   p.group = num_q_heads / num_kv_heads;
   p.num_blocks = num_blocks;
   p.max_seq_len = max_seq_len;
-  p.part_size = ps;
-  p.n_parts_max = n_parts;
+  p.n_splits = n_splits;
   p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
   p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
   p.q_f32 = q_f32;
-  if (n_parts > 1) {
-    const PartLayout lay = part_layout(num_seqs, num_q_heads, n_parts, head_dim);
+  if (n_splits > 1) {
+    const DecodeLayout lay = decode_layout(num_seqs, num_q_heads, n_splits, head_dim);
     auto* base = static_cast<unsigned char*>(workspace);
     p.part_o = reinterpret_cast<float*>(base);
     p.part_m = reinterpret_cast<float*>(base + lay.o_bytes);
     p.part_l = reinterpret_cast<float*>(base + lay.o_bytes + lay.m_bytes);
+    p.piece_first = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes);
+    p.piece_last = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes + lay.idx_bytes);
   }
   (void)workspace_bytes;
   (void)block_size;
@@ -172,7 +208,7 @@ pa_status_t check_decode_args(const void* out, const void* query, const void* ke
                               const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
-                              int32_t partition_size, void* workspace, size_t workspace_bytes) {
+                              int32_t num_splits, void* workspace, size_t workspace_bytes) {
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
@@ -183,9 +219,8 @@ pa_status_t check_decode_args(const void* out, const void* query, const void* ke
     return fail(PA_ERR_SHAPE, "max_seq_len %d needs %d table columns > bt_stride %d", max_seq_len,
                 ceil_div(max_seq_len, block_size), bt_stride);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
-  if (partition_size < 0 || partition_size % 64)
-    return fail(PA_ERR_SHAPE, "partition_size %d must be 0 or a positive multiple of 64", partition_size);
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size);
+  if (num_splits < 0) return fail(PA_ERR_SHAPE, "num_splits %d < 0", num_splits);
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, num_splits);
   if (need && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
@@ -293,26 +328,24 @@ pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t
                     "reshape_and_cache_fp8 launch");
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
-                                 int32_t partition_size) {
-  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_seq_len < 1 || partition_size < 0 ||
-      partition_size % 64)
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t num_splits) {
+  if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_seq_len < 1 || num_splits < 0)
     return 0;
-  const int ps = resolve_partition(partition_size);
-  const int n_parts = ceil_div(max_seq_len, ps);
-  if (n_parts <= 1 || num_seqs == 0) return 0;
-  return part_layout(num_seqs, num_q_heads, n_parts, head_dim).total;
+  const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, max_seq_len);
+  if (n_splits <= 1) return 0;
+  return decode_layout(num_seqs, num_q_heads, n_splits, head_dim).total;
 }
 
 pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                       const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                      int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t partition_size,
+                      int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t num_splits,
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
   pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                                     partition_size, workspace, workspace_bytes);
+                                     num_splits, workspace, workspace_bytes);
   if (st != PA_OK) return st;
   if (dtype == PA_BF16 && num_q_heads / num_kv_heads > pa::kMaxGroup)
     return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGroup);
@@ -324,7 +357,7 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const
   const int kind = dtype == PA_F32 ? pa::kF32 : pa::kBF16;
   return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, kind,
-                    dtype == PA_F32, 1.f, 1.f, partition_size, workspace, workspace_bytes,
+                    dtype == PA_F32, 1.f, 1.f, num_splits, workspace, workspace_bytes,
                     static_cast<hipStream_t>(stream));
 }
 
@@ -332,12 +365,12 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
                           const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t q_dtype, float k_scale,
-                          float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          float v_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream) {
   if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
   pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                                     partition_size, workspace, workspace_bytes);
+                                     num_splits, workspace, workspace_bytes);
   if (st != PA_OK) return st;
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
@@ -350,7 +383,7 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
   }
   return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, pa::kFP8,
-                    q_dtype == PA_F32, k_scale, v_scale, partition_size, workspace, workspace_bytes,
+                    q_dtype == PA_F32, k_scale, v_scale, num_splits, workspace, workspace_bytes,
                     static_cast<hipStream_t>(stream));
 }
 
@@ -400,15 +433,17 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
 }  // namespace
 
 size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
-                                         int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
-  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || head_dim < 1) return 0;
+                                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim) {
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
+    return 0;
   int max_dec = 0;
   for (int s = 0; s < num_seqs; ++s) {
     const int q_len = query_start_loc_host[s + 1] - query_start_loc_host[s];
     if (q_len == 1) max_dec = std::max(max_dec, (int)seq_lens_host[s]);
   }
   if (max_dec == 0) return 0;
-  return pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_dec, 0);
+  return pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_dec, 0);
 }
 
 pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -435,7 +470,7 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
   if (dtype == PA_F32 && !plan.items.empty())
     return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
   const size_t need = pa_prefill_varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads,
-                                                        head_dim);
+                                                        num_kv_heads, head_dim);
   if (need && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))

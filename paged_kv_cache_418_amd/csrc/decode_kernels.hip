@@ -10,15 +10,23 @@
 // contexts are cut into partitions whose partial results are combined with
 // the log-sum-exp rule (tutorial 7: the LSE statistic).
 //
-// Work decomposition (designed for CDNA4, not taken from the pages): one
-// wave per (partition, kv head, sequence).  The q heads that share the kv
-// head (GQA, tutorial 1) are the 16 columns of the matrix-core tiles, so the
-// K/V of a block are read once for all of them.  Each 16-lane quarter of the
-// wave loads one whole token row of the block (coalesced 16-byte loads for
-// bf16 at head size 128); K goes through a small swizzled LDS tile to reach
-// the matrix-core operand layout, V is used from registers.  Masked positions
-// (the partly filled last block) are removed by selection, never by
-// multiplying with zero, so NaN in unused pool slots cannot leak.
+// Work decomposition (designed for CDNA4, not taken from the pages): the
+// blocks of all sequences, laid end to end, are cut into num_splits equal
+// shares per kv head, and one wave takes one share.  A share may end inside
+// a sequence and may cover several short ones; every piece of a sequence
+// that is not the whole sequence leaves a partial result (unnormalised O,
+// running max m, sum l) that the merge kernel combines with the log-sum-exp
+// rule.  Equal shares keep every wave busy until the end of the launch, which
+// fixed-size context partitions of uneven sequences do not.
+//
+// Inside a wave, the q heads that share the kv head (GQA, tutorial 1) are
+// the 16 columns of the matrix-core tiles, so the K/V of a block are read
+// once for all of them.  Each 16-lane quarter of the wave loads one whole
+// token row of the block (coalesced 16-byte loads for bf16 at head size
+// 128); K goes through a small swizzled LDS tile to reach the matrix-core
+// operand layout, V is used from registers.  Masked positions (the partly
+// filled last block) are removed by selection, never by multiplying with
+// zero, so NaN in unused pool slots cannot leak.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -126,7 +134,74 @@ __device__ __forceinline__ float sum_across_rows(float x) {
   return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
 }
 
-// One wave per (partition, kv head, sequence).  Per 16-token block:
+// Blocks of sequence s the decode attends: ceil(seq_len / 16), or 0 when s
+// is not a decode row of a flattened batch (q_len != 1).
+__device__ __forceinline__ int decode_blocks(const DecodeParams& p, int s) {
+  if (p.qsl && p.qsl[s + 1] - p.qsl[s] != 1) return 0;
+  const int L = min(p.seq_lens[s], p.max_seq_len);
+  return L > 0 ? (L + 15) >> 4 : 0;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(x, d, 64);
+    if (lane >= d) x += t;
+  }
+  return x;
+}
+
+// Calls piece(s, b0, b1, nb) for every piece of share `split` (of n_splits):
+// blocks [b0, b1) of sequence s, which has nb blocks in all.  Shares are
+// consecutive ranges of the sequences' blocks laid end to end, so a wave
+// visits its sequences in increasing order.  All arguments are wave-uniform.
+template <typename Fn>
+__device__ __forceinline__ void for_each_piece(const DecodeParams& p, int split, Fn&& piece) {
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+  for (int base = 0; base < p.num_seqs; base += 64) {
+    const int s = base + lane;
+    tot += s < p.num_seqs ? decode_blocks(p, s) : 0;
+  }
+  const long long T = wave_sum_i32(tot);
+  // never more shares than blocks, so no share is empty and the pieces of a
+  // sequence come from consecutive shares
+  const long long n = min((long long)p.n_splits, T);
+  if (split >= n) return;
+  const int lo = (int)(T * split / n), hi = (int)(T * (split + 1) / n);
+  int carry = 0;
+  for (int base = 0; base < p.num_seqs && carry < hi; base += 64) {
+    const int s = base + lane;
+    const int nb = s < p.num_seqs ? decode_blocks(p, s) : 0;
+    const int incl = wave_incl_scan_i32(nb, lane);
+    const int start = carry + incl - nb;
+    unsigned long long hits = __ballot(nb > 0 && start < hi && start + nb > lo);
+    while (hits) {
+      const int ln = __ffsll((long long)hits) - 1;
+      hits &= hits - 1;
+      const int bs = __builtin_amdgcn_readlane(start, ln), nbs = __builtin_amdgcn_readlane(nb, ln);
+      piece(base + ln, max(lo - bs, 0), min(hi - bs, nbs), nbs);
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+}
+
+// Records which shares hold the first and the last piece of sequence s.
+// With a single share every sequence is finished in place and there is no
+// scratch (the index arrays are absent).
+__device__ __forceinline__ void note_piece(const DecodeParams& p, int split, int s, int b0, int b1, int nb) {
+  if (p.n_splits <= 1) return;
+  if (b0 == 0) p.piece_first[s] = split;
+  if (b1 == nb) p.piece_last[s] = split;
+}
+
+// One wave per (share, kv head).  Per 16-token block of each piece:
 //   S[tok][g] = K[tok][:] . Q[g][:]     v_mfma_f32_16x16x32_bf16, K through a swizzled LDS tile
 //   O^T[d][g] += V^T[d][tok] P^T[tok][g] v_mfma_f32_16x16x16_bf16, V straight from registers
 // The K tile rows are read in the order sigma(m) = m/4 + 4*(m%4), so score
@@ -134,26 +209,18 @@ __device__ __forceinline__ float sum_across_rows(float x) {
 // whose V slices the same lane loaded.  P therefore never leaves its lane,
 // and the V^T operand of MFMA j (d = VEC*m + j) is two byte permutes of the
 // lane's own V words.  Two blocks are in flight while one is computed.
+// Blocks [b0, b1) of sequence s (nb blocks in all) for the q heads of kv head kvh.
 template <int D, bool FP8>
-__global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned char* k_lds, int split, int kvh, int s,
+                                             int b0, int b1, int nb) {
   using Sh = DecodeShape<D, FP8>;
   constexpr int VEC = Sh::kVec, W = Sh::kWords;
-  __shared__ __align__(16) unsigned char k_lds[Sh::kLdsBytes];
-
-  const int s = blockIdx.z, kvh = blockIdx.y, part = blockIdx.x;
-  int row = s;
-  if (p.qsl) {
-    const int qa = p.qsl[s], qb = p.qsl[s + 1];
-    if (qb - qa != 1) return;
-    row = qa;
-  }
-  if (row >= p.num_rows) return;
+  const int row = p.qsl ? p.qsl[s] : s;
   const int L = min(p.seq_lens[s], p.max_seq_len);
-  const int tok0 = part * p.part_size;
-  if (tok0 >= L) return;
-  const int n_parts = (L + p.part_size - 1) / p.part_size;
-  const int tok1 = min(L, tok0 + p.part_size);
-  const int nblk = (tok1 - tok0 + 15) >> 4;
+  const int tok0 = b0 * 16;
+  const int tok1 = min(L, b1 * 16);
+  const int nblk = b1 - b0;
+  const bool whole = b0 == 0 && b1 == nb;
 
   const int lane = threadIdx.x;
   const int a = lane >> 4, c = lane & 15;  // row group / column within the row group
@@ -201,7 +268,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
   // Physical block ids of the partition, 64 at a time in one VGPR (lane i holds block
   // win0 + i); a wave-uniform block id is then one v_readlane away.
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + (tok0 >> 4);
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + b0;
   int win0 = 0;
   int bt_win = lane < nblk ? bt[lane] : 0;
 
@@ -324,7 +391,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
   const int h = kvh * G + g;
   // lane (a, g) holds O[g][VEC*(4a + r) + j] in acc[j][r]: 4*VEC consecutive d
   const int d0 = 4 * VEC * a;
-  if (n_parts == 1) {
+  if (whole) {
     const float inv = p.v_scale / l;
     const size_t oi = ((size_t)row * p.num_q_heads + h) * D + d0;
     if (p.q_f32) {
@@ -341,11 +408,11 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int j = 0; j < VEC; j += 4)
-          *reinterpret_cast<u32x2*>(op + VEC * r + j) =
-              u32x2{pack_bf16x2(acc[j][r] * inv, acc[j + 1][r] * inv), pack_bf16x2(acc[j + 2][r] * inv, acc[j + 3][r] * inv)};
+          *reinterpret_cast<u32x2*>(op + VEC * r + j) = u32x2{pack_bf16x2(acc[j][r] * inv, acc[j + 1][r] * inv),
+                                                              pack_bf16x2(acc[j + 2][r] * inv, acc[j + 3][r] * inv)};
     }
   } else {
-    const size_t pi = ((size_t)s * p.num_q_heads + h) * p.n_parts_max + part;
+    const size_t pi = (size_t)(split + s) * p.num_q_heads + h;  // piece id split + s is unique
     float* po = p.part_o + pi * D + d0;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -359,25 +426,27 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-// fp32 pools and queries: vector-ALU kernel, one wave per (partition, q head, sequence).
+template <int D, bool FP8>
+__global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
+  __shared__ __align__(16) unsigned char k_lds[DecodeShape<D, FP8>::kLdsBytes];
+  const int split = blockIdx.x, kvh = blockIdx.y;
+  for_each_piece(p, split, [&](int s, int b0, int b1, int nb) {
+    if (kvh == 0 && threadIdx.x == 0) note_piece(p, split, s, b0, b1, nb);
+    decode_piece<D, FP8>(p, k_lds, split, kvh, s, b0, b1, nb);
+  });
+}
+
+// fp32 pools and queries: vector-ALU kernel, one wave per (share, q head).
 // Lane = (token t = lane % 16, quarter = lane / 16) holding D/4 elements of a row.
 template <int D>
-__global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_f32_piece(const DecodeParams& p, int split, int h, int s, int b0, int b1,
+                                                 int nb) {
   constexpr int QD = D / 4;
-  const int s = blockIdx.z, h = blockIdx.y, part = blockIdx.x;
-  int row = s;
-  if (p.qsl) {
-    const int a = p.qsl[s], b = p.qsl[s + 1];
-    if (b - a != 1) return;
-    row = a;
-  }
-  if (row >= p.num_rows) return;
+  const int row = p.qsl ? p.qsl[s] : s;
   const int L = min(p.seq_lens[s], p.max_seq_len);
-  const int tok0 = part * p.part_size;
-  if (tok0 >= L) return;
-  const int n_parts = (L + p.part_size - 1) / p.part_size;
-  const int tok1 = min(L, tok0 + p.part_size);
-  const int nblk = (tok1 - tok0 + 15) >> 4;
+  const int tok0 = b0 * 16;
+  const int tok1 = min(L, b1 * 16);
+  const int nblk = b1 - b0;
   const int lane = threadIdx.x;
   const int t = lane & 15, quarter = lane >> 4;
   const int kvh = h / p.group;
@@ -390,7 +459,7 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < QD; ++i) o[i] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + (tok0 >> 4);
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + b0;
   const float* kc = reinterpret_cast<const float*>(p.key_cache);
   const float* vc = reinterpret_cast<const float*>(p.value_cache);
 
@@ -398,7 +467,7 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
     int phys = bt[b];
     phys = min(max(phys, 0), p.num_blocks - 1);
     const int pos = tok0 + b * 16 + t;
-    const bool live = pos < L;
+    const bool live = pos < tok1;
     const size_t off = (((size_t)phys * 16 + t) * p.num_kv_heads + kvh) * D + quarter * QD;
     float dot = 0.f;
     if (live) {
@@ -430,12 +499,12 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
     for (int i = 0; i < QD; ++i) o[i] += shfl_xor(o[i], msk);
   }
   if (t == 0) {
-    if (n_parts == 1) {
+    if (b0 == 0 && b1 == nb) {
       float* op = reinterpret_cast<float*>(p.out) + ((size_t)row * p.num_q_heads + h) * D + quarter * QD;
 #pragma unroll
       for (int i = 0; i < QD; ++i) op[i] = o[i] / l;
     } else {
-      const size_t pi = ((size_t)s * p.num_q_heads + h) * p.n_parts_max + part;
+      const size_t pi = (size_t)(split + s) * p.num_q_heads + h;
 #pragma unroll
       for (int i = 0; i < QD; ++i) p.part_o[pi * D + quarter * QD + i] = o[i];
       if (quarter == 0) {
@@ -446,29 +515,36 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
   }
 }
 
-// Log-sum-exp merge of partition partials: one work-group of 256 threads per
-// (q head, sequence); the 4 waves take every 4th partition, then combine.
+template <int D>
+__global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
+  const int split = blockIdx.x, h = blockIdx.y;
+  for_each_piece(p, split, [&](int s, int b0, int b1, int nb) {
+    if (h == 0 && threadIdx.x == 0) note_piece(p, split, s, b0, b1, nb);
+    decode_f32_piece<D>(p, split, h, s, b0, b1, nb);
+  });
+}
+
+// Log-sum-exp merge of the pieces of a sequence: one work-group of 256
+// threads per (q head, sequence); the 4 waves take every 4th piece, then
+// combine.  Pieces of sequence s come from shares first..last and have ids
+// share + s.  Sequences held by a single share were finished in place.
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
   constexpr int PER_LANE = D / 64;
   __shared__ float red_m[4], red_l[4];
   __shared__ float red_o[4][D];
   const int s = blockIdx.y, h = blockIdx.x;
-  int row = s;
-  if (p.qsl) {
-    const int a = p.qsl[s], b = p.qsl[s + 1];
-    if (b - a != 1) return;
-    row = a;
-  }
-  if (row >= p.num_rows) return;
-  const int L = min(p.seq_lens[s], p.max_seq_len);
-  const int n_parts = (L + p.part_size - 1) / p.part_size;
-  if (n_parts <= 1) return;
+  if (decode_blocks(p, s) == 0) return;
+  const int first = p.piece_first[s], last = p.piece_last[s];
+  if (first >= last) return;
+  const int row = p.qsl ? p.qsl[s] : s;
+  const int n = last - first + 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t base = ((size_t)s * p.num_q_heads + h) * p.n_parts_max;
+  const size_t base = (size_t)(first + s) * p.num_q_heads + h;  // piece i: base + i * num_q_heads
+  const size_t step = (size_t)p.num_q_heads;
 
   float M = -INFINITY;
-  for (int i = threadIdx.x; i < n_parts; i += blockDim.x) M = fmaxf(M, p.part_m[base + i]);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, p.part_m[base + i * step]);
 #pragma unroll
   for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, shfl_xor(M, msk));
   if (lane == 0) red_m[wave] = M;
@@ -480,12 +556,13 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
   for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
   float den = 0.f;
 #pragma unroll 4
-  for (int pi = wave; pi < n_parts; pi += 4) {
-    const float w = fast_exp2(p.part_m[base + pi] - M);
-    den += w * p.part_l[base + pi];
-    const float* src = p.part_o + (base + pi) * D + lane * PER_LANE;
+  for (int i = wave; i < n; i += 4) {
+    const size_t pi = base + i * step;
+    const float w = fast_exp2(p.part_m[pi] - M);
+    den += w * p.part_l[pi];
+    const float* src = p.part_o + pi * D + lane * PER_LANE;
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) o[i] += w * src[i];
+    for (int k = 0; k < PER_LANE; ++k) o[k] += w * src[k];
   }
   if (lane == 0) red_l[wave] = den;
 #pragma unroll
@@ -510,17 +587,14 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
 template <int D>
 hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   if (kv == kF32) {
-    const dim3 grid(p.n_parts_max, p.num_q_heads, p.num_seqs);
-    hipLaunchKernelGGL(decode_f32_kernel<D>, grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_f32_kernel<D>, dim3(p.n_splits, p.num_q_heads), dim3(64), 0, stream, p);
+  } else if (kv == kFP8) {
+    hipLaunchKernelGGL((decode_mfma_kernel<D, true>), dim3(p.n_splits, p.num_kv_heads), dim3(64), 0, stream, p);
   } else {
-    const dim3 grid(p.n_parts_max, p.num_kv_heads, p.num_seqs);
-    if (kv == kFP8)
-      hipLaunchKernelGGL((decode_mfma_kernel<D, true>), grid, dim3(64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<D, false>), grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, false>), dim3(p.n_splits, p.num_kv_heads), dim3(64), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_parts_max <= 1) return e;
+  if (e != hipSuccess || p.n_splits <= 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.num_q_heads, p.num_seqs), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

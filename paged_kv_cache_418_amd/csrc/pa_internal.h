@@ -15,7 +15,11 @@ constexpr int kMaxPrefillItems = 640;
 
 enum Dtype { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
-// One decode launch: grid (n_parts_max, num_kv_heads, num_seqs).
+// One decode launch: grid (n_splits, num_kv_heads) (fp32: (n_splits, num_q_heads)).
+// The blocks of all decode sequences, laid end to end, are cut into n_splits
+// equal shares; share c leaves one partial result per sequence piece it
+// holds, under piece id c + s (unique because shares and sequences are both
+// visited in increasing order).
 struct DecodeParams {
   void* out;
   const void* query;
@@ -24,9 +28,11 @@ struct DecodeParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const int32_t* qsl;        // optional: rows of a flattened batch; sequences with q_len != 1 are skipped
-  float* part_o;             // [num_seqs][Hq][n_parts_max][D] partial outputs (unnormalised)
-  float* part_m;             // [num_seqs][Hq][n_parts_max] running max (log2 units)
-  float* part_l;             // [num_seqs][Hq][n_parts_max] sum of weights
+  float* part_o;             // [n_splits + num_seqs][Hq][D] partial outputs (unnormalised)
+  float* part_m;             // [n_splits + num_seqs][Hq] running max (log2 units)
+  float* part_l;             // [n_splits + num_seqs][Hq] sum of weights
+  int32_t* piece_first;      // [num_seqs] share holding the first piece of each sequence
+  int32_t* piece_last;       // [num_seqs] share holding the last piece
   int bt_stride;
   int num_seqs;
   int num_rows;              // rows of query/out (num_seqs, or the flattened token count)
@@ -35,8 +41,7 @@ struct DecodeParams {
   int group;                 // num_q_heads / num_kv_heads
   int num_blocks;
   int max_seq_len;
-  int part_size;             // tokens per partition (multiple of 64)
-  int n_parts_max;
+  int n_splits;
   float scale_log2;          // softmax scale * log2(e) (* k_scale for fp8 pools)
   float v_scale;             // 1, or the fp8 value scale
   int q_f32;                 // query / output are fp32 (else bf16)

@@ -41,13 +41,13 @@ class DevWorkload:
     def max_seq_len(self):
         return int(self.w.seq_lens.max())
 
-    def decode(self, partition_size=0, out=None):
+    def decode(self, num_splits=0, out=None):
         w = self.w
         if w.kv_dtype == "fp8":
             return pk.pa_decode_fp8(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
-                                    w.k_scale, w.v_scale, self.max_seq_len(), partition_size, out=out)
+                                    w.k_scale, w.v_scale, self.max_seq_len(), num_splits, out=out)
         return pk.pa_decode(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
-                            self.max_seq_len(), partition_size, out=out)
+                            self.max_seq_len(), num_splits, out=out)
 
     def prefill(self, out=None):
         w = self.w

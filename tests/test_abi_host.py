@@ -31,14 +31,17 @@ def test_version_and_status_strings(lib):
 
 
 def test_decode_workspace_arithmetic(lib):
-    # 64 sequences, 32 heads, d 128, up to 4096 tokens in 512-token partitions: 8 partials per (seq, head)
-    o = 64 * 32 * 8 * 128 * 4
-    ml = 64 * 32 * 8 * 4
-    assert pk.pa_decode_workspace_bytes(64, 32, 128, 4096, 0) == o + 2 * ml
-    assert pk.pa_decode_workspace_bytes(64, 32, 128, 512, 0) == 0
-    assert pk.pa_decode_workspace_bytes(64, 32, 128, 513, 512) > 0
-    assert pk.pa_decode_workspace_bytes(3, 4, 64, 100, 64) == 2 * 256 + 256 * ((3 * 4 * 2 * 64 * 4 + 255) // 256)
-    assert pk.pa_decode_workspace_bytes(64, 32, 128, 4096, 100) == 0  # invalid partition size
+    # 64 sequences, 32 q heads, d 128, 256 shares: partial slots for 256 + 64 piece ids, then two int32 per sequence
+    pieces = 256 + 64
+    o, ml, idx = pieces * 32 * 128 * 4, pieces * 32 * 4, 256
+    assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 256) == o + 2 * ml + 2 * idx
+    assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 1) == 0          # one share: no scratch
+    # never more shares than blocks: 3 sequences of at most ceil(100/16) = 7 blocks -> 21 shares, 24 piece ids
+    o, ml, idx = 24 * 4 * 64 * 4, 512, 256
+    assert pk.pa_decode_workspace_bytes(3, 4, 2, 64, 100, 1000) == o + 2 * ml + 2 * idx
+    assert pk.pa_decode_workspace_bytes(1, 4, 2, 64, 16, 0) == 0               # a single block
+    assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, -1) == 0         # invalid share count
+    assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) > 0           # automatic
 
 
 def _decode(lib, **kw):
@@ -59,7 +62,7 @@ def _decode(lib, **kw):
     (dict(dtype=b.PA_FP8_E4M3), 3),
     (dict(max_len=0), 2),
     (dict(max_len=256 * 16 + 1), 2),
-    (dict(ps=100), 2),
+    (dict(ps=-1), 2),
     (dict(wsb=16), 4),
     (dict(ws=None), 4),
     (dict(ws=FAKE + 8), 4),
@@ -123,10 +126,10 @@ def test_prefill_rejects(lib):
 
 def test_prefill_workspace_bytes(lib):
     q, s = _host_i32([0, 1, 2, 514]), _host_i32([1000, 10, 700])
-    got = lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 128)
-    assert got == pk.pa_decode_workspace_bytes(3, 32, 128, 1000, 0) > 0
+    got = lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128)
+    assert got == pk.pa_decode_workspace_bytes(3, 32, 8, 128, 1000, 0) > 0
     q2, s2 = _host_i32([0, 512]), _host_i32([700])
-    assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 32, 128) == 0
+    assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 32, 8, 128) == 0
 
 
 def test_binding_refuses_cpu_tensors():

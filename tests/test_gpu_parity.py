@@ -123,15 +123,15 @@ def test_fp8_read_converter_exact():
 
 # ------------------------------------------------------------------ decode
 
-def _decode_case(w, partition_size=0, tol=None):
+def _decode_case(w, num_splits=0, tol=None):
     d = DevWorkload(w)
     d.write_new_tokens()
-    out = d.decode(partition_size)
+    out = d.decode(num_splits)
     torch.cuda.synchronize()
     ref = oracle.attention_for(w, pools=oracle.written_pools(w))
     err = max_err(out, ref)
     tol = TOL[w.kv_dtype if w.kv_dtype == "fp8" else w.q_dtype] if tol is None else tol
-    say(f"  {w.name} partition={partition_size} max_abs_err={err:.3e} tol={tol}")
+    say(f"  {w.name} splits={num_splits} max_abs_err={err:.3e} tol={tol}")
     assert err <= tol
     return err
 
@@ -142,14 +142,14 @@ def test_decode_tiny_fp32():
 
 @pytest.mark.parametrize("kinds", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8"), ("f32", "fp8")])
 @pytest.mark.parametrize("heads", [(4, 2, 64), (32, 8, 128), (16, 1, 128), (8, 8, 64), (12, 4, 128)])
-@pytest.mark.parametrize("partition_size", [0, 64, 4096])
-def test_decode_random(kinds, heads, partition_size):
+@pytest.mark.parametrize("num_splits", [0, 1, 7, 4096])
+def test_decode_random(kinds, heads, num_splits):
     Hq, Hkv, D = heads
-    seed = 200 + Hq + 3 * Hkv + D + partition_size % 97 + len(kinds[1])
+    seed = 200 + Hq + 3 * Hkv + D + num_splits % 97 + len(kinds[1])
     w = wl.random_case(seed, num_seqs=6, ctx_range=(1, 700), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                        q_dtype=kinds[0], kv_dtype=kinds[1], k_scale=0.05, v_scale=0.04)
-    say("decode random", kinds, heads, partition_size)
-    _decode_case(w, partition_size)
+    say("decode random", kinds, heads, num_splits)
+    _decode_case(w, num_splits)
 
 
 def test_decode_llama3_8b_full():
@@ -188,17 +188,27 @@ def test_decode_block_relabeling_bit_identical():
     assert torch.equal(base.view(torch.int16), again.view(torch.int16))
 
 
-def test_decode_partition_sizes_agree_and_repeat_bit_identical():
+def test_decode_split_counts_agree_and_repeat_bit_identical():
     w = wl.random_case(311, num_seqs=4, ctx_range=(500, 3000), num_q_heads=32, num_kv_heads=8, head_dim=128,
                        q_dtype="bf16", kv_dtype="bf16")
     d = DevWorkload(w)
     d.write_new_tokens()
-    outs = {ps: d.decode(ps).float().cpu() for ps in (64, 512, 3072)}
-    for ps in (64, 3072):
-        assert torch.max(torch.abs(outs[ps] - outs[512])).item() < 1.5e-2
-    first = d.decode(512).cpu()
+    say("decode split counts")
+    outs = {n: d.decode(n).float().cpu() for n in (1, 3, 64, 0, 100000)}
+    for n in (3, 64, 0, 100000):
+        assert torch.max(torch.abs(outs[n] - outs[1])).item() < 1.5e-2
+    first = d.decode(0).cpu()
     for _ in range(5):
-        assert torch.equal(d.decode(512).cpu().view(torch.int16), first.view(torch.int16))
+        assert torch.equal(d.decode(0).cpu().view(torch.int16), first.view(torch.int16))
+
+
+def test_decode_many_short_sequences_share_splits():
+    """Shares that cover several whole sequences and sequences cut across shares, ragged lengths, long batch."""
+    w = wl.random_case(321, num_seqs=300, ctx_range=(1, 70), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       q_dtype="bf16", kv_dtype="bf16")
+    say("decode 300 short sequences")
+    for n in (0, 5, 37):
+        _decode_case(w, n)
 
 
 # ------------------------------------------------------------------ prefill (varlen, mixed)
