@@ -1,20 +1,29 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: slot mapping, the KV
-write of the new tokens, then paged attention (decode with split-context
-partitions and the log-sum-exp merge).  The headline workload is the
-Llama-3-8B-shaped decode layer (batch 64, context U[512, 4096], 32 q / 8 kv
-heads, head_dim 128, block 16, bf16); its value is algorithmic KV bytes per
-second.  The mixed continuous-batching step (48 decodes + two 512-token
-chunks) is timed too and gives the prefill TFLOP/s.
+A step is one pass of the whole path over one batch: slot mapping of the new
+tokens, their KV write through the slot mapping, then paged attention.  The
+headline workload is the Llama-3-8B-shaped decode layer (64 sequences,
+context U[512, 4096], 32 q / 8 kv heads, head_dim 128, block 16, bf16); its
+value is KV bytes streamed per second over whole steps.  The mixed
+continuous-batching step (48 decodes + two 512-token chunks, one flattened
+batch) is timed too and gives the prefill TFLOP/s of its two chunks.
 
 Prints one JSON line.  Inputs are seeded and synthetic and resident in HBM
 before the timed region; two copies of the KV pool alternate between steps so
 no step reads KV that the previous step left in the 256 MB last-level cache.
+
+Device time of the dominant kernel comes from HIP events that the library
+records on its own launch stream around each kernel (pa_timing_enable), in a
+second pass of the same steps, so the headline pass carries no extra events.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       [--only decode|mixed|copy]   (copy: a plain 1 GiB device copy, the
+       reference for scaling the FETCH_SIZE / WRITE_SIZE counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,8 +36,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 METRIC = "paged decode KV GB/s (% of HBM peak) + prefill TFLOP/s at 1×MI355X"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "paged_kv_cache_418_amd", "csrc")
+COPY_BYTES = 1 << 30
+DECODE_SOURCES = ["decode_kernels.hip", "pa_device.h", "pa_internal.h"]
 
 
 def _log(*a):
@@ -66,11 +79,6 @@ class Step:
             self.write(kc, vc)
         torch.cuda.synchronize()
 
-    def attend_next(self):
-        kc, vc = self.pools[self.i % len(self.pools)]
-        self.i += 1
-        self.attend(kc, vc)
-
     def write(self, kc, vc):
         w, pk = self.w, self.pk
         pk.pa_slot_mapping(self.bt, self.sl, self.qsl, w.num_tokens, w.block_size, out=self.slots)
@@ -91,6 +99,11 @@ class Step:
             pk.pa_prefill_varlen(self.q, kc, vc, self.bt, self.sl, self.qsl, w.seq_lens, w.query_start_loc, w.scale,
                                  out=self.out, workspace=self.ws)
 
+    def attend_next(self):
+        kc, vc = self.pools[self.i % len(self.pools)]
+        self.i += 1
+        self.attend(kc, vc)
+
     def __call__(self):
         kc, vc = self.pools[self.i % len(self.pools)]
         self.i += 1
@@ -99,6 +112,7 @@ class Step:
 
 
 def time_steps(fn, steps: int, warmup: int):
+    """Mean ms per call over `steps` calls bracketed by synchronisations, plus the wall time."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -113,35 +127,168 @@ def time_steps(fn, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def time_each(fn, reps: int):
-    """Per-call durations (ms) from events recorded around each call on the current stream."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
+def kernel_times(fn, steps: int, kernels):
+    """Mean device ms per launch of each named kernel over `steps` calls, from the library's own events."""
+    import paged_kv_cache_418_amd as pk
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    pk.timing_reset()
+    pk.timing_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    pk.timing_enable(False)
+    out = {}
+    for k in kernels:
+        n, ms = pk.timing_read(k)
+        out[k] = (ms / n if n else None, n)
+    return out
+
+
+def source_hash(*files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str, sources) -> dict:
+    """HBM bytes per launch of a kernel from its committed counter summary (profiles/<name>.txt).
+
+    The summary holds FETCH_SIZE and WRITE_SIZE in KiB per dispatch, the factors that
+    map each to bytes (what the same counter reads for a plain copy of known size) and
+    the hash of the kernel sources they were taken with; a changed source gives None.
+    """
+    path = os.path.join(PROFILES, name + ".txt")
+    if not os.path.exists(path):
+        return {"bytes": None, "why": f"no {os.path.relpath(path, ROOT)}"}
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("source_hash") != source_hash(*sources):
+            return {"bytes": None, "why": "kernel source changed since the counters were taken"}
+        fetch = float(kv["fetch_kib"]) * float(kv["fetch_bytes_per_kib"])
+        write = float(kv["write_kib"]) * float(kv["write_bytes_per_kib"])
+    except (KeyError, ValueError):
+        return {"bytes": None, "why": f"incomplete {os.path.relpath(path, ROOT)}"}
+    return {"bytes": int(round(fetch + write)), "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write))}
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle on a bounded sample of the workload's sequences: KV GB/s on the host cores."""
+    """The oracle on a bounded sample of the workload's sequences (repeated until the budget is spent)."""
     import oracle
-    from paged_kv_cache_418_amd import workloads as wl
     threads = oracle.num_threads()
-    order = list(range(w.num_seqs))
     done_bytes, spent, n = 0, 0.0, 0
-    B = w.block_size
-    while order and spent < budget_s:
-        s = order.pop(0)
-        rows = [int(w.query_start_loc[s])]
+    s = 0
+    while spent < budget_s:
         t0 = time.perf_counter()
-        oracle.attention_for(w, rows=rows)
+        oracle.attention_for(w, rows=[int(w.query_start_loc[s])])
         spent += time.perf_counter() - t0
         done_bytes += 2 * int(w.seq_lens[s]) * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
         n += 1
+        s = (s + 1) % w.num_seqs
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {w.num_seqs} sequences of {w.name} (fp64 C oracle, {spent:.1f} s)"}
+            "sample": f"{n} single-sequence decode rows of {w.name} in turn (fp64 C oracle, OpenMP over q heads, "
+                      f"{spent:.1f} s)"}
+
+
+def bench_decode(args, result):
+    from paged_kv_cache_418_amd import workloads as wl
+    _log("generating llama3_8b_decode_bf16 ...")
+    w = wl.llama3_8b_decode_bf16()
+    st = Step(w)
+    kv_bytes = wl.decode_kv_bytes(w)
+    alg_bytes = wl.decode_alg_bytes(w)
+    _log("timing decode steps ...")
+    ms, wall = time_steps(st, args.steps, args.warmup)
+    kt = kernel_times(st, args.steps, ["slot_mapping", "reshape_and_cache", "decode", "decode_merge"])
+    dec_ms = kt["decode"][0]
+    att_gbps = alg_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = read_traffic("decode_bf16_d128_llama3_8b_traffic", DECODE_SOURCES)
+    result.update({
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3_8b_decode_bf16", "num_seqs": w.num_seqs, "ctx": "U[512,4096]",
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks, "kv_bytes": kv_bytes,
+                   "num_splits": "auto"},
+        "pct_hbm": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "wall_s": round(wall, 4),
+        "roofline": {"kernel": "decode_mfma_kernel<128, bf16>", "bound": "hbm", "achieved": round(att_gbps, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic["bytes"], "alg_bytes_per_launch": alg_bytes,
+                     "launch_ms": round(dec_ms, 5), "launches_timed": kt["decode"][1]},
+        "step_kernels_ms": {k: (round(v[0], 5) if v[0] is not None else None) for k, v in kt.items()},
+    })
+    if traffic["bytes"] is None:
+        result["roofline"]["traffic_note"] = traffic["why"]
+    else:
+        result["roofline"]["traffic_over_alg"] = round(traffic["bytes"] / alg_bytes, 4)
+    if not args.no_cpu:
+        _log("cpu baseline ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+    del st
+    torch.cuda.empty_cache()
+
+
+def bench_mixed(args, result):
+    from paged_kv_cache_418_amd import workloads as wl
+    _log("generating mixed_step_bf16 ...")
+    w = wl.mixed_step_bf16()
+    st = Step(w)
+    ms, _ = time_steps(st, args.steps, args.warmup)
+    flops = wl.prefill_flops(w)
+    del st
+    # the two chunks alone (prefill part) and the 48 decodes alone
+    chunk_w = _sub(w, list(range(48, 50)))
+    cs = Step(chunk_w, copies=1)
+    pre_call_ms, _ = time_steps(cs.attend_next, args.steps, args.warmup)
+    kt = kernel_times(cs.attend_next, args.steps, ["prefill"])
+    pre_ms = kt["prefill"][0]
+    del cs
+    dec_w = _sub(w, list(range(48)))
+    ds = Step(dec_w, copies=2)
+    dms, _ = time_steps(ds.attend_next, args.steps, args.warmup)
+    dec_bytes = wl.decode_kv_bytes(dec_w)
+    del ds
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    mixed = {"workload": "mixed_step_bf16", "ms_per_step": round(ms, 5),
+             "prefill_gflop": round(flops / 1e9, 3),
+             "prefill_kernel_ms": round(pre_ms, 5), "prefill_call_ms": round(pre_call_ms, 5),
+             "prefill_tflops": round(tflops, 2),
+             "prefill_pct_mfma": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+             "prefill_roofline": {"kernel": "prefill_kernel<128>", "bound": "mfma", "achieved": round(tflops, 2),
+                                  "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                                  "alg_flops_per_launch": flops},
+             "decode_part_gbps": round(dec_bytes / (dms * 1e-3) / 1e9, 2),
+             "decode_part_ms": round(dms, 5)}
+    if "metric" in result:
+        result["mixed_step"] = mixed
+    else:
+        result.update({"metric": METRIC, "value": mixed["decode_part_gbps"], "unit": "GB/s", "n_gpus": 1,
+                       "steps": args.steps, "warmup": args.warmup, "ms_per_step": mixed["ms_per_step"],
+                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                       "data": "synthetic", "config": {"workload": "mixed_step_bf16"}, "mixed_step": mixed})
+    torch.cuda.empty_cache()
+
+
+def bench_copy(args, result):
+    """A plain device-to-device copy of 1 GiB: the known-size reference for the HBM byte counters."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms, _ = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+    result.update({"workload": "copy_1GiB", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                   "ms_per_copy": round(ms, 5), "GBps_read_plus_write": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 2)})
 
 
 def main():
@@ -150,81 +297,22 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="decode | mixed (profiling runs)")
+    ap.add_argument("--only", default="", choices=["", "decode", "mixed", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the path has no multi-GPU form in this library (use --gpus 1).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: this library's path runs on a single GPU and has no multi-GPU form; "
+              "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-
-    from paged_kv_cache_418_amd import workloads as wl
+    import paged_kv_cache_418_amd as pk
+    pk.load()
     result = {}
-    if args.only in ("", "decode"):
-        _log("generating llama3_8b_decode_bf16 ...")
-        w = wl.llama3_8b_decode_bf16()
-        st = Step(w)
-        kv_bytes = wl.decode_kv_bytes(w)
-        alg_bytes = wl.decode_alg_bytes(w)
-        _log("timing decode step ...")
-        ms, wall = time_steps(st, args.steps, args.warmup)
-        # attention launch alone (decode kernel + LSE merge), events around each call
-        per = time_each(st.attend_next, max(args.steps, 20))
-        att_ms = float(np.mean(per))
-        att_gbps = alg_bytes / (att_ms * 1e-3) / 1e9
-        result.update({
-            "metric": METRIC,
-            "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
-            "unit": "GB/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(ms, 5),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "llama3_8b_decode_bf16", "num_seqs": w.num_seqs, "ctx": "U[512,4096]",
-                       "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
-                       "num_blocks": w.num_blocks, "kv_bytes": kv_bytes, "partition_size": 512},
-            "pct_hbm": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-            "wall_s": round(wall, 4),
-            "roofline": {"kernel": "paged decode attention (decode_mfma_kernel + decode_merge_kernel)",
-                         "bound": "hbm", "achieved": round(att_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                         "launch_ms": round(att_ms, 5), "alg_bytes_per_launch": alg_bytes},
-        })
-        if not args.no_cpu:
-            _log("cpu baseline ...")
-            result["cpu_baseline"] = cpu_baseline(w)
-        del st
-        torch.cuda.empty_cache()
-
-    if args.only in ("", "mixed"):
-        _log("generating mixed_step_bf16 ...")
-        w = wl.mixed_step_bf16()
-        st = Step(w)
-        ms, _ = time_steps(st, args.steps, args.warmup)
-        flops = wl.prefill_flops(w)
-        # the two chunks alone (prefill part) and the 48 decodes alone
-        del st
-        chunk_w = _sub(w, list(range(48, 50)))
-        dec_w = _sub(w, list(range(48)))
-        cs = Step(chunk_w, copies=1)
-        per_c = time_each(cs.attend_next, max(args.steps, 20))
-        pre_ms = float(np.mean(per_c))
-        del cs
-        ds = Step(dec_w, copies=2)
-        dms, _ = time_steps(ds.attend_next, args.steps, args.warmup)
-        dec_bytes = wl.decode_kv_bytes(dec_w)
-        mixed = {"workload": "mixed_step_bf16", "ms_per_step": round(ms, 5),
-                 "prefill_tflops": round(flops / (pre_ms * 1e-3) / 1e12, 2),
-                 "prefill_pct_mfma": round(100 * flops / (pre_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2),
-                 "prefill_ms": round(pre_ms, 5), "prefill_gflop": round(flops / 1e9, 3),
-                 "decode_part_gbps": round(dec_bytes / (dms * 1e-3) / 1e9, 2),
-                 "decode_part_ms": round(dms, 5)}
-        if "metric" in result:
-            result["mixed_step"] = mixed
-        else:
-            result.update({"metric": METRIC, "value": mixed["decode_part_gbps"], "unit": "GB/s", "n_gpus": 1,
-                           "steps": args.steps, "warmup": args.warmup, "ms_per_step": mixed["ms_per_step"],
-                           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-                           "data": "synthetic", "config": {"workload": "mixed_step_bf16"}, "mixed_step": mixed})
+    if args.only == "copy":
+        bench_copy(args, result)
+    else:
+        if args.only in ("", "decode"):
+            bench_decode(args, result)
+        if args.only in ("", "mixed"):
+            bench_mixed(args, result)
     print(json.dumps(result), flush=True)
 
 

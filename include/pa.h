@@ -207,6 +207,29 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                               int32_t num_blocks, float scale, pa_dtype_t dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * Kernel timing, for measurement.  Not part of the pages' problem statement:
+ * it serves the roofline figures (device time of each kernel of the path).
+ * pa_timing_enable(1): from now on every entry point records a pair of HIP
+ * events on its stream around each kernel it launches (events are created
+ * by the library and reused; no device memory is allocated).  The events
+ * serialise nothing but add a small gap between the kernels of one call.
+ * pa_timing_read(kernel, &count, &total_ms): waits for the recorded events
+ * of that kernel and returns how many launches were timed and their summed
+ * duration in milliseconds.  pa_timing_reset(): zeroes the sums.
+ */
+typedef enum pa_kernel {
+  PA_K_SLOT_MAPPING = 0,    /* pa_slot_mapping */
+  PA_K_RESHAPE_AND_CACHE = 1, /* pa_reshape_and_cache, pa_reshape_and_cache_fp8 */
+  PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode, pa_decode_fp8, decode rows of pa_prefill_varlen) */
+  PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
+  PA_K_PREFILL = 4          /* the varlen prefill kernel */
+} pa_kernel_t;
+
+pa_status_t pa_timing_enable(int on);
+pa_status_t pa_timing_reset(void);
+pa_status_t pa_timing_read(pa_kernel_t kernel, int64_t* count, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

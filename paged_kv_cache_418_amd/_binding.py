@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+KERNELS = {"slot_mapping": 0, "reshape_and_cache": 1, "decode": 2, "decode_merge": 3, "prefill": 4}
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_WORKSPACE",
           5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_HIP"}
 
@@ -68,6 +69,9 @@ def load() -> ctypes.CDLL:
             "pa_prefill_varlen_workspace_bytes": ([P, P, i32, i32, i32, i32], sz),
             "pa_prefill_varlen": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                    ctypes.c_int, P, sz, P], ctypes.c_int),
+            "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
+            "pa_timing_reset": ([], ctypes.c_int),
+            "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -220,3 +224,19 @@ def pa_prefill_varlen(query, key_cache, value_cache, block_tables, seq_lens, que
         sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), None if ws is None else ws.data_ptr(),
         wsb, _stream()))
     return out
+
+
+def timing_enable(on: bool = True) -> None:
+    """Library-side HIP events around every kernel launch (see pa_timing_enable)."""
+    _check("pa_timing_enable", load().pa_timing_enable(1 if on else 0))
+
+
+def timing_reset() -> None:
+    _check("pa_timing_reset", load().pa_timing_reset())
+
+
+def timing_read(kernel: str):
+    """(launches timed, summed device milliseconds) of one kernel of the path."""
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check("pa_timing_read", load().pa_timing_read(KERNELS[kernel], ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

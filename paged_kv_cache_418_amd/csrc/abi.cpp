@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -519,6 +520,113 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
     if (st != PA_OK) return st;
   }
   return ok();
+}
+
+}  // extern "C"
+
+// ---- optional kernel timing ------------------------------------------------
+namespace {
+
+struct TimingState {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  struct Pending {
+    hipEvent_t begin, end;
+  };
+  std::vector<Pending> pending[pa::kNumKernelIds];
+  hipEvent_t open[pa::kNumKernelIds] = {};
+  int64_t count[pa::kNumKernelIds] = {};
+  double total_ms[pa::kNumKernelIds] = {};
+  std::vector<hipEvent_t> spare;
+
+  hipEvent_t take() {
+    if (!spare.empty()) {
+      hipEvent_t e = spare.back();
+      spare.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+  }
+
+  // Folds finished event pairs of one kernel into its totals (waits for them).
+  bool drain(int k) {
+    bool ok = true;
+    for (Pending& pe : pending[k]) {
+      float ms = 0.f;
+      if (hipEventSynchronize(pe.end) != hipSuccess || hipEventElapsedTime(&ms, pe.begin, pe.end) != hipSuccess) {
+        ok = false;
+      } else {
+        ++count[k];
+        total_ms[k] += ms;
+      }
+      spare.push_back(pe.begin);
+      spare.push_back(pe.end);
+    }
+    pending[k].clear();
+    return ok;
+  }
+};
+
+TimingState& timing() {
+  static TimingState* t = new TimingState();  // lives until the process ends
+  return *t;
+}
+
+}  // namespace
+
+namespace pa {
+
+void timing_mark(int kernel, bool begin, hipStream_t stream) {
+  TimingState& t = timing();
+  if (!t.on.load(std::memory_order_relaxed) || kernel < 0 || kernel >= kNumKernelIds) return;
+  std::lock_guard<std::mutex> lk(t.mu);
+  hipEvent_t e = t.take();
+  if (!e) return;
+  if (hipEventRecord(e, stream) != hipSuccess) {
+    t.spare.push_back(e);
+    return;
+  }
+  if (begin) {
+    if (t.open[kernel]) t.spare.push_back(t.open[kernel]);
+    t.open[kernel] = e;
+  } else if (t.open[kernel]) {
+    t.pending[kernel].push_back({t.open[kernel], e});
+    t.open[kernel] = nullptr;
+  } else {
+    t.spare.push_back(e);
+  }
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status_t pa_timing_enable(int on) {
+  timing().on.store(on != 0, std::memory_order_relaxed);
+  return ok();
+}
+
+pa_status_t pa_timing_reset(void) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (int k = 0; k < pa::kNumKernelIds; ++k) {
+    t.drain(k);
+    t.count[k] = 0;
+    t.total_ms[k] = 0.0;
+  }
+  return ok();
+}
+
+pa_status_t pa_timing_read(pa_kernel_t kernel, int64_t* count, double* total_ms) {
+  if (!count || !total_ms) return fail(PA_ERR_NULL, "count and total_ms must not be NULL");
+  if ((int)kernel < 0 || (int)kernel >= pa::kNumKernelIds) return fail(PA_ERR_SHAPE, "unknown kernel id %d", (int)kernel);
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  const bool good = t.drain((int)kernel);
+  *count = t.count[(int)kernel];
+  *total_ms = t.total_ms[(int)kernel];
+  return good ? ok() : fail(PA_ERR_HIP, "a timing event could not be read");
 }
 
 }  // extern "C"

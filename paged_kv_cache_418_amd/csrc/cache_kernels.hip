@@ -94,8 +94,10 @@ __global__ void __launch_bounds__(256) reshape_fp8_kernel(const void* key, const
 hipError_t launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int bt_stride,
                                const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
                                int block_size, hipStream_t stream) {
+  timing_mark(kKSlotMapping, true, stream);
   hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(64), 0, stream, slot_mapping, block_tables, bt_stride,
                      seq_lens, qsl, num_tokens, block_size);
+  timing_mark(kKSlotMapping, false, stream);
   return hipGetLastError();
 }
 
@@ -113,6 +115,7 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t 
   const auto* v8 = reinterpret_cast<const uint8_t*>(value);
   auto* kc8 = reinterpret_cast<uint8_t*>(key_cache);
   auto* vc8 = reinterpret_cast<uint8_t*>(value_cache);
+  timing_mark(kKReshape, true, stream);
   if ((align & 15u) == 0)
     hipLaunchKernelGGL(reshape_kernel<u32x4>, dim3(num_tokens), dim3(threads), 0, stream, k8, v8, ksb, vsb, kc8, vc8,
                        slots, row_bytes, num_slots);
@@ -122,6 +125,7 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t 
   else
     hipLaunchKernelGGL(reshape_kernel<uint16_t>, dim3(num_tokens), dim3(threads), 0, stream, k8, v8, ksb, vsb, kc8,
                        vc8, slots, row_bytes, num_slots);
+  timing_mark(kKReshape, false, stream);
   return hipGetLastError();
 }
 
@@ -132,12 +136,14 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int6
                                         float v_scale, hipStream_t stream) {
   const int row_elems = num_kv_heads * head_dim;
   const int num_slots = num_blocks * block_size;
+  timing_mark(kKReshape, true, stream);
   if (src_f32)
     hipLaunchKernelGGL(reshape_fp8_kernel<true>, dim3(num_tokens), dim3(128), 0, stream, key, value, key_stride,
                        value_stride, key_cache, value_cache, slots, row_elems, num_slots, k_scale, v_scale);
   else
     hipLaunchKernelGGL(reshape_fp8_kernel<false>, dim3(num_tokens), dim3(128), 0, stream, key, value, key_stride,
                        value_stride, key_cache, value_cache, slots, row_elems, num_slots, k_scale, v_scale);
+  timing_mark(kKReshape, false, stream);
   return hipGetLastError();
 }
 

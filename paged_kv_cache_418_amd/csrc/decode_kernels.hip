@@ -586,6 +586,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
 
 template <int D>
 hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
+  timing_mark(kKDecode, true, stream);
   if (kv == kF32) {
     hipLaunchKernelGGL(decode_f32_kernel<D>, dim3(p.n_splits, p.num_q_heads), dim3(64), 0, stream, p);
   } else if (kv == kFP8) {
@@ -593,9 +594,12 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((decode_mfma_kernel<D, false>), dim3(p.n_splits, p.num_kv_heads), dim3(64), 0, stream, p);
   }
+  timing_mark(kKDecode, false, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits <= 1) return e;
+  timing_mark(kKDecodeMerge, true, stream);
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.num_q_heads, p.num_seqs), dim3(256), 0, stream, p);
+  timing_mark(kKDecodeMerge, false, stream);
   return hipGetLastError();
 }
 

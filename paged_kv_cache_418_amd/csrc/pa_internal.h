@@ -67,6 +67,11 @@ struct PrefillParams {
   uint32_t items[kMaxPrefillItems];
 };
 
+// Optional kernel timing (pa_timing_enable): a launch site brackets its
+// kernel with timing_mark(id, true/false, stream); a no-op unless enabled.
+enum KernelId { kKSlotMapping = 0, kKReshape = 1, kKDecode = 2, kKDecodeMerge = 3, kKPrefill = 4, kNumKernelIds = 5 };
+void timing_mark(int kernel, bool begin, hipStream_t stream);
+
 hipError_t launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int bt_stride,
                                const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
                                int block_size, hipStream_t stream);

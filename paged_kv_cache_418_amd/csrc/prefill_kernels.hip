@@ -220,10 +220,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillParams p) {
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid(p.n_items, p.num_q_heads);
+  timing_mark(kKPrefill, true, stream);
   if (head_dim == 128)
     hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, stream, p);
+  timing_mark(kKPrefill, false, stream);
   return hipGetLastError();
 }
 

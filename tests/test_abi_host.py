@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 11
+    assert len(syms) == 14
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -137,3 +137,15 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         pk.pa_slot_mapping(torch.zeros(2, 4, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                            torch.zeros(3, dtype=torch.int32), 2)
+
+
+def test_timing_calls_without_a_gpu(lib):
+    """The timing switch and readout work on the host; nothing was launched, so nothing is counted."""
+    n, ms = ctypes.c_int64(-1), ctypes.c_double(-1.0)
+    assert lib.pa_timing_enable(1) == 0
+    assert lib.pa_timing_reset() == 0
+    assert lib.pa_timing_read(2, ctypes.byref(n), ctypes.byref(ms)) == 0
+    assert n.value == 0 and ms.value == 0.0
+    assert lib.pa_timing_read(99, ctypes.byref(n), ctypes.byref(ms)) == 2
+    assert lib.pa_timing_read(2, None, None) == 1
+    assert lib.pa_timing_enable(0) == 0
