@@ -223,7 +223,8 @@ typedef enum pa_kernel {
   PA_K_RESHAPE_AND_CACHE = 1, /* pa_reshape_and_cache, pa_reshape_and_cache_fp8 */
   PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode, pa_decode_fp8, decode rows of pa_prefill_varlen) */
   PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
-  PA_K_PREFILL = 4          /* the varlen prefill kernel */
+  PA_K_PREFILL = 4,         /* the varlen prefill kernel */
+  PA_K_PREFILL_MERGE = 5    /* the log-sum-exp merge of split prefill row tiles */
 } pa_kernel_t;
 
 pa_status_t pa_timing_enable(int on);

@@ -390,20 +390,32 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
 
 namespace {
 
+// Host plan of a flattened batch ([P2]'s ahead-of-time scheduling: the control
+// plane knows query_start_loc and seq_lens).  Decode rows (q_len == 1) go to the
+// decode kernels.  Chunks are cut into row tiles of 256 / G positions x G q
+// heads; a row tile needs ceil((c + last position + 1) / 64) key tiles.  The
+// key tiles of all row tiles are shared out so that about one work-group per
+// compute unit is busy: a row tile longer than the per-item budget is split
+// into near-equal key ranges whose partial results a merge kernel combines.
 struct VarlenPlan {
   int max_decode_len = 0;        // longest sequence with q_len == 1 (0: none)
   bool any_decode = false;
-  std::vector<uint32_t> items;   // prefill work items, longest first
+  int tile_positions = 0;
+  std::vector<uint64_t> items;   // split pieces first (grouped by row tile), then whole row tiles
+  std::vector<uint64_t> merges;  // one per split row tile
+  int n_split_items = 0;         // items that leave partial results (slots 0 .. n_split_items-1)
 };
 
 pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_tokens, int bt_stride,
-                        VarlenPlan& plan) {
+                        int group, int num_kv_heads, VarlenPlan& plan) {
   if (qsl[0] != 0) return fail(PA_ERR_SHAPE, "query_start_loc_host[0] = %d, expected 0", qsl[0]);
-  struct Item {
-    int64_t cost;
-    uint32_t code;
+  const int P = pa::kPrefillRows / group;
+  plan.tile_positions = P;
+  struct RowTile {
+    int s, rt, n_kt;
   };
-  std::vector<Item> items;
+  std::vector<RowTile> tiles;
+  int64_t total = 0;
   for (int s = 0; s < num_seqs; ++s) {
     const int q_len = qsl[s + 1] - qsl[s];
     if (q_len < 1) return fail(PA_ERR_SHAPE, "sequence %d has q_len %d < 1", s, q_len);
@@ -415,20 +427,72 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
       plan.max_decode_len = std::max(plan.max_decode_len, (int)sl[s]);
       continue;
     }
-    const int tiles = ceil_div(q_len, pa::kPrefillRows);
-    if (s >= (1 << 20) || tiles > 4096) return fail(PA_ERR_UNSUPPORTED, "batch too large for the prefill planner");
     const int c = sl[s] - q_len;
-    for (int t = 0; t < tiles; ++t) {
-      const int r_end = std::min(q_len, (t + 1) * pa::kPrefillRows);
-      items.push_back({(int64_t)(c + r_end), ((uint32_t)s << 12) | (uint32_t)t});
+    const int n_rt = ceil_div(q_len, P);
+    if (s >= (1 << 15) || n_rt >= (1 << 16) || ceil_div(sl[s], pa::kPrefillKeys) >= (1 << 16))
+      return fail(PA_ERR_UNSUPPORTED, "batch too large for the prefill planner");
+    for (int rt = 0; rt < n_rt; ++rt) {
+      const int pos_end = std::min(q_len, (rt + 1) * P);
+      const int n_kt = ceil_div(c + pos_end, pa::kPrefillKeys);
+      tiles.push_back({s, rt, n_kt});
+      total += n_kt;
     }
   }
   if (qsl[num_seqs] != num_tokens)
     return fail(PA_ERR_SHAPE, "query_start_loc_host[num_seqs] = %d != num_tokens %d", qsl[num_seqs], num_tokens);
-  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
-  plan.items.reserve(items.size());
-  for (const Item& it : items) plan.items.push_back(it.code);
+  if (tiles.empty()) return PA_OK;
+  // one work-group per compute unit: the smallest per-item budget (>= 4 key tiles) whose
+  // pieces, ceil(n_kt / budget) per row tile, number at most target_items
+  const int64_t target_items = std::max<int64_t>(1, device_cu_count() / std::max(1, num_kv_heads));
+  int budget = (int)std::max<int64_t>(4, (total + target_items - 1) / target_items);
+  for (;;) {
+    int64_t n = 0;
+    for (const RowTile& t : tiles) n += ceil_div(t.n_kt, budget);
+    if (n <= target_items || budget >= (1 << 16)) break;
+    ++budget;
+  }
+  // longest row tiles first
+  std::stable_sort(tiles.begin(), tiles.end(), [](const RowTile& a, const RowTile& b) { return a.n_kt > b.n_kt; });
+  auto code = [](int s, bool whole, int rt, int k0, int k1) {
+    return (uint64_t)s | ((uint64_t)whole << 15) | ((uint64_t)rt << 16) | ((uint64_t)k0 << 32) | ((uint64_t)k1 << 48);
+  };
+  std::vector<uint64_t> whole_items;
+  for (const RowTile& t : tiles) {
+    const int n = ceil_div(t.n_kt, budget);
+    if (n <= 1) {
+      whole_items.push_back(code(t.s, true, t.rt, 0, t.n_kt));
+      continue;
+    }
+    const int first = (int)plan.items.size();
+    if (first + n >= (1 << 20) || n >= (1 << 12)) return fail(PA_ERR_UNSUPPORTED, "too many prefill splits");
+    for (int i = 0; i < n; ++i)
+      plan.items.push_back(code(t.s, false, t.rt, (int)((int64_t)t.n_kt * i / n), (int)((int64_t)t.n_kt * (i + 1) / n)));
+    plan.merges.push_back((uint64_t)t.s | ((uint64_t)t.rt << 16) | ((uint64_t)first << 32) | ((uint64_t)n << 52));
+  }
+  plan.n_split_items = (int)plan.items.size();
+  plan.items.insert(plan.items.end(), whole_items.begin(), whole_items.end());
   return PA_OK;
+}
+
+// Prefill scratch: partial results of split row-tile pieces, after the decode rows' scratch.
+struct PrefillLayout {
+  size_t o_bytes, m_bytes, total;
+};
+
+PrefillLayout prefill_layout(int n_split_items, int num_kv_heads, int head_dim) {
+  const size_t rows = (size_t)n_split_items * num_kv_heads * pa::kPrefillRows;
+  PrefillLayout L;
+  L.o_bytes = align_up(rows * head_dim * sizeof(float));
+  L.m_bytes = align_up(rows * sizeof(float));
+  L.total = n_split_items ? L.o_bytes + 2 * L.m_bytes : 0;
+  return L;
+}
+
+size_t varlen_workspace(const VarlenPlan& plan, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim) {
+  const size_t dec = plan.max_decode_len
+                         ? pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, plan.max_decode_len, 0)
+                         : 0;
+  return align_up(dec) + prefill_layout(plan.n_split_items, num_kv_heads, head_dim).total;
 }
 
 }  // namespace
@@ -436,15 +500,17 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
 size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
                                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim) {
-  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGroup)
     return 0;
-  int max_dec = 0;
-  for (int s = 0; s < num_seqs; ++s) {
-    const int q_len = query_start_loc_host[s + 1] - query_start_loc_host[s];
-    if (q_len == 1) max_dec = std::max(max_dec, (int)seq_lens_host[s]);
-  }
-  if (max_dec == 0) return 0;
-  return pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_dec, 0);
+  VarlenPlan plan;
+  const std::string saved = g_last_error;
+  const int num_tokens = query_start_loc_host[num_seqs];
+  const pa_status_t st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, INT32_MAX,
+                                     num_q_heads / num_kv_heads, num_kv_heads, plan);
+  g_last_error = saved;
+  if (st != PA_OK) return 0;
+  return varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
 }
 
 pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -466,12 +532,12 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
     return fail(PA_ERR_UNSUPPORTED, "up to %d q heads per kv head", pa::kMaxGroup);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
   VarlenPlan plan;
-  st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride, plan);
+  st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
+                   num_q_heads / num_kv_heads, num_kv_heads, plan);
   if (st != PA_OK) return st;
   if (dtype == PA_F32 && !plan.items.empty())
     return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
-  const size_t need = pa_prefill_varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads,
-                                                        num_kv_heads, head_dim);
+  const size_t need = varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
   if (need && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
@@ -497,6 +563,14 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                     hs);
     if (st != PA_OK) return st;
   }
+  auto* ws = static_cast<unsigned char*>(workspace);
+  const size_t dec_bytes = plan.max_decode_len ? align_up(pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                                                    head_dim, plan.max_decode_len, 0))
+                                               : 0;
+  const PrefillLayout lay = prefill_layout(plan.n_split_items, num_kv_heads, head_dim);
+  float* part_o = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes) : nullptr;
+  float* part_m = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes) : nullptr;
+  float* part_l = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + lay.m_bytes) : nullptr;
   for (size_t i0 = 0; i0 < plan.items.size(); i0 += pa::kMaxPrefillItems) {
     pa::PrefillParams p{};
     p.out = out;
@@ -506,17 +580,39 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
     p.block_tables = block_tables;
     p.seq_lens = seq_lens;
     p.qsl = query_start_loc;
+    p.part_o = part_o;
+    p.part_m = part_m;
+    p.part_l = part_l;
     p.bt_stride = bt_stride;
     p.num_tokens = num_tokens;
     p.num_q_heads = num_q_heads;
     p.num_kv_heads = num_kv_heads;
     p.group = num_q_heads / num_kv_heads;
     p.num_blocks = num_blocks;
+    p.tile_positions = plan.tile_positions;
+    p.item_base = (int)i0;
     p.scale_log2 = scale * 1.4426950408889634f;
     const size_t n = std::min(plan.items.size() - i0, (size_t)pa::kMaxPrefillItems);
     p.n_items = (int)n;
-    std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint32_t));
+    std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint64_t));
     st = hip_status(pa::launch_prefill(p, head_dim, hs), "prefill launch");
+    if (st != PA_OK) return st;
+  }
+  for (size_t i0 = 0; i0 < plan.merges.size(); i0 += pa::kMaxPrefillItems) {
+    pa::PrefillMergeParams p{};
+    p.out = out;
+    p.qsl = query_start_loc;
+    p.part_o = part_o;
+    p.part_m = part_m;
+    p.part_l = part_l;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
+    p.tile_positions = plan.tile_positions;
+    const size_t n = std::min(plan.merges.size() - i0, (size_t)pa::kMaxPrefillItems);
+    p.n_items = (int)n;
+    std::memcpy(p.items, plan.merges.data() + i0, n * sizeof(uint64_t));
+    st = hip_status(pa::launch_prefill_merge(p, head_dim, hs), "prefill merge launch");
     if (st != PA_OK) return st;
   }
   return ok();

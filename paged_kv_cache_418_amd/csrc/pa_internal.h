@@ -9,9 +9,9 @@ namespace pa {
 constexpr int kBlockSize = 16;      // tokens per physical block
 constexpr int kDecodeWaves = 4;     // waves per decode work-group
 constexpr int kMaxGroup = 16;       // q heads per kv head handled by one MFMA column set
-constexpr int kPrefillRows = 128;   // query rows per prefill work-group (4 waves x 32)
+constexpr int kPrefillRows = 256;   // (position, q head) rows per prefill work-group (4 waves x 64)
 constexpr int kPrefillKeys = 64;    // keys per LDS tile in prefill
-constexpr int kMaxPrefillItems = 640;
+constexpr int kMaxPrefillItems = 480;  // work items per launch (kernel-argument space)
 
 enum Dtype { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
@@ -47,6 +47,10 @@ struct DecodeParams {
   int q_f32;                 // query / output are fp32 (else bf16)
 };
 
+// One prefill launch: grid (n_items, num_kv_heads).  Item bits: sequence (15),
+// whole-row-tile flag (1), row tile (16), first key tile (16), end key tile (16).
+// Items that cover only part of their row tile's key tiles come first in the
+// plan; their partial results live in slot item_base + blockIdx.x.
 struct PrefillParams {
   void* out;
   const void* query;
@@ -55,21 +59,49 @@ struct PrefillParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const int32_t* qsl;
+  float* part_o;             // [slots][num_kv_heads][256 rows][D] unnormalised partial outputs
+  float* part_m;             // [slots][num_kv_heads][256 rows] reference maximum (log2 units)
+  float* part_l;             // [slots][num_kv_heads][256 rows] sum of weights
   int bt_stride;
   int num_tokens;
   int num_q_heads;
   int num_kv_heads;
   int group;
   int num_blocks;
+  int tile_positions;        // positions per row tile: 256 / group
+  int item_base;
   float scale_log2;
   int n_items;
-  // work items: (sequence << 12) | query tile; ordered longest first
-  uint32_t items[kMaxPrefillItems];
+  uint64_t items[kMaxPrefillItems];
+};
+
+// Merge of split row tiles: grid (n_items, num_kv_heads).  Item bits: sequence
+// (16), row tile (16), first slot (20), number of slots (12).
+struct PrefillMergeParams {
+  void* out;
+  const int32_t* qsl;
+  const float* part_o;
+  const float* part_m;
+  const float* part_l;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int tile_positions;
+  int n_items;
+  uint64_t items[kMaxPrefillItems];
 };
 
 // Optional kernel timing (pa_timing_enable): a launch site brackets its
 // kernel with timing_mark(id, true/false, stream); a no-op unless enabled.
-enum KernelId { kKSlotMapping = 0, kKReshape = 1, kKDecode = 2, kKDecodeMerge = 3, kKPrefill = 4, kNumKernelIds = 5 };
+enum KernelId {
+  kKSlotMapping = 0,
+  kKReshape = 1,
+  kKDecode = 2,
+  kKDecodeMerge = 3,
+  kKPrefill = 4,
+  kKPrefillMerge = 5,
+  kNumKernelIds = 6
+};
 void timing_mark(int kernel, bool begin, hipStream_t stream);
 
 hipError_t launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int bt_stride,
@@ -91,5 +123,6 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int6
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace pa

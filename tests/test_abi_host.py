@@ -127,9 +127,17 @@ def test_prefill_rejects(lib):
 def test_prefill_workspace_bytes(lib):
     q, s = _host_i32([0, 1, 2, 514]), _host_i32([1000, 10, 700])
     got = lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128)
-    assert got == pk.pa_decode_workspace_bytes(3, 32, 8, 128, 1000, 0) > 0
-    q2, s2 = _host_i32([0, 512]), _host_i32([700])
+    dec = pk.pa_decode_workspace_bytes(3, 32, 8, 128, 1000, 0)
+    assert dec > 0 and got > dec  # decode rows' scratch, then partial results of split prefill row tiles
+    # decode rows only: exactly the decode scratch
+    q1, s1 = _host_i32([0, 1, 2]), _host_i32([1000, 10])
+    assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q1), ctypes.addressof(s1), 2, 32, 8, 128) == \
+        pk.pa_decode_workspace_bytes(2, 32, 8, 128, 1000, 0)
+    # one short chunk (64 positions x 4 heads after 0 cached tokens: 1 key tile) needs no scratch
+    q2, s2 = _host_i32([0, 64]), _host_i32([64])
     assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 32, 8, 128) == 0
+    # invalid grouping
+    assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 30, 8, 128) == 0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -271,3 +271,21 @@ def test_prefill_whole_prompt_equals_chunks_and_decode():
     dec = pk.pa_decode(d.query[L - 1:L].contiguous(), d.k_cache, d.v_cache, d.block_tables,
                        torch.tensor([L], dtype=torch.int32).cuda(), w.scale, L).float().cpu()
     assert torch.max(torch.abs(dec[0] - whole[L - 1])).item() < 1.5e-2
+
+
+@pytest.mark.parametrize("heads", [(32, 8, 128), (16, 1, 64), (12, 4, 128), (48, 3, 128)])
+def test_prefill_long_chunks_split_across_work_items(heads):
+    """Long chunks after long cached prefixes: row tiles cut into several key ranges and merged; GQA groups of
+    16, 3 and 4 (row tiles that leave padding rows); a decode row and a short chunk in the same batch."""
+    Hq, Hkv, D = heads
+    w = wl.build("prefill_long", seed=431, ctx_lens=[2200, 700, 35, 1900], q_lens=[700, 1, 35, 333],
+                 num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype="bf16", kv_dtype="bf16")
+    say("prefill long chunks", heads)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"]
