@@ -524,63 +524,52 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
   });
 }
 
-// Log-sum-exp merge of the pieces of a sequence: one work-group of 256
-// threads per (q head, sequence); the 4 waves take every 4th piece, then
-// combine.  Pieces of sequence s come from shares first..last and have ids
-// share + s.  Sequences held by a single share were finished in place.
+// Log-sum-exp merge of the pieces of a sequence: one wave per (q head,
+// sequence), four per work-group, lanes over d.  Pieces of sequence s come
+// from shares first..last and have ids share + s; the merge runs online over
+// them (running maximum, weight sum and output), so the loads of later pieces
+// do not wait for earlier ones.  Sequences held by a single share were
+// finished in place.
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
   constexpr int PER_LANE = D / 64;
-  __shared__ float red_m[4], red_l[4];
-  __shared__ float red_o[4][D];
-  const int s = blockIdx.y, h = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + wave, s = blockIdx.y;
+  if (h >= p.num_q_heads) return;
   if (decode_blocks(p, s) == 0) return;
   const int first = p.piece_first[s], last = p.piece_last[s];
   if (first >= last) return;
   const int row = p.qsl ? p.qsl[s] : s;
-  const int n = last - first + 1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t base = (size_t)(first + s) * p.num_q_heads + h;  // piece i: base + i * num_q_heads
   const size_t step = (size_t)p.num_q_heads;
-
-  float M = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, p.part_m[base + i * step]);
+  const size_t base = (size_t)(first + s) * step + h;  // piece i: base + i * num_q_heads
+  float M = -INFINITY, den = 0.f, o[PER_LANE];
 #pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, shfl_xor(M, msk));
-  if (lane == 0) red_m[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
-  float o[PER_LANE];
-#pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
-  float den = 0.f;
+  for (int k = 0; k < PER_LANE; ++k) o[k] = 0.f;
 #pragma unroll 4
-  for (int i = wave; i < n; i += 4) {
+  for (int i = 0; i <= last - first; ++i) {
     const size_t pi = base + i * step;
-    const float w = fast_exp2(p.part_m[pi] - M);
-    den += w * p.part_l[pi];
-    const float* src = p.part_o + pi * D + lane * PER_LANE;
+    const float mi = p.part_m[pi], li = p.part_l[pi];
+    float src[PER_LANE];
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) o[k] += w * src[k];
+    for (int k = 0; k < PER_LANE; ++k) src[k] = p.part_o[pi * D + lane * PER_LANE + k];
+    const float Mn = fmaxf(M, mi);
+    const float a = fast_exp2(M - Mn), b = fast_exp2(mi - Mn);
+    den = den * a + li * b;
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) o[k] = o[k] * a + src[k] * b;
+    M = Mn;
   }
-  if (lane == 0) red_l[wave] = den;
+  const float inv = p.v_scale / den;
+  const size_t oi = ((size_t)row * p.num_q_heads + h) * D + lane * PER_LANE;
+  if (p.q_f32) {
 #pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) red_o[wave][lane * PER_LANE + i] = o[i];
-  __syncthreads();
-  if (wave == 0) {
-    const float dsum = red_l[0] + red_l[1] + red_l[2] + red_l[3];
-    const float inv = p.v_scale / dsum;
+    for (int k = 0; k < PER_LANE; ++k) reinterpret_cast<float*>(p.out)[oi + k] = o[k] * inv;
+  } else if constexpr (PER_LANE == 1) {
+    reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(o[0] * inv);
+  } else {
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-      const int d = lane * PER_LANE + i;
-      const float val = (red_o[0][d] + red_o[1][d] + red_o[2][d] + red_o[3][d]) * inv;
-      const size_t oi = ((size_t)row * p.num_q_heads + h) * D + d;
-      if (p.q_f32)
-        reinterpret_cast<float*>(p.out)[oi] = val;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(val);
-    }
+    for (int k = 0; k < PER_LANE; k += 2)
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.out) + oi + k) = pack_bf16x2(o[k] * inv, o[k + 1] * inv);
   }
 }
 
@@ -598,7 +587,7 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits <= 1) return e;
   timing_mark(kKDecodeMerge, true, stream);
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.num_q_heads, p.num_seqs), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((p.num_q_heads + 3) / 4, p.num_seqs), dim3(256), 0, stream, p);
   timing_mark(kKDecodeMerge, false, stream);
   return hipGetLastError();
 }
