@@ -27,6 +27,8 @@
 // item may cover only a range of key tiles (a split of a long row tile); it
 // then leaves (O, m, l) for the merge kernel, which combines the splits with
 // the log-sum-exp rule.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -42,8 +44,12 @@ struct PrefillShape {
   static constexpr int kRowBytes = D * 2;              // one key row of a tile
   static constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row (the swizzle period)
   static constexpr int kTileBytes = kKeys * kRowBytes; // one tensor of one tile
-  static constexpr int kStageBytes = 2 * kTileBytes;   // K then V
-  static constexpr int kStages = 4;
+  static constexpr int kKSlots = 4;                    // K ring: K(t+3) is copied at step t
+  static constexpr int kVSlots = 3;                    // row-major V ring: V(t+3) copied at step t
+  static constexpr int kVtSlots = 3;                   // V^T ring (64 keys x D, 128-byte rows)
+  static constexpr int kVtRowBytes = kKeys * 2;        // one d row of a V^T tile
+  static constexpr int kTransposes = D / 32;           // 512-byte transposing reads per wave per tile
+  static constexpr int kLdsBytes = (kKSlots + kVSlots + kVtSlots) * kTileBytes;
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;           // rows one wave-wide 1 KB copy fills
   static constexpr int kCopies = kTileBytes / 1024 / kWaves;      // copies per wave per tensor per tile
   static constexpr int kKSteps = D / 16;               // 32x32x16 MFMAs over d
@@ -65,6 +71,14 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 #define PA_LDS __attribute__((address_space(3)))
 #define PA_GLOBAL __attribute__((address_space(1)))
 
@@ -74,6 +88,13 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt field");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Same, and also waits for all of this wave's LDS (and scalar-memory) operations.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
 template <int D>
@@ -122,32 +143,46 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   const int lanes_per_row = Sh::kChunks;
   const int copy_row0 = Sh::kRowsPerCopy * Sh::kCopies * wave;  // first row of this wave's slabs
   const int bt0 = min(max(bt[0], 0), p.num_blocks - 1);          // block of key 0 (always written)
-  auto block_of = [&](int tile) {  // physical block of this wave's rows of a tile
-    const int key = tile * Sh::kKeys + copy_row0;
-    return key < kv_end ? bt[key >> 4] : bt0;
-  };
+  // Physical block of this wave's rows of a tile.  The load is unconditional (a key past
+  // the last visible one reads the last visible key's entry, whose rows are then replaced
+  // by key 0's), so the compiler can count it among the loads in flight.
+  auto block_of = [&](int tile) { return bt[min(tile * Sh::kKeys + copy_row0, kv_end - 1) >> 4]; };
   // Rows past the last visible key copy the row of key 0 (written and finite): their
   // scores are masked and their probabilities are 0, so pool data there is never used.
-  auto copy_tile = [&](int tile, int phys, int stage) {
+  // Slab i (0 .. kCopies-1) of this wave's part of one tensor of a tile.
+  auto copy_slab = [&](const uint8_t* base, int tile, int phys, unsigned char* st, int i) {
     phys = min(max(phys, 0), p.num_blocks - 1);
-    unsigned char* st = smem + stage * Sh::kStageBytes;
+    const int row = copy_row0 + Sh::kRowsPerCopy * i + lane / lanes_per_row;
+    const int slot = lane % lanes_per_row;
+    const int chunk = slot ^ (row % Sh::kChunks);
+    const int key = tile * Sh::kKeys + row;
+    const bool live = key < kv_end;
+    const int ph = live ? phys : bt0;
+    const size_t off = ((size_t)ph * 16 + (live ? (key & 15) : 0)) * tok_stride + (size_t)kvh * D * 2 + chunk * 16;
+    unsigned char* dst = st + (copy_row0 + Sh::kRowsPerCopy * i) * Sh::kRowBytes;
+    __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(base + off), (void PA_LDS*)dst, 16, 0, 0);
+  };
+  auto copy_rows = [&](const uint8_t* base, int tile, int phys, unsigned char* st) {
 #pragma unroll
-    for (int i = 0; i < Sh::kCopies; ++i) {
-      const int row = copy_row0 + Sh::kRowsPerCopy * i + lane / lanes_per_row;
-      const int slot = lane % lanes_per_row;
-      const int chunk = slot ^ (row % Sh::kChunks);
-      const int key = tile * Sh::kKeys + row;
-      const bool live = key < kv_end;
-      const int ph = live ? phys : bt0;
-      const size_t off = ((size_t)ph * 16 + (live ? (key & 15) : 0)) * tok_stride + (size_t)kvh * D * 2 + chunk * 16;
-      unsigned char* dst = st + (copy_row0 + Sh::kRowsPerCopy * i) * Sh::kRowBytes;
-      __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(kbase + off), (void PA_LDS*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(vbase + off), (void PA_LDS*)(dst + Sh::kTileBytes), 16,
-                                       0, 0);
-    }
+    for (int i = 0; i < Sh::kCopies; ++i) copy_slab(base, tile, phys, st, i);
+  };
+  // LDS: a ring of four K tiles (tile t in slot (t - kt0) % 4), a ring of three row-major
+  // V tiles and a ring of three transposed V tiles (tile t in slot (t - kt0) % 3).
+  auto k_stage = [&](int tile) { return smem + ((tile - kt0) & 3) * Sh::kTileBytes; };
+  auto v_stage = [&](int tile) { return smem + (Sh::kKSlots + (tile - kt0) % 3) * Sh::kTileBytes; };
+  auto k_addr = [&](int tile) { return (uint32_t)(uintptr_t)k_stage(tile); };
+  auto v_addr = [&](int tile) { return (uint32_t)(uintptr_t)v_stage(tile); };
+  auto vt_addr = [&](int tile) {
+    return (uint32_t)(uintptr_t)(smem + (Sh::kKSlots + Sh::kVSlots + (tile - kt0) % 3) * Sh::kTileBytes);
   };
 
-  // ---- Q^T operand: lane holds q[row rl][16*kk + 8*half .. +7]
+  // block ids of the first four tiles, read before Q so the first copies wait only for them
+  const int ph0 = block_of(kt0), ph1 = block_of(kt0 + 1), ph2 = block_of(kt0 + 2);
+  int phys_next = block_of(kt0 + 3);
+
+  // ---- Q^T operand: lane holds q[row rl][16*kk + 8*half .. +7].  A lane without a row
+  // (past the tile's last position) reads the sequence's first row instead; its results
+  // are never stored.  The loads are unconditional so that the wait below can count them.
   bf16x8 qf[Sh::kKSteps];
   {
     const int h = kvh * G + (R % G);
@@ -155,7 +190,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
                                                      ((size_t)(q0 + (row_ok ? pos0 + R / G : 0)) * p.num_q_heads +
                                                       (row_ok ? h : 0)) * D + 8 * half);
 #pragma unroll
-    for (int kk = 0; kk < Sh::kKSteps; ++kk) qf[kk] = u4_to_bf16x8(row_ok ? qp[2 * kk] : u32x4{0u, 0u, 0u, 0u});
+    for (int kk = 0; kk < Sh::kKSteps; ++kk) qf[kk] = u4_to_bf16x8(qp[2 * kk]);
   }
 
   f32x16 acc[Sh::kDTiles];
@@ -164,81 +199,210 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
   float m_ref = -INFINITY, lsum = 0.f;
+  // the score scale, waited for here so that no wait inside the tile loop is attributed to it
+  float scale_log2 = p.scale_log2;
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(scale_log2));
 
-  // S^T for both 32-key halves of a tile from an LDS stage: two independent MFMA chains.
-  auto scores = [&](f32x16 (&sacc)[2], int stage) {
-    const unsigned char* kl = smem + stage * Sh::kStageBytes;
+  // S^T for both 32-key halves of a tile from a K slot: two independent MFMA chains.  The
+  // lane's K row (key kt*32 + rl) is read in 16-byte chunks 2*kk + half, stored at chunk
+  // (2*kk + half) ^ (rl % kChunks) (32 % kChunks == 0).  Operands are read two k-steps
+  // before their MFMAs so the LDS latency hides behind the matrix cores; the reads are
+  // issued and waited for from asm, like the V reads below.
+  uint32_t koff[Sh::kKSteps];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < Sh::kKSteps; ++kk) {
+  for (int kk = 0; kk < Sh::kKSteps; ++kk)
+    koff[kk] = (uint32_t)(rl * Sh::kRowBytes + (((2 * kk + half) ^ (rl % Sh::kChunks)) << 4));
+  auto k_issue = [&](u32x4 (&x)[2], uint32_t base, auto kk_c) {
+    constexpr int KK = decltype(kk_c)::value;
+    const uint32_t a = base + koff[KK];
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:%3"
+        : "=&v"(x[0]), "=&v"(x[1])
+        : "v"(a), "i"(32 * Sh::kRowBytes)
+        : "memory");
+  };
+  auto k_wait = [&](u32x4 (&x)[2], auto n_c) {
+    constexpr int N = decltype(n_c)::value;
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(N) : "memory");
+  };
+  auto scores = [&](f32x16 (&sacc)[2], uint32_t kbase_lds) {
+    constexpr int kAhead = 2;
+    u32x4 kb[kAhead + 1][2];
+    static_for<0, kAhead>([&](auto kk_c) { k_issue(kb[decltype(kk_c)::value], kbase_lds, kk_c); });
+    static_for<0, Sh::kKSteps>([&](auto kk_c) {
+      constexpr int kk = decltype(kk_c)::value;
+      constexpr int nxt = kk + kAhead;
+      if constexpr (nxt < Sh::kKSteps) {
+        k_issue(kb[nxt % (kAhead + 1)], kbase_lds, std::integral_constant<int, nxt>{});
+        k_wait(kb[kk % (kAhead + 1)], std::integral_constant<int, 2 * kAhead>{});
+      } else {
+        k_wait(kb[kk % (kAhead + 1)], std::integral_constant<int, 2 * (Sh::kKSteps - 1 - kk)>{});
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int key = kt * 32 + rl;
-        const bf16x8 a = u4_to_bf16x8(
-            *reinterpret_cast<const u32x4*>(kl + key * Sh::kRowBytes + (((2 * kk + half) ^ (key % Sh::kChunks)) << 4)));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[kt], 0, 0, 0);
+        const f32x16 c = kk == 0 ? f32x16{} : sacc[kt];
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(kb[kk % (kAhead + 1)][kt]), qf[kk], c, 0, 0, 0);
       }
-    }
+    });
   };
 
-  // V^T operands of O^T += V^T P^T for the 16-key chunk ch, all d tiles n: lane (d = 32n +
-  // l%32, h = l/32) holds keys ch*16 + 4h + 0..3 and ch*16 + 8 + 4h + 0..3.  In each 16-lane
-  // group, ds_read_b64_tr_b16 gives output lane i element k = element i%4 of the 8 bytes
-  // addressed by lane 4k + i/4; so lane 4k + q addresses key kb + k, d 32n + 16*(group%2) + 4q.
-  // The reads are issued from one asm block that also waits for them, so the compiler does
-  // not hold them back behind the copies in flight (the barrier protocol already guarantees
-  // that the stage read here has landed).
-  const int tr_k = (lane & 15) >> 2, tr_q = lane & 3, tr_g = lane >> 4;
-  auto v_operands = [&](const unsigned char* vl, int ch, bf16x8 (&ops)[Sh::kDTiles]) {
-    uint32_t addr[Sh::kDTiles][2];
+  // ---- V^T tiles.  PV needs, per lane, 8 keys of one d in one register quad, while the
+  // pool (and the copied tile) holds rows of d for one key.  Each tile is transposed once
+  // in LDS: wave w turns kTransposes 16(d) x 16(key) blocks of the row-major tile into V^T
+  // rows with ds_read_b64_tr_b16 (in each 16-lane group, output lane i element k is
+  // element i%4 of the 8 bytes addressed by lane 4k + i/4: lane 4k + q addresses key
+  // kb + k at d d0 + 4q, so lane i receives keys kb..kb+3 of d d0 + i) and ds_write_b64.
+  // A V^T row (d) holds the 64 keys in 16-byte chunks 2*ch + h = keys ch*16 + 8*(j/4) +
+  // 4h + j%4, j = 0..7: the order in which the probabilities sit in the S^T registers, so
+  // the operand of chunk ch is one ds_read_b128.  Chunk c of row d is stored at c ^
+  // ((d >> 1) & 7) (rows are half a bank line: reads and writes are conflict-free).
+  constexpr int kTileQuad = Sh::kDTiles;  // V^T operand reads per chunk (one per 32-wide d tile)
+  uint32_t tr_src[Sh::kTransposes], tr_dst[Sh::kTransposes];
+  {
+    const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int n = 0; n < Sh::kDTiles; ++n)
+    for (int j = 0; j < Sh::kTransposes; ++j) {
+      const int blk = wave * Sh::kTransposes + j;  // (d block, key chunk) of the tile
+      const int dblk = blk >> 2, ch = blk & 3;
+      const int key = ch * 16 + 4 * g + (i >> 2);  // the key this lane addresses
+      const int byte = (16 * dblk + 4 * (i & 3)) * 2;
+      tr_src[j] = (uint32_t)(key * Sh::kRowBytes + ((((byte >> 4) ^ (key % Sh::kChunks)) << 4) | (byte & 15)));
+      const int d = 16 * dblk + i;  // the row this lane writes: keys ch*16 + 4g .. +3
+      tr_dst[j] = (uint32_t)(d * Sh::kVtRowBytes + ((((2 * ch + (g & 1)) ^ ((d >> 1) & 7))) << 4) + 8 * (g >> 1));
+    }
+  }
+  auto tr_addrs = [&](uint32_t (&a)[Sh::kTransposes], uint32_t base, const uint32_t (&off)[Sh::kTransposes]) {
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const int key = ch * 16 + 8 * w + 4 * (tr_g >> 1) + tr_k;
-        const int byte = (32 * n + 16 * (tr_g & 1) + 4 * tr_q) * 2;
-        const int phys = (((byte >> 4) ^ (key % Sh::kChunks)) << 4) | (byte & 15);
-        addr[n][w] = (uint32_t)(uintptr_t)(vl + key * Sh::kRowBytes + phys);
-      }
-    u32x2 part[Sh::kDTiles][2];
-    if constexpr (Sh::kDTiles == 4) {
+    for (int j = 0; j < Sh::kTransposes; ++j) a[j] = base + off[j];
+  };
+  // writes the transposed rows (the registers hold landed data)
+  auto tr_write = [&](const u32x2 (&x)[Sh::kTransposes], uint32_t dst) {
+    uint32_t w[Sh::kTransposes];
+    tr_addrs(w, dst, tr_dst);
+    if constexpr (Sh::kTransposes == 4) {
       asm volatile(
-          "ds_read_b64_tr_b16 %0, %8\n\t"
-          "ds_read_b64_tr_b16 %1, %9\n\t"
-          "ds_read_b64_tr_b16 %2, %10\n\t"
-          "ds_read_b64_tr_b16 %3, %11\n\t"
-          "ds_read_b64_tr_b16 %4, %12\n\t"
-          "ds_read_b64_tr_b16 %5, %13\n\t"
-          "ds_read_b64_tr_b16 %6, %14\n\t"
-          "ds_read_b64_tr_b16 %7, %15\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(part[0][0]), "=&v"(part[0][1]), "=&v"(part[1][0]), "=&v"(part[1][1]), "=&v"(part[2][0]),
-            "=&v"(part[2][1]), "=&v"(part[3][0]), "=&v"(part[3][1])
-          : "v"(addr[0][0]), "v"(addr[0][1]), "v"(addr[1][0]), "v"(addr[1][1]), "v"(addr[2][0]), "v"(addr[2][1]),
-            "v"(addr[3][0]), "v"(addr[3][1])
+          "ds_write_b64 %0, %4\n\t"
+          "ds_write_b64 %1, %5\n\t"
+          "ds_write_b64 %2, %6\n\t"
+          "ds_write_b64 %3, %7"
+          :
+          : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3])
           : "memory");
     } else {
+      asm volatile(
+          "ds_write_b64 %0, %2\n\t"
+          "ds_write_b64 %1, %3"
+          :
+          : "v"(w[0]), "v"(w[1]), "v"(x[0]), "v"(x[1])
+          : "memory");
+    }
+  };
+  // the whole transposition of this wave's blocks of a tile, reads waited for at once
+  auto transpose = [&](uint32_t src, uint32_t dst) {
+    u32x2 x[Sh::kTransposes];
+    uint32_t a[Sh::kTransposes];
+    tr_addrs(a, src, tr_src);
+    if constexpr (Sh::kTransposes == 4) {
       asm volatile(
           "ds_read_b64_tr_b16 %0, %4\n\t"
           "ds_read_b64_tr_b16 %1, %5\n\t"
           "ds_read_b64_tr_b16 %2, %6\n\t"
           "ds_read_b64_tr_b16 %3, %7\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=&v"(part[0][0]), "=&v"(part[0][1]), "=&v"(part[1][0]), "=&v"(part[1][1])
-          : "v"(addr[0][0]), "v"(addr[0][1]), "v"(addr[1][0]), "v"(addr[1][1])
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %2\n\t"
+          "ds_read_b64_tr_b16 %1, %3\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1])
+          : "v"(a[0]), "v"(a[1])
           : "memory");
     }
+    tr_write(x, dst);
+  };
+  // lane (d = 32n + rl, h = half) reads chunk 2*ch + h of V^T row d: offset vt_off[ch] + n*32 rows
+  uint32_t vt_off[4];
 #pragma unroll
-    for (int n = 0; n < Sh::kDTiles; ++n)
-      ops[n] = __builtin_bit_cast(bf16x8, u32x4{part[n][0].x, part[n][0].y, part[n][1].x, part[n][1].y});
+  for (int ch = 0; ch < 4; ++ch)
+    vt_off[ch] = (uint32_t)(rl * Sh::kVtRowBytes + (((2 * ch + half) ^ ((rl >> 1) & 7)) << 4));
+  // issue (no wait) the V^T operand reads of one chunk; vt_wait waits for them and hands the
+  // registers on.  Issued from asm: the compiler would otherwise wait for every LDS copy in
+  // flight before an LDS read it cannot tell apart from them.
+  auto vt_issue = [&](u32x4 (&x)[kTileQuad], uint32_t base) {
+    constexpr int kRows32 = 32 * Sh::kVtRowBytes;
+    if constexpr (kTileQuad == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:%5\n\t"
+          "ds_read_b128 %2, %4 offset:%6\n\t"
+          "ds_read_b128 %3, %4 offset:%7"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+          : "v"(base), "i"(kRows32), "i"(2 * kRows32), "i"(3 * kRows32)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b128 %1, %2 offset:%3"
+          : "=&v"(x[0]), "=&v"(x[1])
+          : "v"(base), "i"(kRows32)
+          : "memory");
+    }
+  };
+  auto vt_wait = [&](u32x4 (&x)[kTileQuad], auto n_c) {
+    constexpr int N = decltype(n_c)::value;
+    if constexpr (kTileQuad == 4) {
+      asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(N) : "memory");
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(N) : "memory");
+    }
+  };
+  // the V^T reads of the last chunk plus this wave's transposing reads of the next tile
+  auto vt_issue_tr = [&](u32x4 (&x)[kTileQuad], uint32_t base, u32x2 (&t)[Sh::kTransposes], uint32_t src) {
+    constexpr int kRows32 = 32 * Sh::kVtRowBytes;
+    uint32_t a[Sh::kTransposes];
+    tr_addrs(a, src, tr_src);
+    if constexpr (kTileQuad == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %8 offset:%13\n\t"
+          "ds_read_b128 %2, %8 offset:%14\n\t"
+          "ds_read_b128 %3, %8 offset:%15\n\t"
+          "ds_read_b64_tr_b16 %4, %9\n\t"
+          "ds_read_b64_tr_b16 %5, %10\n\t"
+          "ds_read_b64_tr_b16 %6, %11\n\t"
+          "ds_read_b64_tr_b16 %7, %12"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+          : "v"(base), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(kRows32), "i"(2 * kRows32), "i"(3 * kRows32)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:%7\n\t"
+          "ds_read_b64_tr_b16 %2, %5\n\t"
+          "ds_read_b64_tr_b16 %3, %6"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(t[0]), "=&v"(t[1])
+          : "v"(base), "v"(a[0]), "v"(a[1]), "i"(kRows32)
+          : "memory");
+    }
+  };
+  auto vt_wait_tr = [&](u32x4 (&x)[kTileQuad], u32x2 (&t)[Sh::kTransposes]) {
+    if constexpr (kTileQuad == 4) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
+                   :
+                   : "memory");
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(t[0]), "+v"(t[1]) : : "memory");
+    }
   };
 
-  // Online softmax of one tile's scores and O^T += V^T P^T with V from an LDS stage.
-  auto softmax_pv = [&](f32x16 (&sacc)[2], int key0, int stage) {
-    const unsigned char* vl = smem + stage * Sh::kStageBytes + Sh::kTileBytes;
+  // Online softmax of one tile's scores: P = exp2(s*scale - m) packed to bf16 in pw[chunk]
+  // (16-key chunk ch = 2*half32 + cc), l and the reference maximum m updated.
+  auto softmax = [&](f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4]) {
     // lane's entries: key key0 + kt*32 + 8*(r/4) + 4*half + r%4 of row rl.  Raw scores are
     // masked and maximised; the scale (> 0) is applied inside exp2(fma(s, scale, -m)).
     if (key0 + Sh::kKeys - 1 > wave_first) {
@@ -255,7 +419,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sacc[kt][r]);
-    bmax = max_halves(bmax) * p.scale_log2;
+    bmax = max_halves(bmax) * scale_log2;
     // move the reference maximum only when it is exceeded by more than 8 (log2 units)
     const bool need = bmax > m_ref + 8.f;
     if (__any(need)) {
@@ -267,73 +431,141 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
       m_ref = mnew;
     }
     const float msub = m_ref == -INFINITY ? 0.f : m_ref;
-    // per half: P = exp2(s*scale - m) packed to bf16, then O^T += V^T P^T over its two
-    // 16-key chunks; the second half's exponentials overlap the first half's MFMAs
+    float ps = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      u32x4 pw[2];
-      float ps = 0.f;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[kt][8 * cc + 2 * j], p.scale_log2, -msub));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[kt][8 * cc + 2 * j + 1], p.scale_log2, -msub));
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kt][8 * cc + 2 * j], scale_log2, -msub));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kt][8 * cc + 2 * j + 1], scale_log2, -msub));
           ps += p0 + p1;
-          pw[cc][j] = pack_bf16x2(p0, p1);
+          pw[2 * kt + cc][j] = pack_bf16x2(p0, p1);
         }
-      lsum += ps;
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ch = 2 * kt + cc;
-        const bf16x8 pb = u4_to_bf16x8(pw[cc]);
-        // logical k = 8*half + j  <->  key ch*16 + 8*(j/4) + 4*half + j%4
-        bf16x8 va[Sh::kDTiles];
-        v_operands(vl, ch, va);
-#pragma unroll
-        for (int n = 0; n < Sh::kDTiles; ++n)
-          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[n], pb, acc[n], 0, 0, 0);
-      }
-    }
+    lsum += ps;
   };
 
-  // Pipeline over the item's key tiles t = kt0 .. kt1-1 (stage of tile t: (t - kt0) % 4).
-  // Step t: read the block id of tile t+4, start the copy of tile t+3; the scores of tile
-  // t+1 go to the matrix cores while the softmax of tile t runs, then O += V P for tile t;
-  // finally wait for the copy of tile t+2 (started one step ago) and meet at a barrier.
-  // Vector-memory instructions retire in order and the last ones a step issues are its
-  // 2*kCopies copies, so "everything older than this step's copies has landed" is
-  // vmcnt <= 2*kCopies.  Each block id is read before the copies of its step, so consuming
-  // it never waits for copies still in flight.  Tiles past the item's range are copied too
-  // (valid rows, never used) so that every step is alike.
+  // O^T += V^T P^T for one tile, V^T from the slot at byte address vtbase.  The reads of
+  // chunk ch+1 are in flight while the MFMAs of chunk ch run; between(ch) is called after
+  // they are issued (the copies of the step go there, spread over the matrix-core work
+  // instead of stalling the wave at once).  The wave's share of the transposition of the
+  // next tile (row-major slot tr_from -> V^T slot tr_to) rides along: its reads are issued
+  // with the last chunk's and its rows written after the last MFMAs.
+  auto pv = [&](const u32x4 (&pw)[4], uint32_t vtbase, auto&& between, uint32_t tr_from, uint32_t tr_to) {
+    u32x4 vb[2][kTileQuad];
+    u32x2 tx[Sh::kTransposes];
+    vt_issue(vb[0], vtbase + vt_off[0]);
+    static_for<0, 4>([&](auto ch_c) {
+      constexpr int ch = decltype(ch_c)::value;
+      if constexpr (ch + 2 < 4) {
+        vt_issue(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1]);
+        between(ch);
+        vt_wait(vb[ch & 1], std::integral_constant<int, kTileQuad>{});
+      } else if constexpr (ch + 1 < 4) {
+        vt_issue_tr(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1], tx, tr_from);
+        between(ch);
+        vt_wait(vb[ch & 1], std::integral_constant<int, kTileQuad + Sh::kTransposes>{});
+      } else {
+        between(ch);
+        vt_wait_tr(vb[ch & 1], tx);
+      }
+      const bf16x8 pb = u4_to_bf16x8(pw[ch]);
+#pragma unroll
+      for (int n = 0; n < Sh::kDTiles; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(vb[ch & 1][n]), pb, acc[n], 0, 0, 0);
+    });
+    tr_write(tx, tr_to);
+  };
+
+  // Pipeline over the item's key tiles t = kt0 .. kt1-1, one step per tile between
+  // work-group barriers.  Per tile a wave has a matrix-core part (S = K Q^T and
+  // O += V P, 32 MFMAs) and a vector part (the softmax), about equally long.  The waves
+  // are in two groups, one wave of each on every SIMD, that run the parts in opposite
+  // order, so one group's exponentials issue while the other group's MFMAs run:
+  //   leading group   (waves 0-3): O += V P(t-1), S(t)  | softmax(t) -> P(t)
+  //   following group (waves 4-7): softmax(t) -> P(t)   | O += V P(t), S(t+1)
+  // and every wave transposes its share of V(t+1) into V^T(t+1) during its O += V P.
+  // Step t also reads the block id of tile t+4 and starts the copies of K(t+3) and
+  // V(t+3) (spread over the matrix-core part).  K slot (t+3)%4 last held K(t-1), read at
+  // step t-1; V slot (t+3)%3 last held V(t), transposed at step t-1; V^T slot (t+1)%3
+  // last held V^T(t-2), read at step t-1.  Before the barrier a wave waits for its V^T
+  // writes and for everything older than this step's copies (vector-memory instructions
+  // retire in order and the copies are the last loads of a step: vmcnt <= 2*kCopies),
+  // which covers K(t+2) and V(t+2), the newest tiles step t+1 reads.  Block ids are read
+  // before the copies of their step, so consuming one never waits on copies in flight.
+  // Tiles past the item's range are copied too (valid rows, never used) so that every
+  // step is alike.
   constexpr int kStepLoads = 2 * Sh::kCopies;
   const int wave_tiles_end = min(kt1, wave_last / Sh::kKeys + 1);  // tiles this wave computes
+  const bool leading = wave < Sh::kWaves / 2;
+  auto computes = [&](int tile) { return wave_live && tile < wave_tiles_end; };
   {
-    const int ph0 = block_of(kt0), ph1 = block_of(kt0 + 1), ph2 = block_of(kt0 + 2);
-    int phys_next = block_of(kt0 + 3);
-    copy_tile(kt0, ph0, 0);
-    copy_tile(kt0 + 1, ph1, 1);
-    copy_tile(kt0 + 2, ph2, 2);
-    wait_vmcnt<2 * Sh::kCopies>();  // tiles kt0 and kt0+1 have landed
+    wait_vmcnt<Sh::kKSteps>();  // the block ids have landed; Q may still be in flight
+    copy_rows(kbase, kt0, ph0, k_stage(kt0));
+    copy_rows(vbase, kt0, ph0, v_stage(kt0));
+    copy_rows(kbase, kt0 + 1, ph1, k_stage(kt0 + 1));
+    copy_rows(vbase, kt0 + 1, ph1, v_stage(kt0 + 1));
+    copy_rows(kbase, kt0 + 2, ph2, k_stage(kt0 + 2));
+    copy_rows(vbase, kt0 + 2, ph2, v_stage(kt0 + 2));
+    wait_vmcnt<2 * Sh::kCopies>();  // Q and tiles kt0, kt0+1 have landed
+    __builtin_amdgcn_s_barrier();
+    transpose(v_addr(kt0), vt_addr(kt0));
+    wait_vmcnt_lgkm0<2 * Sh::kCopies>();
     __builtin_amdgcn_s_barrier();
 
-    f32x16 s_cur[2], s_next[2];
-    if (wave_live && kt0 < wave_tiles_end) scores(s_cur, 0);
-
-    auto step = [&](int tile, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-      const int j = tile - kt0;
+    f32x16 sc[2];  // scores of the tile the wave softmaxes next
+    u32x4 pw[4];   // its probabilities, bf16
+    if (!leading && computes(kt0)) scores(sc, k_addr(kt0));
+    for (int tile = kt0; tile < kt1; ++tile) {
       const int phys_new = block_of(tile + 4);
-      copy_tile(tile + 3, phys_next, (j + 3) & 3);
+      // this step's copies: K(t+3) and V(t+3), kCopies slabs each
+      const int phys = phys_next;
+      unsigned char* const k_dst = k_stage(tile + 3);
+      unsigned char* const v_dst = v_stage(tile + 3);
+      auto copy_part = [&](int part) {
+        if (part < Sh::kCopies)
+          copy_slab(kbase, tile + 3, phys, k_dst, part);
+        else if (part < 2 * Sh::kCopies)
+          copy_slab(vbase, tile + 3, phys, v_dst, part - Sh::kCopies);
+      };
+      auto copy_all = [&]() {
+#pragma unroll
+        for (int part = 0; part < 2 * Sh::kCopies; ++part) copy_part(part);
+      };
       phys_next = phys_new;
-      if (wave_live && tile + 1 < wave_tiles_end) scores(sn, (j + 1) & 3);
-      if (wave_live && tile < wave_tiles_end) softmax_pv(sc, tile * Sh::kKeys, j & 3);
-      wait_vmcnt<kStepLoads>();  // tile t+2 has landed (this wave's copies)
+      if (!leading && computes(tile)) softmax(sc, tile * Sh::kKeys, pw);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      // V(t+1) -> V^T(t+1) by every wave (inside its O += V P when it has one); tiles past
+      // the range hold valid rows too, so the transposition is unconditional
+      const uint32_t tr_from = v_addr(tile + 1), tr_to = vt_addr(tile + 1);
+      if (leading) {
+        if (tile > kt0 && computes(tile - 1)) {
+          pv(pw, vt_addr(tile - 1), copy_part, tr_from, tr_to);
+        } else {
+          copy_all();
+          transpose(tr_from, tr_to);
+        }
+        if (computes(tile)) scores(sc, k_addr(tile));
+      } else {
+        if (computes(tile)) {
+          pv(pw, vt_addr(tile), copy_part, tr_from, tr_to);
+        } else {
+          copy_all();
+          transpose(tr_from, tr_to);
+        }
+        if (computes(tile + 1)) scores(sc, k_addr(tile + 1));
+      }
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (leading && computes(tile)) softmax(sc, tile * Sh::kKeys, pw);
+      wait_vmcnt_lgkm0<kStepLoads>();
       __builtin_amdgcn_s_barrier();
-    };
-    for (int tile = kt0; tile < kt1; tile += 2) {
-      step(tile, s_cur, s_next);
-      if (tile + 1 < kt1) step(tile + 1, s_next, s_cur);
     }
+    // the last O += V P of the leading group; V^T(kt1-1)'s slot is not refilled.  (Its
+    // transposition rides along into the slot of V^T(kt1+1), which nothing reads.)
+    if (leading && computes(kt1 - 1)) pv(pw, vt_addr(kt1 - 1), [](int) {}, v_addr(kt1 + 1), vt_addr(kt1 + 1));
     wait_vmcnt<0>();  // no copy may still be writing LDS when the work-group ends
   }
 
@@ -425,8 +657,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
 }  // namespace
 
 size_t prefill_lds_bytes(int head_dim) {
-  return head_dim == 128 ? PrefillShape<128>::kStages * PrefillShape<128>::kStageBytes
-                         : PrefillShape<64>::kStages * PrefillShape<64>::kStageBytes;
+  return head_dim == 128 ? PrefillShape<128>::kLdsBytes : PrefillShape<64>::kLdsBytes;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
