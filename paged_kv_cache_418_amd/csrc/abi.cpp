@@ -482,7 +482,7 @@ struct PrefillLayout {
 PrefillLayout prefill_layout(int n_split_items, int num_kv_heads, int head_dim) {
   const size_t rows = (size_t)n_split_items * num_kv_heads * pa::kPrefillRows;
   PrefillLayout L;
-  L.o_bytes = align_up(rows * head_dim * sizeof(float));
+  L.o_bytes = align_up(rows * head_dim * sizeof(uint16_t));  // fp16 O / l
   L.m_bytes = align_up(rows * sizeof(float));
   L.total = n_split_items ? L.o_bytes + 2 * L.m_bytes : 0;
   return L;
@@ -568,7 +568,7 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                                                                                     head_dim, plan.max_decode_len, 0))
                                                : 0;
   const PrefillLayout lay = prefill_layout(plan.n_split_items, num_kv_heads, head_dim);
-  float* part_o = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes) : nullptr;
+  uint16_t* part_o = plan.n_split_items ? reinterpret_cast<uint16_t*>(ws + dec_bytes) : nullptr;
   float* part_m = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes) : nullptr;
   float* part_l = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + lay.m_bytes) : nullptr;
   for (size_t i0 = 0; i0 < plan.items.size(); i0 += pa::kMaxPrefillItems) {

@@ -26,6 +26,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // Two fp32 -> packed bf16 pair (low half = a), round to nearest even: one
 // v_cvt_pk_bf16_f32 on gfx950.
+// Two fp32 values rounded to fp16 (nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x2_t __attribute__((ext_vector_type(2)));

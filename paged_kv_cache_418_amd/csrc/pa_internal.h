@@ -59,7 +59,7 @@ struct PrefillParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const int32_t* qsl;
-  float* part_o;             // [slots][num_kv_heads][256 rows][D] unnormalised partial outputs
+  uint16_t* part_o;          // [slots][num_kv_heads][256 rows][D] partial outputs divided by their l (fp16)
   float* part_m;             // [slots][num_kv_heads][256 rows] reference maximum (log2 units)
   float* part_l;             // [slots][num_kv_heads][256 rows] sum of weights
   int bt_stride;
@@ -80,7 +80,7 @@ struct PrefillParams {
 struct PrefillMergeParams {
   void* out;
   const int32_t* qsl;
-  const float* part_o;
+  const uint16_t* part_o;    // fp16, divided by l
   const float* part_m;
   const float* part_l;
   int num_q_heads;

@@ -586,15 +586,19 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
                                                   pack_bf16x2(acc[n][4 * rq + 2] * inv, acc[n][4 * rq + 3] * inv)};
       }
   } else {
-    // partial result of a split row tile: slot (launch base + item) x kv head x row
+    // partial result of a split row tile: slot (launch base + item) x kv head x row.  O / l
+    // is bounded by the largest |V| of the row's keys, so fp16 holds it with a relative
+    // error of 2^-11 (a row that saw none of its keys stores 0; its m is -inf).
     const size_t pi = ((size_t)(p.item_base + blockIdx.x) * p.num_kv_heads + kvh) * kPrefillRows + R;
-    float* po = p.part_o + pi * D;
+    uint16_t* po = p.part_o + pi * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int n = 0; n < Sh::kDTiles; ++n)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int d = n * 32 + 8 * rq + 4 * half;
-        *reinterpret_cast<f32x4*>(po + d) = f32x4{acc[n][4 * rq], acc[n][4 * rq + 1], acc[n][4 * rq + 2], acc[n][4 * rq + 3]};
+        *reinterpret_cast<u32x2*>(po + d) = u32x2{pack_f16x2(acc[n][4 * rq] * inv, acc[n][4 * rq + 1] * inv),
+                                                  pack_f16x2(acc[n][4 * rq + 2] * inv, acc[n][4 * rq + 3] * inv)};
       }
     if (half == 0) {
       p.part_m[pi] = m_ref;
@@ -636,12 +640,19 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
       const size_t pi = base + i * slot_step;
       const float mi = p.part_m[pi], li = p.part_l[pi];
       float src[PER_LANE];
+      if constexpr (PER_LANE == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(p.part_o + pi * D + lane * 2);
+        src[0] = f16_bits_to_f32(w & 0xFFFFu);
+        src[1] = f16_bits_to_f32(w >> 16);
+      } else {
 #pragma unroll
-      for (int j = 0; j < PER_LANE; ++j) src[j] = p.part_o[pi * D + lane * PER_LANE + j];
+        for (int j = 0; j < PER_LANE; ++j) src[j] = f16_bits_to_f32(p.part_o[pi * D + lane * PER_LANE + j]);
+      }
       if (mi == -INFINITY) continue;  // this split saw none of the row's keys
+      // split i holds O_i / l_i: weight l_i * 2^(m_i - M)
       const float Mn = fmaxf(M, mi);
-      const float a = fast_exp2(M - Mn), b = fast_exp2(mi - Mn);
-      den = den * a + li * b;
+      const float a = fast_exp2(M - Mn), b = li * fast_exp2(mi - Mn);
+      den = den * a + b;
 #pragma unroll
       for (int j = 0; j < PER_LANE; ++j) o[j] = o[j] * a + src[j] * b;
       M = Mn;
