@@ -180,6 +180,43 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_cascade -- pa_decode for a batch whose sequences all begin with
+ * the same prefix_blocks physical blocks (prefix sharing: [A] §2, two
+ * requests' tables pointing at the same blocks; cascade attention is named in
+ * [A]'s attention-backend table).  The result is pa_decode's: the keys of the
+ * shared prefix and of each sequence's own suffix are attended separately
+ * and combined with the log-sum-exp rule ([B] tutorial 7), so only the order
+ * of fp32 sums differs.  The prefix is read once per group of 16/G sequences
+ * (G = num_q_heads / num_kv_heads <= 16) instead of once per sequence.
+ * Requirements: prefix_blocks >= 1; every seq_lens[s] >= prefix_blocks *
+ * block_size; block_tables[s][j] the same for every s and j < prefix_blocks
+ * (checked under PA_VALIDATE=1, trusted otherwise).  dtype: PA_BF16.
+ * workspace: pa_decode_cascade_workspace_bytes(...) bytes (always needed).
+ * num_splits: waves per kv head for the suffixes, as in pa_decode.  Other
+ * arguments as pa_decode.
+ */
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len, int32_t prefix_blocks,
+                                         int32_t num_splits);
+pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                              pa_dtype_t dtype, int32_t prefix_blocks, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_cascade_fp8 -- pa_decode_cascade over E4M3FN pools, with the
+ * scales and q_dtype of pa_decode_fp8.  [A] §2, [B] tutorials 6 and 7.
+ */
+pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                  const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                  pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t prefix_blocks,
+                                  int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_varlen_workspace_bytes -- scratch pa_prefill_varlen needs for
  * this batch.  query_start_loc_host / seq_lens_host: host copies of the
  * metadata (num_seqs+1 and num_seqs entries).  Returns 0 on invalid input.
@@ -224,7 +261,8 @@ typedef enum pa_kernel {
   PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode, pa_decode_fp8, decode rows of pa_prefill_varlen) */
   PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
   PA_K_PREFILL = 4,         /* the varlen prefill kernel */
-  PA_K_PREFILL_MERGE = 5    /* the log-sum-exp merge of split prefill row tiles */
+  PA_K_PREFILL_MERGE = 5,   /* the log-sum-exp merge of split prefill row tiles */
+  PA_K_DECODE_PREFIX = 6    /* the shared-prefix part of pa_decode_cascade(_fp8) */
 } pa_kernel_t;
 
 pa_status_t pa_timing_enable(int on);

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 KERNELS = {"slot_mapping": 0, "reshape_and_cache": 1, "decode": 2, "decode_merge": 3, "prefill": 4,
-           "prefill_merge": 5}
+           "prefill_merge": 5, "decode_prefix": 6}
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_WORKSPACE",
           5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_HIP"}
 
@@ -67,6 +67,11 @@ def load() -> ctypes.CDLL:
                            P], ctypes.c_int),
             "pa_decode_fp8": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, f32, f32,
                                i32, P, sz, P], ctypes.c_int),
+            "pa_decode_cascade_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
+            "pa_decode_cascade": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32,
+                                   i32, P, sz, P], ctypes.c_int),
+            "pa_decode_cascade_fp8": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                                       f32, f32, i32, i32, P, sz, P], ctypes.c_int),
             "pa_prefill_varlen_workspace_bytes": ([P, P, i32, i32, i32, i32], sz),
             "pa_prefill_varlen": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                    ctypes.c_int, P, sz, P], ctypes.c_int),
@@ -196,6 +201,48 @@ def pa_decode_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: 
         _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
         _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(query),
         float(k_scale), float(v_scale), num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
+def pa_decode_cascade_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                      max_seq_len: int, prefix_blocks: int, num_splits: int = 0) -> int:
+    return int(load().pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                        prefix_blocks, num_splits))
+
+
+def pa_decode_cascade(query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                      prefix_blocks: int, num_splits: int = 0, out=None, workspace=None):
+    """pa_decode for sequences that all start with the same prefix_blocks physical blocks (bf16 pools)."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    out = torch.empty_like(query) if out is None else out
+    need = pa_decode_cascade_workspace_bytes(S, Hq, Hkv, D, max_seq_len, prefix_blocks, num_splits)
+    ws, wsb = _workspace(need, query.device, workspace)
+    _check("pa_decode_cascade", lib.pa_decode_cascade(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(key_cache),
+        prefix_blocks, num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
+def pa_decode_cascade_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: float, k_scale: float,
+                          v_scale: float, max_seq_len: int, prefix_blocks: int, num_splits: int = 0, out=None,
+                          workspace=None):
+    """pa_decode_cascade over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    out = torch.empty_like(query) if out is None else out
+    need = pa_decode_cascade_workspace_bytes(S, Hq, Hkv, D, max_seq_len, prefix_blocks, num_splits)
+    ws, wsb = _workspace(need, query.device, workspace)
+    _check("pa_decode_cascade_fp8", lib.pa_decode_cascade_fp8(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(query),
+        float(k_scale), float(v_scale), prefix_blocks, num_splits, None if ws is None else ws.data_ptr(), wsb,
+        _stream()))
     return out
 
 

@@ -164,12 +164,42 @@ pa_status_t check_attention_shape(int num_q_heads, int num_kv_heads, int head_di
 }
 
 // Shared by pa_decode / pa_decode_fp8 / the decode rows of pa_prefill_varlen.
+// Cascade decode: the shared prefix is cut into `shares` pieces per group of 16/G
+// sequences (enough waves for about decode_waves_per_simd per SIMD); the suffix uses the
+// split decode's layout (every piece partial), then the prefix partials follow.
+int cascade_prefix_shares(int num_seqs, int group, int num_kv_heads, int prefix_blocks) {
+  const int per_group = std::max(1, 16 / std::max(1, group));
+  const int64_t groups = std::max<int64_t>(1, (num_seqs + per_group - 1) / per_group);
+  const int64_t target = (int64_t)decode_waves_per_simd() * 4 * device_cu_count();
+  const int64_t sh = target / std::max<int64_t>(1, groups * num_kv_heads);
+  return (int)std::min<int64_t>(std::max<int64_t>(sh, 1), std::max(prefix_blocks, 1));
+}
+
+struct CascadeLayout {
+  DecodeLayout dec;
+  size_t pre_o_bytes, pre_m_bytes, total;
+  int n_splits, shares;
+};
+
+CascadeLayout cascade_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                             int prefix_blocks, int num_splits) {
+  CascadeLayout L;
+  L.n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, max_seq_len);
+  L.dec = decode_layout(num_seqs, num_q_heads, L.n_splits, head_dim);
+  L.shares = cascade_prefix_shares(num_seqs, num_q_heads / std::max(1, num_kv_heads), num_kv_heads, prefix_blocks);
+  const size_t rows = (size_t)L.shares * num_seqs * num_q_heads;
+  L.pre_o_bytes = align_up(rows * head_dim * sizeof(float));
+  L.pre_m_bytes = align_up(rows * sizeof(float));
+  L.total = L.dec.total + L.pre_o_bytes + 2 * L.pre_m_bytes;
+  return L;
+}
+
 pa_status_t run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                        const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, const int32_t* qsl,
                        int32_t num_seqs, int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
                        int q_f32, float k_scale, float v_scale, int32_t num_splits, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+                       size_t workspace_bytes, hipStream_t stream, int32_t prefix_blocks = 0) {
   const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, max_seq_len);
   pa::DecodeParams p{};
   p.out = out;
@@ -191,7 +221,27 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
   p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
   p.q_f32 = q_f32;
-  if (n_splits > 1) {
+  if (prefix_blocks > 0) {  // cascade: prefix launch, then every suffix piece partial, then the merge
+    const CascadeLayout cl = cascade_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                            prefix_blocks, num_splits);
+    const DecodeLayout& lay = cl.dec;
+    auto* base = static_cast<unsigned char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(base);
+    p.part_m = reinterpret_cast<float*>(base + lay.o_bytes);
+    p.part_l = reinterpret_cast<float*>(base + lay.o_bytes + lay.m_bytes);
+    p.piece_first = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes);
+    p.piece_last = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes + lay.idx_bytes);
+    unsigned char* pre = base + lay.total;
+    p.pre_o = reinterpret_cast<float*>(pre);
+    p.pre_m = reinterpret_cast<float*>(pre + cl.pre_o_bytes);
+    p.pre_l = reinterpret_cast<float*>(pre + cl.pre_o_bytes + cl.pre_m_bytes);
+    p.skip_blocks = prefix_blocks;
+    p.force_partial = 1;
+    p.prefix_blocks = prefix_blocks;
+    p.prefix_shares = cl.shares;
+    hipError_t e = pa::launch_decode_prefix(p, kv_kind, head_dim, stream);
+    if (e != hipSuccess) return hip_status(e, "cascade prefix launch");
+  } else if (n_splits > 1) {
     const DecodeLayout lay = decode_layout(num_seqs, num_q_heads, n_splits, head_dim);
     auto* base = static_cast<unsigned char*>(workspace);
     p.part_o = reinterpret_cast<float*>(base);
@@ -209,7 +259,7 @@ pa_status_t check_decode_args(const void* out, const void* query, const void* ke
                               const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
-                              int32_t num_splits, void* workspace, size_t workspace_bytes) {
+                              int32_t num_splits, void* workspace, size_t workspace_bytes, size_t need_override = SIZE_MAX) {
   if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
@@ -221,7 +271,10 @@ pa_status_t check_decode_args(const void* out, const void* query, const void* ke
                 ceil_div(max_seq_len, block_size), bt_stride);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
   if (num_splits < 0) return fail(PA_ERR_SHAPE, "num_splits %d < 0", num_splits);
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, num_splits);
+  const size_t need = need_override != SIZE_MAX
+                          ? need_override
+                          : pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                      num_splits);
   if (need && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
@@ -386,6 +439,101 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, pa::kFP8,
                     q_dtype == PA_F32, k_scale, v_scale, num_splits, workspace, workspace_bytes,
                     static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// Arguments of a cascade call on top of the decode checks: a prefix of whole blocks
+// inside every sequence, a group of at most 16 q heads, and (PA_VALIDATE=1) tables
+// that really share it.
+pa_status_t check_cascade(const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t block_size, int32_t max_seq_len,
+                          int32_t prefix_blocks) {
+  if (prefix_blocks < 1) return fail(PA_ERR_SHAPE, "prefix_blocks %d < 1", prefix_blocks);
+  if ((int64_t)prefix_blocks * block_size > max_seq_len)
+    return fail(PA_ERR_SHAPE, "prefix of %d blocks longer than max_seq_len %d", prefix_blocks, max_seq_len);
+  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "cascade decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (!validate_enabled() || num_seqs == 0) return PA_OK;
+  std::vector<int32_t> sl, bt;
+  if (!copy_to_host(sl, seq_lens, num_seqs) || !copy_to_host(bt, block_tables, (size_t)num_seqs * bt_stride))
+    return fail(PA_ERR_HIP, "PA_VALIDATE: metadata copy failed");
+  for (int s = 0; s < num_seqs; ++s) {
+    if (sl[s] < prefix_blocks * block_size)
+      return fail(PA_ERR_SHAPE, "PA_VALIDATE: seq_lens[%d] = %d shorter than the shared prefix", s, sl[s]);
+    for (int j = 0; j < prefix_blocks; ++j)
+      if (bt[(size_t)s * bt_stride + j] != bt[j])
+        return fail(PA_ERR_SHAPE, "PA_VALIDATE: block_tables[%d][%d] differs from sequence 0's", s, j);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len, int32_t prefix_blocks,
+                                         int32_t num_splits) {
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads || max_seq_len < 1 ||
+      (head_dim != 64 && head_dim != 128) || num_splits < 0 || prefix_blocks < 1 ||
+      (int64_t)prefix_blocks * pa::kBlockSize > max_seq_len || num_q_heads / num_kv_heads > pa::kMaxGroup)
+    return 0;
+  return cascade_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits).total;
+}
+
+pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                              pa_dtype_t dtype, int32_t prefix_blocks, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "cascade decode: dtype must be PA_BF16");
+  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                        prefix_blocks, num_splits);
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, workspace, workspace_bytes, need);
+  if (st != PA_OK) return st;
+  st = check_cascade(block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, block_size, max_seq_len,
+                     prefix_blocks);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                    pa::kBF16, 0, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                    prefix_blocks);
+}
+
+pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                  const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                  pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t prefix_blocks,
+                                  int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
+  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                        prefix_blocks, num_splits);
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, workspace, workspace_bytes, need);
+  if (st != PA_OK) return st;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  st = check_cascade(block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, block_size, max_seq_len,
+                     prefix_blocks);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                    pa::kFP8, q_dtype == PA_F32, k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream), prefix_blocks);
 }
 
 namespace {

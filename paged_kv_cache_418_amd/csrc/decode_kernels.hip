@@ -136,10 +136,12 @@ __device__ __forceinline__ float sum_across_rows(float x) {
 
 // Blocks of sequence s the decode attends: ceil(seq_len / 16), or 0 when s
 // is not a decode row of a flattened batch (q_len != 1).
+// Blocks of sequence s that its own pieces cover (all of them, or those after the
+// shared prefix of a cascade).
 __device__ __forceinline__ int decode_blocks(const DecodeParams& p, int s) {
   if (p.qsl && p.qsl[s + 1] - p.qsl[s] != 1) return 0;
   const int L = min(p.seq_lens[s], p.max_seq_len);
-  return L > 0 ? (L + 15) >> 4 : 0;
+  return L > 0 ? max(((L + 15) >> 4) - p.skip_blocks, 0) : 0;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int x) {
@@ -196,7 +198,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int split,
 // With a single share every sequence is finished in place and there is no
 // scratch (the index arrays are absent).
 __device__ __forceinline__ void note_piece(const DecodeParams& p, int split, int s, int b0, int b1, int nb) {
-  if (p.n_splits <= 1) return;
+  if (p.n_splits <= 1 && !p.force_partial) return;
   if (b0 == 0) p.piece_first[s] = split;
   if (b1 == nb) p.piece_last[s] = split;
 }
@@ -210,28 +212,39 @@ __device__ __forceinline__ void note_piece(const DecodeParams& p, int split, int
 // and the V^T operand of MFMA j (d = VEC*m + j) is two byte permutes of the
 // lane's own V words.  Two blocks are in flight while one is computed.
 // Blocks [b0, b1) of sequence s (nb blocks in all) for the q heads of kv head kvh.
-template <int D, bool FP8>
+//
+// GROUP (cascade prefix): the 16 columns are 16/G sequences x G heads instead of the G
+// heads of one sequence, so each block of the shared prefix feeds 16/G sequences at
+// once; s is the group's first sequence, split the prefix share, [b0, b1) blocks of
+// the prefix (whole blocks, every key visible).  Otherwise the piece covers blocks
+// [b0, b1) of sequence s after its skip_blocks shared blocks.
+template <int D, bool FP8, bool GROUP = false>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned char* k_lds, int split, int kvh, int s,
                                              int b0, int b1, int nb) {
   using Sh = DecodeShape<D, FP8>;
   constexpr int VEC = Sh::kVec, W = Sh::kWords;
+  const int skip = GROUP ? 0 : p.skip_blocks;
   const int row = p.qsl ? p.qsl[s] : s;
-  const int L = min(p.seq_lens[s], p.max_seq_len);
-  const int tok0 = b0 * 16;
-  const int tok1 = min(L, b1 * 16);
+  const int L = GROUP ? p.prefix_blocks * 16 : min(p.seq_lens[s], p.max_seq_len);
+  const int tok0 = (skip + b0) * 16;
+  const int tok1 = min(L, (skip + b1) * 16);
   const int nblk = b1 - b0;
-  const bool whole = b0 == 0 && b1 == nb;
+  const bool whole = !GROUP && b0 == 0 && b1 == nb && !p.force_partial;
 
   const int lane = threadIdx.x;
   const int a = lane >> 4, c = lane & 15;  // row group / column within the row group
   const int G = p.group;
+  // the lane's column: q head g of query row col_row (col_ok: a real column)
+  const int g = GROUP ? c % G : c;
+  const int col_seq = GROUP ? s + c / G : s;
+  const bool col_ok = GROUP ? (c < (16 / G) * G && col_seq < p.num_seqs) : c < G;
+  const int col_row = GROUP ? col_seq : row;
 
-  // Q^T operand of MFMA kk: lane (a, g = c) holds q[g][8*(a + 4*kk) .. +7]
+  // Q^T operand of MFMA kk: lane (a, column c) holds q[column][8*(a + 4*kk) .. +7]
   bf16x8 qf[Sh::kKSteps];
   {
-    const int g = c;
-    if (g < G) {
-      const size_t qoff = ((size_t)row * p.num_q_heads + kvh * G + g) * D;
+    if (col_ok) {
+      const size_t qoff = ((size_t)col_row * p.num_q_heads + kvh * G + g) * D;
 #pragma unroll
       for (int kk = 0; kk < Sh::kKSteps; ++kk) {
         const int d0 = 8 * (a + 4 * kk);
@@ -268,7 +281,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
   // Physical block ids of the partition, 64 at a time in one VGPR (lane i holds block
   // win0 + i); a wave-uniform block id is then one v_readlane away.
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + b0;
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + skip + b0;
   int win0 = 0;
   int bt_win = lane < nblk ? bt[lane] : 0;
 
@@ -386,12 +399,23 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
   // the four row groups hold partial sums over different tokens of the same head
   l = sum_across_rows(l);
 
-  const int g = c;
-  if (g >= G) return;
+  if (!col_ok) return;
   const int h = kvh * G + g;
-  // lane (a, g) holds O[g][VEC*(4a + r) + j] in acc[j][r]: 4*VEC consecutive d
+  // lane (a, column) holds O[column][VEC*(4a + r) + j] in acc[j][r]: 4*VEC consecutive d
   const int d0 = 4 * VEC * a;
-  if (whole) {
+  if constexpr (GROUP) {
+    const size_t pi = ((size_t)split * p.num_seqs + col_seq) * p.num_q_heads + h;
+    float* po = p.pre_o + pi * D + d0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < VEC; j += 4)
+        *reinterpret_cast<f32x4*>(po + VEC * r + j) = f32x4{acc[j][r], acc[j + 1][r], acc[j + 2][r], acc[j + 3][r]};
+    if (a == 0) {
+      p.pre_m[pi] = m;
+      p.pre_l[pi] = l;
+    }
+  } else if (whole) {
     const float inv = p.v_scale / l;
     const size_t oi = ((size_t)row * p.num_q_heads + h) * D + d0;
     if (p.q_f32) {
@@ -436,6 +460,19 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
   });
 }
 
+// Cascade prefix: one wave per (group of 16/G sequences, prefix share, kv head).  The
+// shared prefix blocks are read once per group (and stay in the last-level cache across
+// groups) instead of once per sequence.
+template <int D, bool FP8>
+__global__ void __launch_bounds__(64) decode_prefix_kernel(DecodeParams p) {
+  __shared__ __align__(16) unsigned char k_lds[DecodeShape<D, FP8>::kLdsBytes];
+  const int share = blockIdx.x % p.prefix_shares, group = blockIdx.x / p.prefix_shares, kvh = blockIdx.y;
+  const int per_group = 16 / p.group;
+  const int b0 = (int)((long long)p.prefix_blocks * share / p.prefix_shares);
+  const int b1 = (int)((long long)p.prefix_blocks * (share + 1) / p.prefix_shares);
+  if (b1 > b0) decode_piece<D, FP8, true>(p, k_lds, share, kvh, group * per_group, b0, b1, p.prefix_blocks);
+}
+
 // fp32 pools and queries: vector-ALU kernel, one wave per (share, q head).
 // Lane = (token t = lane % 16, quarter = lane / 16) holding D/4 elements of a row.
 template <int D>
@@ -459,7 +496,7 @@ __device__ __forceinline__ void decode_f32_piece(const DecodeParams& p, int spli
 #pragma unroll
   for (int i = 0; i < QD; ++i) o[i] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + b0;
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + b0;  // no cascade for fp32 pools
   const float* kc = reinterpret_cast<const float*>(p.key_cache);
   const float* vc = reinterpret_cast<const float*>(p.value_cache);
 
@@ -536,28 +573,36 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.x * 4 + wave, s = blockIdx.y;
   if (h >= p.num_q_heads) return;
-  if (decode_blocks(p, s) == 0) return;
-  const int first = p.piece_first[s], last = p.piece_last[s];
-  if (first >= last) return;
+  const bool own = decode_blocks(p, s) > 0;  // the sequence has pieces of its own
+  if (!own && p.prefix_shares == 0) return;
+  const int first = own ? p.piece_first[s] : 0, last = own ? p.piece_last[s] : -1;
+  if (first >= last && !p.force_partial) return;  // finished in place
   const int row = p.qsl ? p.qsl[s] : s;
   const size_t step = (size_t)p.num_q_heads;
-  const size_t base = (size_t)(first + s) * step + h;  // piece i: base + i * num_q_heads
   float M = -INFINITY, den = 0.f, o[PER_LANE];
 #pragma unroll
   for (int k = 0; k < PER_LANE; ++k) o[k] = 0.f;
-#pragma unroll 4
-  for (int i = 0; i <= last - first; ++i) {
-    const size_t pi = base + i * step;
-    const float mi = p.part_m[pi], li = p.part_l[pi];
+  auto fold = [&](const float* po, float mi, float li) {
     float src[PER_LANE];
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) src[k] = p.part_o[pi * D + lane * PER_LANE + k];
+    for (int k = 0; k < PER_LANE; ++k) src[k] = po[lane * PER_LANE + k];
     const float Mn = fmaxf(M, mi);
     const float a = fast_exp2(M - Mn), b = fast_exp2(mi - Mn);
     den = den * a + li * b;
 #pragma unroll
     for (int k = 0; k < PER_LANE; ++k) o[k] = o[k] * a + src[k] * b;
     M = Mn;
+  };
+  // cascade: the prefix pieces of (s, h) first
+  for (int i = 0; i < p.prefix_shares; ++i) {
+    const size_t pi = ((size_t)i * p.num_seqs + s) * step + h;
+    fold(p.pre_o + pi * D, p.pre_m[pi], p.pre_l[pi]);
+  }
+  const size_t base = (size_t)(first + s) * step + h;  // piece i: base + i * num_q_heads
+#pragma unroll 4
+  for (int i = 0; i <= last - first; ++i) {
+    const size_t pi = base + i * step;
+    fold(p.part_o + pi * D, p.part_m[pi], p.part_l[pi]);
   }
   const float inv = p.v_scale / den;
   const size_t oi = ((size_t)row * p.num_q_heads + h) * D + lane * PER_LANE;
@@ -585,7 +630,7 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   }
   timing_mark(kKDecode, false, stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_splits <= 1) return e;
+  if (e != hipSuccess || (p.n_splits <= 1 && !p.force_partial) || p.num_seqs == 0) return e;
   timing_mark(kKDecodeMerge, true, stream);
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((p.num_q_heads + 3) / 4, p.num_seqs), dim3(256), 0, stream, p);
   timing_mark(kKDecodeMerge, false, stream);
@@ -597,6 +642,25 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream) {
   if (head_dim == 128) return launch_decode_d<128>(p, kv, stream);
   return launch_decode_d<64>(p, kv, stream);
+}
+
+hipError_t launch_decode_prefix(const DecodeParams& p, int kv, int head_dim, hipStream_t stream) {
+  const int groups = (p.num_seqs + 16 / p.group - 1) / (16 / p.group);
+  const dim3 grid(groups * p.prefix_shares, p.num_kv_heads);
+  timing_mark(kKDecodePrefix, true, stream);
+  if (head_dim == 128) {
+    if (kv == kFP8)
+      hipLaunchKernelGGL((decode_prefix_kernel<128, true>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_prefix_kernel<128, false>), grid, dim3(64), 0, stream, p);
+  } else {
+    if (kv == kFP8)
+      hipLaunchKernelGGL((decode_prefix_kernel<64, true>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_prefix_kernel<64, false>), grid, dim3(64), 0, stream, p);
+  }
+  timing_mark(kKDecodePrefix, false, stream);
+  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -42,6 +42,16 @@ struct DecodeParams {
   int num_blocks;
   int max_seq_len;
   int n_splits;
+  // cascade (a prefix of blocks shared by every sequence, attended once per group of
+  // sequences): the suffix launch skips the shared blocks and leaves every piece partial;
+  // the prefix launch writes pre_* partials; the merge folds both in.
+  int skip_blocks;           // leading table entries the per-sequence pieces skip (0 without cascade)
+  int force_partial;         // every piece leaves a partial result, none is finished in place
+  int prefix_blocks;         // shared leading blocks (cascade), else 0
+  int prefix_shares;         // prefix pieces per sequence (cascade), else 0
+  float* pre_o;              // [prefix_shares][num_seqs][Hq][D] prefix partial outputs (unnormalised)
+  float* pre_m;              // [prefix_shares][num_seqs][Hq]
+  float* pre_l;              // [prefix_shares][num_seqs][Hq]
   float scale_log2;          // softmax scale * log2(e) (* k_scale for fp8 pools)
   float v_scale;             // 1, or the fp8 value scale
   int q_f32;                 // query / output are fp32 (else bf16)
@@ -100,7 +110,8 @@ enum KernelId {
   kKDecodeMerge = 3,
   kKPrefill = 4,
   kKPrefillMerge = 5,
-  kNumKernelIds = 6
+  kKDecodePrefix = 6,
+  kNumKernelIds = 7
 };
 void timing_mark(int kernel, bool begin, hipStream_t stream);
 
@@ -121,6 +132,8 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int6
 
 // kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel)
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
+// cascade prefix: grid (groups of 16/G sequences x prefix_shares, kv heads); kBF16 or kFP8
+hipError_t launch_decode_prefix(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream);

@@ -272,9 +272,12 @@ NAMED = {
 
 def random_case(seed: int, *, num_seqs: int, ctx_range=(1, 40), q_lens=None, num_q_heads=4,
                 num_kv_heads=2, head_dim=8, q_dtype="f32", kv_dtype="f32", chunk_range=None,
-                k_scale=1.0, v_scale=1.0, block_size=BLOCK_SIZE, extra_blocks=3) -> Workload:
+                k_scale=1.0, v_scale=1.0, block_size=BLOCK_SIZE, extra_blocks=3,
+                shared_prefix_tokens=0) -> Workload:
     """Small random case: context lengths U[ctx_range]; q_lens all 1 unless given,
-    or drawn U[chunk_range] (capped by the context length) when chunk_range is set."""
+    or drawn U[chunk_range] (capped by the context length) when chunk_range is set.
+    shared_prefix_tokens (a multiple of the block size, below every context length):
+    the sequences' tables begin with the same physical blocks."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(ctx_range[0], ctx_range[1], num_seqs, endpoint=True)
     if q_lens is None:
@@ -286,7 +289,8 @@ def random_case(seed: int, *, num_seqs: int, ctx_range=(1, 40), q_lens=None, num
     return build(f"random_{seed}", seed=seed, rng=rng, ctx_lens=ctx, q_lens=q_lens,
                  num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                  q_dtype=q_dtype, kv_dtype=kv_dtype, num_blocks=nblk + extra_blocks,
-                 k_scale=k_scale, v_scale=v_scale, block_size=block_size)
+                 k_scale=k_scale, v_scale=v_scale, block_size=block_size,
+                 shared_prefix_tokens=shared_prefix_tokens)
 
 
 # --- byte / flop accounting (sizes only; no attention arithmetic) ---------------

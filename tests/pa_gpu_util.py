@@ -49,6 +49,16 @@ class DevWorkload:
         return pk.pa_decode(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
                             self.max_seq_len(), num_splits, out=out)
 
+    def cascade(self, prefix_blocks, num_splits=0, out=None, seq_lens=None):
+        w = self.w
+        sl = self.seq_lens if seq_lens is None else seq_lens
+        if w.kv_dtype == "fp8":
+            return pk.pa_decode_cascade_fp8(self.query, self.k_cache, self.v_cache, self.block_tables, sl, w.scale,
+                                            w.k_scale, w.v_scale, self.max_seq_len(), prefix_blocks, num_splits,
+                                            out=out)
+        return pk.pa_decode_cascade(self.query, self.k_cache, self.v_cache, self.block_tables, sl, w.scale,
+                                    self.max_seq_len(), prefix_blocks, num_splits, out=out)
+
     def prefill(self, out=None):
         w = self.w
         return pk.pa_prefill_varlen(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,

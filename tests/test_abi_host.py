@@ -18,7 +18,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 14
+    assert len(syms) == 17
+    assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -157,3 +158,24 @@ def test_timing_calls_without_a_gpu(lib):
     assert lib.pa_timing_read(99, ctypes.byref(n), ctypes.byref(ms)) == 2
     assert lib.pa_timing_read(2, None, None) == 1
     assert lib.pa_timing_enable(0) == 0
+
+
+def test_cascade_workspace_and_argument_checks(lib):
+    # 128 sequences, 32/8 heads, d 128, 2048-token prefix (128 blocks), 256 suffix waves: the split-decode scratch
+    # (every suffix piece is partial, so it is needed even with one wave) followed by the prefix partials
+    dec = pk.pa_decode_workspace_bytes(128, 32, 8, 128, 3072, 256)
+    got = pk.pa_decode_cascade_workspace_bytes(128, 32, 8, 128, 3072, 128, 256)
+    assert got > dec > 0
+    assert (got - dec) % 256 == 0
+    one = pk.pa_decode_cascade_workspace_bytes(128, 32, 8, 128, 3072, 128, 1)
+    assert one > 0 and pk.pa_decode_workspace_bytes(128, 32, 8, 128, 3072, 1) == 0
+    # invalid: no prefix, prefix longer than max_seq_len, more than 16 q heads per kv head
+    assert pk.pa_decode_cascade_workspace_bytes(128, 32, 8, 128, 3072, 0, 0) == 0
+    assert pk.pa_decode_cascade_workspace_bytes(4, 32, 8, 128, 100, 8, 0) == 0
+    assert pk.pa_decode_cascade_workspace_bytes(4, 64, 2, 128, 3072, 8, 0) == 0
+    # entry points reject bad arguments before touching the device
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 4, 32, 8, 128, 16, 1000, 3072, 0.088]
+    assert lib.pa_decode_cascade(*args, b.PA_F32, 8, 0, FAKE, 1 << 30, None) == 3          # dtype
+    assert lib.pa_decode_cascade(*args, b.PA_BF16, 0, 0, FAKE, 1 << 30, None) == 2         # no prefix
+    assert lib.pa_decode_cascade(*args, b.PA_BF16, 8, 0, FAKE, 16, None) == 4              # workspace too small
+    assert lib.pa_decode_cascade_fp8(*args, b.PA_BF16, 0.05, -1.0, 8, 0, FAKE, 1 << 30, None) == 2  # v_scale

@@ -3,6 +3,8 @@
 Bit-exact: slot mapping, the KV write (fp32/bf16 copies and fp8 codes).
 Attention: max-abs error within 2e-3 (fp32), 1.5e-2 (bf16), 6e-2 (fp8 KV).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -168,6 +170,81 @@ def test_decode_long_context_70b_full():
     w = wl.long_ctx_70b_decode_bf16()
     say("decode long-context 70b full")
     _decode_case(w)
+
+
+# ---- cascade decode (a prefix of physical blocks shared by every sequence)
+
+@pytest.mark.parametrize("kinds", [("bf16", "bf16"), ("bf16", "fp8"), ("f32", "fp8")])
+@pytest.mark.parametrize("heads", [(4, 2, 64), (32, 8, 128), (16, 1, 128), (8, 8, 64), (12, 4, 128)])
+@pytest.mark.parametrize("num_splits", [0, 1, 7])
+def test_cascade_decode_random(kinds, heads, num_splits):
+    Hq, Hkv, D = heads
+    shared = 5  # blocks
+    seed = 700 + Hq + 3 * Hkv + D + num_splits + len(kinds[1]) + len(kinds[0])
+    w = wl.random_case(seed, num_seqs=7, ctx_range=(16 * shared + 1, 16 * shared + 600), num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, q_dtype=kinds[0], kv_dtype=kinds[1], k_scale=0.05,
+                       v_scale=0.04, shared_prefix_tokens=16 * shared)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    tol = TOL[w.kv_dtype if w.kv_dtype == "fp8" else w.q_dtype]
+    for pb in (shared, 2):  # any leading part of a shared prefix is shared too
+        say("cascade random", kinds, heads, num_splits, "prefix blocks", pb)
+        out = d.cascade(pb, num_splits)
+        torch.cuda.synchronize()
+        err = max_err(out, ref)
+        say(f"  max_abs_err={err:.3e} tol={tol}")
+        assert err <= tol
+
+
+def test_cascade_decode_empty_suffix_and_whole_prefix():
+    """A sequence that is exactly the shared prefix (no keys of its own) and a prefix of one block."""
+    w = wl.random_case(731, num_seqs=9, ctx_range=(3 * 16 + 1, 400), num_q_heads=16, num_kv_heads=4, head_dim=128,
+                       q_dtype="bf16", kv_dtype="fp8", k_scale=0.05, v_scale=0.04, shared_prefix_tokens=3 * 16)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    pools = oracle.written_pools(w)
+    sl = w.seq_lens.copy()
+    sl[4] = 3 * 16   # attends to the shared prefix only
+    w2 = dataclasses.replace(w, seq_lens=sl)
+    ref = oracle.attention_for(w2, pools=pools)
+    say("cascade empty suffix")
+    out = d.cascade(3, 0, seq_lens=torch.from_numpy(sl).cuda())
+    torch.cuda.synchronize()
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["fp8"]
+    say("cascade one-block prefix")
+    out = d.cascade(1, 0)
+    torch.cuda.synchronize()
+    assert max_err(out, oracle.attention_for(w, pools=pools)) <= TOL["fp8"]
+
+
+def test_cascade_prefix_shared_fp8_full():
+    w = wl.prefix_shared_fp8_decode()
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    say("cascade prefix-shared fp8 full, prefix blocks", w.shared_prefix_blocks)
+    out = d.cascade(w.shared_prefix_blocks)
+    plain = d.decode()
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e}; vs plain decode {torch.max(torch.abs(out.float() - plain.float())).item():.3e}")
+    assert err <= TOL["fp8"]
+    # the same keys in another summation order: close to the plain decode
+    assert torch.max(torch.abs(out.float() - plain.float())).item() <= TOL["fp8"]
+
+
+def test_cascade_repeat_bit_identical():
+    w = wl.random_case(741, num_seqs=12, ctx_range=(8 * 16 + 1, 900), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                       q_dtype="bf16", kv_dtype="bf16", shared_prefix_tokens=8 * 16)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    say("cascade repeat")
+    first = d.cascade(8).cpu()
+    for _ in range(4):
+        assert torch.equal(d.cascade(8).cpu().view(torch.int16), first.view(torch.int16))
 
 
 def test_decode_block_relabeling_bit_identical():
