@@ -258,11 +258,10 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
 typedef enum pa_kernel {
   PA_K_SLOT_MAPPING = 0,    /* pa_slot_mapping */
   PA_K_RESHAPE_AND_CACHE = 1, /* pa_reshape_and_cache, pa_reshape_and_cache_fp8 */
-  PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode, pa_decode_fp8, decode rows of pa_prefill_varlen) */
+  PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode(_fp8), pa_decode_cascade(_fp8), decode rows of pa_prefill_varlen) */
   PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
   PA_K_PREFILL = 4,         /* the varlen prefill kernel */
-  PA_K_PREFILL_MERGE = 5,   /* the log-sum-exp merge of split prefill row tiles */
-  PA_K_DECODE_PREFIX = 6    /* the shared-prefix part of pa_decode_cascade(_fp8) */
+  PA_K_PREFILL_MERGE = 5    /* the log-sum-exp merge of split prefill row tiles */
 } pa_kernel_t;
 
 pa_status_t pa_timing_enable(int on);

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 KERNELS = {"slot_mapping": 0, "reshape_and_cache": 1, "decode": 2, "decode_merge": 3, "prefill": 4,
-           "prefill_merge": 5, "decode_prefix": 6}
+           "prefill_merge": 5}
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_WORKSPACE",
           5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_HIP"}
 

@@ -165,12 +165,13 @@ pa_status_t check_attention_shape(int num_q_heads, int num_kv_heads, int head_di
 
 // Shared by pa_decode / pa_decode_fp8 / the decode rows of pa_prefill_varlen.
 // Cascade decode: the shared prefix is cut into `shares` pieces per group of 16/G
-// sequences (enough waves for about decode_waves_per_simd per SIMD); the suffix uses the
+// sequences (about one wave per SIMD; they run in the suffix launch); the suffix uses the
 // split decode's layout (every piece partial), then the prefix partials follow.
 int cascade_prefix_shares(int num_seqs, int group, int num_kv_heads, int prefix_blocks) {
   const int per_group = std::max(1, 16 / std::max(1, group));
   const int64_t groups = std::max<int64_t>(1, (num_seqs + per_group - 1) / per_group);
-  const int64_t target = (int64_t)decode_waves_per_simd() * 4 * device_cu_count();
+  // about one prefix wave per SIMD: the suffix waves share the launch
+  const int64_t target = (int64_t)4 * device_cu_count();
   const int64_t sh = target / std::max<int64_t>(1, groups * num_kv_heads);
   return (int)std::min<int64_t>(std::max<int64_t>(sh, 1), std::max(prefix_blocks, 1));
 }
@@ -239,8 +240,8 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
     p.force_partial = 1;
     p.prefix_blocks = prefix_blocks;
     p.prefix_shares = cl.shares;
-    hipError_t e = pa::launch_decode_prefix(p, kv_kind, head_dim, stream);
-    if (e != hipSuccess) return hip_status(e, "cascade prefix launch");
+    const int per_group = 16 / p.group;
+    p.prefix_waves = (num_seqs + per_group - 1) / per_group * cl.shares;
   } else if (n_splits > 1) {
     const DecodeLayout lay = decode_layout(num_seqs, num_q_heads, n_splits, head_dim);
     auto* base = static_cast<unsigned char*>(workspace);

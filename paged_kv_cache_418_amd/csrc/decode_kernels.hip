@@ -450,27 +450,31 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
   }
 }
 
+// With a cascade, the first groups * prefix_shares work-groups of each kv head take the
+// shared prefix (cache-bound: every group re-reads the same blocks) and the rest the
+// suffixes (HBM-bound), so the two overlap in one launch.
+template <int D, bool FP8>
+__device__ __forceinline__ bool prefix_piece(const DecodeParams& p, unsigned char* k_lds, int x, int kvh) {
+  if (p.prefix_shares == 0) return false;
+  const int per_group = 16 / p.group;
+  const int groups = (p.num_seqs + per_group - 1) / per_group;
+  if (x >= groups * p.prefix_shares) return false;
+  const int share = x % p.prefix_shares, group = x / p.prefix_shares;
+  const int b0 = (int)((long long)p.prefix_blocks * share / p.prefix_shares);
+  const int b1 = (int)((long long)p.prefix_blocks * (share + 1) / p.prefix_shares);
+  if (b1 > b0) decode_piece<D, FP8, true>(p, k_lds, share, kvh, group * per_group, b0, b1, p.prefix_blocks);
+  return true;
+}
+
 template <int D, bool FP8>
 __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
   __shared__ __align__(16) unsigned char k_lds[DecodeShape<D, FP8>::kLdsBytes];
-  const int split = blockIdx.x, kvh = blockIdx.y;
+  if (prefix_piece<D, FP8>(p, k_lds, blockIdx.x, blockIdx.y)) return;
+  const int split = blockIdx.x - p.prefix_waves, kvh = blockIdx.y;
   for_each_piece(p, split, [&](int s, int b0, int b1, int nb) {
     if (kvh == 0 && threadIdx.x == 0) note_piece(p, split, s, b0, b1, nb);
     decode_piece<D, FP8>(p, k_lds, split, kvh, s, b0, b1, nb);
   });
-}
-
-// Cascade prefix: one wave per (group of 16/G sequences, prefix share, kv head).  The
-// shared prefix blocks are read once per group (and stay in the last-level cache across
-// groups) instead of once per sequence.
-template <int D, bool FP8>
-__global__ void __launch_bounds__(64) decode_prefix_kernel(DecodeParams p) {
-  __shared__ __align__(16) unsigned char k_lds[DecodeShape<D, FP8>::kLdsBytes];
-  const int share = blockIdx.x % p.prefix_shares, group = blockIdx.x / p.prefix_shares, kvh = blockIdx.y;
-  const int per_group = 16 / p.group;
-  const int b0 = (int)((long long)p.prefix_blocks * share / p.prefix_shares);
-  const int b1 = (int)((long long)p.prefix_blocks * (share + 1) / p.prefix_shares);
-  if (b1 > b0) decode_piece<D, FP8, true>(p, k_lds, share, kvh, group * per_group, b0, b1, p.prefix_blocks);
 }
 
 // fp32 pools and queries: vector-ALU kernel, one wave per (share, q head).
@@ -624,9 +628,11 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   if (kv == kF32) {
     hipLaunchKernelGGL(decode_f32_kernel<D>, dim3(p.n_splits, p.num_q_heads), dim3(64), 0, stream, p);
   } else if (kv == kFP8) {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, true>), dim3(p.n_splits, p.num_kv_heads), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, true>), dim3(p.prefix_waves + p.n_splits, p.num_kv_heads), dim3(64), 0,
+                       stream, p);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, false>), dim3(p.n_splits, p.num_kv_heads), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, false>), dim3(p.prefix_waves + p.n_splits, p.num_kv_heads), dim3(64),
+                       0, stream, p);
   }
   timing_mark(kKDecode, false, stream);
   hipError_t e = hipGetLastError();
@@ -642,25 +648,6 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream) {
   if (head_dim == 128) return launch_decode_d<128>(p, kv, stream);
   return launch_decode_d<64>(p, kv, stream);
-}
-
-hipError_t launch_decode_prefix(const DecodeParams& p, int kv, int head_dim, hipStream_t stream) {
-  const int groups = (p.num_seqs + 16 / p.group - 1) / (16 / p.group);
-  const dim3 grid(groups * p.prefix_shares, p.num_kv_heads);
-  timing_mark(kKDecodePrefix, true, stream);
-  if (head_dim == 128) {
-    if (kv == kFP8)
-      hipLaunchKernelGGL((decode_prefix_kernel<128, true>), grid, dim3(64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_prefix_kernel<128, false>), grid, dim3(64), 0, stream, p);
-  } else {
-    if (kv == kFP8)
-      hipLaunchKernelGGL((decode_prefix_kernel<64, true>), grid, dim3(64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_prefix_kernel<64, false>), grid, dim3(64), 0, stream, p);
-  }
-  timing_mark(kKDecodePrefix, false, stream);
-  return hipGetLastError();
 }
 
 }  // namespace pa

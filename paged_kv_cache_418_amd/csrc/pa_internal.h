@@ -49,6 +49,7 @@ struct DecodeParams {
   int force_partial;         // every piece leaves a partial result, none is finished in place
   int prefix_blocks;         // shared leading blocks (cascade), else 0
   int prefix_shares;         // prefix pieces per sequence (cascade), else 0
+  int prefix_waves;          // work-groups per kv head taking prefix pieces (groups x shares), else 0
   float* pre_o;              // [prefix_shares][num_seqs][Hq][D] prefix partial outputs (unnormalised)
   float* pre_m;              // [prefix_shares][num_seqs][Hq]
   float* pre_l;              // [prefix_shares][num_seqs][Hq]
@@ -110,8 +111,7 @@ enum KernelId {
   kKDecodeMerge = 3,
   kKPrefill = 4,
   kKPrefillMerge = 5,
-  kKDecodePrefix = 6,
-  kNumKernelIds = 7
+  kNumKernelIds = 6
 };
 void timing_mark(int kernel, bool begin, hipStream_t stream);
 
@@ -132,8 +132,7 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int6
 
 // kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel)
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
-// cascade prefix: grid (groups of 16/G sequences x prefix_shares, kv heads); kBF16 or kFP8
-hipError_t launch_decode_prefix(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
+
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream);
