@@ -17,7 +17,7 @@ records on its own launch stream around each kernel (pa_timing_enable), in a
 second pass of the same steps, so the headline pass carries no extra events.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--only decode|mixed|copy]   (copy: a plain 1 GiB device copy, the
+       [--only decode|mixed|cascade|copy]   (copy: a plain 1 GiB device copy, the
        reference for scaling the FETCH_SIZE / WRITE_SIZE counters)
 """
 from __future__ import annotations
@@ -51,10 +51,11 @@ def _log(*a):
 class Step:
     """Device state of one workload and the calls of one step."""
 
-    def __init__(self, w, copies: int = 2):
+    def __init__(self, w, copies: int = 2, cascade: bool = False):
         import paged_kv_cache_418_amd as pk
         self.pk = pk
         self.w = w
+        self.cascade = cascade
         dev = "cuda"
         self.pools = [(w.k_cache.to(dev), w.v_cache.to(dev))]
         for _ in range(copies - 1):
@@ -68,7 +69,10 @@ class Step:
         self.slots = torch.empty(w.num_tokens, dtype=torch.int32, device=dev)
         self.out = torch.empty_like(self.q)
         self.max_len = int(w.seq_lens.max())
-        if w.is_decode:
+        if cascade:
+            nb = pk.pa_decode_cascade_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                                      self.max_len, w.shared_prefix_blocks, 0)
+        elif w.is_decode:
             nb = pk.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, self.max_len, 0)
         else:
             nb = pk.pa_prefill_varlen_workspace_bytes(w.query_start_loc, w.seq_lens, w.num_q_heads, w.num_kv_heads,
@@ -89,7 +93,10 @@ class Step:
 
     def attend(self, kc, vc):
         w, pk = self.w, self.pk
-        if w.is_decode:
+        if self.cascade:
+            pk.pa_decode_cascade_fp8(self.q, kc, vc, self.bt, self.sl, w.scale, w.k_scale, w.v_scale, self.max_len,
+                                     w.shared_prefix_blocks, out=self.out, workspace=self.ws)
+        elif w.is_decode:
             if w.kv_dtype == "fp8":
                 pk.pa_decode_fp8(self.q, kc, vc, self.bt, self.sl, w.scale, w.k_scale, w.v_scale, self.max_len,
                                  out=self.out, workspace=self.ws)
@@ -282,6 +289,32 @@ def bench_mixed(args, result):
     torch.cuda.empty_cache()
 
 
+def bench_cascade(args, result):
+    """Prefix-shared fp8 decode (128 requests, a 2048-token shared prefix, suffixes U[128,1024]): whole steps
+    with the plain decode and with the cascade decode; logical KV bytes (each request's whole context) and
+    unique bytes (the prefix once) per second."""
+    from paged_kv_cache_418_amd import workloads as wl
+    _log("generating prefix_shared_fp8_decode ...")
+    w = wl.prefix_shared_fp8_decode()
+    logical = wl.decode_kv_bytes(w)
+    pre_tok = w.shared_prefix_blocks * w.block_size
+    unique = int(2 * (pre_tok + np.sum(w.seq_lens.astype(np.int64) - pre_tok)) * w.num_kv_heads * w.head_dim *
+                 w.kv_elem_bytes)
+    out = {"workload": "prefix_shared_fp8_decode", "num_seqs": w.num_seqs, "shared_prefix_tokens": pre_tok,
+           "logical_kv_bytes": logical, "unique_kv_bytes": unique}
+    for name, cascade in (("plain", False), ("cascade", True)):
+        st = Step(w, cascade=cascade)
+        ms, _ = time_steps(st, args.steps, args.warmup)
+        kt = kernel_times(st, args.steps, ["decode", "decode_merge"])
+        out[name] = {"ms_per_step": round(ms, 5), "logical_gbps": round(logical / (ms * 1e-3) / 1e9, 1),
+                     "unique_gbps": round(unique / (ms * 1e-3) / 1e9, 1),
+                     "decode_kernel_ms": round(kt["decode"][0], 5), "merge_kernel_ms": round(kt["decode_merge"][0], 5)}
+        del st
+    out["speedup"] = round(out["plain"]["ms_per_step"] / out["cascade"]["ms_per_step"], 3)
+    result["cascade_step"] = out
+    torch.cuda.empty_cache()
+
+
 def bench_copy(args, result):
     """A plain device-to-device copy of 1 GiB: the known-size reference for the HBM byte counters."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -297,7 +330,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", choices=["", "decode", "mixed", "copy"])
+    ap.add_argument("--only", default="", choices=["", "decode", "mixed", "cascade", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library's path runs on a single GPU and has no multi-GPU form; "
@@ -313,6 +346,8 @@ def main():
             bench_decode(args, result)
         if args.only in ("", "mixed"):
             bench_mixed(args, result)
+        if args.only in ("", "cascade"):
+            bench_cascade(args, result)
     print(json.dumps(result), flush=True)
 
 

@@ -78,6 +78,13 @@ DecodeLayout decode_layout(int64_t num_seqs, int64_t heads, int64_t n_splits, in
   return L;
 }
 
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = std::atoi(v);
+  return x >= lo && x <= hi ? x : dflt;
+}
+
 // Compute units of the current device (cached per device; 256 when no device is visible).
 int device_cu_count() {
   static std::atomic<int> cache[64];
@@ -170,8 +177,10 @@ pa_status_t check_attention_shape(int num_q_heads, int num_kv_heads, int head_di
 int cascade_prefix_shares(int num_seqs, int group, int num_kv_heads, int prefix_blocks) {
   const int per_group = std::max(1, 16 / std::max(1, group));
   const int64_t groups = std::max<int64_t>(1, (num_seqs + per_group - 1) / per_group);
-  // about one prefix wave per SIMD: the suffix waves share the launch
-  const int64_t target = (int64_t)4 * device_cu_count();
+  // about one prefix wave per SIMD (PA_CASCADE_PREFIX_WAVES_PER_CU overrides the 4 per CU):
+  // the suffix waves share the launch
+  static const int per_cu = env_int("PA_CASCADE_PREFIX_WAVES_PER_CU", 4, 1, 64);
+  const int64_t target = (int64_t)per_cu * device_cu_count();
   const int64_t sh = target / std::max<int64_t>(1, groups * num_kv_heads);
   return (int)std::min<int64_t>(std::max<int64_t>(sh, 1), std::max(prefix_blocks, 1));
 }
