@@ -245,6 +245,29 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                               size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill_varlen_fp8 -- pa_prefill_varlen over E4M3FN pools (uint8 codes)
+ * with per-tensor scales.  [B] tutorials 5 and 6, [C] core point 2.
+ * K_j = decode(code) * k_scale, V_j = decode(code) * v_scale.  Decode rows
+ * (q_len == 1) read the codes directly as in pa_decode_fp8; the blocks of
+ * the chunk sequences are first copied, as the exact bf16 values of their
+ * codes, into a staging pool in the workspace (its size depends on the
+ * chunk sequences' lengths and on bt_stride), then attended by the bf16
+ * matrix-core kernel with k_scale folded into the score scale and v_scale
+ * into the output.  q_dtype (= out dtype): PA_BF16 (PA_F32 for batches whose
+ * q_len are all 1).  Other arguments as pa_prefill_varlen.
+ */
+size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t bt_stride);
+pa_status_t pa_prefill_varlen_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                  const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                  const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                                  const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale, float v_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing, for measurement.  Not part of the pages' problem statement:
  * it serves the roofline figures (device time of each kernel of the path).
  * pa_timing_enable(1): from now on every entry point records a pair of HIP
@@ -261,7 +284,8 @@ typedef enum pa_kernel {
   PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode(_fp8), pa_decode_cascade(_fp8), decode rows of pa_prefill_varlen) */
   PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
   PA_K_PREFILL = 4,         /* the varlen prefill kernel */
-  PA_K_PREFILL_MERGE = 5    /* the log-sum-exp merge of split prefill row tiles */
+  PA_K_PREFILL_MERGE = 5,   /* the log-sum-exp merge of split prefill row tiles */
+  PA_K_STAGE_FP8 = 6        /* the fp8 -> bf16 staging of chunk sequences in pa_prefill_varlen_fp8 */
 } pa_kernel_t;
 
 pa_status_t pa_timing_enable(int on);

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 KERNELS = {"slot_mapping": 0, "reshape_and_cache": 1, "decode": 2, "decode_merge": 3, "prefill": 4,
-           "prefill_merge": 5}
+           "prefill_merge": 5, "stage_fp8": 6}
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_WORKSPACE",
           5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_HIP"}
 
@@ -75,6 +75,9 @@ def load() -> ctypes.CDLL:
             "pa_prefill_varlen_workspace_bytes": ([P, P, i32, i32, i32, i32], sz),
             "pa_prefill_varlen": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                    ctypes.c_int, P, sz, P], ctypes.c_int),
+            "pa_prefill_varlen_fp8_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
+            "pa_prefill_varlen_fp8": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                       ctypes.c_int, f32, f32, P, sz, P], ctypes.c_int),
             "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_reset": ([], ctypes.c_int),
             "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
@@ -288,3 +291,33 @@ def timing_read(kernel: str):
     n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
     _check("pa_timing_read", load().pa_timing_read(KERNELS[kernel], ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def pa_prefill_varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_q_heads: int, num_kv_heads: int,
+                                          head_dim: int, bt_stride: int) -> int:
+    q = _i32_host(query_start_loc_host)
+    s = _i32_host(seq_lens_host)
+    return int(load().pa_prefill_varlen_fp8_workspace_bytes(q.data_ptr(), s.data_ptr(), s.numel(), num_q_heads,
+                                                            num_kv_heads, head_dim, bt_stride))
+
+
+def pa_prefill_varlen_fp8(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, seq_lens_host,
+                          query_start_loc_host, scale: float, k_scale: float, v_scale: float, out=None,
+                          workspace=None):
+    """pa_prefill_varlen over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
+    lib = load()
+    T, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    qh = _i32_host(query_start_loc_host)
+    sh = _i32_host(seq_lens_host)
+    out = torch.empty_like(query) if out is None else out
+    need = int(lib.pa_prefill_varlen_fp8_workspace_bytes(qh.data_ptr(), sh.data_ptr(), sh.numel(), Hq, Hkv, D,
+                                                         block_tables.shape[1]))
+    ws, wsb = _workspace(need, query.device, workspace)
+    _check("pa_prefill_varlen_fp8", lib.pa_prefill_varlen_fp8(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(),
+        sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), float(k_scale), float(v_scale),
+        None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out

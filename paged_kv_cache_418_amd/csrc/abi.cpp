@@ -653,6 +653,165 @@ size_t varlen_workspace(const VarlenPlan& plan, int num_seqs, int num_q_heads, i
   return align_up(dec) + prefill_layout(plan.n_split_items, num_kv_heads, head_dim).total;
 }
 
+// fp8 prefill staging: bf16 copies of the blocks of every chunk sequence (q_len > 1), then
+// their table rows (same stride as the caller's tables).
+struct StageLayout {
+  int blocks = 0, max_blocks = 0;
+  size_t tables_bytes = 0, pool_bytes = 0, total = 0;
+};
+
+StageLayout stage_layout(const int32_t* qsl, const int32_t* sl, int num_seqs, int bt_stride, int num_kv_heads,
+                         int head_dim) {
+  StageLayout L;
+  int64_t blocks = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (qsl[s + 1] - qsl[s] > 1) {
+      const int nb = ceil_div(std::max(sl[s], 0), pa::kBlockSize);
+      blocks += nb;
+      L.max_blocks = std::max(L.max_blocks, nb);
+    }
+  L.blocks = (int)std::min<int64_t>(blocks, INT32_MAX);
+  L.tables_bytes = align_up((size_t)num_seqs * bt_stride * sizeof(int32_t));
+  L.pool_bytes = align_up((size_t)blocks * pa::kBlockSize * num_kv_heads * head_dim * sizeof(uint16_t));
+  L.total = blocks ? L.tables_bytes + 2 * L.pool_bytes : 0;
+  return L;
+}
+
+// The varlen call for bf16 pools (kv_kind kBF16; dtype PA_F32 allowed for decode-only
+// batches) and for fp8 pools (kFP8: decode rows read the codes directly; the chunk
+// sequences' blocks are first staged as exact bf16 values, see launch_stage_fp8).
+pa_status_t run_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                       const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, pa_dtype_t dtype, int kv_kind, float k_scale, float v_scale,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_SHAPE, "negative num_seqs or num_tokens");
+  if (num_seqs == 0) return num_tokens == 0 ? ok() : fail(PA_ERR_SHAPE, "num_tokens > 0 with no sequences");
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc ||
+      !seq_lens_host || !query_start_loc_host)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, bt_stride);
+  if (st != PA_OK) return st;
+  if (num_q_heads / num_kv_heads > pa::kMaxGroup && (dtype == PA_BF16 || kv_kind == pa::kFP8))
+    return fail(PA_ERR_UNSUPPORTED, "up to %d q heads per kv head", pa::kMaxGroup);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+  VarlenPlan plan;
+  st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
+                   num_q_heads / num_kv_heads, num_kv_heads, plan);
+  if (st != PA_OK) return st;
+  if (dtype == PA_F32 && !plan.items.empty())
+    return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
+  const StageLayout stage = kv_kind == pa::kFP8 ? stage_layout(query_start_loc_host, seq_lens_host, num_seqs, bt_stride,
+                                                                num_kv_heads, head_dim)
+                                                   : StageLayout{};
+  const size_t base_need = varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
+  const size_t need = plan.items.empty() ? base_need : align_up(base_need) + stage.total;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (validate_enabled()) {
+    std::vector<int32_t> q, sl;
+    if (!copy_to_host(q, query_start_loc, num_seqs + 1) || !copy_to_host(sl, seq_lens, num_seqs))
+      return fail(PA_ERR_HIP, "PA_VALIDATE: metadata copy failed");
+    for (int s = 0; s <= num_seqs; ++s)
+      if (q[s] != query_start_loc_host[s]) return fail(PA_ERR_SHAPE, "PA_VALIDATE: host/device query_start_loc differ");
+    for (int s = 0; s < num_seqs; ++s)
+      if (sl[s] != seq_lens_host[s]) return fail(PA_ERR_SHAPE, "PA_VALIDATE: host/device seq_lens differ");
+    int max_len = 1;
+    for (int s = 0; s < num_seqs; ++s) max_len = std::max(max_len, (int)seq_lens_host[s]);
+    st = validate_tables(block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, num_blocks, max_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (plan.any_decode) {
+    st = run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
+                    num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, plan.max_decode_len, scale,
+                    kv_kind == pa::kFP8 ? pa::kFP8 : (dtype == PA_F32 ? pa::kF32 : pa::kBF16), dtype == PA_F32,
+                    k_scale, v_scale, 0, workspace, workspace_bytes, hs);
+    if (st != PA_OK) return st;
+  }
+  auto* ws = static_cast<unsigned char*>(workspace);
+  const size_t dec_bytes = plan.max_decode_len ? align_up(pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                                                    head_dim, plan.max_decode_len, 0))
+                                               : 0;
+  const PrefillLayout lay = prefill_layout(plan.n_split_items, num_kv_heads, head_dim);
+  uint16_t* part_o = plan.n_split_items ? reinterpret_cast<uint16_t*>(ws + dec_bytes) : nullptr;
+  float* part_m = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes) : nullptr;
+  float* part_l = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + lay.m_bytes) : nullptr;
+  // fp8: stage the chunk sequences' blocks, then run the bf16 kernel on the staging pool
+  const void* pk_cache = key_cache;
+  const void* pv_cache = value_cache;
+  const int32_t* p_tables = block_tables;
+  int p_num_blocks = num_blocks;
+  if (kv_kind == pa::kFP8 && !plan.items.empty()) {
+    unsigned char* sbase = ws + align_up(base_need);
+    auto* st_tables = reinterpret_cast<int32_t*>(sbase);
+    auto* st_k = reinterpret_cast<uint16_t*>(sbase + stage.tables_bytes);
+    auto* st_v = reinterpret_cast<uint16_t*>(sbase + stage.tables_bytes + stage.pool_bytes);
+    st = hip_status(pa::launch_stage_fp8(static_cast<const uint8_t*>(key_cache), static_cast<const uint8_t*>(value_cache),
+                                         block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, stage.max_blocks,
+                                         num_kv_heads, head_dim, num_blocks, st_k, st_v, st_tables, hs),
+                    "fp8 staging launch");
+    if (st != PA_OK) return st;
+    pk_cache = st_k;
+    pv_cache = st_v;
+    p_tables = st_tables;
+    p_num_blocks = stage.blocks;
+  }
+  for (size_t i0 = 0; i0 < plan.items.size(); i0 += pa::kMaxPrefillItems) {
+    pa::PrefillParams p{};
+    p.out = out;
+    p.query = query;
+    p.key_cache = pk_cache;
+    p.value_cache = pv_cache;
+    p.block_tables = p_tables;
+    p.seq_lens = seq_lens;
+    p.qsl = query_start_loc;
+    p.part_o = part_o;
+    p.part_m = part_m;
+    p.part_l = part_l;
+    p.bt_stride = bt_stride;
+    p.num_tokens = num_tokens;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
+    p.num_blocks = p_num_blocks;
+    p.tile_positions = plan.tile_positions;
+    p.item_base = (int)i0;
+    p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
+    p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
+    const size_t n = std::min(plan.items.size() - i0, (size_t)pa::kMaxPrefillItems);
+    p.n_items = (int)n;
+    std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint64_t));
+    st = hip_status(pa::launch_prefill(p, head_dim, hs), "prefill launch");
+    if (st != PA_OK) return st;
+  }
+  for (size_t i0 = 0; i0 < plan.merges.size(); i0 += pa::kMaxPrefillItems) {
+    pa::PrefillMergeParams p{};
+    p.out = out;
+    p.qsl = query_start_loc;
+    p.part_o = part_o;
+    p.part_m = part_m;
+    p.part_l = part_l;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
+    p.tile_positions = plan.tile_positions;
+    p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
+    const size_t n = std::min(plan.merges.size() - i0, (size_t)pa::kMaxPrefillItems);
+    p.n_items = (int)n;
+    std::memcpy(p.items, plan.merges.data() + i0, n * sizeof(uint64_t));
+    st = hip_status(pa::launch_prefill_merge(p, head_dim, hs), "prefill merge launch");
+    if (st != PA_OK) return st;
+  }
+  return ok();
+}
+
+
+
 }  // namespace
 
 size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
@@ -679,101 +838,38 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                               int32_t num_blocks, float scale, pa_dtype_t dtype, void* workspace,
                               size_t workspace_bytes, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_BF16 (or PA_F32 for decode rows)");
-  if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_SHAPE, "negative num_seqs or num_tokens");
-  if (num_seqs == 0) return num_tokens == 0 ? ok() : fail(PA_ERR_SHAPE, "num_tokens > 0 with no sequences");
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc ||
-      !seq_lens_host || !query_start_loc_host)
-    return fail(PA_ERR_NULL, "a required pointer is NULL");
-  pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, bt_stride);
-  if (st != PA_OK) return st;
-  if (num_q_heads / num_kv_heads > pa::kMaxGroup && dtype == PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "up to %d q heads per kv head", pa::kMaxGroup);
-  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
-  VarlenPlan plan;
-  st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
-                   num_q_heads / num_kv_heads, num_kv_heads, plan);
-  if (st != PA_OK) return st;
-  if (dtype == PA_F32 && !plan.items.empty())
-    return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
-  const size_t need = varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
-  if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
-    return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (validate_enabled()) {
-    std::vector<int32_t> q, sl;
-    if (!copy_to_host(q, query_start_loc, num_seqs + 1) || !copy_to_host(sl, seq_lens, num_seqs))
-      return fail(PA_ERR_HIP, "PA_VALIDATE: metadata copy failed");
-    for (int s = 0; s <= num_seqs; ++s)
-      if (q[s] != query_start_loc_host[s]) return fail(PA_ERR_SHAPE, "PA_VALIDATE: host/device query_start_loc differ");
-    for (int s = 0; s < num_seqs; ++s)
-      if (sl[s] != seq_lens_host[s]) return fail(PA_ERR_SHAPE, "PA_VALIDATE: host/device seq_lens differ");
-    int max_len = 1;
-    for (int s = 0; s < num_seqs; ++s) max_len = std::max(max_len, (int)seq_lens_host[s]);
-    st = validate_tables(block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, num_blocks, max_len, block_size);
-    if (st != PA_OK) return st;
-  }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (plan.any_decode) {
-    st = run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
-                    num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, plan.max_decode_len, scale,
-                    dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype == PA_F32, 1.f, 1.f, 0, workspace, workspace_bytes,
-                    hs);
-    if (st != PA_OK) return st;
-  }
-  auto* ws = static_cast<unsigned char*>(workspace);
-  const size_t dec_bytes = plan.max_decode_len ? align_up(pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
-                                                                                    head_dim, plan.max_decode_len, 0))
-                                               : 0;
-  const PrefillLayout lay = prefill_layout(plan.n_split_items, num_kv_heads, head_dim);
-  uint16_t* part_o = plan.n_split_items ? reinterpret_cast<uint16_t*>(ws + dec_bytes) : nullptr;
-  float* part_m = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes) : nullptr;
-  float* part_l = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + lay.m_bytes) : nullptr;
-  for (size_t i0 = 0; i0 < plan.items.size(); i0 += pa::kMaxPrefillItems) {
-    pa::PrefillParams p{};
-    p.out = out;
-    p.query = query;
-    p.key_cache = key_cache;
-    p.value_cache = value_cache;
-    p.block_tables = block_tables;
-    p.seq_lens = seq_lens;
-    p.qsl = query_start_loc;
-    p.part_o = part_o;
-    p.part_m = part_m;
-    p.part_l = part_l;
-    p.bt_stride = bt_stride;
-    p.num_tokens = num_tokens;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = num_kv_heads;
-    p.group = num_q_heads / num_kv_heads;
-    p.num_blocks = num_blocks;
-    p.tile_positions = plan.tile_positions;
-    p.item_base = (int)i0;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    const size_t n = std::min(plan.items.size() - i0, (size_t)pa::kMaxPrefillItems);
-    p.n_items = (int)n;
-    std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint64_t));
-    st = hip_status(pa::launch_prefill(p, head_dim, hs), "prefill launch");
-    if (st != PA_OK) return st;
-  }
-  for (size_t i0 = 0; i0 < plan.merges.size(); i0 += pa::kMaxPrefillItems) {
-    pa::PrefillMergeParams p{};
-    p.out = out;
-    p.qsl = query_start_loc;
-    p.part_o = part_o;
-    p.part_m = part_m;
-    p.part_l = part_l;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = num_kv_heads;
-    p.group = num_q_heads / num_kv_heads;
-    p.tile_positions = plan.tile_positions;
-    const size_t n = std::min(plan.merges.size() - i0, (size_t)pa::kMaxPrefillItems);
-    p.n_items = (int)n;
-    std::memcpy(p.items, plan.merges.data() + i0, n * sizeof(uint64_t));
-    st = hip_status(pa::launch_prefill_merge(p, head_dim, hs), "prefill merge launch");
-    if (st != PA_OK) return st;
-  }
-  return ok();
+  return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
+                    seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t bt_stride) {
+  const size_t base = pa_prefill_varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads,
+                                                        num_kv_heads, head_dim);
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_kv_heads < 1 || head_dim < 1 || bt_stride < 1)
+    return base;
+  const StageLayout stage = stage_layout(query_start_loc_host, seq_lens_host, num_seqs, bt_stride, num_kv_heads,
+                                         head_dim);
+  return stage.total ? align_up(base) + stage.total : base;
+}
+
+pa_status_t pa_prefill_varlen_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                  const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                  const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                                  const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale, float v_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16)
+    return fail(PA_ERR_DTYPE, "q_dtype must be PA_BF16 (or PA_F32 for decode rows)");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
+                    seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, scale, q_dtype, pa::kFP8, k_scale, v_scale, workspace, workspace_bytes,
+                    stream);
 }
 
 }  // extern "C"

@@ -82,6 +82,7 @@ struct PrefillParams {
   int tile_positions;        // positions per row tile: 256 / group
   int item_base;
   float scale_log2;
+  float v_scale;             // 1, or the fp8 value scale (pools staged as the codes' exact values)
   int n_items;
   uint64_t items[kMaxPrefillItems];
 };
@@ -98,6 +99,7 @@ struct PrefillMergeParams {
   int num_kv_heads;
   int group;
   int tile_positions;
+  float v_scale;
   int n_items;
   uint64_t items[kMaxPrefillItems];
 };
@@ -111,7 +113,8 @@ enum KernelId {
   kKDecodeMerge = 3,
   kKPrefill = 4,
   kKPrefillMerge = 5,
-  kNumKernelIds = 6
+  kKStageFp8 = 6,
+  kNumKernelIds = 7
 };
 void timing_mark(int kernel, bool begin, hipStream_t stream);
 
@@ -135,6 +138,13 @@ hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_
 
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
+// fp8 prefill: the blocks of every sequence with q_len > 1 copied, as the exact bf16
+// values of their codes, into a compact staging pool (sequence s's blocks from the sum
+// of the block counts of the chunk sequences before it), with its staging table row.
+hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
+                            int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
+                            int max_blocks, int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k,
+                            uint16_t* stage_v, int32_t* stage_tables, hipStream_t stream);
 hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace pa

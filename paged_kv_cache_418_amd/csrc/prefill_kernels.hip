@@ -575,7 +575,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   const int pos = pos0 + R / G, h = kvh * G + (R % G);
   // lane's outputs: d = n*32 + 8*(r/4) + 4*half + r%4
   if (whole) {
-    const float inv = 1.f / l;
+    const float inv = p.v_scale / l;
     uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(q0 + pos) * p.num_q_heads + h) * D;
 #pragma unroll
     for (int n = 0; n < Sh::kDTiles; ++n)
@@ -657,7 +657,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
       for (int j = 0; j < PER_LANE; ++j) o[j] = o[j] * a + src[j] * b;
       M = Mn;
     }
-    const float inv = 1.f / den;
+    const float inv = p.v_scale / den;
     const int h = kvh * G + (R % G);
     uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(q0 + pos) * p.num_q_heads + h) * D + lane * PER_LANE;
 #pragma unroll
@@ -665,7 +665,74 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
   }
 }
 
+// fp8 staging: one work-group of 256 threads per (sequence, 8 blocks).  Sequence s's
+// first staging block is the sum of the block counts of the sequences before it that
+// have q_len > 1 (a block-wide sum over them; the batch's sequence count is small next
+// to the blocks moved).  Each thread turns 16 codes into 16 bf16 values per step.
+__global__ void __launch_bounds__(256) stage_fp8_kernel(const uint8_t* key_cache, const uint8_t* value_cache,
+                                                         const int32_t* block_tables, int bt_stride,
+                                                         const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
+                                                         int row_bytes, int num_blocks, uint16_t* stage_k,
+                                                         uint16_t* stage_v, int32_t* stage_tables) {
+  constexpr int kBlocksPerGroup = 8;
+  __shared__ int red[256];
+  const int s = blockIdx.x;
+  if (qsl[s + 1] - qsl[s] <= 1) return;
+  const int nb = (seq_lens[s] + 15) >> 4;
+  const int j0 = blockIdx.y * kBlocksPerGroup;
+  if (j0 >= nb) return;
+  int acc = 0;
+  for (int t = threadIdx.x; t < s; t += 256) acc += qsl[t + 1] - qsl[t] > 1 ? (seq_lens[t] + 15) >> 4 : 0;
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const int base = red[0];
+  const int j1 = min(nb, j0 + kBlocksPerGroup);
+  const int block_bytes = 16 * row_bytes;  // codes per block (one byte each)
+  for (int j = j0; j < j1; ++j) {
+    const int phys = min(max(block_tables[(size_t)s * bt_stride + j], 0), num_blocks - 1);
+    const int dst = base + j;
+    if (threadIdx.x == 0) stage_tables[(size_t)s * bt_stride + j] = dst;
+    const uint8_t* ks = key_cache + (size_t)phys * block_bytes;
+    const uint8_t* vs = value_cache + (size_t)phys * block_bytes;
+    uint16_t* kd = stage_k + (size_t)dst * block_bytes;
+    uint16_t* vd = stage_v + (size_t)dst * block_bytes;
+    for (int e = threadIdx.x * 16; e < block_bytes; e += 256 * 16) {
+      const u32x4 kc = *reinterpret_cast<const u32x4*>(ks + e);
+      const u32x4 vc = *reinterpret_cast<const u32x4*>(vs + e);
+      u32x4 klo, khi, vlo, vhi;
+      const u32x2 k0 = e4m3x4_to_bf16x4(kc.x), k1 = e4m3x4_to_bf16x4(kc.y), k2 = e4m3x4_to_bf16x4(kc.z),
+                  k3 = e4m3x4_to_bf16x4(kc.w);
+      const u32x2 v0 = e4m3x4_to_bf16x4(vc.x), v1 = e4m3x4_to_bf16x4(vc.y), v2 = e4m3x4_to_bf16x4(vc.z),
+                  v3 = e4m3x4_to_bf16x4(vc.w);
+      klo = u32x4{k0.x, k0.y, k1.x, k1.y};
+      khi = u32x4{k2.x, k2.y, k3.x, k3.y};
+      vlo = u32x4{v0.x, v0.y, v1.x, v1.y};
+      vhi = u32x4{v2.x, v2.y, v3.x, v3.y};
+      *reinterpret_cast<u32x4*>(kd + e) = klo;
+      *reinterpret_cast<u32x4*>(kd + e + 8) = khi;
+      *reinterpret_cast<u32x4*>(vd + e) = vlo;
+      *reinterpret_cast<u32x4*>(vd + e + 8) = vhi;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
+                            int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int max_blocks,
+                            int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k, uint16_t* stage_v,
+                            int32_t* stage_tables, hipStream_t stream) {
+  const dim3 grid(num_seqs, (max_blocks + 7) / 8);
+  timing_mark(kKStageFp8, true, stream);
+  hipLaunchKernelGGL(stage_fp8_kernel, grid, dim3(256), 0, stream, key_cache, value_cache, block_tables, bt_stride,
+                     seq_lens, qsl, num_seqs, num_kv_heads * head_dim, num_blocks, stage_k, stage_v, stage_tables);
+  timing_mark(kKStageFp8, false, stream);
+  return hipGetLastError();
+}
 
 size_t prefill_lds_bytes(int head_dim) {
   return head_dim == 128 ? PrefillShape<128>::kLdsBytes : PrefillShape<64>::kLdsBytes;

@@ -61,6 +61,10 @@ class DevWorkload:
 
     def prefill(self, out=None):
         w = self.w
+        if w.kv_dtype == "fp8":
+            return pk.pa_prefill_varlen_fp8(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                            self.qsl, w.seq_lens, w.query_start_loc, w.scale, w.k_scale, w.v_scale,
+                                            out=out)
         return pk.pa_prefill_varlen(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
                                     self.qsl, w.seq_lens, w.query_start_loc, w.scale, out=out)
 

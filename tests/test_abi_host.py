@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 17
+    assert len(syms) == 19
     assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
@@ -179,3 +179,22 @@ def test_cascade_workspace_and_argument_checks(lib):
     assert lib.pa_decode_cascade(*args, b.PA_BF16, 0, 0, FAKE, 1 << 30, None) == 2         # no prefix
     assert lib.pa_decode_cascade(*args, b.PA_BF16, 8, 0, FAKE, 16, None) == 4              # workspace too small
     assert lib.pa_decode_cascade_fp8(*args, b.PA_BF16, 0.05, -1.0, 8, 0, FAKE, 1 << 30, None) == 2  # v_scale
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def test_prefill_fp8_workspace_adds_staging(lib):
+    # chunks of 40 and 300 tokens on 100- and 900-token contexts: staging = ceil(100/16) + ceil(900/16) = 7 + 57
+    # blocks, bf16 K and V of 16 x 8 x 128 each, plus the staging table rows (3 sequences x 64 columns)
+    q, s = _host_i32([0, 40, 41, 341]), _host_i32([100, 5000, 900])
+    base = lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128)
+    got = lib.pa_prefill_varlen_fp8_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128, 400)
+    pool = _align((7 + 57) * 16 * 8 * 128 * 2)
+    assert got == _align(base) + _align(3 * 400 * 4) + 2 * pool
+    # decode rows only: no staging
+    q1, s1 = _host_i32([0, 1, 2]), _host_i32([1000, 10])
+    assert lib.pa_prefill_varlen_fp8_workspace_bytes(ctypes.addressof(q1), ctypes.addressof(s1), 2, 32, 8, 128,
+                                                     100) == \
+        lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q1), ctypes.addressof(s1), 2, 32, 8, 128)

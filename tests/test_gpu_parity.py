@@ -307,6 +307,57 @@ def test_prefill_varlen_random(seed, heads):
     assert err <= TOL["bf16"]
 
 
+# ---- fp8-KV prefill (blocks of the chunk sequences staged as exact bf16 values)
+
+@pytest.mark.parametrize("seed", [451, 452])
+@pytest.mark.parametrize("heads", [(32, 8, 128), (4, 2, 64), (12, 4, 128)])
+def test_prefill_varlen_fp8_random(seed, heads):
+    Hq, Hkv, D = heads
+    w = wl.random_case(seed, num_seqs=6, ctx_range=(1, 700), chunk_range=(1, 400), num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, q_dtype="bf16", kv_dtype="fp8", k_scale=0.05, v_scale=0.04)
+    say("prefill fp8 random", seed, heads, list(w.q_lens), list(w.seq_lens))
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["fp8"]
+
+
+def test_prefill_fp8_long_chunks_and_decode_rows():
+    """Split row tiles over long fp8 contexts, with decode rows (read as codes) in the same batch."""
+    w = wl.build("prefill_fp8_long", seed=461, ctx_lens=[2200, 700, 35, 1900, 900], q_lens=[700, 1, 35, 333, 1],
+                 num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="fp8", k_scale=0.05,
+                 v_scale=0.04)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    say("prefill fp8 long chunks + decode rows")
+    out = d.prefill()
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["fp8"]
+
+
+def test_prefill_fp8_matches_bf16_on_the_same_values():
+    """The fp8 path on codes equals the bf16 path on the codes' exact bf16 values (scales 1): the staging is exact,
+    so only the summation order of nothing differs -- the two outputs are bit-identical."""
+    w = wl.random_case(471, num_seqs=4, ctx_range=(100, 600), chunk_range=(50, 300), num_q_heads=16, num_kv_heads=4,
+                       head_dim=128, q_dtype="bf16", kv_dtype="fp8", k_scale=1.0, v_scale=1.0)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    say("prefill fp8 vs bf16 of the same values")
+    out8 = d.prefill().cpu()
+    lut = torch.tensor([oracle.fp8_decode(c) for c in range(256)], dtype=torch.float32).to(torch.bfloat16).cuda()
+    kb, vb = lut[d.k_cache.long()], lut[d.v_cache.long()]
+    outb = pk.pa_prefill_varlen(d.query, kb, vb, d.block_tables, d.seq_lens, d.qsl, w.seq_lens, w.query_start_loc,
+                                w.scale).cpu()
+    assert torch.equal(out8.view(torch.int16), outb.view(torch.int16))
+
+
 def test_prefill_decode_rows_fp32():
     w = wl.random_case(411, num_seqs=5, ctx_range=(1, 300), num_q_heads=4, num_kv_heads=2, head_dim=64)
     d = DevWorkload(w)
