@@ -74,6 +74,9 @@ class Step:
                                                       self.max_len, w.shared_prefix_blocks, 0)
         elif w.is_decode:
             nb = pk.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, self.max_len, 0)
+        elif w.kv_dtype == "fp8":
+            nb = pk.pa_prefill_varlen_fp8_workspace_bytes(w.query_start_loc, w.seq_lens, w.num_q_heads,
+                                                          w.num_kv_heads, w.head_dim, w.block_tables.shape[1])
         else:
             nb = pk.pa_prefill_varlen_workspace_bytes(w.query_start_loc, w.seq_lens, w.num_q_heads, w.num_kv_heads,
                                                       w.head_dim)
@@ -102,6 +105,9 @@ class Step:
                                  out=self.out, workspace=self.ws)
             else:
                 pk.pa_decode(self.q, kc, vc, self.bt, self.sl, w.scale, self.max_len, out=self.out, workspace=self.ws)
+        elif w.kv_dtype == "fp8":
+            pk.pa_prefill_varlen_fp8(self.q, kc, vc, self.bt, self.sl, self.qsl, w.seq_lens, w.query_start_loc,
+                                     w.scale, w.k_scale, w.v_scale, out=self.out, workspace=self.ws)
         else:
             pk.pa_prefill_varlen(self.q, kc, vc, self.bt, self.sl, self.qsl, w.seq_lens, w.query_start_loc, w.scale,
                                  out=self.out, workspace=self.ws)
@@ -262,6 +268,12 @@ def bench_mixed(args, result):
     kt = kernel_times(cs.attend_next, args.steps, ["prefill"])
     pre_ms = kt["prefill"][0]
     del cs
+    # the same two chunks over fp8 pools: staging + bf16 kernel + merge
+    w8 = wl.mixed_step_bf16(kv_dtype="fp8")
+    cs8 = Step(_sub(w8, list(range(48, 50))), copies=1)
+    pre8_call_ms, _ = time_steps(cs8.attend_next, args.steps, args.warmup)
+    kt8 = kernel_times(cs8.attend_next, args.steps, ["prefill", "stage_fp8"])
+    del cs8, w8
     dec_w = _sub(w, list(range(48)))
     ds = Step(dec_w, copies=2)
     dms, _ = time_steps(ds.attend_next, args.steps, args.warmup)
@@ -277,6 +289,9 @@ def bench_mixed(args, result):
                                   "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                                   "alg_flops_per_launch": flops},
+             "prefill_fp8": {"call_ms": round(pre8_call_ms, 5), "kernel_ms": round(kt8["prefill"][0], 5),
+                             "staging_ms": round(kt8["stage_fp8"][0], 5),
+                             "call_tflops": round(flops / (pre8_call_ms * 1e-3) / 1e12, 2)},
              "decode_part_gbps": round(dec_bytes / (dms * 1e-3) / 1e9, 2),
              "decode_part_ms": round(dms, 5)}
     if "metric" in result:

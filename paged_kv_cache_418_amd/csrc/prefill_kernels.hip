@@ -665,7 +665,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
   }
 }
 
-// fp8 staging: one work-group of 256 threads per (sequence, 8 blocks).  Sequence s's
+// fp8 staging: one work-group of 256 threads per (sequence, block).  Sequence s's
 // first staging block is the sum of the block counts of the sequences before it that
 // have q_len > 1 (a block-wide sum over them; the batch's sequence count is small next
 // to the blocks moved).  Each thread turns 16 codes into 16 bf16 values per step.
@@ -674,7 +674,7 @@ __global__ void __launch_bounds__(256) stage_fp8_kernel(const uint8_t* key_cache
                                                          const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
                                                          int row_bytes, int num_blocks, uint16_t* stage_k,
                                                          uint16_t* stage_v, int32_t* stage_tables) {
-  constexpr int kBlocksPerGroup = 8;
+  constexpr int kBlocksPerGroup = 1;
   __shared__ int red[256];
   const int s = blockIdx.x;
   if (qsl[s + 1] - qsl[s] <= 1) return;
@@ -726,7 +726,7 @@ hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache
                             int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int max_blocks,
                             int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k, uint16_t* stage_v,
                             int32_t* stage_tables, hipStream_t stream) {
-  const dim3 grid(num_seqs, (max_blocks + 7) / 8);
+  const dim3 grid(num_seqs, max_blocks);
   timing_mark(kKStageFp8, true, stream);
   hipLaunchKernelGGL(stage_fp8_kernel, grid, dim3(256), 0, stream, key_cache, value_cache, block_tables, bt_stride,
                      seq_lens, qsl, num_seqs, num_kv_heads * head_dim, num_blocks, stage_k, stage_v, stage_tables);

@@ -228,16 +228,19 @@ def llama3_8b_decode_bf16(num_seqs: int = 64) -> Workload:
                  q_dtype="bf16", kv_dtype="bf16", max_blocks=256)
 
 
-def mixed_step_bf16(num_decode: int = 48, chunk: int = 512, cached: Sequence[int] = (0, 1536)) -> Workload:
+def mixed_step_bf16(num_decode: int = 48, chunk: int = 512, cached: Sequence[int] = (0, 1536),
+                    kv_dtype: str = "bf16") -> Workload:
     """Mixed continuous-batching step: 48 decodes (ctx U[256,8192]) then two 512-token
-    chunked-prefill chunks with 0 and 1536 cached tokens; 32 q / 8 kv heads, D 128, bf16."""
+    chunked-prefill chunks with 0 and 1536 cached tokens; 32 q / 8 kv heads, D 128, bf16
+    (kv_dtype "fp8": the same step over E4M3 pools with scales K 0.05, V 0.04)."""
     rng = np.random.default_rng(SEED_BASE + 2)
     ctx_dec = rng.integers(256, 8192, num_decode, endpoint=True)
     ctx = list(ctx_dec) + [c + chunk for c in cached]
     ql = [1] * num_decode + [chunk] * len(cached)
-    return build("mixed_step_bf16", seed=SEED_BASE + 2, rng=rng, ctx_lens=ctx, q_lens=ql,
-                 num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16",
-                 max_blocks=512)
+    fp8 = kv_dtype == "fp8"
+    return build("mixed_step_fp8" if fp8 else "mixed_step_bf16", seed=SEED_BASE + 2, rng=rng, ctx_lens=ctx,
+                 q_lens=ql, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype=kv_dtype,
+                 max_blocks=512, k_scale=0.05 if fp8 else 1.0, v_scale=0.04 if fp8 else 1.0)
 
 
 def long_ctx_70b_decode_bf16(num_seqs: int = 8) -> Workload:
