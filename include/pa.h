@@ -132,8 +132,8 @@ pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t
 /*
  * pa_decode_workspace_bytes -- scratch pa_decode / pa_decode_fp8 need.
  * The blocks of all sequences, laid end to end, are cut into num_splits
- * equal shares per kv head (0 = automatic: about two waves per SIMD of the
- * current device, PA_DECODE_WAVES_PER_SIMD overrides the two); a sequence
+ * equal shares per kv head (0 = automatic: about one wave per SIMD of the
+ * current device, PA_DECODE_WAVES_PER_SIMD overrides the one); a sequence
  * split across shares gets partial results that are merged with the
  * log-sum-exp rule ([B] tutorial 7).  The count is capped at
  * num_seqs * ceil(max_seq_len / 16).  Returns 0 when a single share is used
