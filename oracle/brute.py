@@ -37,8 +37,10 @@ def _value(flat, idx: int, kind: str, scale: float) -> float:
 
 
 def attention(query, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, query_start_loc,
-              num_q_heads, num_kv_heads, head_dim, block_size, scale, k_scale=1.0, v_scale=1.0) -> List:
+              num_q_heads, num_kv_heads, head_dim, block_size, scale, k_scale=1.0, v_scale=1.0,
+              window=0) -> List:
     """Inputs are flat Python lists (bf16 as uint16 bit patterns, fp8 as codes).
+    window > 0: the row at position p sees only the keys p - window + 1 .. p (those >= 0).
 
     Returns out[t][h][d] as nested lists of floats."""
     G = num_q_heads // num_kv_heads
@@ -55,6 +57,8 @@ def attention(query, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, 
                 q = [_value(query, (t * num_q_heads + h) * head_dim + d, q_kind, 1.0) for d in range(head_dim)]
                 keys = []
                 for j in range(pos + 1):
+                    if window and j <= pos - window:
+                        continue
                     blk = block_tables[s][j // block_size]
                     base = ((blk * block_size + j % block_size) * num_kv_heads + kvh) * head_dim
                     keys.append(base)
@@ -74,7 +78,7 @@ def attention(query, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, 
     return out
 
 
-def from_workload(w, pools):
+def from_workload(w, pools, window=0):
     """Runs attention() on a workload's tensors (converted to flat lists)."""
     import torch
 
@@ -88,4 +92,4 @@ def from_workload(w, pools):
     return attention(flat(w.query), w.q_dtype, flat(kc), flat(vc), w.kv_dtype,
                      [list(map(int, r)) for r in w.block_tables], [int(v) for v in w.seq_lens],
                      [int(v) for v in w.query_start_loc], w.num_q_heads, w.num_kv_heads, w.head_dim,
-                     w.block_size, float(w.scale), float(w.k_scale), float(w.v_scale))
+                     w.block_size, float(w.scale), float(w.k_scale), float(w.v_scale), window=window)

@@ -207,12 +207,34 @@ int oracle_reshape_and_cache_fp8(const void* key, const void* value, int64_t key
 /* out[r][h][d] (fp64) for the query rows listed in rows[0..n_rows) (all rows
  * 0..T-1 when rows is NULL, n_rows = T).  Returns 0, or -1 on inconsistent
  * metadata. kv values of fp8 pools are decode(code) * k_scale / v_scale. */
+/* Sliding window (window > 0): the row at position pos sees keys max(0, pos - window + 1)
+ * .. pos, a window of `window` tokens ending at its own.  window == 0: every key 0 .. pos.
+ * (The reading of the pages' sliding-window attention; the pages fix no boundary.) */
+int oracle_attention_window(double* out, const void* query, int32_t q_dtype, const void* key_cache,
+                            const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                            const int32_t* rows, int32_t n_rows, int32_t window);
+
 int oracle_attention(double* out, const void* query, int32_t q_dtype, const void* key_cache,
                      const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
                      const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                      const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                      const int32_t* rows, int32_t n_rows) {
+  return oracle_attention_window(out, query, q_dtype, key_cache, value_cache, kv_dtype, k_scale, v_scale,
+                                 block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, num_q_heads,
+                                 num_kv_heads, head_dim, block_size, scale, rows, n_rows, 0);
+}
+
+int oracle_attention_window(double* out, const void* query, int32_t q_dtype, const void* key_cache,
+                            const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                            const int32_t* rows, int32_t n_rows, int32_t window) {
+  if (window < 0) return -1;
   if (num_q_heads % num_kv_heads) return -1;
   int group = num_q_heads / num_kv_heads;
   int T = query_start_loc[num_seqs];
@@ -230,6 +252,7 @@ int oracle_attention(double* out, const void* query, int32_t q_dtype, const void
     int cached = seq_lens[s] - q_len;
     int pos = cached + (t - query_start_loc[s]);
     int kvh = h / group;
+    int j0 = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0; /* first visible key */
     int n_keys = pos + 1;
     double* z = (double*)malloc(sizeof(double) * n_keys);
     double* q = (double*)malloc(sizeof(double) * head_dim);
@@ -237,7 +260,7 @@ int oracle_attention(double* out, const void* query, int32_t q_dtype, const void
       q[d] = load_elem(query, ((int64_t)t * num_q_heads + h) * head_dim + d, q_dtype);
     /* pass 1: scores and their max */
     double m = -INFINITY;
-    for (int j = 0; j < n_keys; ++j) {
+    for (int j = j0; j < n_keys; ++j) {
       int phys = block_tables[(int64_t)s * bt_stride + j / block_size];
       int off = j % block_size;
       int64_t base = (((int64_t)phys * block_size + off) * num_kv_heads + kvh) * head_dim;
@@ -254,7 +277,7 @@ int oracle_attention(double* out, const void* query, int32_t q_dtype, const void
     double l = 0.0;
     double* o = out + ((int64_t)ri * num_q_heads + h) * head_dim;
     for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
-    for (int j = 0; j < n_keys; ++j) {
+    for (int j = j0; j < n_keys; ++j) {
       double w = exp(z[j] - m);
       l += w;
       int phys = block_tables[(int64_t)s * bt_stride + j / block_size];

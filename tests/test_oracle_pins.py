@@ -455,3 +455,66 @@ def test_poison_never_reaches_the_oracle():
     slots = oracle.slot_mapping(w.block_tables, w.seq_lens, w.query_start_loc)
     flat = w.k_cache.reshape(-1, w.num_kv_heads, w.head_dim)
     assert torch.all(flat[torch.from_numpy(slots.astype(np.int64))] == wl.FP8_NAN_CODE)
+
+
+# ---- sliding window (reading: the row at position p sees keys max(0, p - W + 1) .. p)
+
+@pytest.mark.parametrize("kinds", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8")])
+@pytest.mark.parametrize("window", [1, 3, 17])
+def test_window_brute_force_agrees(kinds, window):
+    w = wl.random_case(81 + window, num_seqs=3, ctx_range=(1, 40), chunk_range=(1, 6), num_q_heads=4,
+                       num_kv_heads=2, head_dim=8, q_dtype=kinds[0], kv_dtype=kinds[1], k_scale=0.05,
+                       v_scale=0.04)
+    pools = oracle.written_pools(w)
+    got = oracle.attention_for(w, pools=pools, window=window)
+    ref = np.array(brute.from_workload(w, pools, window=window))
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_window_special_cases():
+    w = wl.random_case(91, num_seqs=4, ctx_range=(5, 90), chunk_range=(1, 12), num_q_heads=8, num_kv_heads=2,
+                       head_dim=16)
+    pools = oracle.written_pools(w)
+    full = oracle.attention_for(w, pools=pools)
+    # a window as long as every context is the full attention, bit for bit
+    assert np.array_equal(oracle.attention_for(w, pools=pools, window=int(w.seq_lens.max())), full)
+    # a window of one token: the row's own value, exactly
+    one = oracle.attention_for(w, pools=pools, window=1)
+    kc, vc = pools
+    G = w.num_q_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        c = int(w.seq_lens[s]) - (q1 - q0)
+        for t in range(q0, q1):
+            p = c + t - q0
+            blk, off = int(w.block_tables[s][p // 16]), p % 16
+            for h in range(w.num_q_heads):
+                assert np.array_equal(one[t, h], vc[blk, off, h // G].double().numpy())
+
+
+def test_window_equals_plain_attention_over_the_window_keys():
+    """A windowed row equals unwindowed attention of the same query over its window's keys, laid out again as a
+    contiguous sequence of its own (another path through the oracle: no window, a rebuilt table)."""
+    W = 23
+    w = wl.random_case(93, num_seqs=3, ctx_range=(30, 120), chunk_range=(1, 10), num_q_heads=4, num_kv_heads=2,
+                       head_dim=16, q_dtype="bf16", kv_dtype="bf16")
+    kc, vc = oracle.written_pools(w)
+    got = oracle.attention_for(w, pools=(kc, vc), window=W)
+    B = 16
+    for s in range(w.num_seqs):
+        q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        c = int(w.seq_lens[s]) - (q1 - q0)
+        for t in range(q0, q1):
+            p = c + t - q0
+            j0 = max(0, p - W + 1)
+            n = p + 1 - j0
+            nb = (n + B - 1) // B
+            k2 = torch.zeros(nb, B, w.num_kv_heads, w.head_dim, dtype=kc.dtype)
+            v2 = torch.zeros_like(k2)
+            for j in range(j0, p + 1):
+                blk, off = int(w.block_tables[s][j // B]), j % B
+                k2[(j - j0) // B, (j - j0) % B] = kc[blk, off]
+                v2[(j - j0) // B, (j - j0) % B] = vc[blk, off]
+            ref = oracle.attention(w.query[t:t + 1], k2, v2, np.arange(nb, dtype=np.int32)[None, :],
+                                   np.array([n], dtype=np.int32), np.array([0, 1], dtype=np.int32), w.scale)
+            assert np.array_equal(got[t], ref[0])
