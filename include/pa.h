@@ -167,6 +167,27 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const
                       void* stream);
 
 /*
+ * pa_decode_window -- pa_decode with sliding-window attention: the query of
+ * sequence s (at position L-1, L = seq_lens[s]) attends to positions
+ * max(0, L-sliding_window) .. L-1 only.  The pages name sliding-window
+ * attention ([A] §5.1, a manager that keeps only the blocks inside the
+ * window; [B] tutorial 1, among the cases that bound KV capacity) without
+ * fixing where the window starts; this library takes the W most recent
+ * positions, the current one included.  Table entries wholly before the
+ * window are not read (a caller may have given those blocks up; PA_VALIDATE=1
+ * still checks every entry).  dtype: PA_BF16.
+ * sliding_window >= 1 (a window of at least seq_lens[s] is pa_decode).
+ * workspace: pa_decode_workspace_bytes(...) with the same max_seq_len.
+ * Other arguments as pa_decode.
+ */
+pa_status_t pa_decode_window(void* out, const void* query, const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                             pa_dtype_t dtype, int32_t sliding_window, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_fp8 -- pa_decode over E4M3FN pools.  [B] tutorial 6.
  * K_j = decode(code) * k_scale, V_j = decode(code) * v_scale (exact values);
  * q_dtype (= out dtype): PA_BF16 or PA_F32 (fp32 queries are rounded to
@@ -243,6 +264,30 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               int32_t num_blocks, float scale, pa_dtype_t dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_varlen_window -- pa_prefill_varlen with sliding-window
+ * attention ([A] §5.1, [B] tutorial 1; the window's start is this library's
+ * reading, as in pa_decode_window): the row at position p attends to
+ * positions max(0, p-sliding_window+1) .. p.  No pool data is read from the
+ * blocks wholly before the window of a sequence's first new row (their table
+ * entries may name any block; PA_VALIDATE=1 still checks them), and 64-key
+ * tiles wholly before it are not computed.  dtype: PA_BF16 (activations and
+ * pools); sliding_window >= 1.  workspace:
+ * pa_prefill_varlen_window_workspace_bytes(...) with the same window (the
+ * work split depends on it; returns 0 on invalid input).  Other arguments as
+ * pa_prefill_varlen.
+ */
+size_t pa_prefill_varlen_window_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t sliding_window);
+pa_status_t pa_prefill_varlen_window(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                     const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                                     const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, float scale, pa_dtype_t dtype, int32_t sliding_window,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_prefill_varlen_fp8 -- pa_prefill_varlen over E4M3FN pools (uint8 codes)

@@ -78,6 +78,11 @@ def load() -> ctypes.CDLL:
             "pa_prefill_varlen_fp8_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
             "pa_prefill_varlen_fp8": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                        ctypes.c_int, f32, f32, P, sz, P], ctypes.c_int),
+            "pa_decode_window": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32,
+                                  i32, P, sz, P], ctypes.c_int),
+            "pa_prefill_varlen_window_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
+            "pa_prefill_varlen_window": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                          ctypes.c_int, i32, P, sz, P], ctypes.c_int),
             "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_reset": ([], ctypes.c_int),
             "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
@@ -207,6 +212,22 @@ def pa_decode_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: 
     return out
 
 
+def pa_decode_window(query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                     sliding_window: int, num_splits: int = 0, out=None, workspace=None):
+    """pa_decode where each query sees only its sequence's last sliding_window positions (bf16 pools)."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    out = torch.empty_like(query) if out is None else out
+    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, num_splits), query.device, workspace)
+    _check("pa_decode_window", lib.pa_decode_window(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(key_cache),
+        sliding_window, num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
 def pa_decode_cascade_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                                       max_seq_len: int, prefix_blocks: int, num_splits: int = 0) -> int:
     return int(load().pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
@@ -274,6 +295,35 @@ def pa_prefill_varlen(query, key_cache, value_cache, block_tables, seq_lens, que
         _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(),
         sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), None if ws is None else ws.data_ptr(),
         wsb, _stream()))
+    return out
+
+
+def pa_prefill_varlen_window_workspace_bytes(query_start_loc_host, seq_lens_host, num_q_heads: int,
+                                             num_kv_heads: int, head_dim: int, sliding_window: int) -> int:
+    q = _i32_host(query_start_loc_host)
+    s = _i32_host(seq_lens_host)
+    return int(load().pa_prefill_varlen_window_workspace_bytes(q.data_ptr(), s.data_ptr(), s.numel(), num_q_heads,
+                                                               num_kv_heads, head_dim, sliding_window))
+
+
+def pa_prefill_varlen_window(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, seq_lens_host,
+                             query_start_loc_host, scale: float, sliding_window: int, out=None, workspace=None):
+    """pa_prefill_varlen where the row at position p sees positions p-sliding_window+1 .. p (bf16)."""
+    lib = load()
+    T, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    qh = _i32_host(query_start_loc_host)
+    sh = _i32_host(seq_lens_host)
+    out = torch.empty_like(query) if out is None else out
+    need = int(lib.pa_prefill_varlen_window_workspace_bytes(qh.data_ptr(), sh.data_ptr(), sh.numel(), Hq, Hkv, D,
+                                                            sliding_window))
+    ws, wsb = _workspace(need, query.device, workspace)
+    _check("pa_prefill_varlen_window", lib.pa_prefill_varlen_window(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(),
+        sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), sliding_window,
+        None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
 
 

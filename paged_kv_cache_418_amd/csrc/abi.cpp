@@ -214,8 +214,11 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
                        int32_t num_seqs, int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
                        int q_f32, float k_scale, float v_scale, int32_t num_splits, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream, int32_t prefix_blocks = 0) {
-  const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, max_seq_len);
+                       size_t workspace_bytes, hipStream_t stream, int32_t prefix_blocks = 0,
+                       int32_t sliding_window = 0) {
+  // a window of W keys spans at most W/16 + 2 blocks of each sequence
+  const int span = sliding_window > 0 ? std::min<int64_t>(max_seq_len, (int64_t)sliding_window + 16) : max_seq_len;
+  const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, span);
   pa::DecodeParams p{};
   p.out = out;
   p.query = query;
@@ -233,6 +236,7 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   p.num_blocks = num_blocks;
   p.max_seq_len = max_seq_len;
   p.n_splits = n_splits;
+  p.window = sliding_window > 0 ? sliding_window : 0;
   p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
   p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
   p.q_f32 = q_f32;
@@ -571,12 +575,12 @@ struct VarlenPlan {
 };
 
 pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_tokens, int bt_stride,
-                        int group, int num_kv_heads, VarlenPlan& plan) {
+                        int group, int num_kv_heads, VarlenPlan& plan, int window = 0) {
   if (qsl[0] != 0) return fail(PA_ERR_SHAPE, "query_start_loc_host[0] = %d, expected 0", qsl[0]);
   const int P = pa::kPrefillRows / group;
   plan.tile_positions = P;
   struct RowTile {
-    int s, rt, n_kt;
+    int s, rt, n_kt, kt_lo;  // key tiles kt_lo .. kt_lo + n_kt - 1
   };
   std::vector<RowTile> tiles;
   int64_t total = 0;
@@ -597,8 +601,10 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
       return fail(PA_ERR_UNSUPPORTED, "batch too large for the prefill planner");
     for (int rt = 0; rt < n_rt; ++rt) {
       const int pos_end = std::min(q_len, (rt + 1) * P);
-      const int n_kt = ceil_div(c + pos_end, pa::kPrefillKeys);
-      tiles.push_back({s, rt, n_kt});
+      // a sliding window hides the key tiles below the tile's first row's window
+      const int kt_lo = window > 0 ? std::max(c + rt * P - window + 1, 0) / pa::kPrefillKeys : 0;
+      const int n_kt = ceil_div(c + pos_end, pa::kPrefillKeys) - kt_lo;
+      tiles.push_back({s, rt, n_kt, kt_lo});
       total += n_kt;
     }
   }
@@ -624,13 +630,14 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
   for (const RowTile& t : tiles) {
     const int n = ceil_div(t.n_kt, budget);
     if (n <= 1) {
-      whole_items.push_back(code(t.s, true, t.rt, 0, t.n_kt));
+      whole_items.push_back(code(t.s, true, t.rt, t.kt_lo, t.kt_lo + t.n_kt));
       continue;
     }
     const int first = (int)plan.items.size();
     if (first + n >= (1 << 20) || n >= (1 << 12)) return fail(PA_ERR_UNSUPPORTED, "too many prefill splits");
     for (int i = 0; i < n; ++i)
-      plan.items.push_back(code(t.s, false, t.rt, (int)((int64_t)t.n_kt * i / n), (int)((int64_t)t.n_kt * (i + 1) / n)));
+      plan.items.push_back(code(t.s, false, t.rt, t.kt_lo + (int)((int64_t)t.n_kt * i / n),
+                                t.kt_lo + (int)((int64_t)t.n_kt * (i + 1) / n)));
     plan.merges.push_back((uint64_t)t.s | ((uint64_t)t.rt << 16) | ((uint64_t)first << 32) | ((uint64_t)n << 52));
   }
   plan.n_split_items = (int)plan.items.size();
@@ -657,6 +664,18 @@ size_t varlen_workspace(const VarlenPlan& plan, int num_seqs, int num_q_heads, i
                          ? pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, plan.max_decode_len, 0)
                          : 0;
   return align_up(dec) + prefill_layout(plan.n_split_items, num_kv_heads, head_dim).total;
+}
+
+// pa_prefill_varlen(_window)_workspace_bytes without the argument checks.
+size_t varlen_workspace_bytes(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int window) {
+  VarlenPlan plan;
+  const std::string saved = g_last_error;
+  const pa_status_t st = plan_varlen(qsl, sl, num_seqs, qsl[num_seqs], INT32_MAX, num_q_heads / num_kv_heads,
+                                     num_kv_heads, plan, window);
+  g_last_error = saved;
+  if (st != PA_OK) return 0;
+  return varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
 }
 
 // fp8 prefill staging: bf16 copies of the blocks of every chunk sequence (q_len > 1), then
@@ -692,7 +711,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
                        const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, float scale, pa_dtype_t dtype, int kv_kind, float k_scale, float v_scale,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream, int32_t sliding_window = 0) {
   if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_SHAPE, "negative num_seqs or num_tokens");
   if (num_seqs == 0) return num_tokens == 0 ? ok() : fail(PA_ERR_SHAPE, "num_tokens > 0 with no sequences");
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc ||
@@ -705,7 +724,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
   VarlenPlan plan;
   st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
-                   num_q_heads / num_kv_heads, num_kv_heads, plan);
+                   num_q_heads / num_kv_heads, num_kv_heads, plan, sliding_window);
   if (st != PA_OK) return st;
   if (dtype == PA_F32 && !plan.items.empty())
     return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
@@ -736,7 +755,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     st = run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
                     num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, plan.max_decode_len, scale,
                     kv_kind == pa::kFP8 ? pa::kFP8 : (dtype == PA_F32 ? pa::kF32 : pa::kBF16), dtype == PA_F32,
-                    k_scale, v_scale, 0, workspace, workspace_bytes, hs);
+                    k_scale, v_scale, 0, workspace, workspace_bytes, hs, 0, sliding_window);
     if (st != PA_OK) return st;
   }
   auto* ws = static_cast<unsigned char*>(workspace);
@@ -789,6 +808,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     p.item_base = (int)i0;
     p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
     p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
+    p.window = sliding_window > 0 ? sliding_window : 0;
     const size_t n = std::min(plan.items.size() - i0, (size_t)pa::kMaxPrefillItems);
     p.n_items = (int)n;
     std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint64_t));
@@ -826,14 +846,43 @@ size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, co
   if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
       num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGroup)
     return 0;
-  VarlenPlan plan;
-  const std::string saved = g_last_error;
-  const int num_tokens = query_start_loc_host[num_seqs];
-  const pa_status_t st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, INT32_MAX,
-                                     num_q_heads / num_kv_heads, num_kv_heads, plan);
-  g_last_error = saved;
-  if (st != PA_OK) return 0;
-  return varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
+  return varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                0);
+}
+
+size_t pa_prefill_varlen_window_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t sliding_window) {
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGroup || sliding_window < 1)
+    return 0;
+  return varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                sliding_window);
+}
+
+pa_status_t pa_decode_window(void* out, const void* query, const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype,
+                             int32_t sliding_window, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "sliding-window decode: dtype must be PA_BF16");
+  if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                    pa::kBF16, 0, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                    0, sliding_window);
 }
 
 pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -847,6 +896,21 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
   return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
                     seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                     block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_prefill_varlen_window(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                     const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                                     const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, float scale, pa_dtype_t dtype, int32_t sliding_window,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "sliding-window prefill: dtype must be PA_BF16");
+  if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
+  return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
+                    seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream,
+                    sliding_window);
 }
 
 size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,

@@ -162,12 +162,22 @@ __device__ __forceinline__ float sum_across_rows(float x) {
 
 // Blocks of sequence s the decode attends: ceil(seq_len / 16), or 0 when s
 // is not a decode row of a flattened batch (q_len != 1).
-// Blocks of sequence s that its own pieces cover (all of them, or those after the
-// shared prefix of a cascade).
+// First visible key of sequence s: L - window with a sliding window, else 0.
+__device__ __forceinline__ int decode_first_key(const DecodeParams& p, int L) {
+  return p.window > 0 ? max(L - p.window, 0) : 0;
+}
+
+// Leading blocks of sequence s its own pieces skip: the shared prefix of a cascade, or the
+// blocks wholly before a sliding window.
+__device__ __forceinline__ int decode_skip(const DecodeParams& p, int L) {
+  return p.window > 0 ? decode_first_key(p, L) >> 4 : p.skip_blocks;
+}
+
+// Blocks of sequence s that its own pieces cover.
 __device__ __forceinline__ int decode_blocks(const DecodeParams& p, int s) {
   if (p.qsl && p.qsl[s + 1] - p.qsl[s] != 1) return 0;
   const int L = min(p.seq_lens[s], p.max_seq_len);
-  return L > 0 ? max(((L + 15) >> 4) - p.skip_blocks, 0) : 0;
+  return L > 0 ? max(((L + 15) >> 4) - decode_skip(p, L), 0) : 0;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int x) {
@@ -249,9 +259,10 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
                                              int b0, int b1, int nb) {
   using Sh = DecodeShape<D, FP8>;
   constexpr int VEC = Sh::kVec, W = Sh::kWords;
-  const int skip = GROUP ? 0 : p.skip_blocks;
   const int row = p.qsl ? p.qsl[s] : s;
   const int L = GROUP ? p.prefix_blocks * 16 : min(p.seq_lens[s], p.max_seq_len);
+  const int skip = GROUP ? 0 : decode_skip(p, L);
+  const int key_lo = GROUP ? 0 : decode_first_key(p, L);  // keys below it are outside the window
   const int tok0 = (skip + b0) * 16;
   const int tok1 = min(L, (skip + b1) * 16);
   const int nblk = b1 - b0;
@@ -389,7 +400,8 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
     float bmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool live = blk_tok + a + 4 * i < tok1;
+      const int tok = blk_tok + a + 4 * i;
+      const bool live = tok < tok1 && tok >= key_lo;
       z[i] = live ? sacc[i] * p.scale_log2 : -INFINITY;
       bmax = fmaxf(bmax, z[i]);
     }

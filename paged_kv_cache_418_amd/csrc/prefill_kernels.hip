@@ -97,7 +97,9 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-template <int D>
+// WINDOW: sliding-window attention (p.window > 0), a variant of its own so that the
+// plain causal kernel keeps its register budget.
+template <int D, bool WINDOW>
 __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   using Sh = PrefillShape<D>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -142,13 +144,18 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   const size_t tok_stride = (size_t)p.num_kv_heads * D * 2;
   const int lanes_per_row = Sh::kChunks;
   const int copy_row0 = Sh::kRowsPerCopy * Sh::kCopies * wave;  // first row of this wave's slabs
-  const int bt0 = min(max(bt[0], 0), p.num_blocks - 1);          // block of key 0 (always written)
+  // Keys no row of the tile sees are not read from the pool: those past the last visible
+  // key and, with a sliding window, those before the first row's first visible key (their
+  // blocks may have been given up).  Their rows copy a filler key that is always written
+  // and finite -- key 0, or with a window the last visible key -- and their scores are
+  // masked, so the probabilities that meet the filler are 0.
+  const int fill_key = WINDOW ? kv_end - 1 : 0;
+  const int key_first = WINDOW ? c + pos0 - p.window + 1 : 0;
+  const int bt_fill = min(max(bt[fill_key >> 4], 0), p.num_blocks - 1);
   // Physical block of this wave's rows of a tile.  The load is unconditional (a key past
-  // the last visible one reads the last visible key's entry, whose rows are then replaced
-  // by key 0's), so the compiler can count it among the loads in flight.
+  // the last visible one reads the last visible key's entry; any entry read is clamped
+  // into the pool), so the compiler can count it among the loads in flight.
   auto block_of = [&](int tile) { return bt[min(tile * Sh::kKeys + copy_row0, kv_end - 1) >> 4]; };
-  // Rows past the last visible key copy the row of key 0 (written and finite): their
-  // scores are masked and their probabilities are 0, so pool data there is never used.
   // Slab i (0 .. kCopies-1) of this wave's part of one tensor of a tile.
   auto copy_slab = [&](const uint8_t* base, int tile, int phys, unsigned char* st, int i) {
     phys = min(max(phys, 0), p.num_blocks - 1);
@@ -156,9 +163,10 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
     const int slot = lane % lanes_per_row;
     const int chunk = slot ^ (row % Sh::kChunks);
     const int key = tile * Sh::kKeys + row;
-    const bool live = key < kv_end;
-    const int ph = live ? phys : bt0;
-    const size_t off = ((size_t)ph * 16 + (live ? (key & 15) : 0)) * tok_stride + (size_t)kvh * D * 2 + chunk * 16;
+    const bool live = key < kv_end && (!WINDOW || key >= key_first);
+    const int ph = live ? phys : bt_fill;
+    const size_t off = ((size_t)ph * 16 + ((live ? key : fill_key) & 15)) * tok_stride + (size_t)kvh * D * 2 +
+                       chunk * 16;
     unsigned char* dst = st + (copy_row0 + Sh::kRowsPerCopy * i) * Sh::kRowBytes;
     __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(base + off), (void PA_LDS*)dst, 16, 0, 0);
   };
@@ -405,7 +413,21 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   auto softmax = [&](f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4]) {
     // lane's entries: key key0 + kt*32 + 8*(r/4) + 4*half + r%4 of row rl.  Raw scores are
     // masked and maximised; the scale (> 0) is applied inside exp2(fma(s, scale, -m)).
-    if (key0 + Sh::kKeys - 1 > wave_first) {
+    // a tile needs masking if it reaches past some row's position, or (sliding window) below
+    // some row's first visible key
+    if constexpr (WINDOW) {
+      if (key0 + Sh::kKeys - 1 > wave_first || key0 < wave_last - p.window + 1) {
+        // visible: 0 <= row_pos - key < window, one unsigned comparison
+        const uint32_t rel = (uint32_t)(row_pos - key0 - 4 * half);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t dist = rel - (uint32_t)(kt * 32 + 8 * (r >> 2) + (r & 3));
+            sacc[kt][r] = dist < (uint32_t)p.window ? sacc[kt][r] : -INFINITY;
+          }
+      }
+    } else if (key0 + Sh::kKeys - 1 > wave_first) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -498,6 +520,8 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   // step is alike.
   constexpr int kStepLoads = 2 * Sh::kCopies;
   const int wave_tiles_end = min(kt1, wave_last / Sh::kKeys + 1);  // tiles this wave computes
+  // (a sliding window's lower edge is left to the item's key range and to masking: a wave
+  // that also skipped its own leading tiles would need registers the kernel does not have)
   const bool leading = wave < Sh::kWaves / 2;
   auto computes = [&](int tile) { return wave_live && tile < wave_tiles_end; };
   {
@@ -742,14 +766,21 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
   const dim3 grid(p.n_items, p.num_kv_heads);
   const size_t lds = prefill_lds_bytes(head_dim);
   timing_mark(kKPrefill, true, stream);
+  auto launch = [&](auto kernel, int threads) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), lds, stream, p);
+  };
   if (head_dim == 128) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<128>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(PrefillShape<128>::kThreads), lds, stream, p);
+    if (p.window > 0)
+      launch(&prefill_kernel<128, true>, PrefillShape<128>::kThreads);
+    else
+      launch(&prefill_kernel<128, false>, PrefillShape<128>::kThreads);
   } else {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<64>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(PrefillShape<64>::kThreads), lds, stream, p);
+    if (p.window > 0)
+      launch(&prefill_kernel<64, true>, PrefillShape<64>::kThreads);
+    else
+      launch(&prefill_kernel<64, false>, PrefillShape<64>::kThreads);
   }
   timing_mark(kKPrefill, false, stream);
   return hipGetLastError();

@@ -59,6 +59,16 @@ class DevWorkload:
         return pk.pa_decode_cascade(self.query, self.k_cache, self.v_cache, self.block_tables, sl, w.scale,
                                     self.max_seq_len(), prefix_blocks, num_splits, out=out)
 
+    def decode_window(self, window, num_splits=0, out=None):
+        w = self.w
+        return pk.pa_decode_window(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
+                                   self.max_seq_len(), window, num_splits, out=out)
+
+    def prefill_window(self, window, out=None):
+        w = self.w
+        return pk.pa_prefill_varlen_window(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                           self.qsl, w.seq_lens, w.query_start_loc, w.scale, window, out=out)
+
     def prefill(self, out=None):
         w = self.w
         if w.kv_dtype == "fp8":

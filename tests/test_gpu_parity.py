@@ -417,3 +417,93 @@ def test_prefill_long_chunks_split_across_work_items(heads):
     err = max_err(out, ref)
     say(f"  max_abs_err={err:.3e}")
     assert err <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ sliding window
+# The row at position p sees positions max(0, p - W + 1) .. p (the oracle's reading of the pages' sliding-window
+# attention).  Table columns wholly before what the kernels read point at the NaN-filled poison block, so a read
+# of them would show as a non-finite output.
+
+def _poison_columns(w, first_col):
+    bt = w.block_tables.copy()
+    for s, c in enumerate(first_col):
+        bt[s, :c] = w.poison_block
+    return dataclasses.replace(w, block_tables=bt)
+
+
+def _window_case(w, window, run, tol):
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = run(d)
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w), window=window)
+    err = max_err(out, ref)
+    say(f"  window={window} max_abs_err={err:.3e}")
+    assert err <= tol
+    return out
+
+
+@pytest.mark.parametrize("heads", [(32, 8, 128), (4, 2, 64), (16, 1, 128)])
+@pytest.mark.parametrize("window", [1, 16, 100, 5000])
+@pytest.mark.parametrize("num_splits", [0, 7])
+def test_decode_window_random(heads, window, num_splits):
+    Hq, Hkv, D = heads
+    w = wl.random_case(600 + window % 89 + Hq + num_splits, num_seqs=6, ctx_range=(1, 700), num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, q_dtype="bf16", kv_dtype="bf16")
+    # decode reads blocks from the one holding position L - W on
+    w = _poison_columns(w, [max(int(L) - window, 0) // 16 for L in w.seq_lens])
+    say("decode window", heads, window, num_splits, list(w.seq_lens))
+    _window_case(w, window, lambda d: d.decode_window(window, num_splits), TOL["bf16"])
+
+
+def test_decode_window_llama3_8b_full():
+    """The 8B decode layer (64 sequences of 1000-3000 tokens) with a 1024-token window: agrees with the oracle on
+    every row and with the full-attention entry point when the window covers every sequence."""
+    w = wl.llama3_8b_decode_bf16()
+    say("decode window llama3_8b")
+    _window_case(w, 1024, lambda d: d.decode_window(1024), TOL["bf16"])
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    a = d.decode_window(int(w.seq_lens.max()))
+    b = d.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("seed", [611, 612])
+@pytest.mark.parametrize("heads", [(32, 8, 128), (4, 2, 64), (12, 4, 128)])
+@pytest.mark.parametrize("window", [1, 37, 200, 100000])
+def test_prefill_window_random(seed, heads, window):
+    Hq, Hkv, D = heads
+    w = wl.random_case(seed + window % 97, num_seqs=6, ctx_range=(1, 700), chunk_range=(1, 400), num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, q_dtype="bf16", kv_dtype="bf16")
+    first = []
+    for L, ql in zip(w.seq_lens, w.q_lens):
+        L, ql = int(L), int(ql)
+        # no data is read from blocks wholly before the window of a chunk's first row (position L - ql) or of a
+        # decode row (position L - 1)
+        first.append(max(L - ql - window + 1, 0) // 16)
+    w = _poison_columns(w, first)
+    say("prefill window", seed, heads, window, list(w.q_lens), list(w.seq_lens))
+    _window_case(w, window, lambda d: d.prefill_window(window), TOL["bf16"])
+
+
+@pytest.mark.parametrize("window", [64, 300, 1000])
+def test_prefill_window_long_chunks_split(window):
+    """Long chunks whose row tiles are cut into key ranges (some pieces see none of a row's window) and merged."""
+    w = wl.build("prefill_long_window", seed=641, ctx_lens=[2200, 700, 35, 1900], q_lens=[700, 1, 35, 333],
+                 num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    w = _poison_columns(w, [max(int(L) - int(ql) - window + 1, 0) // 16 for L, ql in zip(w.seq_lens, w.q_lens)])
+    say("prefill window long", window)
+    _window_case(w, window, lambda d: d.prefill_window(window), TOL["bf16"])
+
+
+def test_prefill_window_covering_everything_is_full_attention():
+    w = wl.random_case(655, num_seqs=5, ctx_range=(1, 900), chunk_range=(1, 500), num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    a = d.prefill_window(int(w.seq_lens.max()))
+    b = d.prefill()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
