@@ -41,7 +41,7 @@ METRIC = "paged decode KV GB/s (% of HBM peak) + prefill TFLOP/s at 1×MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "paged_kv_cache_418_amd", "csrc")
 COPY_BYTES = 1 << 30
-DECODE_SOURCES = ["decode_kernels.hip", "pa_device.h", "pa_internal.h"]
+DECODE_SOURCES = ["decode_kernels.hip", "pa_device.h", "pa_internal.h", "abi.cpp"]  # abi.cpp: launch shape
 
 
 def _log(*a):
@@ -51,11 +51,12 @@ def _log(*a):
 class Step:
     """Device state of one workload and the calls of one step."""
 
-    def __init__(self, w, copies: int = 2, cascade: bool = False):
+    def __init__(self, w, copies: int = 2, cascade: bool = False, window: int = 0):
         import paged_kv_cache_418_amd as pk
         self.pk = pk
         self.w = w
         self.cascade = cascade
+        self.window = window
         dev = "cuda"
         self.pools = [(w.k_cache.to(dev), w.v_cache.to(dev))]
         for _ in range(copies - 1):
@@ -74,6 +75,9 @@ class Step:
                                                       self.max_len, w.shared_prefix_blocks, 0)
         elif w.is_decode:
             nb = pk.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, self.max_len, 0)
+        elif window:
+            nb = pk.pa_prefill_varlen_window_workspace_bytes(w.query_start_loc, w.seq_lens, w.num_q_heads,
+                                                             w.num_kv_heads, w.head_dim, window)
         elif w.kv_dtype == "fp8":
             nb = pk.pa_prefill_varlen_fp8_workspace_bytes(w.query_start_loc, w.seq_lens, w.num_q_heads,
                                                           w.num_kv_heads, w.head_dim, w.block_tables.shape[1])
@@ -99,6 +103,12 @@ class Step:
         if self.cascade:
             pk.pa_decode_cascade_fp8(self.q, kc, vc, self.bt, self.sl, w.scale, w.k_scale, w.v_scale, self.max_len,
                                      w.shared_prefix_blocks, out=self.out, workspace=self.ws)
+        elif self.window and w.is_decode:
+            pk.pa_decode_window(self.q, kc, vc, self.bt, self.sl, w.scale, self.max_len, self.window, out=self.out,
+                                workspace=self.ws)
+        elif self.window:
+            pk.pa_prefill_varlen_window(self.q, kc, vc, self.bt, self.sl, self.qsl, w.seq_lens, w.query_start_loc,
+                                        w.scale, self.window, out=self.out, workspace=self.ws)
         elif w.is_decode:
             if w.kv_dtype == "fp8":
                 pk.pa_decode_fp8(self.q, kc, vc, self.bt, self.sl, w.scale, w.k_scale, w.v_scale, self.max_len,
@@ -330,6 +340,40 @@ def bench_cascade(args, result):
     torch.cuda.empty_cache()
 
 
+def bench_window(args, result):
+    """Sliding-window attention on two of the workloads above: the Llama-3-8B decode layer with a 1024-token window
+    (bytes of the windowed keys per second) and the mixed step's two prefill chunks with a 256-token window (FLOPs
+    of the visible pairs per second)."""
+    from paged_kv_cache_418_amd import workloads as wl
+    window_dec, window_pre = 1024, 256
+    _log("generating llama3_8b_decode_bf16 (window) ...")
+    w = wl.llama3_8b_decode_bf16()
+    st = Step(w, window=window_dec)
+    ms, _ = time_steps(st, args.steps, args.warmup)
+    kt = kernel_times(st, args.steps, ["decode", "decode_merge"])
+    kv = wl.decode_window_kv_bytes(w, window_dec)
+    dec_ms = kt["decode"][0]
+    out = {"decode": {"workload": "llama3_8b_decode_bf16", "window": window_dec, "window_kv_bytes": kv,
+                      "ms_per_step": round(ms, 5), "decode_kernel_ms": round(dec_ms, 5),
+                      "merge_kernel_ms": round(kt["decode_merge"][0], 5),
+                      "kernel_gbps": round(kv / (dec_ms * 1e-3) / 1e9, 1),
+                      "kernel_frac_hbm": round(kv / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
+    del st
+    _log("generating mixed_step_bf16 chunks (window) ...")
+    cw = _sub(wl.mixed_step_bf16(), [48, 49])
+    cs = Step(cw, copies=1, window=window_pre)
+    call_ms, _ = time_steps(cs.attend_next, args.steps, args.warmup)
+    kt = kernel_times(cs.attend_next, args.steps, ["prefill", "prefill_merge"])
+    flops = wl.prefill_flops(cw, window=window_pre)
+    pre_ms = kt["prefill"][0]
+    out["prefill"] = {"workload": "mixed_step_bf16 chunks 512@0 + 512@1536", "window": window_pre,
+                      "gflop": round(flops / 1e9, 3), "call_ms": round(call_ms, 5), "kernel_ms": round(pre_ms, 5),
+                      "kernel_tflops": round(flops / (pre_ms * 1e-3) / 1e12, 2)}
+    del cs
+    result["window"] = out
+    torch.cuda.empty_cache()
+
+
 def bench_copy(args, result):
     """A plain device-to-device copy of 1 GiB: the known-size reference for the HBM byte counters."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -345,7 +389,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", choices=["", "decode", "mixed", "cascade", "copy"])
+    ap.add_argument("--only", default="", choices=["", "decode", "mixed", "cascade", "window", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library's path runs on a single GPU and has no multi-GPU form; "
@@ -363,6 +407,8 @@ def main():
             bench_mixed(args, result)
         if args.only in ("", "cascade"):
             bench_cascade(args, result)
+        if args.only in ("", "window"):
+            bench_window(args, result)
     print(json.dumps(result), flush=True)
 
 

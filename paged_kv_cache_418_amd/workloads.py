@@ -341,8 +341,9 @@ def visible_pairs(w: Workload, rows: Optional[np.ndarray] = None) -> int:
     return total
 
 
-def prefill_flops(w: Workload, only_chunks: bool = True) -> int:
-    """4 * Hq * D flops per visible (row, key) pair (QK^T and PV, multiply+add each)."""
+def prefill_flops(w: Workload, only_chunks: bool = True, window: int = 0) -> int:
+    """4 * Hq * D flops per visible (row, key) pair (QK^T and PV, multiply+add each); with a sliding window the
+    row at position p sees min(p + 1, window) keys."""
     ql = w.q_lens
     pairs = 0
     for s in range(w.num_seqs):
@@ -350,5 +351,15 @@ def prefill_flops(w: Workload, only_chunks: bool = True) -> int:
         if only_chunks and q == 1:
             continue
         c = int(w.seq_lens[s] - q)
-        pairs += q * c + q * (q + 1) // 2
+        if window > 0:
+            pos = np.arange(c, c + q, dtype=np.int64)
+            pairs += int(np.minimum(pos + 1, window).sum())
+        else:
+            pairs += q * c + q * (q + 1) // 2
     return 4 * w.num_q_heads * w.head_dim * pairs
+
+
+def decode_window_kv_bytes(w: Workload, window: int) -> int:
+    """K+V bytes of the keys a windowed decode row sees: min(seq_len, window) per sequence."""
+    toks = np.minimum(w.seq_lens.astype(np.int64), window)
+    return int(2 * toks.sum() * w.num_kv_heads * w.head_dim * w.kv_elem_bytes)

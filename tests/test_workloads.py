@@ -53,6 +53,10 @@ def test_mixed_step_layout():
     assert list(w.seq_lens[-2:]) == [512, 2048]
     _check_tables(w)
     assert wl.prefill_flops(w) == 4 * 32 * 128 * (131328 + 917760)
+    # a 256-token window: the chunk at 0 sees 1..256 keys then 256 (32896 + 256*256 pairs), the chunk at 1536
+    # sees 256 keys on every row; a window past every position is the causal count
+    assert wl.prefill_flops(w, window=256) == 4 * 32 * 128 * (32896 + 65536 + 512 * 256)
+    assert wl.prefill_flops(w, window=2048) == wl.prefill_flops(w)
 
 
 def test_generation_is_deterministic():
