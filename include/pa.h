@@ -73,7 +73,9 @@ typedef enum pa_status {
   PA_ERR_DTYPE = 3,       /* dtype not valid for this entry point */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
   PA_ERR_UNSUPPORTED = 5, /* valid but not implemented (e.g. head_dim 96) */
-  PA_ERR_HIP = 6          /* the HIP runtime reported an error */
+  PA_ERR_HIP = 6,         /* the HIP runtime reported an error */
+  PA_ERR_NO_SPACE = 7,    /* block pool: not enough free blocks (nothing was changed) */
+  PA_ERR_STATE = 8        /* block pool: unknown request, or a call out of order */
 } pa_status_t;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype_t;
@@ -311,6 +313,102 @@ pa_status_t pa_prefill_varlen_fp8(void* out, const void* query, const uint8_t* k
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                   int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale, float v_scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host block pool -- the control plane that hands out the physical blocks
+ * whose ids fill block_tables.  Host memory only; no device call.
+ * [A] §5.1: a doubly linked free list with O(1) allocation and release, a
+ * prefix-cache map from block hash to block, per-block reference counts and
+ * hashes.  [C] core point 1: allocate_slots takes ceil(tokens / block_size)
+ * blocks from the head of the free list after checking that enough are free,
+ * and records them per request (17 tokens of 16-token blocks: 2 blocks).
+ * [C] core point 3: each full block's hash chains the previous block's hash,
+ * the block's tokens and extra identity (salt, adapter, ...), and
+ * find_longest_cache_hit returns the longest run of cached leading blocks.
+ * [B] tutorials 3-4: the null block, eviction of cached free blocks, several
+ * physical copies of one hash.
+ *
+ * Conventions: block 0 is the null block.  It is never handed out and never
+ * counted as free; pa_pool_release_before puts it in the table entries it
+ * releases (the kernels never read those entries' data with a sliding window
+ * that excludes them).  A block whose reference count drops to 0 goes to the
+ * tail of the free list and keeps its hash: it can still be hit (and leaves
+ * the free list again when it is) until it is handed out from the head, which
+ * evicts its hash.  Releases go from a request's last block to its first, so
+ * tail blocks are evicted first.  A pool is not thread-safe: one thread at a
+ * time.  Failures return a status (pa_last_error has the message) and leave
+ * the pool unchanged.
+ */
+typedef struct pa_block_pool pa_block_pool_t;
+
+/* A pool of num_blocks blocks (>= 2; ids 1 .. num_blocks-1 start free, in order). */
+pa_status_t pa_pool_create(int32_t num_blocks, int32_t block_size, pa_block_pool_t** pool);
+void pa_pool_destroy(pa_block_pool_t* pool);
+/* Blocks in the free list (cached or not); -1 for a NULL pool. */
+int32_t pa_pool_num_free(const pa_block_pool_t* pool);
+
+/*
+ * Hashes of the num_tokens / block_size full blocks of a token sequence
+ * (host int32 tokens), written to hashes (host): h_i = FNV-1a-64 of the
+ * little-endian bytes of (h_{i-1}, the block's block_size tokens, extra_key),
+ * h_{-1} = 0.  Returns the number of full blocks, -1 on invalid arguments.  A
+ * partial last block has no hash.  The 64-bit hash is trusted: two different
+ * prefixes with the same hash would share blocks.
+ */
+int32_t pa_pool_hash_blocks(const int32_t* tokens, int32_t num_tokens, int32_t block_size, uint64_t extra_key,
+                            uint64_t* hashes);
+
+/*
+ * The longest run hashes[0..n-1] that is cached: writes a cached block for
+ * each to blocks (the oldest physical copy) and returns n (0 .. num_hashes),
+ * -1 on invalid arguments.  Changes nothing (pass the blocks to
+ * pa_pool_allocate_slots to take them).
+ */
+int32_t pa_pool_find_longest_cache_hit(const pa_block_pool_t* pool, const uint64_t* hashes, int32_t num_hashes,
+                                       int32_t* blocks);
+
+/*
+ * Makes request_id hold ceil(num_tokens / block_size) blocks.  On the first
+ * call for a request, hit_blocks (cached blocks, e.g. from
+ * pa_pool_find_longest_cache_hit) become its leading blocks: each gains a
+ * reference and leaves the free list if it was there.  The rest come from the
+ * head of the free list (reference count 1; a cached one loses its hash).
+ * Later calls (growing a running request) pass no hits.  PA_ERR_NO_SPACE if
+ * the free list is too short, with nothing changed.  num_blocks (optional):
+ * the request's block count afterwards.
+ */
+pa_status_t pa_pool_allocate_slots(pa_block_pool_t* pool, int64_t request_id, int32_t num_tokens,
+                                   const int32_t* hit_blocks, int32_t num_hit_blocks, int32_t* num_blocks);
+
+/*
+ * Commits the hashes of the request's first num_full_blocks blocks once their
+ * K/V are written (hashes: as from pa_pool_hash_blocks over the request's
+ * tokens).  Blocks already cached and null entries are skipped; a hash that
+ * is already cached gains another physical copy.
+ */
+pa_status_t pa_pool_cache_blocks(pa_block_pool_t* pool, int64_t request_id, const uint64_t* hashes,
+                                 int32_t num_full_blocks);
+
+/*
+ * Sliding window ([A] §5.1's manager that keeps only the blocks inside the
+ * window): releases every block of the request wholly before token position
+ * `position` (entries j < position / block_size) and puts the null block in
+ * their table entries.  For a window of W and a next step whose first new row
+ * is at position p, pass p - W + 1.
+ */
+pa_status_t pa_pool_release_before(pa_block_pool_t* pool, int64_t request_id, int32_t position);
+
+/* Releases all of the request's blocks (last to first) and forgets it. */
+pa_status_t pa_pool_free(pa_block_pool_t* pool, int64_t request_id);
+
+/* Copies up to max_blocks of the request's table (host int32) to out; returns its length, -1 if unknown. */
+int32_t pa_pool_block_table(const pa_block_pool_t* pool, int64_t request_id, int32_t* out, int32_t max_blocks);
+
+/* Inspection: a block's reference count, whether it is in the free list, and its hash (if it has one). */
+pa_status_t pa_pool_block_state(const pa_block_pool_t* pool, int32_t block, int32_t* ref_count, int32_t* is_free,
+                                int32_t* has_hash, uint64_t* hash);
+/* Inspection: the free list from head to tail (up to max_blocks ids); returns its length. */
+int32_t pa_pool_free_queue(const pa_block_pool_t* pool, int32_t* out, int32_t max_blocks);
 
 /*
  * Kernel timing, for measurement.  Not part of the pages' problem statement:

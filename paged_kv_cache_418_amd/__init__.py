@@ -5,7 +5,7 @@ functions re-exported here are its ctypes binding and take GPU torch tensors.
 ``workloads`` holds the seeded synthetic inputs.
 """
 from ._binding import (  # noqa: F401
-    PA_BF16, PA_F32, PA_FP8_E4M3, PAError, abi_version, header_symbols, load, pa_decode, pa_decode_cascade,
+    BlockPool, pool_hash_blocks, PA_BF16, PA_F32, PA_FP8_E4M3, PAError, abi_version, header_symbols, load, pa_decode, pa_decode_cascade,
     pa_decode_cascade_fp8, pa_decode_cascade_workspace_bytes, pa_decode_fp8, pa_decode_window,
     pa_decode_workspace_bytes, pa_prefill_varlen, pa_prefill_varlen_fp8, pa_prefill_varlen_fp8_workspace_bytes,
     pa_prefill_varlen_window, pa_prefill_varlen_window_workspace_bytes, pa_prefill_varlen_workspace_bytes,

@@ -13,6 +13,7 @@ import re
 import threading
 from typing import Optional
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +84,19 @@ def load() -> ctypes.CDLL:
             "pa_prefill_varlen_window_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
             "pa_prefill_varlen_window": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                           ctypes.c_int, i32, P, sz, P], ctypes.c_int),
+            "pa_pool_create": ([i32, i32, ctypes.POINTER(P)], ctypes.c_int),
+            "pa_pool_destroy": ([P], None),
+            "pa_pool_num_free": ([P], i32),
+            "pa_pool_hash_blocks": ([P, i32, i32, ctypes.c_uint64, P], i32),
+            "pa_pool_find_longest_cache_hit": ([P, P, i32, P], i32),
+            "pa_pool_allocate_slots": ([P, i64, i32, P, i32, ctypes.POINTER(i32)], ctypes.c_int),
+            "pa_pool_cache_blocks": ([P, i64, P, i32], ctypes.c_int),
+            "pa_pool_release_before": ([P, i64, i32], ctypes.c_int),
+            "pa_pool_free": ([P, i64], ctypes.c_int),
+            "pa_pool_block_table": ([P, i64, P, i32], i32),
+            "pa_pool_block_state": ([P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                     ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+            "pa_pool_free_queue": ([P, P, i32], i32),
             "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_reset": ([], ctypes.c_int),
             "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
@@ -371,3 +385,91 @@ def pa_prefill_varlen_fp8(query, key_cache, value_cache, block_tables, seq_lens,
         sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), float(k_scale), float(v_scale),
         None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
+
+
+# ---- host block pool (pa_pool_*)
+
+def _np_i32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def pool_hash_blocks(tokens, block_size: int = 16, extra_key: int = 0) -> np.ndarray:
+    """Chained hashes of the full blocks of a token sequence (uint64)."""
+    t = _np_i32(tokens)
+    out = np.zeros(max(len(t) // block_size, 1), dtype=np.uint64)
+    n = load().pa_pool_hash_blocks(t.ctypes.data, len(t), block_size, ctypes.c_uint64(extra_key), out.ctypes.data)
+    if n < 0:
+        raise ValueError("pa_pool_hash_blocks: invalid arguments")
+    return out[:n]
+
+
+class BlockPool:
+    """The library's host block pool (block 0 is the null block)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        _check("pa_pool_create", self._lib.pa_pool_create(num_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pa_pool_num_free(self._h))
+
+    def find_longest_cache_hit(self, hashes) -> list:
+        hs = np.ascontiguousarray(np.asarray(hashes, dtype=np.uint64))
+        out = np.zeros(max(len(hs), 1), dtype=np.int32)
+        n = self._lib.pa_pool_find_longest_cache_hit(self._h, hs.ctypes.data, len(hs), out.ctypes.data)
+        return out[:n].tolist()
+
+    def allocate_slots(self, request_id: int, num_tokens: int, hit_blocks=()) -> int:
+        hb = _np_i32(list(hit_blocks))
+        n = ctypes.c_int32(0)
+        _check("pa_pool_allocate_slots", self._lib.pa_pool_allocate_slots(
+            self._h, request_id, num_tokens, hb.ctypes.data if len(hb) else None, len(hb), ctypes.byref(n)))
+        return int(n.value)
+
+    def cache_blocks(self, request_id: int, hashes, num_full_blocks: int) -> None:
+        hs = np.ascontiguousarray(np.asarray(hashes, dtype=np.uint64))
+        _check("pa_pool_cache_blocks", self._lib.pa_pool_cache_blocks(
+            self._h, request_id, hs.ctypes.data if len(hs) else None, num_full_blocks))
+
+    def release_before(self, request_id: int, position: int) -> None:
+        _check("pa_pool_release_before", self._lib.pa_pool_release_before(self._h, request_id, position))
+
+    def free(self, request_id: int) -> None:
+        _check("pa_pool_free", self._lib.pa_pool_free(self._h, request_id))
+
+    def block_table(self, request_id: int) -> list:
+        n = self._lib.pa_pool_block_table(self._h, request_id, None, 0)
+        if n < 0:
+            raise KeyError(request_id)
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._lib.pa_pool_block_table(self._h, request_id, out.ctypes.data, n)
+        return out[:n].tolist()
+
+    def block_state(self, block: int):
+        """(ref_count, is_free, hash or None) of one block."""
+        r, f, hh = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        h = ctypes.c_uint64()
+        _check("pa_pool_block_state", self._lib.pa_pool_block_state(self._h, block, ctypes.byref(r), ctypes.byref(f),
+                                                                     ctypes.byref(hh), ctypes.byref(h)))
+        return int(r.value), bool(f.value), (int(h.value) if hh.value else None)
+
+    def free_queue(self) -> list:
+        n = self._lib.pa_pool_free_queue(self._h, None, 0)
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._lib.pa_pool_free_queue(self._h, out.ctypes.data, n)
+        return out[:n].tolist()

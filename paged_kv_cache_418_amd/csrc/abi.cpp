@@ -37,6 +37,21 @@ pa_status_t ok() {
   return PA_OK;
 }
 
+}  // namespace
+
+// The failure message of the host-only parts of the library (the block pool).
+pa_status_t pa::set_error(pa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+namespace {
+
 pa_status_t hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return ok();
   return fail(PA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
@@ -317,6 +332,8 @@ const char* pa_status_string(pa_status_t status) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_SPACE: return "not enough free blocks";
+    case PA_ERR_STATE: return "unknown request or call out of order";
   }
   return "unknown status";
 }

@@ -4,7 +4,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Records the thread-local failure message (pa_last_error) and returns st.
+pa_status_t set_error(pa_status_t st, const char* fmt, ...);
 
 constexpr int kBlockSize = 16;      // tokens per physical block
 constexpr int kDecodeWaves = 4;     // waves per decode work-group

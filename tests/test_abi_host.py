@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 22
+    assert len(syms) == 34
     assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert pk.abi_version() == 1
-    for code in range(7):
+    for code in range(9):
         assert lib.pa_status_string(code)
     assert lib.pa_last_error() is not None
 
