@@ -68,6 +68,8 @@ def _load():
                                              i32, i32, f32, P, i32]
             lib.oracle_attention_window.argtypes = [P, P, i32, P, P, i32, f64, f64, P, i32, P, P, i32, i32,
                                                     i32, i32, i32, f32, P, i32, i32]
+            lib.oracle_attention_local.argtypes = [P, P, i32, P, P, i32, f64, f64, P, i32, P, P, i32, i32,
+                                                   i32, i32, i32, f32, P, i32, i32]
             lib.oracle_num_threads.restype = i32
             lib.oracle_set_threads.argtypes = [i32]
             _lib = lib
@@ -159,10 +161,13 @@ def reshape_and_cache_fp8(key, value, key_cache, value_cache, slots, k_scale: fl
 
 
 def attention(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, scale: float,
-              k_scale: float = 1.0, v_scale: float = 1.0, rows=None, window: int = 0) -> np.ndarray:
+              k_scale: float = 1.0, v_scale: float = 1.0, rows=None, window: int = 0,
+              chunk: int = 0) -> np.ndarray:
     """fp64 attention output [n_rows, Hq, D] for the given query rows (all rows when None).
 
-    window > 0: sliding window, the row at position p sees keys max(0, p - window + 1) .. p."""
+    window > 0: sliding window, the row at position p sees keys max(0, p - window + 1) .. p.
+    chunk > 0: chunked local attention, the row at position p sees keys p - p % chunk .. p."""
+    assert not (window and chunk)
     q = _np(query)
     kc, vc = _np(key_cache), _np(value_cache)
     bt = _np(block_tables).astype(np.int32, copy=False)
@@ -178,19 +183,19 @@ def attention(query, key_cache, value_cache, block_tables, seq_lens, query_start
         rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
         n_rows = rows_arr.shape[0]
     out = np.empty((n_rows, Hq, D), dtype=np.float64)
-    rc = _load().oracle_attention_window(_ptr(out), _ptr(q), _kind_of(query), _ptr(kc), _ptr(vc),
-                                         _kind_of(key_cache), float(k_scale), float(v_scale), _ptr(bt),
-                                         bt.shape[1], _ptr(sl), _ptr(qsl), sl.shape[0], Hq, Hkv, D, B, float(scale),
-                                         None if rows_arr is None else _ptr(rows_arr), n_rows, int(window))
+    fn, arg = (_load().oracle_attention_local, int(chunk)) if chunk else (_load().oracle_attention_window, int(window))
+    rc = fn(_ptr(out), _ptr(q), _kind_of(query), _ptr(kc), _ptr(vc), _kind_of(key_cache), float(k_scale),
+            float(v_scale), _ptr(bt), bt.shape[1], _ptr(sl), _ptr(qsl), sl.shape[0], Hq, Hkv, D, B, float(scale),
+            None if rows_arr is None else _ptr(rows_arr), n_rows, arg)
     assert rc == 0
     return out
 
 
-def attention_for(w, rows=None, pools=None, window: int = 0) -> np.ndarray:
+def attention_for(w, rows=None, pools=None, window: int = 0, chunk: int = 0) -> np.ndarray:
     """attention() on a workload's arrays; pools = (k_cache, v_cache) after the new tokens were written."""
     kc, vc = pools if pools is not None else (w.k_cache, w.v_cache)
     return attention(w.query, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc, w.scale,
-                     w.k_scale, w.v_scale, rows=rows, window=window)
+                     w.k_scale, w.v_scale, rows=rows, window=window, chunk=chunk)
 
 
 def written_pools(w):

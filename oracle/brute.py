@@ -38,9 +38,11 @@ def _value(flat, idx: int, kind: str, scale: float) -> float:
 
 def attention(query, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, query_start_loc,
               num_q_heads, num_kv_heads, head_dim, block_size, scale, k_scale=1.0, v_scale=1.0,
-              window=0) -> List:
+              window=0, chunk=0) -> List:
     """Inputs are flat Python lists (bf16 as uint16 bit patterns, fp8 as codes).
     window > 0: the row at position p sees only the keys p - window + 1 .. p (those >= 0).
+    chunk > 0: the row at position p sees only the keys of its own chunk of positions,
+    [chunk * (p // chunk), p].
 
     Returns out[t][h][d] as nested lists of floats."""
     G = num_q_heads // num_kv_heads
@@ -58,6 +60,8 @@ def attention(query, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, 
                 keys = []
                 for j in range(pos + 1):
                     if window and j <= pos - window:
+                        continue
+                    if chunk and j // chunk != pos // chunk:
                         continue
                     blk = block_tables[s][j // block_size]
                     base = ((blk * block_size + j % block_size) * num_kv_heads + kvh) * head_dim
@@ -78,7 +82,7 @@ def attention(query, q_kind, k_cache, v_cache, kv_kind, block_tables, seq_lens, 
     return out
 
 
-def from_workload(w, pools, window=0):
+def from_workload(w, pools, window=0, chunk=0):
     """Runs attention() on a workload's tensors (converted to flat lists)."""
     import torch
 
@@ -92,4 +96,5 @@ def from_workload(w, pools, window=0):
     return attention(flat(w.query), w.q_dtype, flat(kc), flat(vc), w.kv_dtype,
                      [list(map(int, r)) for r in w.block_tables], [int(v) for v in w.seq_lens],
                      [int(v) for v in w.query_start_loc], w.num_q_heads, w.num_kv_heads, w.head_dim,
-                     w.block_size, float(w.scale), float(w.k_scale), float(w.v_scale), window=window)
+                     w.block_size, float(w.scale), float(w.k_scale), float(w.v_scale), window=window,
+                     chunk=chunk)

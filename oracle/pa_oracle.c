@@ -207,15 +207,24 @@ int oracle_reshape_and_cache_fp8(const void* key, const void* value, int64_t key
 /* out[r][h][d] (fp64) for the query rows listed in rows[0..n_rows) (all rows
  * 0..T-1 when rows is NULL, n_rows = T).  Returns 0, or -1 on inconsistent
  * metadata. kv values of fp8 pools are decode(code) * k_scale / v_scale. */
-/* Sliding window (window > 0): the row at position pos sees keys max(0, pos - window + 1)
- * .. pos, a window of `window` tokens ending at its own.  window == 0: every key 0 .. pos.
- * (The reading of the pages' sliding-window attention; the pages fix no boundary.) */
-int oracle_attention_window(double* out, const void* query, int32_t q_dtype, const void* key_cache,
-                            const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
-                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
-                            const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                            const int32_t* rows, int32_t n_rows, int32_t window);
+/* Which keys a row sees.  Sliding window (window > 0): the row at position pos sees keys
+ * max(0, pos - window + 1) .. pos, a window of `window` tokens ending at its own.  Chunked
+ * local attention (chunk > 0): the positions are cut into chunks of `chunk` (0 .. chunk-1,
+ * chunk .. 2*chunk-1, ...) and the row sees the keys of its own chunk up to itself,
+ * pos - pos % chunk .. pos.  Neither: every key 0 .. pos.  (Readings of the pages'
+ * sliding-window and chunked-local attention; the pages name them but fix no boundary.) */
+static int first_visible_key(int pos, int32_t window, int32_t chunk) {
+  if (chunk > 0) return pos - pos % chunk;
+  if (window > 0 && pos - window + 1 > 0) return pos - window + 1;
+  return 0;
+}
+
+static int attention_rows(double* out, const void* query, int32_t q_dtype, const void* key_cache,
+                          const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
+                          const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                          const int32_t* rows, int32_t n_rows, int32_t window, int32_t chunk);
 
 int oracle_attention(double* out, const void* query, int32_t q_dtype, const void* key_cache,
                      const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
@@ -223,9 +232,9 @@ int oracle_attention(double* out, const void* query, int32_t q_dtype, const void
                      const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                      const int32_t* rows, int32_t n_rows) {
-  return oracle_attention_window(out, query, q_dtype, key_cache, value_cache, kv_dtype, k_scale, v_scale,
-                                 block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, num_q_heads,
-                                 num_kv_heads, head_dim, block_size, scale, rows, n_rows, 0);
+  return attention_rows(out, query, q_dtype, key_cache, value_cache, kv_dtype, k_scale, v_scale, block_tables,
+                        bt_stride, seq_lens, query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, scale, rows, n_rows, 0, 0);
 }
 
 int oracle_attention_window(double* out, const void* query, int32_t q_dtype, const void* key_cache,
@@ -235,6 +244,29 @@ int oracle_attention_window(double* out, const void* query, int32_t q_dtype, con
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                             const int32_t* rows, int32_t n_rows, int32_t window) {
   if (window < 0) return -1;
+  return attention_rows(out, query, q_dtype, key_cache, value_cache, kv_dtype, k_scale, v_scale, block_tables,
+                        bt_stride, seq_lens, query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, scale, rows, n_rows, window, 0);
+}
+
+int oracle_attention_local(double* out, const void* query, int32_t q_dtype, const void* key_cache,
+                           const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
+                           const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                           const int32_t* rows, int32_t n_rows, int32_t chunk) {
+  if (chunk < 0) return -1;
+  return attention_rows(out, query, q_dtype, key_cache, value_cache, kv_dtype, k_scale, v_scale, block_tables,
+                        bt_stride, seq_lens, query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, scale, rows, n_rows, 0, chunk);
+}
+
+static int attention_rows(double* out, const void* query, int32_t q_dtype, const void* key_cache,
+                          const void* value_cache, int32_t kv_dtype, double k_scale, double v_scale,
+                          const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                          const int32_t* rows, int32_t n_rows, int32_t window, int32_t chunk) {
   if (num_q_heads % num_kv_heads) return -1;
   int group = num_q_heads / num_kv_heads;
   int T = query_start_loc[num_seqs];
@@ -252,7 +284,7 @@ int oracle_attention_window(double* out, const void* query, int32_t q_dtype, con
     int cached = seq_lens[s] - q_len;
     int pos = cached + (t - query_start_loc[s]);
     int kvh = h / group;
-    int j0 = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0; /* first visible key */
+    int j0 = first_visible_key(pos, window, chunk);
     int n_keys = pos + 1;
     double* z = (double*)malloc(sizeof(double) * n_keys);
     double* q = (double*)malloc(sizeof(double) * head_dim);

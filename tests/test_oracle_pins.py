@@ -518,3 +518,75 @@ def test_window_equals_plain_attention_over_the_window_keys():
             ref = oracle.attention(w.query[t:t + 1], k2, v2, np.arange(nb, dtype=np.int32)[None, :],
                                    np.array([n], dtype=np.int32), np.array([0, 1], dtype=np.int32), w.scale)
             assert np.array_equal(got[t], ref[0])
+
+
+# ---- chunked local attention (reading: positions are cut into chunks of C; the row at position p sees the keys
+# of its own chunk up to itself, C * (p // C) .. p)
+
+@pytest.mark.parametrize("kinds", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8")])
+@pytest.mark.parametrize("chunk", [1, 5, 16])
+def test_local_brute_force_agrees(kinds, chunk):
+    w = wl.random_case(121 + chunk, num_seqs=3, ctx_range=(1, 40), chunk_range=(1, 6), num_q_heads=4,
+                       num_kv_heads=2, head_dim=8, q_dtype=kinds[0], kv_dtype=kinds[1], k_scale=0.05,
+                       v_scale=0.04)
+    pools = oracle.written_pools(w)
+    got = oracle.attention_for(w, pools=pools, chunk=chunk)
+    ref = np.array(brute.from_workload(w, pools, chunk=chunk))
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_local_special_cases():
+    w = wl.random_case(131, num_seqs=4, ctx_range=(5, 90), chunk_range=(1, 12), num_q_heads=8, num_kv_heads=2,
+                       head_dim=16)
+    pools = oracle.written_pools(w)
+    full = oracle.attention_for(w, pools=pools)
+    # one chunk holding every position is the full attention, bit for bit
+    assert np.array_equal(oracle.attention_for(w, pools=pools, chunk=int(w.seq_lens.max())), full)
+    kc, vc = pools
+    G = w.num_q_heads // w.num_kv_heads
+    C = 7
+    loc = oracle.attention_for(w, pools=pools, chunk=C)
+    ones = oracle.attention_for(w, pools=pools, chunk=1)
+    win = oracle.attention_for(w, pools=pools, window=C)
+    for s in range(w.num_seqs):
+        q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        c = int(w.seq_lens[s]) - (q1 - q0)
+        for t in range(q0, q1):
+            p = c + t - q0
+            blk, off = int(w.block_tables[s][p // 16]), p % 16
+            own = np.stack([vc[blk, off, h // G].double().numpy() for h in range(w.num_q_heads)])
+            # chunks of one position, and the first row of every chunk: the row's own value, exactly
+            assert np.array_equal(ones[t], own)
+            if p % C == 0:
+                assert np.array_equal(loc[t], own)
+            # the last row of a chunk sees exactly the C keys a window of C gives it
+            if p % C == C - 1:
+                assert np.array_equal(loc[t], win[t])
+
+
+def test_local_equals_plain_attention_over_the_chunk_keys():
+    """A row equals unchunked attention of the same query over its chunk's keys up to itself, laid out again as a
+    sequence of its own (no chunking, a rebuilt table)."""
+    C = 20
+    w = wl.random_case(133, num_seqs=3, ctx_range=(30, 120), chunk_range=(1, 10), num_q_heads=4, num_kv_heads=2,
+                       head_dim=16, q_dtype="bf16", kv_dtype="bf16")
+    kc, vc = oracle.written_pools(w)
+    got = oracle.attention_for(w, pools=(kc, vc), chunk=C)
+    B = 16
+    for s in range(w.num_seqs):
+        q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        c = int(w.seq_lens[s]) - (q1 - q0)
+        for t in range(q0, q1):
+            p = c + t - q0
+            j0 = (p // C) * C
+            n = p + 1 - j0
+            nb = (n + B - 1) // B
+            k2 = torch.zeros(nb, B, w.num_kv_heads, w.head_dim, dtype=kc.dtype)
+            v2 = torch.zeros_like(k2)
+            for j in range(j0, p + 1):
+                blk, off = int(w.block_tables[s][j // B]), j % B
+                k2[(j - j0) // B, (j - j0) % B] = kc[blk, off]
+                v2[(j - j0) // B, (j - j0) % B] = vc[blk, off]
+            ref = oracle.attention(w.query[t:t + 1], k2, v2, np.arange(nb, dtype=np.int32)[None, :],
+                                   np.array([n], dtype=np.int32), np.array([0, 1], dtype=np.int32), w.scale)
+            assert np.array_equal(got[t], ref[0])
