@@ -190,6 +190,24 @@ pa_status_t pa_decode_window(void* out, const void* query, const void* key_cache
                              size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_local -- pa_decode with chunked local attention ([A] §5.1 lists
+ * a chunked-local attention manager beside the sliding-window one, without
+ * its boundary; this library's reading: positions are cut into chunks of
+ * chunk_size tokens, 0 .. C-1, C .. 2C-1, ..., and a row sees the keys of its
+ * own chunk up to itself).  The query of sequence s (at position L-1) attends
+ * to positions C*((L-1) div C) .. L-1.  Table entries wholly before that
+ * chunk are not read.  dtype: PA_BF16; chunk_size >= 1.  workspace:
+ * pa_decode_workspace_bytes(...) with the same max_seq_len.  Other arguments
+ * as pa_decode.
+ */
+pa_status_t pa_decode_local(void* out, const void* query, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                            pa_dtype_t dtype, int32_t chunk_size, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_fp8 -- pa_decode over E4M3FN pools.  [B] tutorial 6.
  * K_j = decode(code) * k_scale, V_j = decode(code) * v_scale (exact values);
  * q_dtype (= out dtype): PA_BF16 or PA_F32 (fp32 queries are rounded to
@@ -290,6 +308,26 @@ pa_status_t pa_prefill_varlen_window(void* out, const void* query, const void* k
                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                      int32_t num_blocks, float scale, pa_dtype_t dtype, int32_t sliding_window,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_varlen_local -- pa_prefill_varlen with chunked local attention
+ * (the reading of pa_decode_local): the row at position p attends to
+ * positions C*(p div C) .. p, C = chunk_size >= 1.  No pool data is read from
+ * the blocks wholly before the chunk of a sequence's first new row.  dtype:
+ * PA_BF16.  workspace: pa_prefill_varlen_local_workspace_bytes(...) with the
+ * same chunk_size (0 on invalid input).  Other arguments as
+ * pa_prefill_varlen.
+ */
+size_t pa_prefill_varlen_local_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t chunk_size);
+pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                    const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                    const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                                    const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, float scale, pa_dtype_t dtype, int32_t chunk_size,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_prefill_varlen_fp8 -- pa_prefill_varlen over E4M3FN pools (uint8 codes)

@@ -24,7 +24,7 @@ PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 KERNELS = {"slot_mapping": 0, "reshape_and_cache": 1, "decode": 2, "decode_merge": 3, "prefill": 4,
            "prefill_merge": 5, "stage_fp8": 6}
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_WORKSPACE",
-          5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_HIP"}
+          5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_HIP", 7: "PA_ERR_NO_SPACE", 8: "PA_ERR_STATE"}
 
 _lock = threading.Lock()
 _lib = None
@@ -84,6 +84,11 @@ def load() -> ctypes.CDLL:
             "pa_prefill_varlen_window_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
             "pa_prefill_varlen_window": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                           ctypes.c_int, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_local": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32,
+                                 i32, P, sz, P], ctypes.c_int),
+            "pa_prefill_varlen_local_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
+            "pa_prefill_varlen_local": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                         ctypes.c_int, i32, P, sz, P], ctypes.c_int),
             "pa_pool_create": ([i32, i32, ctypes.POINTER(P)], ctypes.c_int),
             "pa_pool_destroy": ([P], None),
             "pa_pool_num_free": ([P], i32),
@@ -242,6 +247,22 @@ def pa_decode_window(query, key_cache, value_cache, block_tables, seq_lens, scal
     return out
 
 
+def pa_decode_local(query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                    chunk_size: int, num_splits: int = 0, out=None, workspace=None):
+    """pa_decode where each query sees only the keys of its own chunk of chunk_size positions (bf16 pools)."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    out = torch.empty_like(query) if out is None else out
+    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, num_splits), query.device, workspace)
+    _check("pa_decode_local", lib.pa_decode_local(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(key_cache),
+        chunk_size, num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
 def pa_decode_cascade_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                                       max_seq_len: int, prefix_blocks: int, num_splits: int = 0) -> int:
     return int(load().pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
@@ -337,6 +358,35 @@ def pa_prefill_varlen_window(query, key_cache, value_cache, block_tables, seq_le
         _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
         _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(),
         sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), sliding_window,
+        None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
+def pa_prefill_varlen_local_workspace_bytes(query_start_loc_host, seq_lens_host, num_q_heads: int,
+                                            num_kv_heads: int, head_dim: int, chunk_size: int) -> int:
+    q = _i32_host(query_start_loc_host)
+    s = _i32_host(seq_lens_host)
+    return int(load().pa_prefill_varlen_local_workspace_bytes(q.data_ptr(), s.data_ptr(), s.numel(), num_q_heads,
+                                                              num_kv_heads, head_dim, chunk_size))
+
+
+def pa_prefill_varlen_local(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, seq_lens_host,
+                            query_start_loc_host, scale: float, chunk_size: int, out=None, workspace=None):
+    """pa_prefill_varlen where the row at position p sees positions chunk_size*(p // chunk_size) .. p (bf16)."""
+    lib = load()
+    T, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    qh = _i32_host(query_start_loc_host)
+    sh = _i32_host(seq_lens_host)
+    out = torch.empty_like(query) if out is None else out
+    need = int(lib.pa_prefill_varlen_local_workspace_bytes(qh.data_ptr(), sh.data_ptr(), sh.numel(), Hq, Hkv, D,
+                                                           chunk_size))
+    ws, wsb = _workspace(need, query.device, workspace)
+    _check("pa_prefill_varlen_local", lib.pa_prefill_varlen_local(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(),
+        sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), chunk_size,
         None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
 

@@ -230,9 +230,10 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
                        int q_f32, float k_scale, float v_scale, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, hipStream_t stream, int32_t prefix_blocks = 0,
-                       int32_t sliding_window = 0) {
-  // a window of W keys spans at most W/16 + 2 blocks of each sequence
-  const int span = sliding_window > 0 ? std::min<int64_t>(max_seq_len, (int64_t)sliding_window + 16) : max_seq_len;
+                       int32_t sliding_window = 0, int32_t local_chunk = 0) {
+  // a window (or local chunk) of W keys spans at most W/16 + 2 blocks of each sequence
+  const int vis = sliding_window > 0 ? sliding_window : local_chunk;
+  const int span = vis > 0 ? std::min<int64_t>(max_seq_len, (int64_t)vis + 16) : max_seq_len;
   const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, span);
   pa::DecodeParams p{};
   p.out = out;
@@ -252,6 +253,7 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   p.max_seq_len = max_seq_len;
   p.n_splits = n_splits;
   p.window = sliding_window > 0 ? sliding_window : 0;
+  p.chunk = local_chunk > 0 ? local_chunk : 0;
   p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
   p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
   p.q_f32 = q_f32;
@@ -592,7 +594,7 @@ struct VarlenPlan {
 };
 
 pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_tokens, int bt_stride,
-                        int group, int num_kv_heads, VarlenPlan& plan, int window = 0) {
+                        int group, int num_kv_heads, VarlenPlan& plan, int window = 0, int chunk = 0) {
   if (qsl[0] != 0) return fail(PA_ERR_SHAPE, "query_start_loc_host[0] = %d, expected 0", qsl[0]);
   const int P = pa::kPrefillRows / group;
   plan.tile_positions = P;
@@ -619,7 +621,9 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
     for (int rt = 0; rt < n_rt; ++rt) {
       const int pos_end = std::min(q_len, (rt + 1) * P);
       // a sliding window hides the key tiles below the tile's first row's window
-      const int kt_lo = window > 0 ? std::max(c + rt * P - window + 1, 0) / pa::kPrefillKeys : 0;
+      const int first = c + rt * P;
+      const int lo = chunk > 0 ? first - first % chunk : window > 0 ? std::max(first - window + 1, 0) : 0;
+      const int kt_lo = lo / pa::kPrefillKeys;
       const int n_kt = ceil_div(c + pos_end, pa::kPrefillKeys) - kt_lo;
       tiles.push_back({s, rt, n_kt, kt_lo});
       total += n_kt;
@@ -685,11 +689,11 @@ size_t varlen_workspace(const VarlenPlan& plan, int num_seqs, int num_q_heads, i
 
 // pa_prefill_varlen(_window)_workspace_bytes without the argument checks.
 size_t varlen_workspace_bytes(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_q_heads, int num_kv_heads,
-                              int head_dim, int window) {
+                              int head_dim, int window, int chunk = 0) {
   VarlenPlan plan;
   const std::string saved = g_last_error;
   const pa_status_t st = plan_varlen(qsl, sl, num_seqs, qsl[num_seqs], INT32_MAX, num_q_heads / num_kv_heads,
-                                     num_kv_heads, plan, window);
+                                     num_kv_heads, plan, window, chunk);
   g_last_error = saved;
   if (st != PA_OK) return 0;
   return varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
@@ -728,7 +732,8 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
                        const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, float scale, pa_dtype_t dtype, int kv_kind, float k_scale, float v_scale,
-                       void* workspace, size_t workspace_bytes, void* stream, int32_t sliding_window = 0) {
+                       void* workspace, size_t workspace_bytes, void* stream, int32_t sliding_window = 0,
+                       int32_t local_chunk = 0) {
   if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_SHAPE, "negative num_seqs or num_tokens");
   if (num_seqs == 0) return num_tokens == 0 ? ok() : fail(PA_ERR_SHAPE, "num_tokens > 0 with no sequences");
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc ||
@@ -741,7 +746,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
   VarlenPlan plan;
   st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
-                   num_q_heads / num_kv_heads, num_kv_heads, plan, sliding_window);
+                   num_q_heads / num_kv_heads, num_kv_heads, plan, sliding_window, local_chunk);
   if (st != PA_OK) return st;
   if (dtype == PA_F32 && !plan.items.empty())
     return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
@@ -772,7 +777,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     st = run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
                     num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, plan.max_decode_len, scale,
                     kv_kind == pa::kFP8 ? pa::kFP8 : (dtype == PA_F32 ? pa::kF32 : pa::kBF16), dtype == PA_F32,
-                    k_scale, v_scale, 0, workspace, workspace_bytes, hs, 0, sliding_window);
+                    k_scale, v_scale, 0, workspace, workspace_bytes, hs, 0, sliding_window, local_chunk);
     if (st != PA_OK) return st;
   }
   auto* ws = static_cast<unsigned char*>(workspace);
@@ -826,6 +831,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
     p.v_scale = kv_kind == pa::kFP8 ? v_scale : 1.f;
     p.window = sliding_window > 0 ? sliding_window : 0;
+    p.chunk = local_chunk > 0 ? local_chunk : 0;
     const size_t n = std::min(plan.items.size() - i0, (size_t)pa::kMaxPrefillItems);
     p.n_items = (int)n;
     std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint64_t));
@@ -928,6 +934,56 @@ pa_status_t pa_prefill_varlen_window(void* out, const void* query, const void* k
                     seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                     block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream,
                     sliding_window);
+}
+
+size_t pa_prefill_varlen_local_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t chunk_size) {
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGroup || chunk_size < 1)
+    return 0;
+  return varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                0, chunk_size);
+}
+
+pa_status_t pa_decode_local(void* out, const void* query, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype,
+                            int32_t chunk_size, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "chunked local decode: dtype must be PA_BF16");
+  if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                    pa::kBF16, 0, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                    0, 0, chunk_size);
+}
+
+pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                    const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                    const int32_t* query_start_loc, const int32_t* seq_lens_host,
+                                    const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, float scale, pa_dtype_t dtype, int32_t chunk_size,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "chunked local prefill: dtype must be PA_BF16");
+  if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
+  return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
+                    seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream, 0,
+                    chunk_size);
 }
 
 size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,

@@ -162,15 +162,17 @@ __device__ __forceinline__ float sum_across_rows(float x) {
 
 // Blocks of sequence s the decode attends: ceil(seq_len / 16), or 0 when s
 // is not a decode row of a flattened batch (q_len != 1).
-// First visible key of sequence s: L - window with a sliding window, else 0.
+// First visible key of a sequence of L >= 1 tokens: L - window with a sliding window, the
+// start of the last position's chunk with chunked local attention, else 0.
 __device__ __forceinline__ int decode_first_key(const DecodeParams& p, int L) {
+  if (p.chunk > 0) return (L - 1) - (L - 1) % p.chunk;
   return p.window > 0 ? max(L - p.window, 0) : 0;
 }
 
 // Leading blocks of sequence s its own pieces skip: the shared prefix of a cascade, or the
-// blocks wholly before a sliding window.
+// blocks wholly before the visible keys (sliding window, local chunk).
 __device__ __forceinline__ int decode_skip(const DecodeParams& p, int L) {
-  return p.window > 0 ? decode_first_key(p, L) >> 4 : p.skip_blocks;
+  return (p.window > 0 || p.chunk > 0) ? decode_first_key(p, L) >> 4 : p.skip_blocks;
 }
 
 // Blocks of sequence s that its own pieces cover.

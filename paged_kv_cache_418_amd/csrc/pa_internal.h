@@ -51,6 +51,7 @@ struct DecodeParams {
   // sequences): the suffix launch skips the shared blocks and leaves every piece partial;
   // the prefix launch writes pre_* partials; the merge folds both in.
   int window;                // sliding window (> 0): the query at position L-1 sees keys L-window .. L-1
+  int chunk;                 // chunked local attention (> 0): the query at L-1 sees keys C*((L-1) div C) .. L-1
   int skip_blocks;           // leading table entries the per-sequence pieces skip (0 without cascade)
   int force_partial;         // every piece leaves a partial result, none is finished in place
   int prefix_blocks;         // shared leading blocks (cascade), else 0
@@ -90,6 +91,7 @@ struct PrefillParams {
   float scale_log2;
   float v_scale;             // 1, or the fp8 value scale (pools staged as the codes' exact values)
   int window;                // sliding window (> 0): the row at position p sees keys p-window+1 .. p
+  int chunk;                 // chunked local attention (> 0): the row at position p sees keys C*(p div C) .. p
   int n_items;
   uint64_t items[kMaxPrefillItems];
 };

@@ -97,8 +97,9 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// WINDOW: sliding-window attention (p.window > 0), a variant of its own so that the
-// plain causal kernel keeps its register budget.
+// WINDOW: a lower edge on the visible keys as well -- a sliding window (p.window > 0: the
+// row at p sees p-window+1 .. p) or chunked local attention (p.chunk > 0: C*(p div C) .. p)
+// -- a variant of its own so that the plain causal kernel keeps its register budget.
 template <int D, bool WINDOW>
 __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   using Sh = PrefillShape<D>;
@@ -133,6 +134,10 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   const int wave_first = c + pos0 + (32 * wave) / G;
   const int wave_last = c + min(pos_end - 1, pos0 + (32 * wave + 31) / G);
   const bool wave_live = 32 * wave < P * G && pos0 + (32 * wave) / G < pos_end;
+  // WINDOW: first visible key of the row at position q (non-decreasing in q)
+  auto first_visible = [&](int q) { return p.chunk > 0 ? q - q % p.chunk : q - p.window + 1; };
+  const uint32_t row_span = WINDOW ? (uint32_t)(row_pos - first_visible(row_pos) + 1) : 0u;  // keys the row sees
+  const int wave_lo_max = WINDOW ? first_visible(wave_last) : 0;  // largest first visible key of the wave
 
   // ---- copy role: each wave copies kCopies 1 KB slabs of K and of V per tile.  Slab
   // kCopies*wave + i holds rows kRowsPerCopy*(kCopies*wave + i) ...; lane = (row in slab,
@@ -150,7 +155,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   // and finite -- key 0, or with a window the last visible key -- and their scores are
   // masked, so the probabilities that meet the filler are 0.
   const int fill_key = WINDOW ? kv_end - 1 : 0;
-  const int key_first = WINDOW ? c + pos0 - p.window + 1 : 0;
+  const int key_first = WINDOW ? first_visible(c + pos0) : 0;
   const int bt_fill = min(max(bt[fill_key >> 4], 0), p.num_blocks - 1);
   // Physical block of this wave's rows of a tile.  The load is unconditional (a key past
   // the last visible one reads the last visible key's entry; any entry read is clamped
@@ -413,18 +418,18 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   auto softmax = [&](f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4]) {
     // lane's entries: key key0 + kt*32 + 8*(r/4) + 4*half + r%4 of row rl.  Raw scores are
     // masked and maximised; the scale (> 0) is applied inside exp2(fma(s, scale, -m)).
-    // a tile needs masking if it reaches past some row's position, or (sliding window) below
-    // some row's first visible key
+    // a tile needs masking if it reaches past some row's position, or (WINDOW) below some
+    // row's first visible key
     if constexpr (WINDOW) {
-      if (key0 + Sh::kKeys - 1 > wave_first || key0 < wave_last - p.window + 1) {
-        // visible: 0 <= row_pos - key < window, one unsigned comparison
+      if (key0 + Sh::kKeys - 1 > wave_first || key0 < wave_lo_max) {
+        // visible: 0 <= row_pos - key < row_span, one unsigned comparison
         const uint32_t rel = (uint32_t)(row_pos - key0 - 4 * half);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const uint32_t dist = rel - (uint32_t)(kt * 32 + 8 * (r >> 2) + (r & 3));
-            sacc[kt][r] = dist < (uint32_t)p.window ? sacc[kt][r] : -INFINITY;
+            sacc[kt][r] = dist < row_span ? sacc[kt][r] : -INFINITY;
           }
       }
     } else if (key0 + Sh::kKeys - 1 > wave_first) {
@@ -772,12 +777,12 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
     hipLaunchKernelGGL(kernel, grid, dim3(threads), lds, stream, p);
   };
   if (head_dim == 128) {
-    if (p.window > 0)
+    if (p.window > 0 || p.chunk > 0)
       launch(&prefill_kernel<128, true>, PrefillShape<128>::kThreads);
     else
       launch(&prefill_kernel<128, false>, PrefillShape<128>::kThreads);
   } else {
-    if (p.window > 0)
+    if (p.window > 0 || p.chunk > 0)
       launch(&prefill_kernel<64, true>, PrefillShape<64>::kThreads);
     else
       launch(&prefill_kernel<64, false>, PrefillShape<64>::kThreads);

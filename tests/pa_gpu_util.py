@@ -69,6 +69,16 @@ class DevWorkload:
         return pk.pa_prefill_varlen_window(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
                                            self.qsl, w.seq_lens, w.query_start_loc, w.scale, window, out=out)
 
+    def decode_local(self, chunk, num_splits=0, out=None):
+        w = self.w
+        return pk.pa_decode_local(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
+                                  self.max_seq_len(), chunk, num_splits, out=out)
+
+    def prefill_local(self, chunk, out=None):
+        w = self.w
+        return pk.pa_prefill_varlen_local(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                          self.qsl, w.seq_lens, w.query_start_loc, w.scale, chunk, out=out)
+
     def prefill(self, out=None):
         w = self.w
         if w.kv_dtype == "fp8":

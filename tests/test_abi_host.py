@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 34
+    assert len(syms) == 37
     assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
@@ -215,3 +215,18 @@ def test_window_workspace_and_argument_checks(lib):
            128, 16, 1000, 0.088]
     assert lib.pa_prefill_varlen_window(*pre, b.PA_F32, 128, FAKE, 1 << 30, None) == 3  # dtype
     assert lib.pa_prefill_varlen_window(*pre, b.PA_BF16, -5, FAKE, 1 << 30, None) == 2  # window
+
+
+def test_local_workspace_and_argument_checks(lib):
+    q, s = _host_i32([0, 40, 41, 341]), _host_i32([100, 5000, 900])
+    args = (ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128)
+    base = lib.pa_prefill_varlen_workspace_bytes(*args)
+    assert lib.pa_prefill_varlen_local_workspace_bytes(*args, 5000) == base  # one chunk: causal work
+    assert lib.pa_prefill_varlen_local_workspace_bytes(*args, 0) == 0
+    dec = [FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 4, 32, 8, 128, 16, 1000, 3072, 0.088]
+    assert lib.pa_decode_local(*dec, b.PA_F32, 128, 0, FAKE, 1 << 30, None) == 3       # dtype
+    assert lib.pa_decode_local(*dec, b.PA_BF16, 0, 0, FAKE, 1 << 30, None) == 2       # chunk
+    pre = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, ctypes.addressof(s), ctypes.addressof(q), 3, 341, 32, 8,
+           128, 16, 1000, 0.088]
+    assert lib.pa_prefill_varlen_local(*pre, b.PA_F32, 128, FAKE, 1 << 30, None) == 3  # dtype
+    assert lib.pa_prefill_varlen_local(*pre, b.PA_BF16, 0, FAKE, 1 << 30, None) == 2   # chunk

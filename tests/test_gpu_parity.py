@@ -507,3 +507,68 @@ def test_prefill_window_covering_everything_is_full_attention():
     b = d.prefill()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ chunked local attention
+# The row at position p sees positions C*(p // C) .. p (the oracle's reading of the pages' chunked-local
+# attention).  Table columns wholly before what the kernels read point at the NaN block.
+
+def _local_case(w, chunk, run, tol):
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = run(d)
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w), chunk=chunk)
+    err = max_err(out, ref)
+    say(f"  chunk={chunk} max_abs_err={err:.3e}")
+    assert err <= tol
+    return out
+
+
+@pytest.mark.parametrize("heads", [(32, 8, 128), (4, 2, 64), (16, 1, 128)])
+@pytest.mark.parametrize("chunk", [1, 16, 100, 5000])
+@pytest.mark.parametrize("num_splits", [0, 7])
+def test_decode_local_random(heads, chunk, num_splits):
+    Hq, Hkv, D = heads
+    w = wl.random_case(700 + chunk % 89 + Hq + num_splits, num_seqs=6, ctx_range=(1, 700), num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, q_dtype="bf16", kv_dtype="bf16")
+    # decode reads blocks from the one holding the start of position L-1's chunk
+    w = _poison_columns(w, [((int(L) - 1) // chunk * chunk) // 16 for L in w.seq_lens])
+    say("decode local", heads, chunk, num_splits, list(w.seq_lens))
+    _local_case(w, chunk, lambda d: d.decode_local(chunk, num_splits), TOL["bf16"])
+
+
+@pytest.mark.parametrize("seed", [711, 712])
+@pytest.mark.parametrize("heads", [(32, 8, 128), (4, 2, 64), (12, 4, 128)])
+@pytest.mark.parametrize("chunk", [1, 37, 200, 100000])
+def test_prefill_local_random(seed, heads, chunk):
+    Hq, Hkv, D = heads
+    w = wl.random_case(seed + chunk % 97, num_seqs=6, ctx_range=(1, 700), chunk_range=(1, 400), num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, q_dtype="bf16", kv_dtype="bf16")
+    # no data is read from blocks wholly before the chunk of a sequence's first new row
+    w = _poison_columns(w, [((int(L) - int(ql)) // chunk * chunk) // 16 for L, ql in zip(w.seq_lens, w.q_lens)])
+    say("prefill local", seed, heads, chunk, list(w.q_lens), list(w.seq_lens))
+    _local_case(w, chunk, lambda d: d.prefill_local(chunk), TOL["bf16"])
+
+
+@pytest.mark.parametrize("chunk", [64, 300, 1000])
+def test_prefill_local_long_chunks_split(chunk):
+    w = wl.build("prefill_long_local", seed=741, ctx_lens=[2200, 700, 35, 1900], q_lens=[700, 1, 35, 333],
+                 num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    w = _poison_columns(w, [((int(L) - int(ql)) // chunk * chunk) // 16 for L, ql in zip(w.seq_lens, w.q_lens)])
+    say("prefill local long", chunk)
+    _local_case(w, chunk, lambda d: d.prefill_local(chunk), TOL["bf16"])
+
+
+def test_local_with_one_chunk_is_full_attention():
+    w = wl.random_case(755, num_seqs=5, ctx_range=(1, 900), chunk_range=(1, 500), num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    big = int(w.seq_lens.max())
+    a, b_ = d.prefill_local(big), d.prefill()
+    dw = DevWorkload(wl.llama3_8b_decode_bf16())
+    dw.write_new_tokens()
+    c_, d_ = dw.decode_local(int(dw.w.seq_lens.max())), dw.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b_) and torch.equal(c_, d_)
