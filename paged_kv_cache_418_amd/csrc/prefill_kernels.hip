@@ -598,53 +598,65 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
     wait_vmcnt<0>();  // no copy may still be writing LDS when the work-group ends
   }
 
+  // ---- epilogue.  The lane's outputs (d = n*32 + 8*(r/4) + 4*half + r%4 of row rl) are
+  // scattered 8-byte pieces of 32 rows; stored as they are, every store instruction would
+  // touch 32 lines.  Each wave stages its 32 rows in LDS (free now; 16-byte chunks XOR-
+  // swizzled by row so that the 8-byte writes spread over the banks) and stores whole
+  // rows from there: 16 bytes per lane, 64/kChunks rows per instruction.
+  __syncthreads();  // every wave is done with the rings
   if (!wave_live) return;
   const float l = sum_halves(lsum);
-  if (!row_ok) return;
-  const int pos = pos0 + R / G, h = kvh * G + (R % G);
-  // lane's outputs: d = n*32 + 8*(r/4) + 4*half + r%4
-  if (whole) {
-    const float inv = p.v_scale / l;
-    uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(q0 + pos) * p.num_q_heads + h) * D;
+  const float inv = whole ? p.v_scale / l : (l > 0.f ? 1.f / l : 0.f);  // rows without a position: never stored
+  unsigned char* const stage = smem + wave * 32 * Sh::kRowBytes;
 #pragma unroll
-    for (int n = 0; n < Sh::kDTiles; ++n)
+  for (int n = 0; n < Sh::kDTiles; ++n)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d = n * 32 + 8 * rq + 4 * half;
-        *reinterpret_cast<u32x2*>(op + d) = u32x2{pack_bf16x2(acc[n][4 * rq] * inv, acc[n][4 * rq + 1] * inv),
-                                                  pack_bf16x2(acc[n][4 * rq + 2] * inv, acc[n][4 * rq + 3] * inv)};
-      }
-  } else {
-    // partial result of a split row tile: slot (launch base + item) x kv head x row.  O / l
-    // is bounded by the largest |V| of the row's keys, so fp16 holds it with a relative
-    // error of 2^-11 (a row that saw none of its keys stores 0; its m is -inf).
-    const size_t pi = ((size_t)(p.item_base + blockIdx.x) * p.num_kv_heads + kvh) * kPrefillRows + R;
-    uint16_t* po = p.part_o + pi * D;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int n = 0; n < Sh::kDTiles; ++n)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d = n * 32 + 8 * rq + 4 * half;
-        *reinterpret_cast<u32x2*>(po + d) = u32x2{pack_f16x2(acc[n][4 * rq] * inv, acc[n][4 * rq + 1] * inv),
-                                                  pack_f16x2(acc[n][4 * rq + 2] * inv, acc[n][4 * rq + 3] * inv)};
-      }
-    if (half == 0) {
-      p.part_m[pi] = m_ref;
-      p.part_l[pi] = l;
+    for (int rq = 0; rq < 4; ++rq) {
+      const int chunk = (n * 4 + rq) ^ (rl % Sh::kChunks);
+      const float a0 = acc[n][4 * rq] * inv, a1 = acc[n][4 * rq + 1] * inv;
+      const float a2 = acc[n][4 * rq + 2] * inv, a3 = acc[n][4 * rq + 3] * inv;
+      // split pieces keep O / l in fp16: bounded by the largest |V| of the row's keys, a
+      // relative error of 2^-11 (a row that saw none of its keys stores 0; its m is -inf)
+      const u32x2 v = whole ? u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)}
+                            : u32x2{pack_f16x2(a0, a1), pack_f16x2(a2, a3)};
+      *reinterpret_cast<u32x2*>(stage + rl * Sh::kRowBytes + chunk * 16 + half * 8) = v;
     }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // partial results of a split row tile: slot (launch base + item) x kv head x row
+  const size_t slot_row0 = ((size_t)(p.item_base + blockIdx.x) * p.num_kv_heads + kvh) * kPrefillRows + 32 * wave;
+  constexpr int kRowsPerStore = 64 / Sh::kChunks;
+  const int sc_chunk = lane % Sh::kChunks;
+#pragma unroll
+  for (int it = 0; it < 32 / kRowsPerStore; ++it) {
+    const int row = it * kRowsPerStore + lane / Sh::kChunks;
+    const u32x4 v =
+        *reinterpret_cast<const u32x4*>(stage + row * Sh::kRowBytes + ((sc_chunk ^ (row % Sh::kChunks)) << 4));
+    const int Rw = 32 * wave + row;
+    if (Rw >= P * G || pos0 + Rw / G >= pos_end) continue;
+    uint16_t* dst = whole ? reinterpret_cast<uint16_t*>(p.out) +
+                                ((size_t)(q0 + pos0 + Rw / G) * p.num_q_heads + kvh * G + Rw % G) * D
+                          : p.part_o + (slot_row0 + row) * D;
+    *reinterpret_cast<u32x4*>(dst + sc_chunk * 8) = v;
+  }
+  if (!whole && half == 0 && row_ok) {
+    p.part_m[slot_row0 + rl] = m_ref;
+    p.part_l[slot_row0 + rl] = l;
   }
 }
 
-// Log-sum-exp merge of the splits of a row tile: grid (row tiles x 32 groups of
-// 8 rows, kv heads), one wave per two rows, lanes over d (coalesced).  Splits
-// of one row tile are consecutive items, so their slots are first .. first+n-1.
-// The merge runs online over the splits (running maximum, weight sum and
-// output), so the loads of later splits do not wait for earlier ones.
+// Log-sum-exp merge of the splits of a row tile: grid (row tiles x 8 groups of 32 rows,
+// kv heads), 256 threads.  A wave takes 8 rows; D/8 lanes cover one row, 8 elements (16
+// bytes of fp16 partial, 16 bytes of bf16 output) each, so every load and store moves whole
+// rows.  Split i of a row holds O_i / l_i with its reference maximum m_i (log2 units) and
+// weight sum l_i; it enters with weight l_i * 2^(m_i - M), folded online over the splits.
 template <int D>
 __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p) {
-  constexpr int PER_LANE = D / 64;
-  const uint64_t item = p.items[blockIdx.x >> 5];
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerPass = 64 / kLanesPerRow;
+  constexpr int kRowsPerWave = 8;
+  const uint64_t item = p.items[blockIdx.x >> 3];
   const int s = (int)(item & 0xFFFFu);
   const int rt = (int)((item >> 16) & 0xFFFFu);
   const int first = (int)((item >> 32) & 0xFFFFFu), n = (int)(item >> 52);
@@ -654,43 +666,38 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
   const int q_len = p.qsl[s + 1] - q0;
   const int pos0 = rt * P;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane / kLanesPerRow, c = lane % kLanesPerRow;
   const size_t slot_step = (size_t)p.num_kv_heads * kPrefillRows;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int R = (blockIdx.x & 31) * 8 + wave * 2 + k;
+  for (int k = 0; k < kRowsPerWave / kRowsPerPass; ++k) {
+    const int R = (blockIdx.x & 7) * 32 + wave * kRowsPerWave + k * kRowsPerPass + sub;
     const int pos = pos0 + R / G;
     if (R >= P * G || pos >= q_len) continue;
     const size_t base = ((size_t)first * p.num_kv_heads + kvh) * kPrefillRows + R;
-    float M = -INFINITY, den = 0.f, o[PER_LANE];
+    float M = -INFINITY, den = 0.f, o[8];
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) o[j] = 0.f;
+    for (int j = 0; j < 8; ++j) o[j] = 0.f;
 #pragma unroll 4
     for (int i = 0; i < n; ++i) {
       const size_t pi = base + i * slot_step;
       const float mi = p.part_m[pi], li = p.part_l[pi];
-      float src[PER_LANE];
-      if constexpr (PER_LANE == 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(p.part_o + pi * D + lane * 2);
-        src[0] = f16_bits_to_f32(w & 0xFFFFu);
-        src[1] = f16_bits_to_f32(w >> 16);
-      } else {
-#pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) src[j] = f16_bits_to_f32(p.part_o[pi * D + lane * PER_LANE + j]);
-      }
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p.part_o + pi * D + c * 8);
       if (mi == -INFINITY) continue;  // this split saw none of the row's keys
-      // split i holds O_i / l_i: weight l_i * 2^(m_i - M)
       const float Mn = fmaxf(M, mi);
       const float a = fast_exp2(M - Mn), b = li * fast_exp2(mi - Mn);
       den = den * a + b;
 #pragma unroll
-      for (int j = 0; j < PER_LANE; ++j) o[j] = o[j] * a + src[j] * b;
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = o[2 * j] * a + f16_bits_to_f32(w[j] & 0xFFFFu) * b;
+        o[2 * j + 1] = o[2 * j + 1] * a + f16_bits_to_f32(w[j] >> 16) * b;
+      }
       M = Mn;
     }
     const float inv = p.v_scale / den;
     const int h = kvh * G + (R % G);
-    uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(q0 + pos) * p.num_q_heads + h) * D + lane * PER_LANE;
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) op[j] = f32_to_bf16(o[j] * inv);
+    uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(q0 + pos) * p.num_q_heads + h) * D + c * 8;
+    *reinterpret_cast<u32x4*>(op) = u32x4{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                                          pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
   }
 }
 
@@ -792,7 +799,7 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
 }
 
 hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.n_items * 32, p.num_kv_heads);
+  const dim3 grid(p.n_items * 8, p.num_kv_heads);
   timing_mark(kKPrefillMerge, true, stream);
   if (head_dim == 128)
     hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(256), 0, stream, p);
