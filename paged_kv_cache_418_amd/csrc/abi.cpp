@@ -633,14 +633,26 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
     return fail(PA_ERR_SHAPE, "query_start_loc_host[num_seqs] = %d != num_tokens %d", qsl[num_seqs], num_tokens);
   if (tiles.empty()) return PA_OK;
   // one work-group per compute unit: the smallest per-item budget (>= 4 key tiles) whose
-  // pieces, ceil(n_kt / budget) per row tile, number at most target_items
+  // pieces, ceil(n_kt / budget) per row tile, number at most target_items.  With at least
+  // as many row tiles as that, nothing is split (the longest-first list keeps the compute
+  // units busy by itself).  The piece count does not grow with the budget: bisection.
   const int64_t target_items = std::max<int64_t>(1, device_cu_count() / std::max(1, num_kv_heads));
-  int budget = (int)std::max<int64_t>(4, (total + target_items - 1) / target_items);
-  for (;;) {
+  int max_kt = 1;
+  for (const RowTile& t : tiles) max_kt = std::max(max_kt, t.n_kt);
+  auto pieces = [&](int b) {
     int64_t n = 0;
-    for (const RowTile& t : tiles) n += ceil_div(t.n_kt, budget);
-    if (n <= target_items || budget >= (1 << 16)) break;
-    ++budget;
+    for (const RowTile& t : tiles) n += ceil_div(t.n_kt, b);
+    return n;
+  };
+  int budget = max_kt;
+  if ((int64_t)tiles.size() < target_items) {
+    int lo = (int)std::min<int64_t>(max_kt, std::max<int64_t>(4, (total + target_items - 1) / target_items));
+    int hi = max_kt;  // pieces(max_kt) = row tiles < target_items
+    while (lo < hi) {
+      const int mid = lo + (hi - lo) / 2;
+      if (pieces(mid) <= target_items) hi = mid; else lo = mid + 1;
+    }
+    budget = lo;
   }
   // longest row tiles first
   std::stable_sort(tiles.begin(), tiles.end(), [](const RowTile& a, const RowTile& b) { return a.n_kt > b.n_kt; });
