@@ -284,6 +284,14 @@ def bench_mixed(args, result):
     pre8_call_ms, _ = time_steps(cs8.attend_next, args.steps, args.warmup)
     kt8 = kernel_times(cs8.attend_next, args.steps, ["prefill", "stage_fp8"])
     del cs8, w8
+    # steady state: long prompts, where launch, first tiles and tail are small next to the tile loop
+    lw = wl.long_prefill_bf16()
+    ls = Step(lw, copies=1)
+    long_call_ms, _ = time_steps(ls.attend_next, max(5, args.steps // 5), 2)
+    ktl = kernel_times(ls.attend_next, max(5, args.steps // 5), ["prefill"])
+    long_flops = wl.prefill_flops(lw)
+    del ls, lw
+    mfma_peak = pk_mod().probe_mfma_peak()
     dec_w = _sub(w, list(range(48)))
     ds = Step(dec_w, copies=2)
     dms, _ = time_steps(ds.attend_next, args.steps, args.warmup)
@@ -298,7 +306,18 @@ def bench_mixed(args, result):
              "prefill_roofline": {"kernel": "prefill_kernel<128>", "bound": "mfma", "achieved": round(tflops, 2),
                                   "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                                  "peak_measured": round(mfma_peak, 1),
+                                  "frac_of_measured": round(tflops / mfma_peak, 4),
                                   "alg_flops_per_launch": flops},
+             "prefill_long": {"workload": "long_prefill_bf16 (4 prompts x 4096 tokens, causal, empty caches)",
+                              "gflop": round(long_flops / 1e9, 2), "call_ms": round(long_call_ms, 4),
+                              "kernel_ms": round(ktl["prefill"][0], 4),
+                              "call_tflops": round(long_flops / (long_call_ms * 1e-3) / 1e12, 1),
+                              "call_frac_of_peak": round(long_flops / (long_call_ms * 1e-3) / 1e12 /
+                                                         BF16_MFMA_PEAK_TFLOPS, 4),
+                              "call_frac_of_measured_peak": round(long_flops / (long_call_ms * 1e-3) / 1e12 /
+                                                                  mfma_peak, 4)},
+             "mfma_measured_peak_tflops": round(mfma_peak, 1),
              "prefill_fp8": {"call_ms": round(pre8_call_ms, 5), "kernel_ms": round(kt8["prefill"][0], 5),
                              "staging_ms": round(kt8["stage_fp8"][0], 5),
                              "call_tflops": round(flops / (pre8_call_ms * 1e-3) / 1e12, 2)},
@@ -338,6 +357,11 @@ def bench_cascade(args, result):
     out["speedup"] = round(out["plain"]["ms_per_step"] / out["cascade"]["ms_per_step"], 3)
     result["cascade_step"] = out
     torch.cuda.empty_cache()
+
+
+def pk_mod():
+    import paged_kv_cache_418_amd as pk
+    return pk._binding
 
 
 def bench_window(args, result):

@@ -470,6 +470,17 @@ typedef enum pa_kernel {
 } pa_kernel_t;
 
 pa_status_t pa_timing_enable(int on);
+
+/*
+ * pa_probe_mfma_peak -- measurement only (the denominator of a measured
+ * matrix-core peak beside the published one; not part of the pages'
+ * problem).  Launches blocks work-groups of 256 threads; each wave runs
+ * iters rounds of four independent v_mfma_f32_32x32x16_bf16 (32768 FLOP
+ * each) on register operands and writes one float per thread to out
+ * (device, blocks * 256 floats).  Time it with events on `stream`:
+ * FLOP = blocks * 4 waves * iters * 4 * 32768.
+ */
+pa_status_t pa_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream);
 pa_status_t pa_timing_reset(void);
 pa_status_t pa_timing_read(pa_kernel_t kernel, int64_t* count, double* total_ms);
 

@@ -102,6 +102,7 @@ def load() -> ctypes.CDLL:
             "pa_pool_block_state": ([P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32),
                                      ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
             "pa_pool_free_queue": ([P, P, i32], i32),
+            "pa_probe_mfma_peak": ([P, i32, i32, P], ctypes.c_int),
             "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_reset": ([], ctypes.c_int),
             "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
@@ -523,3 +524,20 @@ class BlockPool:
         out = np.zeros(max(n, 1), dtype=np.int32)
         self._lib.pa_pool_free_queue(self._h, out.ctypes.data, n)
         return out[:n].tolist()
+
+
+def probe_mfma_peak(blocks: int = 512, iters: int = 20000, reps: int = 3) -> float:
+    """Measured bf16 matrix-core rate (TFLOP/s) of v_mfma_f32_32x32x16_bf16 on this GPU (best of reps)."""
+    lib = load()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    best = None
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _check("pa_probe_mfma_peak", lib.pa_probe_mfma_peak(out.data_ptr(), blocks, iters, _stream()))
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    flop = blocks * 4 * iters * 4 * 32768.0
+    return flop / (best * 1e-3) / 1e12

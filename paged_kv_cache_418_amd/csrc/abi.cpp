@@ -1107,6 +1107,12 @@ void timing_mark(int kernel, bool begin, hipStream_t stream) {
 
 extern "C" {
 
+pa_status_t pa_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (!out) return fail(PA_ERR_NULL, "pa_probe_mfma_peak: out is NULL");
+  if (blocks < 1 || iters < 1) return fail(PA_ERR_SHAPE, "pa_probe_mfma_peak: blocks and iters must be >= 1");
+  return hip_status(pa::launch_mfma_peak(out, blocks, iters, static_cast<hipStream_t>(stream)), "mfma probe launch");
+}
+
 pa_status_t pa_timing_enable(int on) {
   timing().on.store(on != 0, std::memory_order_relaxed);
   return ok();

@@ -155,5 +155,7 @@ hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache
                             int max_blocks, int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k,
                             uint16_t* stage_v, int32_t* stage_tables, hipStream_t stream);
 hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream);
+// matrix-core peak probe (measurement only): blocks x 256 threads, 4 x iters MFMAs per wave
+hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t stream);
 
 }  // namespace pa

@@ -798,6 +798,35 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
   return hipGetLastError();
 }
 
+// Matrix-core peak probe: every wave runs `iters` rounds of four independent
+// v_mfma_f32_32x32x16_bf16 (the prefill kernel's instruction) on register operands and
+// writes one sum per lane, so nothing is optimised away.  256 threads per work-group.
+__global__ void __launch_bounds__(256) mfma_peak_kernel(float* out, int iters) {
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  // normal bf16 operands (1.0, 0.5, 0.25, ...): no denormal inputs
+  const u32x4 a{0x3f803f80u, 0x3f003f00u, 0x3e803e80u, 0x3f803f00u}, b{0x3f003f80u, 0x3e803f80u, 0x3f803f80u, 0x3f003f00u};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(a), u4_to_bf16x8(b), acc[i], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[i][r];
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
+hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(256), 0, stream, out, iters);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid(p.n_items * 8, p.num_kv_heads);
   timing_mark(kKPrefillMerge, true, stream);

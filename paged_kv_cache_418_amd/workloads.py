@@ -264,12 +264,20 @@ def prefix_shared_fp8_decode(num_seqs: int = 128) -> Workload:
                  k_scale=0.05, v_scale=0.04)
 
 
+def long_prefill_bf16(num_seqs: int = 4, prompt: int = 4096) -> Workload:
+    """Steady-state prefill: 4 prompts of 4096 tokens from empty caches (each a single chunk, causal), 32 q / 8
+    kv heads, D 128, bf16 -- long enough that the kernel's fixed costs (launch, first tiles, tail) are small."""
+    return build("long_prefill_bf16", seed=SEED_BASE + 5, ctx_lens=[prompt] * num_seqs, q_lens=[prompt] * num_seqs,
+                 num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+
+
 NAMED = {
     "tiny_fp32_decode": tiny_fp32_decode,
     "llama3_8b_decode_bf16": llama3_8b_decode_bf16,
     "mixed_step_bf16": mixed_step_bf16,
     "long_ctx_70b_decode_bf16": long_ctx_70b_decode_bf16,
     "prefix_shared_fp8_decode": prefix_shared_fp8_decode,
+    "long_prefill_bf16": long_prefill_bf16,
 }
 
 

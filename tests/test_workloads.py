@@ -37,7 +37,8 @@ def _check_poison(w):
     assert np.array_equal(bad, ~cov)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32_decode", "llama3_8b_decode_bf16", "prefix_shared_fp8_decode"])
+@pytest.mark.parametrize("name", ["tiny_fp32_decode", "llama3_8b_decode_bf16", "prefix_shared_fp8_decode",
+                                  "long_prefill_bf16"])
 def test_named_workloads_are_valid(name):
     w = wl.NAMED[name]()
     _check_tables(w)
