@@ -70,6 +70,7 @@ class Step:
         self.slots = torch.empty(w.num_tokens, dtype=torch.int32, device=dev)
         self.out = torch.empty_like(self.q)
         self.max_len = int(w.seq_lens.max())
+        self.max_q = int(w.q_lens.max())
         if cascade:
             nb = pk.pa_decode_cascade_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                                       self.max_len, w.shared_prefix_blocks, 0)
@@ -91,12 +92,11 @@ class Step:
         torch.cuda.synchronize()
 
     def write(self, kc, vc):
+        """Slot mapping and KV write, one launch (the slot array is stored too)."""
         w, pk = self.w, self.pk
-        pk.pa_slot_mapping(self.bt, self.sl, self.qsl, w.num_tokens, w.block_size, out=self.slots)
-        if w.kv_dtype == "fp8":
-            pk.pa_reshape_and_cache_fp8(self.nk, self.nv, kc, vc, self.slots, w.k_scale, w.v_scale)
-        else:
-            pk.pa_reshape_and_cache(self.nk, self.nv, kc, vc, self.slots)
+        scales = dict(k_scale=w.k_scale, v_scale=w.v_scale) if w.kv_dtype == "fp8" else {}
+        pk.pa_write_kv(self.nk, self.nv, kc, vc, self.bt, self.sl, self.qsl, self.max_q, slot_mapping=self.slots,
+                       **scales)
 
     def attend(self, kc, vc):
         w, pk = self.w, self.pk
@@ -228,7 +228,7 @@ def bench_decode(args, result):
     alg_bytes = wl.decode_alg_bytes(w)
     _log("timing decode steps ...")
     ms, wall = time_steps(st, args.steps, args.warmup)
-    kt = kernel_times(st, args.steps, ["slot_mapping", "reshape_and_cache", "decode", "decode_merge"])
+    kt = kernel_times(st, args.steps, ["reshape_and_cache", "decode", "decode_merge"])
     dec_ms = kt["decode"][0]
     att_gbps = alg_bytes / (dec_ms * 1e-3) / 1e9
     traffic = read_traffic("decode_bf16_d128_llama3_8b_traffic", DECODE_SOURCES)

@@ -132,6 +132,32 @@ pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t
                                      pa_dtype_t src_dtype, float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_write_kv -- pa_slot_mapping and pa_reshape_and_cache in one launch
+ * ([B] tutorial 3, [A] §2-§3): for new row i of sequence s, slot =
+ * block_tables[s][p / block_size] * block_size + p % block_size with p =
+ * seq_lens[s] - q_len_s + i (-1 past the table), and the row's K/V (all kv
+ * heads) is copied to cache[slot / block_size][slot % block_size] when 0 <=
+ * slot < num_blocks * block_size.  Bit-identical to the two calls; the
+ * device slot array is not needed.  slot_mapping: optional device int32
+ * [num_tokens] output (NULL: not stored).  max_q_len: host bound on every
+ * q_len (rows past it are not written; checked under PA_VALIDATE=1).
+ * key/value strides, dtype and pools as pa_reshape_and_cache.
+ */
+pa_status_t pa_write_kv(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,
+                        void* key_cache, void* value_cache, int32_t* slot_mapping, const int32_t* block_tables,
+                        int32_t bt_stride, const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                        int32_t num_tokens, int32_t max_q_len, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks, pa_dtype_t dtype, void* stream);
+
+/* pa_write_kv into E4M3FN pools: the codes of pa_reshape_and_cache_fp8 ([B] tutorial 6). */
+pa_status_t pa_write_kv_fp8(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,
+                            uint8_t* key_cache, uint8_t* value_cache, int32_t* slot_mapping,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            pa_dtype_t src_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * pa_decode_workspace_bytes -- scratch pa_decode / pa_decode_fp8 need.
  * The blocks of all sequences, laid end to end, are cut into num_splits
  * equal shares per kv head (0 = automatic: about one wave per SIMD of the

@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
                                      ctypes.c_int),
             "pa_reshape_and_cache_fp8": ([P, P, i64, i64, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, f32, f32,
                                           P], ctypes.c_int),
+            "pa_write_kv": ([P, P, i64, i64, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int,
+                             P], ctypes.c_int),
+            "pa_write_kv_fp8": ([P, P, i64, i64, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                 ctypes.c_int, f32, f32, P], ctypes.c_int),
             "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
             "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32, P, sz,
                            P], ctypes.c_int),
@@ -192,6 +196,27 @@ def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k
         _dev(key, "key"), _dev(value, "value"), key.stride(0), value.stride(0), _dev(key_cache, "key_cache"),
         _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"), T, H, D, B, NB, _dtype_code(key),
         float(k_scale), float(v_scale), _stream()))
+
+
+def pa_write_kv(key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc, max_q_len: int,
+                slot_mapping=None, k_scale: float = None, v_scale: float = None):
+    """Slot mapping + KV write in one launch (fp8 pools when k_scale/v_scale are given); returns slot_mapping."""
+    lib = load()
+    T, H, D = key.shape
+    if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
+        raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
+    NB, B = key_cache.shape[0], key_cache.shape[1]
+    S = seq_lens.shape[0]
+    sm = None if slot_mapping is None else _dev(slot_mapping, "slot_mapping")
+    common = (_dev(key, "key"), _dev(value, "value"), key.stride(0), value.stride(0), _dev(key_cache, "key_cache"),
+              _dev(value_cache, "value_cache"), sm, _dev(block_tables, "block_tables"), block_tables.shape[1],
+              _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), S, T, max_q_len, H, D, B, NB)
+    if k_scale is None:
+        _check("pa_write_kv", lib.pa_write_kv(*common, _dtype_code(key_cache), _stream()))
+    else:
+        _check("pa_write_kv_fp8", lib.pa_write_kv_fp8(*common, _dtype_code(key), float(k_scale), float(v_scale),
+                                                      _stream()))
+    return slot_mapping
 
 
 def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_seq_len: int,

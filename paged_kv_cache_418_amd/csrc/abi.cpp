@@ -421,6 +421,83 @@ pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t
                     "reshape_and_cache_fp8 launch");
 }
 
+namespace {
+
+pa_status_t check_write_kv(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,
+                           const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                           int32_t bt_stride, const int32_t* seq_lens, const int32_t* query_start_loc,
+                           int32_t num_seqs, int32_t num_tokens, int32_t max_q_len, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks) {
+  if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0) return fail(PA_ERR_SHAPE, "negative count");
+  if (num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1 || bt_stride < 1)
+    return fail(PA_ERR_SHAPE, "non-positive num_kv_heads/head_dim/block_size/num_blocks/bt_stride");
+  if (key_tok_stride < (int64_t)num_kv_heads * head_dim || value_tok_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "token stride smaller than num_kv_heads * head_dim");
+  if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_SHAPE, "pool has more than 2^31 slots");
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (validate_enabled()) {
+    std::vector<int32_t> q;
+    if (!copy_to_host(q, query_start_loc, num_seqs + 1)) return fail(PA_ERR_HIP, "PA_VALIDATE: copy failed");
+    if (q[num_seqs] != num_tokens)
+      return fail(PA_ERR_SHAPE, "PA_VALIDATE: query_start_loc[num_seqs] = %d != num_tokens %d", q[num_seqs],
+                  num_tokens);
+    for (int s = 0; s < num_seqs; ++s)
+      if (q[s + 1] - q[s] > max_q_len)
+        return fail(PA_ERR_SHAPE, "PA_VALIDATE: sequence %d has q_len %d > max_q_len %d", s, q[s + 1] - q[s],
+                    max_q_len);
+    pa_status_t st = validate_tables(block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, INT32_MAX,
+                                     num_blocks, block_size);
+    if (st != PA_OK) return st;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status_t pa_write_kv(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,
+                        void* key_cache, void* value_cache, int32_t* slot_mapping, const int32_t* block_tables,
+                        int32_t bt_stride, const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                        int32_t num_tokens, int32_t max_q_len, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks, pa_dtype_t dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  pa_status_t st = check_write_kv(key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                                  bt_stride, seq_lens, query_start_loc, num_seqs, num_tokens, max_q_len, num_kv_heads,
+                                  head_dim, block_size, num_blocks);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return ok();
+  return hip_status(pa::launch_write_kv(key, value, key_tok_stride, value_tok_stride, key_cache, value_cache,
+                                        slot_mapping, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
+                                        num_tokens, max_q_len, num_kv_heads, head_dim, block_size, num_blocks,
+                                        dtype == PA_F32 ? pa::kF32 : pa::kBF16, 1.f, 1.f,
+                                        static_cast<hipStream_t>(stream)),
+                    "write_kv launch");
+}
+
+pa_status_t pa_write_kv_fp8(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,
+                            uint8_t* key_cache, uint8_t* value_cache, int32_t* slot_mapping,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            pa_dtype_t src_dtype, float k_scale, float v_scale, void* stream) {
+  if (src_dtype != PA_F32 && src_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "src_dtype must be PA_F32 or PA_BF16");
+  if ((num_kv_heads * head_dim) % 8) return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * head_dim must be a multiple of 8");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  pa_status_t st = check_write_kv(key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                                  bt_stride, seq_lens, query_start_loc, num_seqs, num_tokens, max_q_len, num_kv_heads,
+                                  head_dim, block_size, num_blocks);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return ok();
+  return hip_status(pa::launch_write_kv(key, value, key_tok_stride, value_tok_stride, key_cache, value_cache,
+                                        slot_mapping, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
+                                        num_tokens, max_q_len, num_kv_heads, head_dim, block_size, num_blocks,
+                                        src_dtype == PA_F32 ? pa::kFP8 + 1 : pa::kFP8, k_scale, v_scale,
+                                        static_cast<hipStream_t>(stream)),
+                    "write_kv_fp8 launch");
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_seq_len, int32_t num_splits) {
   if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_seq_len < 1 || num_splits < 0)

@@ -31,14 +31,19 @@ __global__ void __launch_bounds__(256) slot_mapping_kernel(int32_t* slots, const
   }
 }
 
-// One work-group per token; threads copy VEC-byte chunks of all kv heads.
+// Slot of new row i of a sequence with `cached` tokens before this step (-1 when its
+// position lies past the table).
+__device__ __forceinline__ int row_slot(const int32_t* bt, int bt_stride, int cached, int i, int block_size) {
+  const int pos = cached + i;
+  const int logical = pos / block_size;
+  return (pos >= 0 && logical < bt_stride) ? bt[logical] * block_size + (pos - logical * block_size) : -1;
+}
+
+// The work-group's threads copy token t's K and V rows (all kv heads) in VecT chunks.
 template <typename VecT>
-__global__ void __launch_bounds__(256) reshape_kernel(const uint8_t* key, const uint8_t* value, int64_t key_stride_b,
-                                                      int64_t value_stride_b, uint8_t* key_cache, uint8_t* value_cache,
-                                                      const int32_t* slots, int row_bytes, int num_slots) {
-  const int t = blockIdx.x;
-  const int slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
+__device__ __forceinline__ void copy_token(const uint8_t* key, const uint8_t* value, int64_t key_stride_b,
+                                           int64_t value_stride_b, uint8_t* key_cache, uint8_t* value_cache, int t,
+                                           int slot, int row_bytes) {
   const int n = row_bytes / (int)sizeof(VecT);
   const VecT* ks = reinterpret_cast<const VecT*>(key + (int64_t)t * key_stride_b);
   const VecT* vs = reinterpret_cast<const VecT*>(value + (int64_t)t * value_stride_b);
@@ -50,15 +55,11 @@ __global__ void __launch_bounds__(256) reshape_kernel(const uint8_t* key, const 
   }
 }
 
-// fp8: each thread quantises 8 consecutive elements (one 8-byte store).
+// fp8: each thread quantises 8 consecutive elements of token t (one 8-byte store per pool).
 template <bool SRC_F32>
-__global__ void __launch_bounds__(256) reshape_fp8_kernel(const void* key, const void* value, int64_t key_stride,
-                                                          int64_t value_stride, uint8_t* key_cache,
-                                                          uint8_t* value_cache, const int32_t* slots, int row_elems,
-                                                          int num_slots, float k_scale, float v_scale) {
-  const int t = blockIdx.x;
-  const int slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
+__device__ __forceinline__ void quantize_token(const void* key, const void* value, int64_t key_stride,
+                                               int64_t value_stride, uint8_t* key_cache, uint8_t* value_cache, int t,
+                                               int slot, int row_elems, float k_scale, float v_scale) {
   for (int c = threadIdx.x; c < row_elems / 8; c += blockDim.x) {
     float xk[8], xv[8];
     if constexpr (SRC_F32) {
@@ -86,6 +87,62 @@ __global__ void __launch_bounds__(256) reshape_fp8_kernel(const void* key, const
     }
     *reinterpret_cast<u32x2*>(key_cache + (int64_t)slot * row_elems + c * 8) = u32x2{kw[0], kw[1]};
     *reinterpret_cast<u32x2*>(value_cache + (int64_t)slot * row_elems + c * 8) = u32x2{vw[0], vw[1]};
+  }
+}
+
+// One work-group per token; threads copy VEC-byte chunks of all kv heads.
+template <typename VecT>
+__global__ void __launch_bounds__(256) reshape_kernel(const uint8_t* key, const uint8_t* value, int64_t key_stride_b,
+                                                      int64_t value_stride_b, uint8_t* key_cache, uint8_t* value_cache,
+                                                      const int32_t* slots, int row_bytes, int num_slots) {
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  copy_token<VecT>(key, value, key_stride_b, value_stride_b, key_cache, value_cache, t, slot, row_bytes);
+}
+
+template <bool SRC_F32>
+__global__ void __launch_bounds__(256) reshape_fp8_kernel(const void* key, const void* value, int64_t key_stride,
+                                                          int64_t value_stride, uint8_t* key_cache,
+                                                          uint8_t* value_cache, const int32_t* slots, int row_elems,
+                                                          int num_slots, float k_scale, float v_scale) {
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  quantize_token<SRC_F32>(key, value, key_stride, value_stride, key_cache, value_cache, t, slot, row_elems, k_scale,
+                          v_scale);
+}
+
+// Slot mapping and KV write in one launch: grid (num_seqs, ceil(max_q_len / kWriteTokens));
+// work-group (s, g) takes new rows g*kWriteTokens .. of sequence s, computes each row's slot
+// as slot_mapping_kernel does (stored when slots_out is given), and writes the row as the
+// reshape kernels do (skipped for slots outside the pool).
+constexpr int kWriteTokens = 4;
+
+template <typename VecT, int KIND>  // KIND 0: copy; 1: fp8 from bf16; 2: fp8 from fp32
+__global__ void __launch_bounds__(128) write_kv_kernel(const void* key, const void* value, int64_t key_stride,
+                                                       int64_t value_stride, uint8_t* key_cache, uint8_t* value_cache,
+                                                       int32_t* slots_out, const int32_t* block_tables, int bt_stride,
+                                                       const int32_t* seq_lens, const int32_t* qsl, int num_tokens,
+                                                       int block_size, int num_slots, int row, float k_scale,
+                                                       float v_scale) {
+  const int s = blockIdx.x;
+  const int q0 = qsl[s], q_len = qsl[s + 1] - q0;
+  const int cached = seq_lens[s] - q_len;
+  const int* bt = block_tables + (size_t)s * bt_stride;
+  const int i1 = min(q_len, (int)(blockIdx.y + 1) * kWriteTokens);
+  for (int i = blockIdx.y * kWriteTokens; i < i1; ++i) {
+    const int t = q0 + i;
+    if (t < 0 || t >= num_tokens) continue;
+    const int slot = row_slot(bt, bt_stride, cached, i, block_size);
+    if (slots_out && threadIdx.x == 0) slots_out[t] = slot;
+    if (slot < 0 || slot >= num_slots) continue;
+    if constexpr (KIND == 0)  // key_stride / value_stride in bytes, row in bytes
+      copy_token<VecT>(reinterpret_cast<const uint8_t*>(key), reinterpret_cast<const uint8_t*>(value), key_stride,
+                       value_stride, key_cache, value_cache, t, slot, row);
+    else  // strides in elements, row in elements
+      quantize_token<KIND == 2>(key, value, key_stride, value_stride, key_cache, value_cache, t, slot, row, k_scale,
+                                v_scale);
   }
 }
 
@@ -143,6 +200,49 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int6
   else
     hipLaunchKernelGGL(reshape_fp8_kernel<false>, dim3(num_tokens), dim3(128), 0, stream, key, value, key_stride,
                        value_stride, key_cache, value_cache, slots, row_elems, num_slots, k_scale, v_scale);
+  timing_mark(kKReshape, false, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv(const void* key, const void* value, int64_t key_stride, int64_t value_stride,
+                           void* key_cache, void* value_cache, int32_t* slots_out, const int32_t* block_tables,
+                           int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
+                           int max_q_len, int num_kv_heads, int head_dim, int block_size, int num_blocks, int kind,
+                           float k_scale, float v_scale, hipStream_t stream) {
+  const dim3 grid(num_seqs, (max_q_len + kWriteTokens - 1) / kWriteTokens);
+  const int num_slots = num_blocks * block_size;
+  auto* kc8 = reinterpret_cast<uint8_t*>(key_cache);
+  auto* vc8 = reinterpret_cast<uint8_t*>(value_cache);
+  const int row_elems = num_kv_heads * head_dim;
+  timing_mark(kKReshape, true, stream);
+  if (kind == kFP8 + 0 || kind == kFP8 + 1) {  // fp8 pools: kind kFP8 (bf16 source) or kFP8 + 1 (fp32 source)
+    if (kind == kFP8)
+      hipLaunchKernelGGL((write_kv_kernel<uint32_t, 1>), grid, dim3(128), 0, stream, key, value, key_stride,
+                         value_stride, kc8, vc8, slots_out, block_tables, bt_stride, seq_lens, qsl, num_tokens,
+                         block_size, num_slots, row_elems, k_scale, v_scale);
+    else
+      hipLaunchKernelGGL((write_kv_kernel<uint32_t, 2>), grid, dim3(128), 0, stream, key, value, key_stride,
+                         value_stride, kc8, vc8, slots_out, block_tables, bt_stride, seq_lens, qsl, num_tokens,
+                         block_size, num_slots, row_elems, k_scale, v_scale);
+  } else {
+    const int elem = kind == kF32 ? 4 : 2;
+    const int row_bytes = row_elems * elem;
+    const int64_t ksb = key_stride * elem, vsb = value_stride * elem;
+    const uintptr_t align = (uintptr_t)key | (uintptr_t)value | (uintptr_t)key_cache | (uintptr_t)value_cache |
+                            (uintptr_t)ksb | (uintptr_t)vsb | (uintptr_t)row_bytes;
+    if ((align & 15u) == 0)
+      hipLaunchKernelGGL((write_kv_kernel<u32x4, 0>), grid, dim3(128), 0, stream, key, value, ksb, vsb, kc8, vc8,
+                         slots_out, block_tables, bt_stride, seq_lens, qsl, num_tokens, block_size, num_slots,
+                         row_bytes, 1.f, 1.f);
+    else if ((align & 3u) == 0)
+      hipLaunchKernelGGL((write_kv_kernel<uint32_t, 0>), grid, dim3(128), 0, stream, key, value, ksb, vsb, kc8, vc8,
+                         slots_out, block_tables, bt_stride, seq_lens, qsl, num_tokens, block_size, num_slots,
+                         row_bytes, 1.f, 1.f);
+    else
+      hipLaunchKernelGGL((write_kv_kernel<uint16_t, 0>), grid, dim3(128), 0, stream, key, value, ksb, vsb, kc8, vc8,
+                         slots_out, block_tables, bt_stride, seq_lens, qsl, num_tokens, block_size, num_slots,
+                         row_bytes, 1.f, 1.f);
+  }
   timing_mark(kKReshape, false, stream);
   return hipGetLastError();
 }

@@ -142,6 +142,15 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int6
                                         int block_size, int num_blocks, int src_f32, float k_scale,
                                         float v_scale, hipStream_t stream);
 
+// Slot mapping and KV write in one launch.  kind: kF32 / kBF16 (plain copy, strides in
+// elements of that type), kFP8 (E4M3 pools from a bf16 source) or kFP8 + 1 (from fp32);
+// slots_out optional.  Work-groups: num_seqs x ceil(max_q_len / 4).
+hipError_t launch_write_kv(const void* key, const void* value, int64_t key_stride, int64_t value_stride,
+                           void* key_cache, void* value_cache, int32_t* slots_out, const int32_t* block_tables,
+                           int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
+                           int max_q_len, int num_kv_heads, int head_dim, int block_size, int num_blocks, int kind,
+                           float k_scale, float v_scale, hipStream_t stream);
+
 // kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel)
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
 

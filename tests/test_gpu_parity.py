@@ -68,6 +68,48 @@ def test_reshape_and_cache_strided_source_and_skipped_slots():
     assert torch.equal(dv.cpu().view(torch.int16), vc.view(torch.int16))
 
 
+@pytest.mark.parametrize("kinds", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8"), ("f32", "fp8")])
+@pytest.mark.parametrize("seed", [121, 122])
+def test_write_kv_fused_bit_exact(kinds, seed):
+    """pa_write_kv(_fp8) (slot mapping and KV write in one launch) equals the oracle's slot mapping and write, bit
+    for bit: ragged chunks and decode rows, a max_q_len bound above every q_len, with and without the slot output."""
+    w = wl.random_case(seed, num_seqs=9, ctx_range=(1, 300), chunk_range=(1, 70), q_dtype=kinds[0],
+                       kv_dtype=kinds[1], num_kv_heads=4, num_q_heads=8, head_dim=128, k_scale=0.05, v_scale=0.04)
+    say("write_kv fused", kinds, seed, list(w.q_lens))
+    d = DevWorkload(w)
+    scales = dict(k_scale=w.k_scale, v_scale=w.v_scale) if w.kv_dtype == "fp8" else {}
+    slots = torch.full((w.num_tokens,), -7, dtype=torch.int32, device="cuda")
+    pk.pa_write_kv(d.new_k, d.new_v, d.k_cache, d.v_cache, d.block_tables, d.seq_lens, d.qsl,
+                   int(w.q_lens.max()) + 5, slot_mapping=slots, **scales)
+    kc, vc = oracle.written_pools(w)
+    assert np.array_equal(slots.cpu().numpy(), oracle.slot_mapping(w.block_tables, w.seq_lens, w.query_start_loc))
+    assert torch.equal(d.k_cache.cpu().view(torch.uint8), kc.view(torch.uint8))
+    assert torch.equal(d.v_cache.cpu().view(torch.uint8), vc.view(torch.uint8))
+    # no slot output, same pools
+    d2 = DevWorkload(w)
+    pk.pa_write_kv(d2.new_k, d2.new_v, d2.k_cache, d2.v_cache, d2.block_tables, d2.seq_lens, d2.qsl,
+                   int(w.q_lens.max()), **scales)
+    assert torch.equal(d2.k_cache.cpu().view(torch.uint8), kc.view(torch.uint8))
+    assert torch.equal(d2.v_cache.cpu().view(torch.uint8), vc.view(torch.uint8))
+
+
+def test_write_kv_fused_decode_batch_and_empty():
+    w = wl.llama3_8b_decode_bf16()
+    say("write_kv fused llama3_8b")
+    d = DevWorkload(w)
+    slots = pk.pa_write_kv(d.new_k, d.new_v, d.k_cache, d.v_cache, d.block_tables, d.seq_lens, d.qsl, 1,
+                           slot_mapping=torch.empty(w.num_tokens, dtype=torch.int32, device="cuda"))
+    kc, vc = oracle.written_pools(w)
+    assert np.array_equal(slots.cpu().numpy(), oracle.slot_mapping(w.block_tables, w.seq_lens, w.query_start_loc))
+    assert torch.equal(d.k_cache.cpu().view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(d.v_cache.cpu().view(torch.int16), vc.view(torch.int16))
+    # zero tokens: nothing written, no launch
+    before = d.k_cache.clone()
+    pk.pa_write_kv(d.new_k[:0], d.new_v[:0], d.k_cache, d.v_cache, d.block_tables[:0], d.seq_lens[:0], d.qsl[:1], 0)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), d.k_cache.view(torch.int16))  # bit patterns: the pool holds NaN
+
+
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_fp8_write_exhaustive_bf16_patterns(src):
     """Every bf16 bit pattern (as bf16 or its exact fp32) through the fp8 write, both scales."""
