@@ -398,6 +398,28 @@ def bench_window(args, result):
     torch.cuda.empty_cache()
 
 
+def bench_long(args, result):
+    """The 70B-layer long-context decode (8 sequences of 32k-128k tokens, 64 q / 8 kv heads): one pool copy is
+    already ten times the 256 MB MALL."""
+    from paged_kv_cache_418_amd import workloads as wl
+    _log("generating long_ctx_70b_decode_bf16 ...")
+    w = wl.long_ctx_70b_decode_bf16()
+    st = Step(w, copies=1)
+    steps = max(5, args.steps // 5)
+    ms, _ = time_steps(st, steps, 2)
+    kt = kernel_times(st, steps, ["decode", "decode_merge"])
+    kv = wl.decode_kv_bytes(w)
+    alg = wl.decode_alg_bytes(w)
+    dec_ms = kt["decode"][0]
+    result["long_context"] = {"workload": "long_ctx_70b_decode_bf16", "kv_bytes": kv, "ms_per_step": round(ms, 4),
+                              "step_gbps": round(kv / (ms * 1e-3) / 1e9, 1),
+                              "decode_kernel_ms": round(dec_ms, 4), "merge_kernel_ms": round(kt["decode_merge"][0], 4),
+                              "kernel_gbps": round(alg / (dec_ms * 1e-3) / 1e9, 1),
+                              "kernel_frac_hbm": round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del st, w
+    torch.cuda.empty_cache()
+
+
 def bench_copy(args, result):
     """A plain device-to-device copy of 1 GiB: the known-size reference for the HBM byte counters."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -413,7 +435,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", choices=["", "decode", "mixed", "cascade", "window", "copy"])
+    ap.add_argument("--only", default="", choices=["", "decode", "mixed", "cascade", "window", "long", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library's path runs on a single GPU and has no multi-GPU form; "
@@ -433,6 +455,8 @@ def main():
             bench_cascade(args, result)
         if args.only in ("", "window"):
             bench_window(args, result)
+        if args.only in ("", "long"):
+            bench_long(args, result)
     print(json.dumps(result), flush=True)
 
 

@@ -244,3 +244,23 @@ def test_prefill_plan_is_fast_on_long_prompts(lib):
         got = lib.pa_prefill_varlen_workspace_bytes(qsl.ctypes.data, sl.ctypes.data, n, 32, 8, 128)
         assert time.perf_counter() - t0 < 0.5
         assert got == 0
+
+
+def test_empty_batches_return_ok_without_touching_memory(lib):
+    """num_seqs = 0 (or no tokens) is a valid call on every entry point: it returns PA_OK before any device access
+    (the pointers here are not device memory)."""
+    q0, s0 = _host_i32([0]), _host_i32([0])
+    dec = [FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 0, 32, 8, 128, 16, 1000, 3072, 0.088]
+    assert lib.pa_decode(*dec, b.PA_BF16, 0, None, 0, None) == 0
+    assert lib.pa_decode_fp8(*dec, b.PA_BF16, 0.05, 0.04, 0, None, 0, None) == 0
+    assert lib.pa_decode_window(*dec, b.PA_BF16, 64, 0, None, 0, None) == 0
+    assert lib.pa_decode_local(*dec, b.PA_BF16, 64, 0, None, 0, None) == 0
+    pre = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, ctypes.addressof(s0), ctypes.addressof(q0), 0, 0, 32, 8,
+           128, 16, 1000, 0.088]
+    assert lib.pa_prefill_varlen(*pre, b.PA_BF16, None, 0, None) == 0
+    assert lib.pa_prefill_varlen_window(*pre, b.PA_BF16, 64, None, 0, None) == 0
+    assert lib.pa_prefill_varlen_local(*pre, b.PA_BF16, 64, None, 0, None) == 0
+    assert lib.pa_slot_mapping(FAKE, FAKE, 64, FAKE, FAKE, 0, 0, 16, None) == 0
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, 1024, 1024, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, b.PA_BF16, None) == 0
+    assert lib.pa_write_kv(FAKE, FAKE, 1024, 1024, FAKE, FAKE, None, FAKE, 64, FAKE, FAKE, 0, 0, 0, 8, 128, 16, 100,
+                           b.PA_BF16, None) == 0

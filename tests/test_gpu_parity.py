@@ -498,6 +498,19 @@ def test_decode_window_random(heads, window, num_splits):
     _window_case(w, window, lambda d: d.decode_window(window, num_splits), TOL["bf16"])
 
 
+@pytest.mark.parametrize("mask", [("window", 4096), ("local", 8192)])
+def test_decode_window_and_local_long_context_70b_full(mask):
+    """The 70B long-context layer (8 sequences of 32k-128k tokens, G = 8): a 4096-token window and 8192-token local
+    chunks, whose first visible block lies thousands of table columns in; every row against the oracle."""
+    kind, n = mask
+    w = wl.long_ctx_70b_decode_bf16()
+    say("decode", kind, n, "long-context 70b")
+    if kind == "window":
+        _window_case(w, n, lambda d: d.decode_window(n), TOL["bf16"])
+    else:
+        _local_case(w, n, lambda d: d.decode_local(n), TOL["bf16"])
+
+
 def test_decode_window_llama3_8b_full():
     """The 8B decode layer (64 sequences of 1000-3000 tokens) with a 1024-token window: agrees with the oracle on
     every row and with the full-attention entry point when the window covers every sequence."""
