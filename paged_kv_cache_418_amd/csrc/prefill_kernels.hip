@@ -106,12 +106,16 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
 
   // ---- work item
-  const uint64_t item = p.items[blockIdx.x];
+  // grid (kv heads, items): the dispatcher walks x fastest, so every kv head's item i
+  // starts before any head's item i+1 -- with items listed longest first, the work-groups
+  // start in longest-first order across the heads, and the short items fill the tail
+  const int item_idx = blockIdx.y;
+  const uint64_t item = p.items[item_idx];
   const int s = (int)(item & 0x7FFFu);
   const bool whole = (item >> 15) & 1u;
   const int rt = (int)((item >> 16) & 0xFFFFu);
   const int kt0 = (int)((item >> 32) & 0xFFFFu), kt1 = (int)(item >> 48);
-  const int kvh = blockIdx.y;
+  const int kvh = blockIdx.x;
   const int G = p.group;
   const int P = p.tile_positions;         // positions per row tile (rows = P * G <= 256)
   const int q0 = p.qsl[s];
@@ -625,7 +629,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // partial results of a split row tile: slot (launch base + item) x kv head x row
-  const size_t slot_row0 = ((size_t)(p.item_base + blockIdx.x) * p.num_kv_heads + kvh) * kPrefillRows + 32 * wave;
+  const size_t slot_row0 = ((size_t)(p.item_base + item_idx) * p.num_kv_heads + kvh) * kPrefillRows + 32 * wave;
   constexpr int kRowsPerStore = 64 / Sh::kChunks;
   const int sc_chunk = lane % Sh::kChunks;
 #pragma unroll
@@ -775,7 +779,7 @@ size_t prefill_lds_bytes(int head_dim) {
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.n_items, p.num_kv_heads);
+  const dim3 grid(p.num_kv_heads, p.n_items);
   const size_t lds = prefill_lds_bytes(head_dim);
   timing_mark(kKPrefill, true, stream);
   auto launch = [&](auto kernel, int threads) {
