@@ -83,6 +83,13 @@ typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype_t;
 /* ABI version (PA_ABI_VERSION of the built library). */
 int pa_abi_version(void);
 
+/*
+ * Metadata validation for every later call on any thread: on = 1 checks the
+ * device metadata on the host before each call (the checks PA_VALIDATE=1
+ * enables), 0 trusts it, -1 returns to the PA_VALIDATE environment setting.
+ */
+pa_status_t pa_set_validate(int on);
+
 /* Static text for a status code. */
 const char* pa_status_string(pa_status_t status);
 

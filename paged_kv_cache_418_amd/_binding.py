@@ -107,6 +107,7 @@ def load() -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
             "pa_pool_free_queue": ([P, P, i32], i32),
             "pa_probe_mfma_peak": ([P, i32, i32, P], ctypes.c_int),
+            "pa_set_validate": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_reset": ([], ctypes.c_int),
             "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
@@ -415,6 +416,12 @@ def pa_prefill_varlen_local(query, key_cache, value_cache, block_tables, seq_len
         sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), chunk_size,
         None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
+
+
+def set_validate(on: int) -> None:
+    """1: check device metadata on the host before every call (PA_VALIDATE's checks); 0: trust it; -1: follow the
+    PA_VALIDATE environment variable."""
+    _check("pa_set_validate", load().pa_set_validate(int(on)))
 
 
 def timing_enable(on: bool = True) -> None:

@@ -57,7 +57,12 @@ pa_status_t hip_status(hipError_t e, const char* where) {
   return fail(PA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// -1: follow PA_VALIDATE; 0 / 1: set by pa_set_validate
+std::atomic<int> g_validate_override{-1};
+
 bool validate_enabled() {
+  const int o = g_validate_override.load(std::memory_order_relaxed);
+  if (o >= 0) return o != 0;
   static const bool on = [] {
     const char* v = std::getenv("PA_VALIDATE");
     return v && v[0] && std::strcmp(v, "0") != 0;
@@ -1183,6 +1188,11 @@ void timing_mark(int kernel, bool begin, hipStream_t stream) {
 }  // namespace pa
 
 extern "C" {
+
+pa_status_t pa_set_validate(int on) {
+  g_validate_override.store(on < 0 ? -1 : (on != 0 ? 1 : 0), std::memory_order_relaxed);
+  return ok();
+}
 
 pa_status_t pa_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream) {
   if (!out) return fail(PA_ERR_NULL, "pa_probe_mfma_peak: out is NULL");
