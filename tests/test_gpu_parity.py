@@ -627,3 +627,26 @@ def test_local_with_one_chunk_is_full_attention():
     c_, d_ = dw.decode_local(int(dw.w.seq_lens.max())), dw.decode()
     torch.cuda.synchronize()
     assert torch.equal(a, b_) and torch.equal(c_, d_)
+
+
+# ------------------------------------------------------------------ determinism (LDS hazards, races)
+
+@pytest.mark.parametrize("variant", ["bf16", "fp8", "window", "local", "decode"])
+def test_repeat_runs_are_bit_identical(variant):
+    """Ten runs of the same call give the same bits: a missing wait on an LDS ring slot, a read of a register
+    before its load landed, or a race between work-groups would show as run-to-run differences.  The mixed step
+    (decode rows + split long chunks) exercises the decode, prefill and both merge kernels."""
+    w = wl.mixed_step_bf16(kv_dtype="fp8" if variant == "fp8" else "bf16")
+    say("repeat", variant)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    run = {"bf16": d.prefill, "fp8": d.prefill, "window": lambda: d.prefill_window(700),
+           "local": lambda: d.prefill_local(640), "decode": None}[variant]
+    if variant == "decode":
+        dd = DevWorkload(wl.llama3_8b_decode_bf16())
+        dd.write_new_tokens()
+        run = dd.decode
+    first = run().clone()
+    for _ in range(9):
+        again = run()
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
