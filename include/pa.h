@@ -146,8 +146,9 @@ pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t
  * heads) is copied to cache[slot / block_size][slot % block_size] when 0 <=
  * slot < num_blocks * block_size.  Bit-identical to the two calls; the
  * device slot array is not needed.  slot_mapping: optional device int32
- * [num_tokens] output (NULL: not stored).  max_q_len: host bound on every
- * q_len (rows past it are not written; checked under PA_VALIDATE=1).
+ * [num_tokens] output (NULL: not stored).  max_q_len: a host estimate of the
+ * longest q_len that sizes the launch (a sequence with more rows still gets
+ * all of them written, by fewer work-groups; 0 writes nothing).
  * key/value strides, dtype and pools as pa_reshape_and_cache.
  */
 pa_status_t pa_write_kv(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,

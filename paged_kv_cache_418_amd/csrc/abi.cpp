@@ -448,10 +448,6 @@ pa_status_t check_write_kv(const void* key, const void* value, int64_t key_tok_s
     if (q[num_seqs] != num_tokens)
       return fail(PA_ERR_SHAPE, "PA_VALIDATE: query_start_loc[num_seqs] = %d != num_tokens %d", q[num_seqs],
                   num_tokens);
-    for (int s = 0; s < num_seqs; ++s)
-      if (q[s + 1] - q[s] > max_q_len)
-        return fail(PA_ERR_SHAPE, "PA_VALIDATE: sequence %d has q_len %d > max_q_len %d", s, q[s + 1] - q[s],
-                    max_q_len);
     pa_status_t st = validate_tables(block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, INT32_MAX,
                                      num_blocks, block_size);
     if (st != PA_OK) return st;

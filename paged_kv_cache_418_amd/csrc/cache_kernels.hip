@@ -113,8 +113,9 @@ __global__ void __launch_bounds__(256) reshape_fp8_kernel(const void* key, const
                           v_scale);
 }
 
-// Slot mapping and KV write in one launch: grid (num_seqs, ceil(max_q_len / kWriteTokens));
-// work-group (s, g) takes new rows g*kWriteTokens .. of sequence s, computes each row's slot
+// Slot mapping and KV write in one launch: grid (num_seqs, min(ceil(max_q_len / kWriteTokens),
+// 65535)); work-group (s, g) takes the groups of kWriteTokens new rows g, g + gridDim.y, ... of
+// sequence s, computes each row's slot
 // as slot_mapping_kernel does (stored when slots_out is given), and writes the row as the
 // reshape kernels do (skipped for slots outside the pool).
 constexpr int kWriteTokens = 4;
@@ -130,19 +131,22 @@ __global__ void __launch_bounds__(128) write_kv_kernel(const void* key, const vo
   const int q0 = qsl[s], q_len = qsl[s + 1] - q0;
   const int cached = seq_lens[s] - q_len;
   const int* bt = block_tables + (size_t)s * bt_stride;
-  const int i1 = min(q_len, (int)(blockIdx.y + 1) * kWriteTokens);
-  for (int i = blockIdx.y * kWriteTokens; i < i1; ++i) {
-    const int t = q0 + i;
-    if (t < 0 || t >= num_tokens) continue;
-    const int slot = row_slot(bt, bt_stride, cached, i, block_size);
-    if (slots_out && threadIdx.x == 0) slots_out[t] = slot;
-    if (slot < 0 || slot >= num_slots) continue;
-    if constexpr (KIND == 0)  // key_stride / value_stride in bytes, row in bytes
-      copy_token<VecT>(reinterpret_cast<const uint8_t*>(key), reinterpret_cast<const uint8_t*>(value), key_stride,
-                       value_stride, key_cache, value_cache, t, slot, row);
-    else  // strides in elements, row in elements
-      quantize_token<KIND == 2>(key, value, key_stride, value_stride, key_cache, value_cache, t, slot, row, k_scale,
-                                v_scale);
+  // row groups blockIdx.y, blockIdx.y + gridDim.y, ... of kWriteTokens rows (the grid's y extent is capped)
+  for (int g0 = blockIdx.y * kWriteTokens; g0 < q_len; g0 += gridDim.y * kWriteTokens) {
+    const int i1 = min(q_len, g0 + kWriteTokens);
+    for (int i = g0; i < i1; ++i) {
+      const int t = q0 + i;
+      if (t < 0 || t >= num_tokens) continue;
+      const int slot = row_slot(bt, bt_stride, cached, i, block_size);
+      if (slots_out && threadIdx.x == 0) slots_out[t] = slot;
+      if (slot < 0 || slot >= num_slots) continue;
+      if constexpr (KIND == 0)  // key_stride / value_stride in bytes, row in bytes
+        copy_token<VecT>(reinterpret_cast<const uint8_t*>(key), reinterpret_cast<const uint8_t*>(value), key_stride,
+                         value_stride, key_cache, value_cache, t, slot, row);
+      else  // strides in elements, row in elements
+        quantize_token<KIND == 2>(key, value, key_stride, value_stride, key_cache, value_cache, t, slot, row, k_scale,
+                                  v_scale);
+    }
   }
 }
 
@@ -209,7 +213,7 @@ hipError_t launch_write_kv(const void* key, const void* value, int64_t key_strid
                            int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
                            int max_q_len, int num_kv_heads, int head_dim, int block_size, int num_blocks, int kind,
                            float k_scale, float v_scale, hipStream_t stream) {
-  const dim3 grid(num_seqs, (max_q_len + kWriteTokens - 1) / kWriteTokens);
+  const dim3 grid(num_seqs, std::min((max_q_len + kWriteTokens - 1) / kWriteTokens, 65535));
   const int num_slots = num_blocks * block_size;
   auto* kc8 = reinterpret_cast<uint8_t*>(key_cache);
   auto* vc8 = reinterpret_cast<uint8_t*>(value_cache);

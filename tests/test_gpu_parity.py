@@ -85,12 +85,13 @@ def test_write_kv_fused_bit_exact(kinds, seed):
     assert np.array_equal(slots.cpu().numpy(), oracle.slot_mapping(w.block_tables, w.seq_lens, w.query_start_loc))
     assert torch.equal(d.k_cache.cpu().view(torch.uint8), kc.view(torch.uint8))
     assert torch.equal(d.v_cache.cpu().view(torch.uint8), vc.view(torch.uint8))
-    # no slot output, same pools
-    d2 = DevWorkload(w)
-    pk.pa_write_kv(d2.new_k, d2.new_v, d2.k_cache, d2.v_cache, d2.block_tables, d2.seq_lens, d2.qsl,
-                   int(w.q_lens.max()), **scales)
-    assert torch.equal(d2.k_cache.cpu().view(torch.uint8), kc.view(torch.uint8))
-    assert torch.equal(d2.v_cache.cpu().view(torch.uint8), vc.view(torch.uint8))
+    # no slot output, same pools; and a launch sized for q_len 1 still writes every row of the chunks
+    for bound in (int(w.q_lens.max()), 1):
+        d2 = DevWorkload(w)
+        pk.pa_write_kv(d2.new_k, d2.new_v, d2.k_cache, d2.v_cache, d2.block_tables, d2.seq_lens, d2.qsl, bound,
+                       **scales)
+        assert torch.equal(d2.k_cache.cpu().view(torch.uint8), kc.view(torch.uint8))
+        assert torch.equal(d2.v_cache.cpu().view(torch.uint8), vc.view(torch.uint8))
 
 
 def test_write_kv_fused_decode_batch_and_empty():
