@@ -705,7 +705,8 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
   }
 }
 
-// fp8 staging: one work-group of 256 threads per (sequence, block).  Sequence s's
+// fp8 staging: one work-group of 256 threads per (sequence, block) -- blocks past the grid's
+// capped y extent (65535) go to work-group y, y + gridDim.y, ....  Sequence s's
 // first staging block is the sum of the block counts of the sequences before it that
 // have q_len > 1 (a block-wide sum over them; the batch's sequence count is small next
 // to the blocks moved).  Each thread turns 16 codes into 16 bf16 values per step.
@@ -714,13 +715,11 @@ __global__ void __launch_bounds__(256) stage_fp8_kernel(const uint8_t* key_cache
                                                          const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
                                                          int row_bytes, int num_blocks, uint16_t* stage_k,
                                                          uint16_t* stage_v, int32_t* stage_tables) {
-  constexpr int kBlocksPerGroup = 1;
   __shared__ int red[256];
   const int s = blockIdx.x;
   if (qsl[s + 1] - qsl[s] <= 1) return;
   const int nb = (seq_lens[s] + 15) >> 4;
-  const int j0 = blockIdx.y * kBlocksPerGroup;
-  if (j0 >= nb) return;
+  if ((int)blockIdx.y >= nb) return;
   int acc = 0;
   for (int t = threadIdx.x; t < s; t += 256) acc += qsl[t + 1] - qsl[t] > 1 ? (seq_lens[t] + 15) >> 4 : 0;
   red[threadIdx.x] = acc;
@@ -730,9 +729,8 @@ __global__ void __launch_bounds__(256) stage_fp8_kernel(const uint8_t* key_cache
     __syncthreads();
   }
   const int base = red[0];
-  const int j1 = min(nb, j0 + kBlocksPerGroup);
   const int block_bytes = 16 * row_bytes;  // codes per block (one byte each)
-  for (int j = j0; j < j1; ++j) {
+  for (int j = blockIdx.y; j < nb; j += gridDim.y) {  // the grid's y extent is capped
     const int phys = min(max(block_tables[(size_t)s * bt_stride + j], 0), num_blocks - 1);
     const int dst = base + j;
     if (threadIdx.x == 0) stage_tables[(size_t)s * bt_stride + j] = dst;
@@ -766,7 +764,7 @@ hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache
                             int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int max_blocks,
                             int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k, uint16_t* stage_v,
                             int32_t* stage_tables, hipStream_t stream) {
-  const dim3 grid(num_seqs, max_blocks);
+  const dim3 grid(num_seqs, std::min(max_blocks, 65535));
   timing_mark(kKStageFp8, true, stream);
   hipLaunchKernelGGL(stage_fp8_kernel, grid, dim3(256), 0, stream, key_cache, value_cache, block_tables, bt_stride,
                      seq_lens, qsl, num_seqs, num_kv_heads * head_dim, num_blocks, stage_k, stage_v, stage_tables);
