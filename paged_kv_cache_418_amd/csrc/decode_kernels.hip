@@ -629,7 +629,7 @@ template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
   constexpr int PER_LANE = D / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.x * 4 + wave, s = blockIdx.y;
+  const int h = blockIdx.y * 4 + wave, s = blockIdx.x;  // sequences on x: no 65535 limit on the batch
   if (h >= p.num_q_heads) return;
   const bool own = decode_blocks(p, s) > 0;  // the sequence has pieces of its own
   if (!own && p.prefix_shares == 0) return;
@@ -692,7 +692,7 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (p.n_splits <= 1 && !p.force_partial) || p.num_seqs == 0) return e;
   timing_mark(kKDecodeMerge, true, stream);
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((p.num_q_heads + 3) / 4, p.num_seqs), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.num_seqs, (p.num_q_heads + 3) / 4), dim3(256), 0, stream, p);
   timing_mark(kKDecodeMerge, false, stream);
   return hipGetLastError();
 }
