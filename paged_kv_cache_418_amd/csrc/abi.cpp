@@ -132,6 +132,13 @@ int decode_waves_per_simd() {
 // Shares the decode work of each kv head is cut into: num_splits if positive,
 // else enough waves to give every SIMD of the device decode_waves_per_simd()
 // of them; never more than the blocks there can be.
+// Blocks' worth of time a decode piece costs to start (PA_DECODE_PIECE_COST): the share
+// planner counts it for every sequence, so shares that start several pieces hold fewer blocks.
+int decode_piece_cost() {
+  static const int c = env_int("PA_DECODE_PIECE_COST", 3, 0, 64);
+  return c;
+}
+
 int resolve_splits(int num_splits, int num_seqs, int num_kv_heads, int max_seq_len, int waves_factor = 1) {
   const int64_t max_blocks = (int64_t)num_seqs * ((max_seq_len + 15) / 16);
   int64_t w = num_splits > 0 ? num_splits
@@ -257,6 +264,7 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   p.num_blocks = num_blocks;
   p.max_seq_len = max_seq_len;
   p.n_splits = n_splits;
+  p.piece_cost = decode_piece_cost();
   p.window = sliding_window > 0 ? sliding_window : 0;
   p.chunk = local_chunk > 0 ? local_chunk : 0;
   p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);

@@ -198,20 +198,25 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
 }
 
 // Calls piece(s, b0, b1, nb) for every piece of share `split` (of n_splits):
-// blocks [b0, b1) of sequence s, which has nb blocks in all.  Shares are
-// consecutive ranges of the sequences' blocks laid end to end, so a wave
-// visits its sequences in increasing order.  All arguments are wave-uniform.
+// blocks [b0, b1) of sequence s, which has nb blocks in all.  The sequences are laid
+// end to end, each as p.piece_cost units (the cost of starting a piece: its Q, its
+// table window, the pipeline's first loads, in blocks' worth of time) followed by its
+// nb blocks, and cut into n_splits equal shares of units; a share's piece of s is the
+// blocks it holds (a share holding only the start units of s has no piece of it).
+// Shares are consecutive, so a wave visits its sequences in increasing order and the
+// pieces of a sequence come from consecutive shares.  All arguments are wave-uniform.
 template <typename Fn>
 __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int split, Fn&& piece) {
   const int lane = threadIdx.x & 63;
+  const int c = p.piece_cost;
   int tot = 0;
   for (int base = 0; base < p.num_seqs; base += 64) {
     const int s = base + lane;
-    tot += s < p.num_seqs ? decode_blocks(p, s) : 0;
+    const int nb = s < p.num_seqs ? decode_blocks(p, s) : 0;
+    tot += nb > 0 ? nb + c : 0;
   }
   const long long T = wave_sum_i32(tot);
-  // never more shares than blocks, so no share is empty and the pieces of a
-  // sequence come from consecutive shares
+  // never more shares than units, so no share is empty
   const long long n = min((long long)p.n_splits, T);
   if (split >= n) return;
   const int lo = (int)(T * split / n), hi = (int)(T * (split + 1) / n);
@@ -219,8 +224,9 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int split,
   for (int base = 0; base < p.num_seqs && carry < hi; base += 64) {
     const int s = base + lane;
     const int nb = s < p.num_seqs ? decode_blocks(p, s) : 0;
-    const int incl = wave_incl_scan_i32(nb, lane);
-    const int start = carry + incl - nb;
+    const int w = nb > 0 ? nb + c : 0;
+    const int incl = wave_incl_scan_i32(w, lane);
+    const int start = carry + incl - w + c;  // units before block 0 of s
     unsigned long long hits = __ballot(nb > 0 && start < hi && start + nb > lo);
     while (hits) {
       const int ln = __ffsll((long long)hits) - 1;

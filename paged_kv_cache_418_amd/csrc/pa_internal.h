@@ -47,6 +47,7 @@ struct DecodeParams {
   int num_blocks;
   int max_seq_len;
   int n_splits;
+  int piece_cost;            // blocks' worth of time a piece costs to start (share planning), >= 0
   // cascade (a prefix of blocks shared by every sequence, attended once per group of
   // sequences): the suffix launch skips the shared blocks and leaves every piece partial;
   // the prefix launch writes pre_* partials; the merge folds both in.
