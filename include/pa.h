@@ -33,7 +33,9 @@
  *    0 .. seq_len-q_len+i of its own sequence (causal, bottom-right aligned).
  *  - GQA: q head h reads kv head h / (num_q_heads / num_kv_heads).
  *  - Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
- *    num_kv_heads; bf16/fp8 paths need num_q_heads/num_kv_heads <= 16.
+ *    num_kv_heads, at most 256 q heads per kv head (the cascade decode: at
+ *    most 16).  The decode takes a kv head's q heads 16 at a time, so above 16
+ *    per kv head the K/V of a block are read once per group of 16.
  *  - dtypes: PA_F32, PA_BF16 for activations and pools; PA_FP8_E4M3 pools
  *    hold OCP E4M3FN codes (bias 7, max 448, no infinities).  The output has
  *    the query's dtype; fp32 accumulation throughout; bf16 results are rounded

@@ -139,6 +139,13 @@ int decode_piece_cost() {
   return c;
 }
 
+// Waves per share of a decode launch: a kv head's q heads go 16 at a time to the matrix-core
+// columns, so a kv head with more than 16 of them takes one wave per group of 16.
+int decode_columns(int num_q_heads, int num_kv_heads) {
+  const int group = num_q_heads / std::max(1, num_kv_heads);
+  return num_kv_heads * std::max(1, (group + 15) / 16);
+}
+
 int resolve_splits(int num_splits, int num_seqs, int num_kv_heads, int max_seq_len, int waves_factor = 1) {
   const int64_t max_blocks = (int64_t)num_seqs * ((max_seq_len + 15) / 16);
   int64_t w = num_splits > 0 ? num_splits
@@ -246,7 +253,7 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   // a window (or local chunk) of W keys spans at most W/16 + 2 blocks of each sequence
   const int vis = sliding_window > 0 ? sliding_window : local_chunk;
   const int span = vis > 0 ? std::min<int64_t>(max_seq_len, (int64_t)vis + 16) : max_seq_len;
-  const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, span);
+  const int n_splits = resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), span);
   pa::DecodeParams p{};
   p.out = out;
   p.query = query;
@@ -261,6 +268,7 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
+  p.head_groups = (p.group + 15) / 16;  // 1 for a cascade (at most 16 q heads per kv head)
   p.num_blocks = num_blocks;
   p.max_seq_len = max_seq_len;
   p.n_splits = n_splits;
@@ -511,7 +519,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t max_seq_len, int32_t num_splits) {
   if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_seq_len < 1 || num_splits < 0)
     return 0;
-  const int n_splits = resolve_splits(num_splits, num_seqs, num_kv_heads, max_seq_len);
+  if (num_q_heads % num_kv_heads) return 0;
+  const int n_splits = resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), max_seq_len);
   if (n_splits <= 1) return 0;
   return decode_layout(num_seqs, num_q_heads, n_splits, head_dim).total;
 }
@@ -526,8 +535,8 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                                      num_splits, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (dtype == PA_BF16 && num_q_heads / num_kv_heads > pa::kMaxGroup)
-    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (dtype == PA_BF16 && num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGqa);
   if (num_seqs == 0) return ok();
   if (validate_enabled()) {
     st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
@@ -553,8 +562,8 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
   if (st != PA_OK) return st;
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
-  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
-    return fail(PA_ERR_UNSUPPORTED, "fp8 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "fp8 decode supports up to %d q heads per kv head", pa::kMaxGqa);
   if (num_seqs == 0) return ok();
   if (validate_enabled()) {
     st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
@@ -839,8 +848,8 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     return fail(PA_ERR_NULL, "a required pointer is NULL");
   pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, bt_stride);
   if (st != PA_OK) return st;
-  if (num_q_heads / num_kv_heads > pa::kMaxGroup && (dtype == PA_BF16 || kv_kind == pa::kFP8))
-    return fail(PA_ERR_UNSUPPORTED, "up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "up to %d q heads per kv head", pa::kMaxGqa);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
   VarlenPlan plan;
   st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
@@ -965,7 +974,7 @@ size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, co
                                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim) {
   if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGroup)
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa)
     return 0;
   return varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                 0);
@@ -975,7 +984,7 @@ size_t pa_prefill_varlen_window_workspace_bytes(const int32_t* query_start_loc_h
                                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                                 int32_t head_dim, int32_t sliding_window) {
   if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGroup || sliding_window < 1)
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa || sliding_window < 1)
     return 0;
   return varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                 sliding_window);
@@ -993,8 +1002,8 @@ pa_status_t pa_decode_window(void* out, const void* query, const void* key_cache
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                                      num_splits, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
-    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGqa);
   if (num_seqs == 0) return ok();
   if (validate_enabled()) {
     st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
@@ -1038,7 +1047,7 @@ size_t pa_prefill_varlen_local_workspace_bytes(const int32_t* query_start_loc_ho
                                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                                int32_t head_dim, int32_t chunk_size) {
   if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGroup || chunk_size < 1)
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa || chunk_size < 1)
     return 0;
   return varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                 0, chunk_size);
@@ -1056,8 +1065,8 @@ pa_status_t pa_decode_local(void* out, const void* query, const void* key_cache,
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                                      num_splits, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
-    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGroup);
+  if (num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGqa);
   if (num_seqs == 0) return ok();
   if (validate_enabled()) {
     st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);

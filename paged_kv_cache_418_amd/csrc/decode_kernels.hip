@@ -255,7 +255,9 @@ __device__ __forceinline__ void note_piece(const DecodeParams& p, int split, int
 // whose V slices the same lane loaded.  P therefore never leaves its lane,
 // and the V^T operand of MFMA j (d = VEC*m + j) is two byte permutes of the
 // lane's own V words.  Two blocks are in flight while one is computed.
-// Blocks [b0, b1) of sequence s (nb blocks in all) for the q heads of kv head kvh.
+// Blocks [b0, b1) of sequence s (nb blocks in all) for q heads 16*hg .. 16*hg+15 of kv
+// head kvh (all of them when the kv head has at most 16; more take one wave per group
+// of 16, each reading the blocks).
 //
 // GROUP (cascade prefix): the 16 columns are 16/G sequences x G heads instead of the G
 // heads of one sequence, so each block of the shared prefix feeds 16/G sequences at
@@ -264,7 +266,7 @@ __device__ __forceinline__ void note_piece(const DecodeParams& p, int split, int
 // [b0, b1) of sequence s after its skip_blocks shared blocks.
 template <int D, bool FP8, bool GROUP = false>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned char* k_lds, int split, int kvh, int s,
-                                             int b0, int b1, int nb) {
+                                             int b0, int b1, int nb, int hg = 0) {
   using Sh = DecodeShape<D, FP8>;
   constexpr int VEC = Sh::kVec, W = Sh::kWords;
   const int row = p.qsl ? p.qsl[s] : s;
@@ -280,9 +282,9 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
   const int a = lane >> 4, c = lane & 15;  // row group / column within the row group
   const int G = p.group;
   // the lane's column: q head g of query row col_row (col_ok: a real column)
-  const int g = GROUP ? c % G : c;
+  const int g = GROUP ? c % G : 16 * hg + c;
   const int col_seq = GROUP ? s + c / G : s;
-  const bool col_ok = GROUP ? (c < (16 / G) * G && col_seq < p.num_seqs) : c < G;
+  const bool col_ok = GROUP ? (c < (16 / G) * G && col_seq < p.num_seqs) : g < G;
   const int col_row = GROUP ? col_seq : row;
 
   // Q^T operand of MFMA kk: lane (a, column c) holds q[column][8*(a + 4*kk) .. +7]
@@ -529,11 +531,13 @@ __device__ __forceinline__ bool prefix_piece(const DecodeParams& p, unsigned cha
 template <int D, bool FP8>
 __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
   __shared__ __align__(16) unsigned char k_lds[DecodeShape<D, FP8>::kLdsBytes];
-  if (prefix_piece<D, FP8>(p, k_lds, blockIdx.x, blockIdx.y)) return;
-  const int split = blockIdx.x - p.prefix_waves, kvh = blockIdx.y;
+  // grid y: (kv head, group of 16 of its q heads); a cascade has one group per kv head
+  const int kvh = blockIdx.y / p.head_groups, hg = blockIdx.y % p.head_groups;
+  if (prefix_piece<D, FP8>(p, k_lds, blockIdx.x, kvh)) return;
+  const int split = blockIdx.x - p.prefix_waves;
   for_each_piece(p, split, [&](int s, int b0, int b1, int nb) {
-    if (kvh == 0 && threadIdx.x == 0) note_piece(p, split, s, b0, b1, nb);
-    decode_piece<D, FP8>(p, k_lds, split, kvh, s, b0, b1, nb);
+    if (blockIdx.y == 0 && threadIdx.x == 0) note_piece(p, split, s, b0, b1, nb);
+    decode_piece<D, FP8>(p, k_lds, split, kvh, s, b0, b1, nb, hg);
   });
 }
 
@@ -688,11 +692,11 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   if (kv == kF32) {
     hipLaunchKernelGGL(decode_f32_kernel<D>, dim3(p.n_splits, p.num_q_heads), dim3(64), 0, stream, p);
   } else if (kv == kFP8) {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, true>), dim3(p.prefix_waves + p.n_splits, p.num_kv_heads), dim3(64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, true>), dim3(p.prefix_waves + p.n_splits, p.num_kv_heads * p.head_groups),
+                       dim3(64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, false>), dim3(p.prefix_waves + p.n_splits, p.num_kv_heads), dim3(64),
-                       0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, false>),
+                       dim3(p.prefix_waves + p.n_splits, p.num_kv_heads * p.head_groups), dim3(64), 0, stream, p);
   }
   timing_mark(kKDecode, false, stream);
   hipError_t e = hipGetLastError();

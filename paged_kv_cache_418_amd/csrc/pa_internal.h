@@ -13,7 +13,9 @@ pa_status_t set_error(pa_status_t st, const char* fmt, ...);
 
 constexpr int kBlockSize = 16;      // tokens per physical block
 constexpr int kDecodeWaves = 4;     // waves per decode work-group
-constexpr int kMaxGroup = 16;       // q heads per kv head handled by one MFMA column set
+constexpr int kMaxGroup = 16;       // q heads per kv head handled by one MFMA column set (cascade limit)
+constexpr int kMaxGqa = 256;        // q heads per kv head: decode takes them 16 at a time, prefill packs
+                                    // at least one position of them into a 256-row tile
 constexpr int kPrefillRows = 256;   // (position, q head) rows per prefill work-group (4 waves x 64)
 constexpr int kPrefillKeys = 64;    // keys per LDS tile in prefill
 constexpr int kMaxPrefillItems = 480;  // work items per launch (kernel-argument space)
@@ -44,6 +46,7 @@ struct DecodeParams {
   int num_q_heads;
   int num_kv_heads;
   int group;                 // num_q_heads / num_kv_heads
+  int head_groups;           // ceil(group / 16): the matrix-core columns take 16 q heads of a kv head at a time
   int num_blocks;
   int max_seq_len;
   int n_splits;

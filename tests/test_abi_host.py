@@ -43,6 +43,10 @@ def test_decode_workspace_arithmetic(lib):
     assert pk.pa_decode_workspace_bytes(1, 4, 2, 64, 16, 0) == 0               # a single block
     assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, -1) == 0         # invalid share count
     assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) > 0           # automatic
+    # a kv head with 32 q heads takes two waves per share (16 matrix-core columns each): the automatic plan of
+    # 32 q heads over 1 kv head is that of 32 over 2
+    assert pk.pa_decode_workspace_bytes(64, 32, 1, 128, 4096, 0) == pk.pa_decode_workspace_bytes(64, 32, 2, 128, 4096, 0)
+    assert pk.pa_decode_workspace_bytes(64, 32, 1, 128, 4096, 0) > 0
 
 
 def _decode(lib, **kw):
@@ -67,7 +71,7 @@ def _decode(lib, **kw):
     (dict(wsb=16), 4),
     (dict(ws=None), 4),
     (dict(ws=FAKE + 8), 4),
-    (dict(Hq=256, Hkv=8), 5),
+    (dict(Hq=8 * 257, Hkv=8), 5),  # more than 256 q heads per kv head
     (dict(scale=float("inf")), 2),
     (dict(NB=0), 2),
 ])
@@ -139,6 +143,10 @@ def test_prefill_workspace_bytes(lib):
     assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 32, 8, 128) == 0
     # invalid grouping
     assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 30, 8, 128) == 0
+    assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 257, 1, 128) == 0
+    # 32 q heads per kv head: 8 positions per 256-row tile, so the 64-token chunk spans 8 row tiles (no split)
+    assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q2), ctypes.addressof(s2), 1, 32, 1, 128) == 0
+    assert lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 64, 2, 128) > 0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -215,6 +215,85 @@ def test_decode_long_context_70b_full():
     _decode_case(w)
 
 
+# ---- more than 16 q heads per kv head (MQA-like grouping, [P1] tutorial 1): the decode takes a kv head's
+# q heads 16 at a time (one wave per group, a partial last group when G is not a multiple of 16); the
+# prefill packs 256 / G positions per row tile
+
+@pytest.mark.parametrize("heads", [(32, 1, 128), (48, 1, 64), (64, 2, 128)])
+@pytest.mark.parametrize("kinds", [("bf16", "bf16"), ("bf16", "fp8"), ("f32", "f32")])
+@pytest.mark.parametrize("num_splits", [0, 5])
+def test_decode_many_q_heads_per_kv_head(heads, kinds, num_splits):
+    Hq, Hkv, D = heads
+    seed = 760 + Hq + Hkv + num_splits + len(kinds[1])
+    w = wl.random_case(seed, num_seqs=6, ctx_range=(1, 700), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                       q_dtype=kinds[0], kv_dtype=kinds[1], k_scale=0.05, v_scale=0.04)
+    say("decode G>16", heads, kinds, num_splits, list(w.seq_lens))
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = d.decode(num_splits)
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, ref)
+    tol = TOL[w.kv_dtype if w.kv_dtype == "fp8" else w.q_dtype]
+    say(f"  max_abs_err={err:.3e} tol={tol}")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("heads", [(32, 1, 128), (48, 1, 64), (64, 2, 128)])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_many_q_heads_per_kv_head(heads, kv):
+    Hq, Hkv, D = heads
+    w = wl.random_case(780 + Hq + Hkv + len(kv), num_seqs=6, ctx_range=(1, 500), chunk_range=(1, 200), num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, q_dtype="bf16", kv_dtype=kv, k_scale=0.05, v_scale=0.04)
+    say("prefill G>16", heads, kv, list(w.q_lens), list(w.seq_lens))
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["fp8" if kv == "fp8" else "bf16"]
+
+
+def test_window_and_local_many_q_heads_per_kv_head():
+    w = wl.random_case(797, num_seqs=6, ctx_range=(1, 600), chunk_range=(1, 150), num_q_heads=32, num_kv_heads=1,
+                       head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    pools = oracle.written_pools(w)
+    for window in (1, 37, 300):
+        say("window G=32", window)
+        out = d.prefill_window(window)
+        torch.cuda.synchronize()
+        err = max_err(out, oracle.attention_for(w, pools=pools, window=window))
+        say(f"  max_abs_err={err:.3e}")
+        assert err <= TOL["bf16"]
+    dw = wl.random_case(798, num_seqs=6, ctx_range=(1, 900), num_q_heads=32, num_kv_heads=1, head_dim=128,
+                        q_dtype="bf16", kv_dtype="bf16")
+    dd = DevWorkload(dw)
+    dd.write_new_tokens()
+    dpools = oracle.written_pools(dw)
+    for window in (16, 100):
+        say("decode window G=32", window)
+        out = dd.decode_window(window)
+        torch.cuda.synchronize()
+        err = max_err(out, oracle.attention_for(dw, pools=dpools, window=window))
+        assert err <= TOL["bf16"]
+    say("decode local G=32")
+    out = dd.decode_local(64)
+    torch.cuda.synchronize()
+    assert max_err(out, oracle.attention_for(dw, pools=dpools, chunk=64)) <= TOL["bf16"]
+
+
+def test_cascade_refuses_more_than_16_q_heads_per_kv_head():
+    w = wl.random_case(799, num_seqs=4, ctx_range=(65, 200), num_q_heads=32, num_kv_heads=1, head_dim=128,
+                       q_dtype="bf16", kv_dtype="bf16", shared_prefix_tokens=64)
+    d = DevWorkload(w)
+    with pytest.raises(pk.PAError):
+        d.cascade(4)
+
+
 # ---- cascade decode (a prefix of physical blocks shared by every sequence)
 
 @pytest.mark.parametrize("kinds", [("bf16", "bf16"), ("bf16", "fp8"), ("f32", "fp8")])
