@@ -51,8 +51,9 @@
  *    The contents of device arrays are trusted, except that block ids are
  *    clamped to [0, num_blocks) and positions past max_seq_len are not read;
  *    setting the environment variable PA_VALIDATE=1 makes every call copy the
- *    metadata to the host (a synchronising step) and reject inconsistent
- *    contents with PA_ERR_SHAPE.
+ *    metadata to the host (it first waits for all work on the device, then
+ *    copies) and reject inconsistent contents with PA_ERR_SHAPE.  Such calls
+ *    synchronise, so they cannot be captured in a graph.
  *  - Thread safety: calls are independent; calls on different streams may run
  *    concurrently as long as they do not share output or workspace memory.
  */

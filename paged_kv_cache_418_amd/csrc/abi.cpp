@@ -74,6 +74,9 @@ template <typename T>
 bool copy_to_host(std::vector<T>& dst, const T* src, size_t n) {
   dst.resize(n);
   if (n == 0) return true;
+  // the metadata may have been written by work still queued on any stream of the device (the
+  // caller's stream need not be the null stream, which a blocking copy alone would order with)
+  if (hipDeviceSynchronize() != hipSuccess) return false;
   return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
 }
 
