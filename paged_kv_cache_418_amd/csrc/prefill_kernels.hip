@@ -406,14 +406,12 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
           : "memory");
     }
   };
-  auto vt_wait_tr = [&](u32x4 (&x)[kTileQuad], u32x2 (&t)[Sh::kTransposes]) {
-    if constexpr (kTileQuad == 4) {
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
-                   :
-                   : "memory");
+  // waits for this wave's transposing reads (the last LDS reads it issued)
+  auto tr_wait = [&](u32x2 (&t)[Sh::kTransposes]) {
+    if constexpr (Sh::kTransposes == 4) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]) : : "memory");
     } else {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(t[0]), "+v"(t[1]) : : "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]) : : "memory");
     }
   };
 
@@ -499,13 +497,16 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
         vt_wait(vb[ch & 1], std::integral_constant<int, kTileQuad + Sh::kTransposes>{});
       } else {
         between(ch);
-        vt_wait_tr(vb[ch & 1], tx);
+        // the last chunk's operands were read before the transposing reads, and LDS reads
+        // return in order: its MFMAs wait only for them, the transposed rows after
+        vt_wait(vb[ch & 1], std::integral_constant<int, Sh::kTransposes>{});
       }
       const bf16x8 pb = u4_to_bf16x8(pw[ch]);
 #pragma unroll
       for (int n = 0; n < Sh::kDTiles; ++n)
         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(vb[ch & 1][n]), pb, acc[n], 0, 0, 0);
     });
+    tr_wait(tx);
     tr_write(tx, tr_to);
   };
 
