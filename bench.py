@@ -256,6 +256,19 @@ def bench_decode(args, result):
         result["roofline"]["traffic_note"] = traffic["why"]
     else:
         result["roofline"]["traffic_over_alg"] = round(traffic["bytes"] / alg_bytes, 4)
+    _log("generating llama3_8b_decode_fp8 ...")
+    w8 = wl.llama3_8b_decode_fp8()
+    st8 = Step(w8)
+    ms8, _ = time_steps(st8, args.steps, args.warmup)
+    kt8 = kernel_times(st8, args.steps, ["decode", "decode_merge"])
+    kv8 = wl.decode_kv_bytes(w8)
+    result["fp8_kv_decode"] = {
+        "workload": "llama3_8b_decode_fp8 (the same batch with E4M3 pools, K scale 0.05, V scale 0.04)",
+        "kv_bytes": kv8, "ms_per_step": round(ms8, 5), "decode_kernel_ms": round(kt8["decode"][0], 5),
+        "merge_kernel_ms": round(kt8["decode_merge"][0], 5),
+        "kernel_gbps": round(kv8 / (kt8["decode"][0] * 1e-3) / 1e9, 1),
+        "kernel_frac_hbm": round(kv8 / (kt8["decode"][0] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del st8, w8
     if not args.no_cpu:
         _log("cpu baseline ...")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -120,16 +120,18 @@ int device_cu_count() {
   return n;
 }
 
-// Decode waves per SIMD the automatic split aims at (PA_DECODE_WAVES_PER_SIMD, default 1:
-// with streaming loads one wave per SIMD, two blocks in flight each, beat two on a
-// Llama-3-8B layer, 89 against 96 us).
-int decode_waves_per_simd() {
-  static const int w = [] {
+// Decode waves per SIMD the automatic split aims at: PA_DECODE_WAVES_PER_SIMD when set, else
+// one for bf16/fp32 pools (with streaming loads one wave per SIMD, two blocks in flight each,
+// beat two on a Llama-3-8B layer, 89 against 96 us) and two for fp8 pools (a block is half the
+// bytes for the same per-block work: on the same layer with E4M3 pools 53 us at two waves, 60
+// at one, 54 at three, 63 at four).
+int decode_waves_per_simd(bool fp8) {
+  static const int env = [] {
     const char* v = std::getenv("PA_DECODE_WAVES_PER_SIMD");
     const int x = v ? std::atoi(v) : 0;
-    return x >= 1 && x <= 16 ? x : 1;
+    return x >= 1 && x <= 16 ? x : 0;
   }();
-  return w;
+  return env ? env : (fp8 ? 2 : 1);
 }
 
 // Shares the decode work of each kv head is cut into: num_splits if positive,
@@ -149,10 +151,11 @@ int decode_columns(int num_q_heads, int num_kv_heads) {
   return num_kv_heads * std::max(1, (group + 15) / 16);
 }
 
-int resolve_splits(int num_splits, int num_seqs, int num_kv_heads, int max_seq_len, int waves_factor = 1) {
+int resolve_splits(int num_splits, int num_seqs, int num_kv_heads, int max_seq_len, int waves_factor = 1,
+                   bool fp8 = false) {
   const int64_t max_blocks = (int64_t)num_seqs * ((max_seq_len + 15) / 16);
   int64_t w = num_splits > 0 ? num_splits
-                             : (int64_t)waves_factor * decode_waves_per_simd() * 4 * device_cu_count() /
+                             : (int64_t)waves_factor * decode_waves_per_simd(fp8) * 4 * device_cu_count() /
                                    std::max(1, num_kv_heads);
   w = std::min<int64_t>(std::max<int64_t>(w, 1), std::max<int64_t>(max_blocks, 1));
   return (int)std::min<int64_t>(w, 1 << 20);
@@ -256,7 +259,8 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   // a window (or local chunk) of W keys spans at most W/16 + 2 blocks of each sequence
   const int vis = sliding_window > 0 ? sliding_window : local_chunk;
   const int span = vis > 0 ? std::min<int64_t>(max_seq_len, (int64_t)vis + 16) : max_seq_len;
-  const int n_splits = resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), span);
+  const int n_splits =
+      resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), span, 1, kv_kind == pa::kFP8);
   pa::DecodeParams p{};
   p.out = out;
   p.query = query;
@@ -523,7 +527,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_seq_len < 1 || num_splits < 0)
     return 0;
   if (num_q_heads % num_kv_heads) return 0;
-  const int n_splits = resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), max_seq_len);
+  // sized for the larger automatic share count (fp8 pools); a bf16 or fp32 call uses part of it
+  const int n_splits =
+      resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), max_seq_len, 1, true);
   if (n_splits <= 1) return 0;
   return decode_layout(num_seqs, num_q_heads, n_splits, head_dim).total;
 }

@@ -76,8 +76,14 @@ struct BlockRegs {
 #ifndef PA_DECODE_IN_FLIGHT
 #define PA_DECODE_IN_FLIGHT 2
 #endif
-// blocks whose loads are in flight per wave while one is computed (register sets)
-constexpr int kInFlight = PA_DECODE_IN_FLIGHT;
+#ifndef PA_DECODE_IN_FLIGHT_FP8
+#define PA_DECODE_IN_FLIGHT_FP8 2
+#endif
+// blocks whose loads are in flight per wave while one is computed (register sets); an fp8
+// block is half the bytes of a bf16 one, but more sets did not help it (Llama-3-8B layer with
+// E4M3 pools at one wave per SIMD: 2 sets 60 us, 3 60, 4 64, 6 65): fp8 takes more waves instead
+template <bool FP8>
+constexpr int kInFlight = FP8 ? PA_DECODE_IN_FLIGHT_FP8 : PA_DECODE_IN_FLIGHT;
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -446,15 +452,16 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
   // (no effect on m, l or the output).  Measured on the Llama-3-8B layer at one wave per
   // SIMD: 2 sets 89 us, 3 sets 92, 4 sets 94 (1 set 88 with more waves): the memory
   // system, not the wave's latency, is the limit.
-  BlockRegs<D, FP8> rs[kInFlight];
-  static_for<0, kInFlight>([&](auto i_c) {
+  constexpr int kSets = kInFlight<FP8>;
+  BlockRegs<D, FP8> rs[kSets];
+  static_for<0, kSets>([&](auto i_c) {
     issue(rs[decltype(i_c)::value], decltype(i_c)::value);
     __builtin_amdgcn_sched_barrier(0);
   });
-  for (int b = 0; b < nblk; b += kInFlight) {
-    static_for<0, kInFlight>([&](auto i_c) {
+  for (int b = 0; b < nblk; b += kSets) {
+    static_for<0, kSets>([&](auto i_c) {
       constexpr int i = decltype(i_c)::value;
-      compute(rs[i], b + i, rs[i], b + i + kInFlight);
+      compute(rs[i], b + i, rs[i], b + i + kSets);
     });
   }
 

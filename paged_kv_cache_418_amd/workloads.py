@@ -228,6 +228,15 @@ def llama3_8b_decode_bf16(num_seqs: int = 64) -> Workload:
                  q_dtype="bf16", kv_dtype="bf16", max_blocks=256)
 
 
+def llama3_8b_decode_fp8(num_seqs: int = 64) -> Workload:
+    """The Llama-3-8B decode layer's batch with E4M3 pools (K scale 0.05, V scale 0.04) and bf16 queries."""
+    rng = np.random.default_rng(SEED_BASE + 1)
+    ctx = rng.integers(512, 4096, num_seqs, endpoint=True)
+    return build("llama3_8b_decode_fp8", seed=SEED_BASE + 1, rng=rng, ctx_lens=ctx,
+                 q_lens=[1] * num_seqs, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 q_dtype="bf16", kv_dtype="fp8", max_blocks=256, k_scale=0.05, v_scale=0.04)
+
+
 def mixed_step_bf16(num_decode: int = 48, chunk: int = 512, cached: Sequence[int] = (0, 1536),
                     kv_dtype: str = "bf16") -> Workload:
     """Mixed continuous-batching step: 48 decodes (ctx U[256,8192]) then two 512-token
