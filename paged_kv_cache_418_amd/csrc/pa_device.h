@@ -76,16 +76,13 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
 }
 
 // Four E4M3 codes (one dword) -> four bf16 values (exact: E4M3 values are a
-// subset of bf16), through the gfx950 fp8 -> fp32 converter.
+// subset of bf16), two per gfx950 fp8 -> bf16 pair conversion at unit scale;
+// code i of the dword lands in bf16 lane i (low half first).
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  u32x2 r;
-  // the fp32 values are exact bf16 values: keep the top halves
-  r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
-  r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
-  return r;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
