@@ -283,6 +283,7 @@ def long_prefill_bf16(num_seqs: int = 4, prompt: int = 4096) -> Workload:
 NAMED = {
     "tiny_fp32_decode": tiny_fp32_decode,
     "llama3_8b_decode_bf16": llama3_8b_decode_bf16,
+    "llama3_8b_decode_fp8": llama3_8b_decode_fp8,
     "mixed_step_bf16": mixed_step_bf16,
     "long_ctx_70b_decode_bf16": long_ctx_70b_decode_bf16,
     "prefix_shared_fp8_decode": prefix_shared_fp8_decode,

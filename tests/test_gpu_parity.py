@@ -203,6 +203,13 @@ def test_decode_llama3_8b_full():
     _decode_case(w)
 
 
+def test_decode_llama3_8b_fp8_full():
+    """The same batch over E4M3 pools (the fp8 leg of the bench), element by element at full size."""
+    w = wl.llama3_8b_decode_fp8()
+    say("decode llama3_8b fp8 full")
+    _decode_case(w)
+
+
 def test_decode_prefix_shared_fp8_full():
     w = wl.prefix_shared_fp8_decode()
     say("decode prefix-shared fp8 full")

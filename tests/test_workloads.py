@@ -47,6 +47,17 @@ def test_named_workloads_are_valid(name):
     assert w.new_k.shape == (w.num_tokens, w.num_kv_heads, w.head_dim)
 
 
+def test_llama3_8b_fp8_batch_matches_the_bf16_one():
+    """The fp8-KV decode batch is the bf16 batch's layout (same lengths, tables and pool size) over E4M3 pools."""
+    w8, wb = wl.llama3_8b_decode_fp8(), wl.llama3_8b_decode_bf16()
+    _check_tables(w8)
+    _check_poison(w8)
+    assert np.array_equal(w8.seq_lens, wb.seq_lens) and np.array_equal(w8.block_tables, wb.block_tables)
+    assert w8.k_cache.dtype == torch.uint8 and w8.k_cache.shape == wb.k_cache.shape
+    assert (w8.k_scale, w8.v_scale) == (0.05, 0.04)
+    assert wl.decode_kv_bytes(w8) * 2 == wl.decode_kv_bytes(wb)
+
+
 def test_mixed_step_layout():
     w = wl.mixed_step_bf16()
     assert w.num_tokens == 1072 and w.num_seqs == 50
