@@ -239,9 +239,10 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
         : "v"(a), "i"(32 * Sh::kRowBytes)
         : "memory");
   };
-  auto k_wait = [&](u32x4 (&x)[2], auto n_c) {
+  // waits until at most N LDS reads issued after x's are in flight (reads return in order)
+  auto op_wait = [&](u32x4& x, auto n_c) {
     constexpr int N = decltype(n_c)::value;
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(N) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N) : "memory");
   };
   auto scores = [&](f32x16 (&sacc)[2], uint32_t kbase_lds) {
     constexpr int kAhead = 2;
@@ -250,17 +251,16 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
     static_for<0, Sh::kKSteps>([&](auto kk_c) {
       constexpr int kk = decltype(kk_c)::value;
       constexpr int nxt = kk + kAhead;
-      if constexpr (nxt < Sh::kKSteps) {
-        k_issue(kb[nxt % (kAhead + 1)], kbase_lds, std::integral_constant<int, nxt>{});
-        k_wait(kb[kk % (kAhead + 1)], std::integral_constant<int, 2 * kAhead>{});
-      } else {
-        k_wait(kb[kk % (kAhead + 1)], std::integral_constant<int, 2 * (Sh::kKSteps - 1 - kk)>{});
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      if constexpr (nxt < Sh::kKSteps) k_issue(kb[nxt % (kAhead + 1)], kbase_lds, std::integral_constant<int, nxt>{});
+      // reads issued after this k-step's two: the next steps' (at most kAhead of them)
+      constexpr int kLater = 2 * (nxt < Sh::kKSteps ? kAhead : Sh::kKSteps - 1 - kk);
+      // each MFMA waits for its own operand only
+      static_for<0, 2>([&](auto kt_c) {
+        constexpr int kt = decltype(kt_c)::value;
+        op_wait(kb[kk % (kAhead + 1)][kt], std::integral_constant<int, kLater + 1 - kt>{});
         const f32x16 c = kk == 0 ? f32x16{} : sacc[kt];
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(kb[kk % (kAhead + 1)][kt]), qf[kk], c, 0, 0, 0);
-      }
+      });
     });
   };
 
@@ -346,8 +346,8 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch)
     vt_off[ch] = (uint32_t)(rl * Sh::kVtRowBytes + (((2 * ch + half) ^ ((rl >> 1) & 7)) << 4));
-  // issue (no wait) the V^T operand reads of one chunk; vt_wait waits for them and hands the
-  // registers on.  Issued from asm: the compiler would otherwise wait for every LDS copy in
+  // issue (no wait) the V^T operand reads of one chunk; op_wait waits for each of them and
+  // hands the register on.  Issued from asm: the compiler would otherwise wait for every LDS copy in
   // flight before an LDS read it cannot tell apart from them.
   auto vt_issue = [&](u32x4 (&x)[kTileQuad], uint32_t base) {
     constexpr int kRows32 = 32 * Sh::kVtRowBytes;
@@ -367,14 +367,6 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
           : "=&v"(x[0]), "=&v"(x[1])
           : "v"(base), "i"(kRows32)
           : "memory");
-    }
-  };
-  auto vt_wait = [&](u32x4 (&x)[kTileQuad], auto n_c) {
-    constexpr int N = decltype(n_c)::value;
-    if constexpr (kTileQuad == 4) {
-      asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(N) : "memory");
-    } else {
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(N) : "memory");
     }
   };
   // the V^T reads of the last chunk plus this wave's transposing reads of the next tile
@@ -490,21 +482,23 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
       if constexpr (ch + 2 < 4) {
         vt_issue(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1]);
         between(ch);
-        vt_wait(vb[ch & 1], std::integral_constant<int, kTileQuad>{});
       } else if constexpr (ch + 1 < 4) {
         vt_issue_tr(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1], tx, tr_from);
         between(ch);
-        vt_wait(vb[ch & 1], std::integral_constant<int, kTileQuad + Sh::kTransposes>{});
       } else {
         between(ch);
-        // the last chunk's operands were read before the transposing reads, and LDS reads
-        // return in order: its MFMAs wait only for them, the transposed rows after
-        vt_wait(vb[ch & 1], std::integral_constant<int, Sh::kTransposes>{});
       }
+      // reads issued after this chunk's: the next chunk's operands and (from chunk 2 on) the
+      // transposing reads; the last chunk's operands were read before the transposing reads,
+      // so its MFMAs wait only for them, the transposed rows after.  Each MFMA waits for its
+      // own operand only.
+      constexpr int kLater = ch < 2 ? kTileQuad : ch == 2 ? kTileQuad + Sh::kTransposes : Sh::kTransposes;
       const bf16x8 pb = u4_to_bf16x8(pw[ch]);
-#pragma unroll
-      for (int n = 0; n < Sh::kDTiles; ++n)
+      static_for<0, kTileQuad>([&](auto n_c) {
+        constexpr int n = decltype(n_c)::value;
+        op_wait(vb[ch & 1][n], std::integral_constant<int, kLater + kTileQuad - 1 - n>{});
         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(vb[ch & 1][n]), pb, acc[n], 0, 0, 0);
+      });
     });
     tr_wait(tx);
     tr_write(tx, tr_to);
