@@ -481,12 +481,8 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
       constexpr int ch = decltype(ch_c)::value;
       if constexpr (ch + 2 < 4) {
         vt_issue(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1]);
-        between(ch);
       } else if constexpr (ch + 1 < 4) {
         vt_issue_tr(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1], tx, tr_from);
-        between(ch);
-      } else {
-        between(ch);
       }
       // reads issued after this chunk's: the next chunk's operands and (from chunk 2 on) the
       // transposing reads; the last chunk's operands were read before the transposing reads,
@@ -498,6 +494,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
         constexpr int n = decltype(n_c)::value;
         op_wait(vb[ch & 1][n], std::integral_constant<int, kLater + kTileQuad - 1 - n>{});
         acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(vb[ch & 1][n]), pb, acc[n], 0, 0, 0);
+        if constexpr (n == 0) between(ch);  // the step's copy of this chunk, beside the first MFMA
       });
     });
     tr_wait(tx);
