@@ -134,9 +134,6 @@ int decode_waves_per_simd(bool fp8) {
   return env ? env : (fp8 ? 2 : 1);
 }
 
-// Shares the decode work of each kv head is cut into: num_splits if positive,
-// else enough waves to give every SIMD of the device decode_waves_per_simd()
-// of them; never more than the blocks there can be.
 // Blocks' worth of time a decode piece costs to start (PA_DECODE_PIECE_COST): the share
 // planner counts it for every sequence, so shares that start several pieces hold fewer blocks.
 int decode_piece_cost() {
@@ -151,6 +148,9 @@ int decode_columns(int num_q_heads, int num_kv_heads) {
   return num_kv_heads * std::max(1, (group + 15) / 16);
 }
 
+// Shares the decode work of each kv head is cut into: num_splits if positive,
+// else enough waves to give every SIMD of the device decode_waves_per_simd()
+// of them; never more than the blocks there can be.
 int resolve_splits(int num_splits, int num_seqs, int num_kv_heads, int max_seq_len, int waves_factor = 1,
                    bool fp8 = false) {
   const int64_t max_blocks = (int64_t)num_seqs * ((max_seq_len + 15) / 16);
