@@ -314,7 +314,10 @@ size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, co
  * query/out: [num_tokens][num_q_heads][head_dim]; dtype PA_BF16 (PA_F32 is
  * accepted for batches whose q_len are all 1).  The host copies of
  * query_start_loc and seq_lens plan the work (the control plane is on the
- * CPU) and must equal the device arrays.
+ * CPU) and must equal the device arrays.  scale must be positive and finite
+ * (PA_ERR_SHAPE otherwise; the same holds for every pa_prefill_varlen*
+ * entry point): the kernel keeps the running maximum of raw scores and
+ * applies the scale inside the exponential.
  */
 pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
                               const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
@@ -496,7 +499,11 @@ int32_t pa_pool_free_queue(const pa_block_pool_t* pool, int32_t* out, int32_t ma
  * serialise nothing but add a small gap between the kernels of one call.
  * pa_timing_read(kernel, &count, &total_ms): waits for the recorded events
  * of that kernel and returns how many launches were timed and their summed
- * duration in milliseconds.  pa_timing_reset(): zeroes the sums.
+ * duration in milliseconds.  pa_timing_read_launches(kernel, ms, max, &n):
+ * the same wait, then the duration of each launch timed since the last reset
+ * (the first 2^20 of them), in launch order: n = how many are kept, of which
+ * the first min(n, max) are copied to ms (host, may be NULL when max is 0).
+ * pa_timing_reset(): zeroes the sums and forgets the durations.
  */
 typedef enum pa_kernel {
   PA_K_SLOT_MAPPING = 0,    /* pa_slot_mapping */
@@ -522,6 +529,7 @@ pa_status_t pa_timing_enable(int on);
 pa_status_t pa_probe_mfma_peak(float* out, int32_t blocks, int32_t iters, void* stream);
 pa_status_t pa_timing_reset(void);
 pa_status_t pa_timing_read(pa_kernel_t kernel, int64_t* count, double* total_ms);
+pa_status_t pa_timing_read_launches(pa_kernel_t kernel, float* ms, int32_t max_launches, int32_t* n);
 
 #ifdef __cplusplus
 }

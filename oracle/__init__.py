@@ -52,8 +52,9 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_LIB)
+            # ORACLE_LIBRARY names another build of pa_oracle.c (the AddressSanitizer build)
+            path = os.environ.get("ORACLE_LIBRARY") or build()
+            lib = ctypes.CDLL(path)
             P = ctypes.c_void_p
             i32, i64, f32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
             lib.oracle_fp8_decode.argtypes = [ctypes.c_uint8]

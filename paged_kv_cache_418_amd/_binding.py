@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libpa.so")
+# PA_LIBRARY names another build of the same library (the AddressSanitizer build of asan_check.py)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_PKG, "libpa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
@@ -111,6 +112,7 @@ def load() -> ctypes.CDLL:
             "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_reset": ([], ctypes.c_int),
             "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+            "pa_timing_read_launches": ([ctypes.c_int, P, i32, ctypes.POINTER(i32)], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -174,9 +176,30 @@ def pa_slot_mapping(block_tables, seq_lens, query_start_loc, num_tokens: int, bl
     return out
 
 
+def _check_kv_write(key, value, key_cache, value_cache, fp8: bool) -> None:
+    """The pools take the new rows byte for byte (or quantise them): dtypes and [Hkv, D] must agree."""
+    if key.dim() != 3 or value.shape != key.shape:
+        raise ValueError("key and value must both be [num_tokens, num_kv_heads, head_dim]")
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("key_cache and value_cache must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    if tuple(key_cache.shape[2:]) != tuple(key.shape[1:]):
+        raise ValueError(f"pool rows {tuple(key_cache.shape[2:])} differ from the new rows {tuple(key.shape[1:])}")
+    if key.dtype != value.dtype:
+        raise ValueError(f"key dtype {key.dtype} differs from value dtype {value.dtype}")
+    if key_cache.dtype != value_cache.dtype:
+        raise ValueError(f"key_cache dtype {key_cache.dtype} differs from value_cache dtype {value_cache.dtype}")
+    if fp8:
+        if key_cache.dtype != torch.uint8 or key.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("fp8 pools are uint8 E4M3 codes written from float32 or bfloat16 rows")
+    elif key.dtype != key_cache.dtype or key.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"the pools ({key_cache.dtype}) must have the new rows' dtype ({key.dtype}), float32 or "
+                         "bfloat16")
+
+
 def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
     """Writes key/value [T, Hkv, D] (token stride may exceed Hkv*D) into the pools."""
     lib = load()
+    _check_kv_write(key, value, key_cache, value_cache, fp8=False)
     T, H, D = key.shape
     if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
         raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
@@ -189,6 +212,7 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
 
 def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale: float, v_scale: float):
     lib = load()
+    _check_kv_write(key, value, key_cache, value_cache, fp8=True)
     T, H, D = key.shape
     if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
         raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
@@ -203,6 +227,7 @@ def pa_write_kv(key, value, key_cache, value_cache, block_tables, seq_lens, quer
                 slot_mapping=None, k_scale: float = None, v_scale: float = None):
     """Slot mapping + KV write in one launch (fp8 pools when k_scale/v_scale are given); returns slot_mapping."""
     lib = load()
+    _check_kv_write(key, value, key_cache, value_cache, fp8=k_scale is not None)
     T, H, D = key.shape
     if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
         raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
@@ -438,6 +463,16 @@ def timing_read(kernel: str):
     n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
     _check("pa_timing_read", load().pa_timing_read(KERNELS[kernel], ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def timing_launches(kernel: str) -> list:
+    """Device milliseconds of each timed launch of one kernel since the last reset, in launch order."""
+    lib = load()
+    n = ctypes.c_int32(0)
+    _check("pa_timing_read_launches", lib.pa_timing_read_launches(KERNELS[kernel], None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_float * max(n.value, 1))()
+    _check("pa_timing_read_launches", lib.pa_timing_read_launches(KERNELS[kernel], buf, n.value, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]
 
 
 def pa_prefill_varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_q_heads: int, num_kv_heads: int,

@@ -790,9 +790,9 @@ struct PrefillLayout {
 PrefillLayout prefill_layout(int n_split_items, int num_kv_heads, int head_dim) {
   const size_t rows = (size_t)n_split_items * num_kv_heads * pa::kPrefillRows;
   PrefillLayout L;
-  L.o_bytes = align_up(rows * head_dim * sizeof(uint16_t));  // fp16 O / l
-  L.m_bytes = align_up(rows * sizeof(float));
-  L.total = n_split_items ? L.o_bytes + 2 * L.m_bytes : 0;
+  L.o_bytes = align_up(rows * head_dim * sizeof(uint16_t));  // (O / l) / sigma, fp16
+  L.m_bytes = align_up(rows * sizeof(float));                  // m, l and sigma: one fp32 each per row
+  L.total = n_split_items ? L.o_bytes + 3 * L.m_bytes : 0;
   return L;
 }
 
@@ -859,7 +859,9 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   if (st != PA_OK) return st;
   if (num_q_heads / num_kv_heads > pa::kMaxGqa)
     return fail(PA_ERR_UNSUPPORTED, "up to %d q heads per kv head", pa::kMaxGqa);
-  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+  // the prefill kernel masks raw scores and applies the scale inside exp2(s * scale - m),
+  // which orders the scores correctly only for a positive scale
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(PA_ERR_SHAPE, "scale must be positive and finite");
   VarlenPlan plan;
   st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
                    num_q_heads / num_kv_heads, num_kv_heads, plan, sliding_window, local_chunk);
@@ -904,6 +906,8 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   uint16_t* part_o = plan.n_split_items ? reinterpret_cast<uint16_t*>(ws + dec_bytes) : nullptr;
   float* part_m = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes) : nullptr;
   float* part_l = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + lay.m_bytes) : nullptr;
+  float* part_s =
+      plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + 2 * lay.m_bytes) : nullptr;
   // fp8: stage the chunk sequences' blocks, then run the bf16 kernel on the staging pool
   const void* pk_cache = key_cache;
   const void* pv_cache = value_cache;
@@ -936,6 +940,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     p.part_o = part_o;
     p.part_m = part_m;
     p.part_l = part_l;
+    p.part_s = part_s;
     p.bt_stride = bt_stride;
     p.num_tokens = num_tokens;
     p.num_q_heads = num_q_heads;
@@ -961,6 +966,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     p.part_o = part_o;
     p.part_m = part_m;
     p.part_l = part_l;
+    p.part_s = part_s;
     p.num_q_heads = num_q_heads;
     p.num_kv_heads = num_kv_heads;
     p.group = num_q_heads / num_kv_heads;
@@ -1146,7 +1152,9 @@ struct TimingState {
   hipEvent_t open[pa::kNumKernelIds] = {};
   int64_t count[pa::kNumKernelIds] = {};
   double total_ms[pa::kNumKernelIds] = {};
+  std::vector<float> launch_ms[pa::kNumKernelIds];  // each timed launch, in order (the first kMaxKept)
   std::vector<hipEvent_t> spare;
+  static constexpr size_t kMaxKept = 1 << 20;
 
   hipEvent_t take() {
     if (!spare.empty()) {
@@ -1168,6 +1176,7 @@ struct TimingState {
       } else {
         ++count[k];
         total_ms[k] += ms;
+        if (launch_ms[k].size() < kMaxKept) launch_ms[k].push_back(ms);
       }
       spare.push_back(pe.begin);
       spare.push_back(pe.end);
@@ -1234,8 +1243,21 @@ pa_status_t pa_timing_reset(void) {
     t.drain(k);
     t.count[k] = 0;
     t.total_ms[k] = 0.0;
+    t.launch_ms[k].clear();
   }
   return ok();
+}
+
+pa_status_t pa_timing_read_launches(pa_kernel_t kernel, float* ms, int32_t max_launches, int32_t* n) {
+  if (!n || (max_launches > 0 && !ms)) return fail(PA_ERR_NULL, "n (and ms when max_launches > 0) must not be NULL");
+  if ((int)kernel < 0 || (int)kernel >= pa::kNumKernelIds) return fail(PA_ERR_SHAPE, "unknown kernel id %d", (int)kernel);
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  const bool good = t.drain((int)kernel);
+  const std::vector<float>& v = t.launch_ms[(int)kernel];
+  *n = (int32_t)std::min<size_t>(v.size(), INT32_MAX);
+  for (int32_t i = 0; i < std::min(*n, max_launches); ++i) ms[i] = v[i];
+  return good ? ok() : fail(PA_ERR_HIP, "a timing event could not be read");
 }
 
 pa_status_t pa_timing_read(pa_kernel_t kernel, int64_t* count, double* total_ms) {

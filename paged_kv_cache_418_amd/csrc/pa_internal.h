@@ -16,7 +16,7 @@ constexpr int kDecodeWaves = 4;     // waves per decode work-group
 constexpr int kMaxGroup = 16;       // q heads per kv head handled by one MFMA column set (cascade limit)
 constexpr int kMaxGqa = 256;        // q heads per kv head: decode takes them 16 at a time, prefill packs
                                     // at least one position of them into a 256-row tile
-constexpr int kPrefillRows = 256;   // (position, q head) rows per prefill work-group (4 waves x 64)
+constexpr int kPrefillRows = 256;   // (position, q head) rows per prefill work-group (8 waves x 32)
 constexpr int kPrefillKeys = 64;    // keys per LDS tile in prefill
 constexpr int kMaxPrefillItems = 480;  // work items per launch (kernel-argument space)
 
@@ -69,10 +69,10 @@ struct DecodeParams {
   int q_f32;                 // query / output are fp32 (else bf16)
 };
 
-// One prefill launch: grid (n_items, num_kv_heads).  Item bits: sequence (15),
+// One prefill launch: grid (num_kv_heads, n_items).  Item bits: sequence (15),
 // whole-row-tile flag (1), row tile (16), first key tile (16), end key tile (16).
 // Items that cover only part of their row tile's key tiles come first in the
-// plan; their partial results live in slot item_base + blockIdx.x.
+// plan; their partial results live in slot item_base + blockIdx.y.
 struct PrefillParams {
   void* out;
   const void* query;
@@ -81,9 +81,10 @@ struct PrefillParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const int32_t* qsl;
-  uint16_t* part_o;          // [slots][num_kv_heads][256 rows][D] partial outputs divided by their l (fp16)
+  uint16_t* part_o;          // [slots][num_kv_heads][256 rows][D] (O / l) / sigma, fp16
   float* part_m;             // [slots][num_kv_heads][256 rows] reference maximum (log2 units)
   float* part_l;             // [slots][num_kv_heads][256 rows] sum of weights
+  float* part_s;             // [slots][num_kv_heads][256 rows] sigma: a power of two, 2^15 * sigma > max |O / l|
   int bt_stride;
   int num_tokens;
   int num_q_heads;
@@ -105,9 +106,10 @@ struct PrefillParams {
 struct PrefillMergeParams {
   void* out;
   const int32_t* qsl;
-  const uint16_t* part_o;    // fp16, divided by l
+  const uint16_t* part_o;    // (O / l) / sigma, fp16
   const float* part_m;
   const float* part_l;
+  const float* part_s;
   int num_q_heads;
   int num_kv_heads;
   int group;

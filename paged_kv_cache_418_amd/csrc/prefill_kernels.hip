@@ -595,33 +595,75 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   }
 
   // ---- epilogue.  The lane's outputs (d = n*32 + 8*(r/4) + 4*half + r%4 of row rl) are
-  // scattered 8-byte pieces of 32 rows; stored as they are, every store instruction would
-  // touch 32 lines.  Each wave stages its 32 rows in LDS (free now; 16-byte chunks XOR-
-  // swizzled by row so that the 8-byte writes spread over the banks) and stores whole
-  // rows from there: 16 bytes per lane, 64/kChunks rows per instruction.
+  // scattered pieces of 32 rows; stored as they are, every store instruction would touch 32
+  // lines.  Each wave stages its 32 rows in LDS (free now; 16-byte chunks XOR-swizzled by
+  // row so that the writes spread over the banks) and stores whole rows from there, 16
+  // bytes per lane.  A whole row tile stores bf16 outputs; a split piece stores O / l in
+  // fp16 with a per-row scale (below), its reference maximum m and weight sum l, for the
+  // merge.
   __syncthreads();  // every wave is done with the rings
   if (!wave_live) return;
   const float l = sum_halves(lsum);
-  const float inv = whole ? p.v_scale / l : (l > 0.f ? 1.f / l : 0.f);  // rows without a position: never stored
+  const float inv = whole ? p.v_scale / l : (l > 0.f ? 1.f / l : 0.f);  // a row that saw no key stores 0
+  const size_t slot_row0 = ((size_t)(p.item_base + item_idx) * p.num_kv_heads + kvh) * kPrefillRows + 32 * wave;
+  if (whole) {
+    unsigned char* const stage = smem + wave * 32 * Sh::kRowBytes;
+#pragma unroll
+    for (int n = 0; n < Sh::kDTiles; ++n)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int chunk = (n * 4 + rq) ^ (rl % Sh::kChunks);
+        const float a0 = acc[n][4 * rq] * inv, a1 = acc[n][4 * rq + 1] * inv;
+        const float a2 = acc[n][4 * rq + 2] * inv, a3 = acc[n][4 * rq + 3] * inv;
+        *reinterpret_cast<u32x2*>(stage + rl * Sh::kRowBytes + chunk * 16 + half * 8) =
+            u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int kRowsPerStore = 64 / Sh::kChunks;
+    const int sc_chunk = lane % Sh::kChunks;
+#pragma unroll
+    for (int it = 0; it < 32 / kRowsPerStore; ++it) {
+      const int row = it * kRowsPerStore + lane / Sh::kChunks;
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(stage + row * Sh::kRowBytes + ((sc_chunk ^ (row % Sh::kChunks)) << 4));
+      const int Rw = 32 * wave + row;
+      if (Rw >= P * G || pos0 + Rw / G >= pos_end) continue;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) +
+                      ((size_t)(q0 + pos0 + Rw / G) * p.num_q_heads + kvh * G + Rw % G) * D;
+      *reinterpret_cast<u32x4*>(dst + sc_chunk * 8) = v;
+    }
+    return;
+  }
+  // split piece: O / l in fp16 scaled by a per-row power of two sigma = 2^(E-15), where
+  // 2^(E-1) <= the row's largest |O / l| < 2^E, so every stored value is below 2^15 (fp16
+  // holds up to 65504) and the rounding error is at most 2^-11 of that largest magnitude,
+  // whatever the range of V.  sigma goes to the merge beside m and l.
+  float amax = 0.f;
+#pragma unroll
+  for (int n = 0; n < Sh::kDTiles; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[n][r]));
+  amax = max_halves(amax) * inv;  // the row's two lanes hold its D values between them
+  int e2 = 0;
+  (void)frexpf(amax, &e2);  // amax = f * 2^e2, f in [0.5, 1) (e2 = 0 for amax = 0)
+  const float sigma = ldexpf(1.f, e2 - 15);
+  const float mul = inv * ldexpf(1.f, 15 - e2);
   unsigned char* const stage = smem + wave * 32 * Sh::kRowBytes;
 #pragma unroll
   for (int n = 0; n < Sh::kDTiles; ++n)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int chunk = (n * 4 + rq) ^ (rl % Sh::kChunks);
-      const float a0 = acc[n][4 * rq] * inv, a1 = acc[n][4 * rq + 1] * inv;
-      const float a2 = acc[n][4 * rq + 2] * inv, a3 = acc[n][4 * rq + 3] * inv;
-      // split pieces keep O / l in fp16: bounded by the largest |V| of the row's keys, a
-      // relative error of 2^-11 (a row that saw none of its keys stores 0; its m is -inf)
-      const u32x2 v = whole ? u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)}
-                            : u32x2{pack_f16x2(a0, a1), pack_f16x2(a2, a3)};
-      *reinterpret_cast<u32x2*>(stage + rl * Sh::kRowBytes + chunk * 16 + half * 8) = v;
+      const float a0 = acc[n][4 * rq] * mul, a1 = acc[n][4 * rq + 1] * mul;
+      const float a2 = acc[n][4 * rq + 2] * mul, a3 = acc[n][4 * rq + 3] * mul;
+      *reinterpret_cast<u32x2*>(stage + rl * Sh::kRowBytes + chunk * 16 + half * 8) =
+          u32x2{pack_f16x2(a0, a1), pack_f16x2(a2, a3)};
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // partial results of a split row tile: slot (launch base + item) x kv head x row
-  const size_t slot_row0 = ((size_t)(p.item_base + item_idx) * p.num_kv_heads + kvh) * kPrefillRows + 32 * wave;
   constexpr int kRowsPerStore = 64 / Sh::kChunks;
   const int sc_chunk = lane % Sh::kChunks;
 #pragma unroll
@@ -631,22 +673,24 @@ __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
         *reinterpret_cast<const u32x4*>(stage + row * Sh::kRowBytes + ((sc_chunk ^ (row % Sh::kChunks)) << 4));
     const int Rw = 32 * wave + row;
     if (Rw >= P * G || pos0 + Rw / G >= pos_end) continue;
-    uint16_t* dst = whole ? reinterpret_cast<uint16_t*>(p.out) +
-                                ((size_t)(q0 + pos0 + Rw / G) * p.num_q_heads + kvh * G + Rw % G) * D
-                          : p.part_o + (slot_row0 + row) * D;
-    *reinterpret_cast<u32x4*>(dst + sc_chunk * 8) = v;
+    *reinterpret_cast<u32x4*>(p.part_o + (slot_row0 + row) * D + sc_chunk * 8) = v;
   }
-  if (!whole && half == 0 && row_ok) {
+  if (half == 0 && row_ok) {
     p.part_m[slot_row0 + rl] = m_ref;
     p.part_l[slot_row0 + rl] = l;
+    p.part_s[slot_row0 + rl] = sigma;
   }
 }
 
 // Log-sum-exp merge of the splits of a row tile: grid (row tiles x 8 groups of 32 rows,
 // kv heads), 256 threads.  A wave takes 8 rows; D/8 lanes cover one row, 8 elements (16
 // bytes of fp16 partial, 16 bytes of bf16 output) each, so every load and store moves whole
-// rows.  Split i of a row holds O_i / l_i with its reference maximum m_i (log2 units) and
-// weight sum l_i; it enters with weight l_i * 2^(m_i - M), folded online over the splits.
+// rows.  Split i of a row holds (O_i / l_i) / sigma_i in fp16 with its scale sigma_i, its
+// reference maximum m_i (log2 units) and weight sum l_i; it enters with weight
+// l_i * 2^(m_i - M), folded online over the splits.  A split that saw none of the row's keys
+// (m_i = -inf), or whose weight underflows to 0 next to the running maximum, is skipped
+// rather than multiplied, so no 0 * inf can arise.  The split holding the row's largest
+// score has l_i >= 1, so the weight sum is never 0.
 template <int D>
 __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p) {
   constexpr int kLanesPerRow = D / 8;
@@ -676,16 +720,19 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
 #pragma unroll 4
     for (int i = 0; i < n; ++i) {
       const size_t pi = base + i * slot_step;
-      const float mi = p.part_m[pi], li = p.part_l[pi];
+      const float mi = p.part_m[pi], li = p.part_l[pi], si = p.part_s[pi];
       const u32x4 w = *reinterpret_cast<const u32x4*>(p.part_o + pi * D + c * 8);
       if (mi == -INFINITY) continue;  // this split saw none of the row's keys
       const float Mn = fmaxf(M, mi);
-      const float a = fast_exp2(M - Mn), b = li * fast_exp2(mi - Mn);
+      const float b = li * fast_exp2(mi - Mn);
+      if (b == 0.f) continue;  // negligible next to the running maximum (then Mn == M)
+      const float a = fast_exp2(M - Mn);  // 0 for the first split that counts
+      const float bs = b * si;
       den = den * a + b;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        o[2 * j] = o[2 * j] * a + f16_bits_to_f32(w[j] & 0xFFFFu) * b;
-        o[2 * j + 1] = o[2 * j + 1] * a + f16_bits_to_f32(w[j] >> 16) * b;
+        o[2 * j] = o[2 * j] * a + f16_bits_to_f32(w[j] & 0xFFFFu) * bs;
+        o[2 * j + 1] = o[2 * j + 1] * a + f16_bits_to_f32(w[j] >> 16) * bs;
       }
       M = Mn;
     }

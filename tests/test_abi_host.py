@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 41
+    assert len(syms) == 42
     assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
@@ -112,11 +112,11 @@ def _host_i32(vals):
     return arr
 
 
-def _prefill(lib, qsl, sl, dtype=b.PA_BF16, T=None, ws=FAKE, wsb=1 << 30, bt_stride=64):
+def _prefill(lib, qsl, sl, dtype=b.PA_BF16, T=None, ws=FAKE, wsb=1 << 30, bt_stride=64, scale=0.088):
     q, s = _host_i32(qsl), _host_i32(sl)
     T = qsl[-1] if T is None else T
     return lib.pa_prefill_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, bt_stride, FAKE, FAKE, ctypes.addressof(s),
-                                 ctypes.addressof(q), len(sl), T, 32, 8, 128, 16, 1000, 0.088, dtype, ws, wsb, None)
+                                 ctypes.addressof(q), len(sl), T, 32, 8, 128, 16, 1000, scale, dtype, ws, wsb, None)
 
 
 def test_prefill_rejects(lib):
@@ -127,6 +127,9 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, [0, 5, 9], [10, 10], dtype=b.PA_F32) == 3  # chunks need bf16
     assert _prefill(lib, [0, 1, 2], [3000, 10], ws=None, bt_stride=256) == 4  # decode rows over 512 need scratch
     assert _prefill(lib, [0, 5, 9], [2000, 10], bt_stride=64) == 2  # more blocks than table columns
+    assert _prefill(lib, [0, 5, 9], [10, 10], scale=0.0) == 2       # the scale must be positive
+    assert _prefill(lib, [0, 5, 9], [10, 10], scale=-0.088) == 2
+    assert _prefill(lib, [0, 1, 2], [10, 10], scale=-0.088) == 2   # decode rows only: the same contract
 
 
 def test_prefill_workspace_bytes(lib):
@@ -154,6 +157,41 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         pk.pa_slot_mapping(torch.zeros(2, 4, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                            torch.zeros(3, dtype=torch.int32), 2)
+
+
+@pytest.mark.parametrize("fn", ["reshape", "write_kv"])
+def test_binding_refuses_mismatched_kv_write(fn):
+    """The KV write copies rows byte for byte: rows and pools of different dtypes or [Hkv, D] are refused before
+    any device call (the tensors here are on the host, and the dtype checks come first)."""
+    import torch
+
+    def call(key, value, kc, vc, **kw):
+        if fn == "reshape":
+            if kw:
+                return pk.pa_reshape_and_cache_fp8(key, value, kc, vc, torch.zeros(2, dtype=torch.int32), **kw)
+            return pk.pa_reshape_and_cache(key, value, kc, vc, torch.zeros(2, dtype=torch.int32))
+        z = torch.zeros(2, dtype=torch.int32)
+        return pk.pa_write_kv(key, value, kc, vc, torch.zeros(1, 4, dtype=torch.int32), z[:1], z, 2, **kw)
+
+    bf, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+    k = torch.zeros(2, 8, 128, dtype=bf)
+    pool = torch.zeros(4, 16, 8, 128, dtype=bf)
+    with pytest.raises(ValueError, match="dtype"):
+        call(k, k, pool.float(), pool.float())                  # bf16 rows into an fp32 pool
+    with pytest.raises(ValueError, match="dtype"):
+        call(k.float(), k.float(), pool, pool)                  # fp32 rows into a bf16 pool
+    with pytest.raises(ValueError, match="dtype"):
+        call(k, k.float(), pool, pool)                          # key and value differ
+    with pytest.raises(ValueError, match="differ"):
+        call(k, k, torch.zeros(4, 16, 4, 128, dtype=bf), torch.zeros(4, 16, 4, 128, dtype=bf))  # [Hkv, D]
+    with pytest.raises(ValueError, match="uint8"):
+        call(k, k, pool, pool, k_scale=0.05, v_scale=0.04)     # fp8 scales with a bf16 pool
+    with pytest.raises(ValueError, match="uint8"):
+        call(k.to(u8), k.to(u8), pool.to(u8), pool.to(u8), k_scale=0.05, v_scale=0.04)  # codes as the source
+    with pytest.raises(ValueError, match="GPU tensor"):
+        call(k, k, pool, pool)                                  # consistent: only the host placement is refused
+    with pytest.raises(ValueError, match="GPU tensor"):
+        call(k.to(f32), k.to(f32), pool.to(u8), pool.to(u8), k_scale=0.05, v_scale=0.04)
 
 
 def test_timing_calls_without_a_gpu(lib):

@@ -548,6 +548,27 @@ def test_prefill_long_chunks_split_across_work_items(heads):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("vscale", [1e5, 1e6])
+def test_prefill_split_rows_keep_large_values(vscale):
+    """V far beyond fp16's range (|V| up to about 5e6) on row tiles split across work items: the split pieces'
+    partial outputs keep the unsplit path's fp32 range, so the merged rows stay finite and match the oracle.
+    Multiplying V by s multiplies the exact output by s and every rounding on the V side in proportion (the
+    probabilities do not change), so the bar is the bf16 tolerance times s."""
+    w = wl.build("prefill_long", seed=433, ctx_lens=[2200, 700, 1900], q_lens=[700, 1, 333], num_q_heads=32,
+                 num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    w = dataclasses.replace(w, v_cache=(w.v_cache.float() * vscale).to(torch.bfloat16),
+                            new_v=(w.new_v.float() * vscale).to(torch.bfloat16))
+    say("prefill split rows, |V| scaled by", vscale)
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e} (bar {TOL['bf16'] * vscale:.3e})")
+    assert err <= TOL["bf16"] * vscale
+
+
 # ------------------------------------------------------------------ sliding window
 # The row at position p sees positions max(0, p - W + 1) .. p (the oracle's reading of the pages' sliding-window
 # attention).  Table columns wholly before what the kernels read point at the NaN-filled poison block, so a read
