@@ -247,6 +247,25 @@ pa_status_t pa_decode_local(void* out, const void* query, const void* key_cache,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_static -- pa_decode that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, result and errors as pa_decode (without workspace and
+ * workspace_bytes).  Its scratch is a file-scope device array of the library,
+ * 32 MiB (33554432 bytes) per GPU, held from the first call on that GPU until
+ * the process ends; a batch whose pa_decode_workspace_bytes(...) exceeds it is
+ * refused with PA_ERR_WORKSPACE before anything is enqueued.  Every call on
+ * one GPU shares that array, which keeps the last call's contents (nothing in
+ * it needs to start at zero): calls that overlap on one GPU (on different
+ * streams, or from different threads) race and must not be issued.
+ */
+pa_status_t pa_decode_static(void* out, const void* query, const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                             pa_dtype_t dtype, int32_t num_splits, void* stream);
+
+/*
  * pa_decode_fp8 -- pa_decode over E4M3FN pools.  [B] tutorial 6.
  * K_j = decode(code) * k_scale, V_j = decode(code) * v_scale (exact values);
  * q_dtype (= out dtype): PA_BF16 or PA_F32 (fp32 queries are rounded to

@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
             "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
             "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32, P, sz,
                            P], ctypes.c_int),
+            "pa_decode_static": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32,
+                                  P], ctypes.c_int),
             "pa_decode_fp8": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, f32, f32,
                                i32, P, sz, P], ctypes.c_int),
             "pa_decode_cascade_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
@@ -264,6 +266,21 @@ def pa_decode(query, key_cache, value_cache, block_tables, seq_lens, scale: floa
         _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
         _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(key_cache),
         num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
+def pa_decode_static(query, key_cache, value_cache, block_tables, seq_lens, scale: float, max_seq_len: int,
+                     num_splits: int = 0, out=None):
+    """pa_decode with the library's static scratch (no workspace, no allocation by the library)."""
+    lib = load()
+    S, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    out = torch.empty_like(query) if out is None else out
+    _check("pa_decode_static", lib.pa_decode_static(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(key_cache),
+        num_splits, _stream()))
     return out
 
 

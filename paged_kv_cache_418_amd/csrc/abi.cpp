@@ -558,6 +558,42 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const
                     static_cast<hipStream_t>(stream));
 }
 
+pa_status_t pa_decode_static(void* out, const void* query, const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                             pa_dtype_t dtype, int32_t num_splits, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, nullptr, 0, /*need_override=*/0);
+  if (st != PA_OK) return st;
+  if (dtype == PA_BF16 && num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGqa);
+  const size_t need =
+      pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, num_splits);
+  if (need > pa::kStaticScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode_static: this batch needs %zu bytes of scratch, more than the library's static %zu "
+                "(use pa_decode with a workspace, or fewer sequences, heads or splits)",
+                need, pa::kStaticScratchBytes);
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  void* ws = nullptr;
+  if (need) {
+    st = hip_status(pa::static_scratch(&ws), "pa_decode_static: device address of the static scratch");
+    if (st != PA_OK) return st;
+  }
+  const int kind = dtype == PA_F32 ? pa::kF32 : pa::kBF16;
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, kind,
+                    dtype == PA_F32, 1.f, 1.f, num_splits, ws, need ? pa::kStaticScratchBytes : 0,
+                    static_cast<hipStream_t>(stream));
+}
+
 pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
                           const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

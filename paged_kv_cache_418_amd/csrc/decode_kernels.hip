@@ -27,6 +27,7 @@
 // operand layout, V is used from registers.  Masked positions (the partly
 // filled last block) are removed by selection, never by multiplying with
 // zero, so NaN in unused pool slots cannot leak.
+#include <mutex>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -715,6 +716,33 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of the decode entry point that allocates nothing (pa_decode_static): a
+// file-scope device array, one copy per GPU at its own address, held until the process
+// ends.  Host code never passes the array's name (a host-side stand-in) to a kernel: it
+// looks up the device address once per device, with that device current, and passes that.
+// Nothing in it needs to start at zero: the merge reads only what the decode launch before
+// it wrote.  Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream) {
   if (head_dim == 128) return launch_decode_d<128>(p, kv, stream);

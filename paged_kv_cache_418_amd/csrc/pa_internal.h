@@ -160,6 +160,12 @@ hipError_t launch_write_kv(const void* key, const void* value, int64_t key_strid
 // kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel)
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
 
+// The decode's static scratch (pa_decode_static): its size, and its device address on the
+// current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(void** ptr);
+
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
 // fp8 prefill: the blocks of every sequence with q_len > 1 copied, as the exact bf16
