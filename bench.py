@@ -448,7 +448,7 @@ def bench_mixed(args, result):
     st = Step(w)
     ms, _, per = time_steps(st, args.steps, args.warmup)
     kt_step = kernel_times(st, args.steps, ["reshape_and_cache", "decode", "decode_merge", "prefill",
-                                            "prefill_merge"])
+                                            "prefill_merge", "fused"])
     flops = wl.prefill_flops(w)
     rec, par = (None, None)
     if not args.no_cpu:

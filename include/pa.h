@@ -531,10 +531,22 @@ typedef enum pa_kernel {
   PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
   PA_K_PREFILL = 4,         /* the varlen prefill kernel */
   PA_K_PREFILL_MERGE = 5,   /* the log-sum-exp merge of split prefill row tiles */
-  PA_K_STAGE_FP8 = 6        /* the fp8 -> bf16 staging of chunk sequences in pa_prefill_varlen_fp8 */
+  PA_K_STAGE_FP8 = 6,       /* the fp8 -> bf16 staging of chunk sequences in pa_prefill_varlen_fp8 */
+  PA_K_FUSED = 7            /* decode rows and prefill chunks of a mixed batch in one launch (pa_prefill_varlen*) */
 } pa_kernel_t;
 
 pa_status_t pa_timing_enable(int on);
+
+/*
+ * pa_set_fused(mode) -- how pa_prefill_varlen* run a batch that has both decode rows and
+ * chunks: 0 = a decode launch, then a prefill launch; 1 = one launch holding both when the
+ * host estimate says it ends sooner (the default); 2 = one launch whenever it can hold the
+ * batch's prefill items (at most 440); -1 = follow the environment variable PA_FUSED
+ * (0 / 1 / 2, default 1).  The result does not depend on the mode beyond the last bits (the
+ * decode rows' split counts differ); the workspace size does, so query
+ * pa_prefill_varlen*_workspace_bytes under the same mode.  PA_ERR_SHAPE for other values.
+ */
+pa_status_t pa_set_fused(int mode);
 
 /*
  * pa_probe_mfma_peak -- measurement only (the denominator of a measured

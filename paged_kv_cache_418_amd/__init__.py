@@ -10,5 +10,6 @@ from ._binding import (  # noqa: F401
     pa_decode_workspace_bytes, pa_prefill_varlen, pa_prefill_varlen_fp8, pa_prefill_varlen_fp8_workspace_bytes,
     pa_prefill_varlen_local, pa_prefill_varlen_local_workspace_bytes, pa_prefill_varlen_window,
     pa_prefill_varlen_window_workspace_bytes, pa_prefill_varlen_workspace_bytes,
-    pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_write_kv, set_validate, timing_enable,
+    pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_write_kv, set_fused, set_validate,
+    timing_enable,
     timing_read, timing_reset)

@@ -23,7 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 KERNELS = {"slot_mapping": 0, "reshape_and_cache": 1, "decode": 2, "decode_merge": 3, "prefill": 4,
-           "prefill_merge": 5, "stage_fp8": 6}
+           "prefill_merge": 5, "stage_fp8": 6, "fused": 7}
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_WORKSPACE",
           5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_HIP", 7: "PA_ERR_NO_SPACE", 8: "PA_ERR_STATE"}
 
@@ -111,6 +111,7 @@ def load() -> ctypes.CDLL:
             "pa_pool_free_queue": ([P, P, i32], i32),
             "pa_probe_mfma_peak": ([P, i32, i32, P], ctypes.c_int),
             "pa_set_validate": ([ctypes.c_int], ctypes.c_int),
+            "pa_set_fused": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "pa_timing_reset": ([], ctypes.c_int),
             "pa_timing_read": ([ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
@@ -464,6 +465,12 @@ def set_validate(on: int) -> None:
     """1: check device metadata on the host before every call (PA_VALIDATE's checks); 0: trust it; -1: follow the
     PA_VALIDATE environment variable."""
     _check("pa_set_validate", load().pa_set_validate(int(on)))
+
+
+def set_fused(mode: int) -> None:
+    """How a batch with decode rows and chunks runs: 0 two launches, 1 one launch when estimated faster (default),
+    2 one launch whenever possible, -1 follow PA_FUSED."""
+    _check("pa_set_fused", load().pa_set_fused(int(mode)))
 
 
 def timing_enable(on: bool = True) -> None:

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["abi.cpp", "block_pool.cpp", "cache_kernels.hip", "decode_kernels.hip", "prefill_kernels.hip"]
+SOURCES = ["abi.cpp", "block_pool.cpp", "cache_kernels.hip", "decode_kernels.hip", "prefill_kernels.hip",
+           "fused_kernels.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [

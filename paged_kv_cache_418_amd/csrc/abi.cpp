@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <functional>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -59,6 +60,20 @@ pa_status_t hip_status(hipError_t e, const char* where) {
 
 // -1: follow PA_VALIDATE; 0 / 1: set by pa_set_validate
 std::atomic<int> g_validate_override{-1};
+
+// -1: follow PA_FUSED (default 1); 0 / 1 / 2 set by pa_set_fused
+std::atomic<int> g_fused_override{-1};
+
+int fused_mode() {
+  const int o = g_fused_override.load(std::memory_order_relaxed);
+  if (o >= 0) return o;
+  static const int env = [] {
+    const char* v = std::getenv("PA_FUSED");
+    const int x = v && *v ? std::atoi(v) : 1;
+    return x >= 0 && x <= 2 ? x : 1;
+  }();
+  return env;
+}
 
 bool validate_enabled() {
   const int o = g_validate_override.load(std::memory_order_relaxed);
@@ -249,13 +264,14 @@ CascadeLayout cascade_layout(int num_seqs, int num_q_heads, int num_kv_heads, in
   return L;
 }
 
-pa_status_t run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-                       const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, const int32_t* qsl,
-                       int32_t num_seqs, int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
-                       int q_f32, float k_scale, float v_scale, int32_t num_splits, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream, int32_t prefix_blocks = 0,
-                       int32_t sliding_window = 0, int32_t local_chunk = 0) {
+// The parameters of one decode launch (its share count and workspace layout).
+pa::DecodeParams make_decode_params(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                    const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                    const int32_t* qsl, int32_t num_seqs, int32_t num_rows, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len, float scale,
+                                    int kv_kind, int q_f32, float k_scale, float v_scale, int32_t num_splits,
+                                    void* workspace, int32_t prefix_blocks, int32_t sliding_window,
+                                    int32_t local_chunk) {
   // a window (or local chunk) of W keys spans at most W/16 + 2 blocks of each sequence
   const int vis = sliding_window > 0 ? sliding_window : local_chunk;
   const int span = vis > 0 ? std::min<int64_t>(max_seq_len, (int64_t)vis + 16) : max_seq_len;
@@ -276,7 +292,6 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.head_groups = (p.group + 15) / 16;  // 1 for a cascade (at most 16 q heads per kv head)
-  p.num_blocks = num_blocks;
   p.max_seq_len = max_seq_len;
   p.n_splits = n_splits;
   p.piece_cost = decode_piece_cost();
@@ -315,6 +330,21 @@ pa_status_t run_decode(void* out, const void* query, const void* key_cache, cons
     p.piece_first = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes);
     p.piece_last = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes + lay.idx_bytes);
   }
+  return p;
+}
+
+pa_status_t run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, const int32_t* qsl,
+                       int32_t num_seqs, int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
+                       int q_f32, float k_scale, float v_scale, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, int32_t prefix_blocks = 0,
+                       int32_t sliding_window = 0, int32_t local_chunk = 0) {
+  pa::DecodeParams p = make_decode_params(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, qsl,
+                                          num_seqs, num_rows, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                          scale, kv_kind, q_f32, k_scale, v_scale, num_splits, workspace,
+                                          prefix_blocks, sliding_window, local_chunk);
+  p.num_blocks = num_blocks;
   (void)workspace_bytes;
   (void)block_size;
   return hip_status(pa::launch_decode(p, kv_kind, head_dim, stream), "decode launch");
@@ -731,10 +761,13 @@ struct VarlenPlan {
   std::vector<uint64_t> items;   // split pieces first (grouped by row tile), then whole row tiles
   std::vector<uint64_t> merges;  // one per split row tile
   int n_split_items = 0;         // items that leave partial results (slots 0 .. n_split_items-1)
+  int max_item_tiles = 0;        // key tiles of the longest item
+  int64_t total_tiles = 0;       // key tiles of all items (one kv head)
 };
 
 pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_tokens, int bt_stride,
-                        int group, int num_kv_heads, VarlenPlan& plan, int window = 0, int chunk = 0) {
+                        int group, int num_kv_heads, VarlenPlan& plan, int window = 0, int chunk = 0,
+                        int items_per_head = 0) {
   if (qsl[0] != 0) return fail(PA_ERR_SHAPE, "query_start_loc_host[0] = %d, expected 0", qsl[0]);
   const int P = pa::kPrefillRows / group;
   plan.tile_positions = P;
@@ -776,7 +809,8 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
   // pieces, ceil(n_kt / budget) per row tile, number at most target_items.  With at least
   // as many row tiles as that, nothing is split (the longest-first list keeps the compute
   // units busy by itself).  The piece count does not grow with the budget: bisection.
-  const int64_t target_items = std::max<int64_t>(1, device_cu_count() / std::max(1, num_kv_heads));
+  const int64_t target_items =
+      items_per_head > 0 ? items_per_head : std::max<int64_t>(1, device_cu_count() / std::max(1, num_kv_heads));
   int max_kt = 1;
   for (const RowTile& t : tiles) max_kt = std::max(max_kt, t.n_kt);
   auto pieces = [&](int b) {
@@ -815,6 +849,9 @@ pa_status_t plan_varlen(const int32_t* qsl, const int32_t* sl, int num_seqs, int
   }
   plan.n_split_items = (int)plan.items.size();
   plan.items.insert(plan.items.end(), whole_items.begin(), whole_items.end());
+  plan.total_tiles = total;
+  for (const uint64_t it : plan.items)
+    plan.max_item_tiles = std::max(plan.max_item_tiles, (int)(it >> 48) - (int)((it >> 32) & 0xFFFFu));
   return PA_OK;
 }
 
@@ -839,16 +876,103 @@ size_t varlen_workspace(const VarlenPlan& plan, int num_seqs, int num_q_heads, i
   return align_up(dec) + prefill_layout(plan.n_split_items, num_kv_heads, head_dim).total;
 }
 
+// A batch with decode rows and prefill chunks runs both in one launch (launch_fused) when
+// the host estimate says that ends sooner than the two launches one after the other.  The
+// estimate (measured on the MI355X with the mixed continuous-batching step): the decode
+// work-groups stream K/V at PA_FUSED_CU_GBPS (default 29 GB/s) per compute unit they hold,
+// up to PA_FUSED_DECODE_GBPS (default 6000 GB/s) in all; a prefill work item takes
+// PA_FUSED_TILE_NS (default 2200 ns) per 64-key tile plus 5 us, and the items of each kv
+// head go longest first to the least loaded of the compute units left to them.  The decode
+// work-groups get Q compute units and the prefill items the rest, for the Q (multiples of 8
+// from a quarter of the device) that minimises the larger of the two times (the largest
+// such Q).  PA_FUSED=0 turns fusing off, 2 fuses every batch it can (pa_set_fused switches
+// the same at run time); PA_FUSED_DECODE_CUS fixes Q (measurement).
+struct StepPlan {
+  VarlenPlan plan;
+  bool fused = false;
+  int n_decode_wgs = 0;   // decode work-groups of the fused launch
+  int decode_splits = 0;  // decode shares per column of the fused launch
+};
+
+constexpr int kFusedDecodeWaves = 8;  // decode waves per work-group of a fused launch
+
+pa_status_t plan_step(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_tokens, int bt_stride,
+                      int num_q_heads, int num_kv_heads, int head_dim, int kv_elem, int window, int chunk,
+                      StepPlan& sp) {
+  const int group = num_q_heads / num_kv_heads;
+  pa_status_t st = plan_varlen(qsl, sl, num_seqs, num_tokens, bt_stride, group, num_kv_heads, sp.plan, window, chunk);
+  if (st != PA_OK) return st;
+  const int mode = fused_mode();
+  if (mode == 0 || !sp.plan.any_decode || sp.plan.items.empty() ||
+      sp.plan.items.size() > (size_t)pa::kMaxPrefillItems)
+    return PA_OK;
+  static const double tile_s = env_int("PA_FUSED_TILE_NS", 2200, 100, 1000000) * 1e-9;
+  static const double bw = env_int("PA_FUSED_DECODE_GBPS", 6000, 100, 100000) * 1e9;
+  static const double bw_cu = env_int("PA_FUSED_CU_GBPS", 29, 1, 100000) * 1e9;
+  const double item_s = 5e-6;
+  const int C = device_cu_count();
+  double dec_bytes = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    if (qsl[s + 1] - qsl[s] != 1) continue;
+    const int vis_lim = window > 0 ? window + 16 : chunk > 0 ? chunk + 16 : INT32_MAX;
+    dec_bytes += 2.0 * std::min(sl[s], vis_lim) * num_kv_heads * head_dim * kv_elem;
+  }
+  auto t_dec = [&](int q) { return dec_bytes / std::min(bw, bw_cu * q); };
+  // the kv heads' items run side by side (the grid interleaves them), each head on cus / Hkv
+  // compute units: greedy longest-first makespan of one head's items
+  auto t_pre = [&](const VarlenPlan& pl, int cus) {
+    const int slots = std::max(1, cus / num_kv_heads);
+    std::vector<double> load(slots, 0.0);
+    std::vector<int> tiles;
+    tiles.reserve(pl.items.size());
+    for (const uint64_t it : pl.items) tiles.push_back((int)(it >> 48) - (int)((it >> 32) & 0xFFFFu));
+    std::sort(tiles.begin(), tiles.end(), std::greater<int>());
+    for (const int t : tiles) {
+      double& lo = *std::min_element(load.begin(), load.end());
+      lo += t * tile_s + item_s;
+    }
+    return *std::max_element(load.begin(), load.end());
+  };
+  const double t_seq = dec_bytes / bw + t_pre(sp.plan, C);
+  double best = mode == 2 ? 1e30 : t_seq * 0.95;  // fuse only for a clear gain (mode 2: always)
+  int best_q = 0;
+  VarlenPlan best_plan;
+  const std::string saved = g_last_error;
+  static const int forced_q = env_int("PA_FUSED_DECODE_CUS", 0, 0, 1 << 20);  // measurement: fix Q
+  for (int q = std::max(8, C / 4); q <= C - num_kv_heads; q += 8) {
+    if (forced_q > 0 && q != forced_q) continue;
+    const int cus = C - q;
+    VarlenPlan pl;
+    if (plan_varlen(qsl, sl, num_seqs, num_tokens, bt_stride, group, num_kv_heads, pl, window, chunk,
+                    std::max(1, cus / num_kv_heads)) != PA_OK ||
+        pl.items.size() > (size_t)pa::kMaxPrefillItems)
+      continue;
+    const double t = std::max(t_dec(q), t_pre(pl, cus));
+    if (t <= best || forced_q > 0) {  // ties: the larger share for the decode stream
+      best = t;
+      best_q = q;
+      best_plan = std::move(pl);
+    }
+  }
+  g_last_error = saved;
+  if (best_q == 0) return PA_OK;
+  sp.fused = true;
+  sp.plan = std::move(best_plan);
+  sp.n_decode_wgs = best_q;
+  sp.decode_splits = std::max(1, best_q * kFusedDecodeWaves / decode_columns(num_q_heads, num_kv_heads));
+  return PA_OK;
+}
+
 // pa_prefill_varlen(_window)_workspace_bytes without the argument checks.
 size_t varlen_workspace_bytes(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_q_heads, int num_kv_heads,
-                              int head_dim, int window, int chunk = 0) {
-  VarlenPlan plan;
+                              int head_dim, int window, int chunk = 0, int kv_elem = 2) {
+  StepPlan sp;
   const std::string saved = g_last_error;
-  const pa_status_t st = plan_varlen(qsl, sl, num_seqs, qsl[num_seqs], INT32_MAX, num_q_heads / num_kv_heads,
-                                     num_kv_heads, plan, window, chunk);
+  const pa_status_t st = plan_step(qsl, sl, num_seqs, qsl[num_seqs], INT32_MAX, num_q_heads, num_kv_heads, head_dim,
+                                   kv_elem, window, chunk, sp);
   g_last_error = saved;
   if (st != PA_OK) return 0;
-  return varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
+  return varlen_workspace(sp.plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
 }
 
 // fp8 prefill staging: bf16 copies of the blocks of every chunk sequence (q_len > 1), then
@@ -898,10 +1022,11 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   // the prefill kernel masks raw scores and applies the scale inside exp2(s * scale - m),
   // which orders the scores correctly only for a positive scale
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(PA_ERR_SHAPE, "scale must be positive and finite");
-  VarlenPlan plan;
-  st = plan_varlen(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride,
-                   num_q_heads / num_kv_heads, num_kv_heads, plan, sliding_window, local_chunk);
+  StepPlan sp;
+  st = plan_step(query_start_loc_host, seq_lens_host, num_seqs, num_tokens, bt_stride, num_q_heads, num_kv_heads,
+                 head_dim, kv_kind == pa::kFP8 ? 1 : 2, sliding_window, local_chunk, sp);
   if (st != PA_OK) return st;
+  const VarlenPlan& plan = sp.plan;
   if (dtype == PA_F32 && !plan.items.empty())
     return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
   const StageLayout stage = kv_kind == pa::kFP8 ? stage_layout(query_start_loc_host, seq_lens_host, num_seqs, bt_stride,
@@ -927,11 +1052,12 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     if (st != PA_OK) return st;
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (plan.any_decode) {
+  const int dec_kind = kv_kind == pa::kFP8 ? pa::kFP8 : (dtype == PA_F32 ? pa::kF32 : pa::kBF16);
+  if (plan.any_decode && !sp.fused) {
     st = run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
                     num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, plan.max_decode_len, scale,
-                    kv_kind == pa::kFP8 ? pa::kFP8 : (dtype == PA_F32 ? pa::kF32 : pa::kBF16), dtype == PA_F32,
-                    k_scale, v_scale, 0, workspace, workspace_bytes, hs, 0, sliding_window, local_chunk);
+                    dec_kind, dtype == PA_F32, k_scale, v_scale, 0, workspace, workspace_bytes, hs, 0, sliding_window,
+                    local_chunk);
     if (st != PA_OK) return st;
   }
   auto* ws = static_cast<unsigned char*>(workspace);
@@ -964,8 +1090,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     p_tables = st_tables;
     p_num_blocks = stage.blocks;
   }
-  for (size_t i0 = 0; i0 < plan.items.size(); i0 += pa::kMaxPrefillItems) {
-    pa::PrefillParams p{};
+  auto prefill_params = [&](size_t i0, pa::PrefillParams& p) {
     p.out = out;
     p.query = query;
     p.key_cache = pk_cache;
@@ -992,8 +1117,29 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     const size_t n = std::min(plan.items.size() - i0, (size_t)pa::kMaxPrefillItems);
     p.n_items = (int)n;
     std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint64_t));
-    st = hip_status(pa::launch_prefill(p, head_dim, hs), "prefill launch");
+  };
+  if (sp.fused) {  // decode waves and prefill items in one launch (plan_step keeps the items to one launch)
+    pa::FusedParams f{};
+    f.dec = make_decode_params(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens,
+                               query_start_loc, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                               plan.max_decode_len, scale, dec_kind, dtype == PA_F32, k_scale, v_scale,
+                               sp.decode_splits, workspace, 0, sliding_window, local_chunk);
+    f.dec.num_blocks = num_blocks;
+    prefill_params(0, f.pre);
+    f.decode_waves_per_wg = kFusedDecodeWaves;
+    f.decode_waves = (f.dec.prefix_waves + f.dec.n_splits) * decode_columns(num_q_heads, num_kv_heads);
+    f.n_decode_wgs = (f.decode_waves + kFusedDecodeWaves - 1) / kFusedDecodeWaves;
+    st = hip_status(pa::launch_fused(f, head_dim, kv_kind == pa::kFP8, hs), "fused decode + prefill launch");
     if (st != PA_OK) return st;
+    st = hip_status(pa::launch_decode_merge(f.dec, head_dim, hs), "decode merge launch");
+    if (st != PA_OK) return st;
+  } else {
+    for (size_t i0 = 0; i0 < plan.items.size(); i0 += pa::kMaxPrefillItems) {
+      pa::PrefillParams p{};
+      prefill_params(i0, p);
+      st = hip_status(pa::launch_prefill(p, head_dim, hs), "prefill launch");
+      if (st != PA_OK) return st;
+    }
   }
   for (size_t i0 = 0; i0 < plan.merges.size(); i0 += pa::kMaxPrefillItems) {
     pa::PrefillMergeParams p{};
@@ -1147,10 +1293,11 @@ pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* ke
 size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
                                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                              int32_t head_dim, int32_t bt_stride) {
-  const size_t base = pa_prefill_varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads,
-                                                        num_kv_heads, head_dim);
-  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_kv_heads < 1 || head_dim < 1 || bt_stride < 1)
-    return base;
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      head_dim < 1 || bt_stride < 1 || num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return 0;
+  const size_t base = varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
+                                             head_dim, 0, 0, /*kv_elem=*/1);
   const StageLayout stage = stage_layout(query_start_loc_host, seq_lens_host, num_seqs, bt_stride, num_kv_heads,
                                          head_dim);
   return stage.total ? align_up(base) + stage.total : base;
@@ -1258,6 +1405,12 @@ extern "C" {
 
 pa_status_t pa_set_validate(int on) {
   g_validate_override.store(on < 0 ? -1 : (on != 0 ? 1 : 0), std::memory_order_relaxed);
+  return ok();
+}
+
+pa_status_t pa_set_fused(int mode) {
+  if (mode < -1 || mode > 2) return fail(PA_ERR_SHAPE, "pa_set_fused: mode %d outside -1 .. 2", mode);
+  g_fused_override.store(mode, std::memory_order_relaxed);
   return ok();
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -88,5 +90,15 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Calls f(integral_constant<int, i>) for i = I .. N-1 (unrolled at compile time).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 
 }  // namespace pa

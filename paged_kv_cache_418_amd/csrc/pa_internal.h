@@ -18,7 +18,8 @@ constexpr int kMaxGqa = 256;        // q heads per kv head: decode takes them 16
                                     // at least one position of them into a 256-row tile
 constexpr int kPrefillRows = 256;   // (position, q head) rows per prefill work-group (8 waves x 32)
 constexpr int kPrefillKeys = 64;    // keys per LDS tile in prefill
-constexpr int kMaxPrefillItems = 480;  // work items per launch (kernel-argument space)
+constexpr int kMaxPrefillItems = 440;  // work items per launch (kernel-argument space: a fused launch
+                                       // carries them beside the decode parameters in 4 KB)
 
 enum Dtype { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
@@ -119,6 +120,20 @@ struct PrefillMergeParams {
   uint64_t items[kMaxPrefillItems];
 };
 
+// One launch of decode waves and prefill items (a mixed batch): grid (n_decode_wgs +
+// pre.n_items * pre.num_kv_heads) x 512 threads.  Work-group w < n_decode_wgs runs decode
+// waves g = w * decode_waves_per_wg + wave (< decode_waves), each the decode kernel's wave
+// (share g / Y, column g % Y, Y = num_kv_heads * head_groups); the others run prefill items
+// (item (w - n_decode_wgs) / num_kv_heads of kv head (w - n_decode_wgs) % num_kv_heads).
+struct FusedParams {
+  DecodeParams dec;
+  PrefillParams pre;
+  int n_decode_wgs;
+  int decode_waves_per_wg;   // 1 .. 8
+  int decode_waves;          // (prefix_waves + n_splits) * Y
+};
+static_assert(sizeof(FusedParams) <= 4096, "kernel arguments of a fused launch exceed 4 KB");
+
 // Optional kernel timing (pa_timing_enable): a launch site brackets its
 // kernel with timing_mark(id, true/false, stream); a no-op unless enabled.
 enum KernelId {
@@ -129,7 +144,8 @@ enum KernelId {
   kKPrefill = 4,
   kKPrefillMerge = 5,
   kKStageFp8 = 6,
-  kNumKernelIds = 7
+  kKFused = 7,
+  kNumKernelIds = 8
 };
 void timing_mark(int kernel, bool begin, hipStream_t stream);
 
@@ -159,6 +175,11 @@ hipError_t launch_write_kv(const void* key, const void* value, int64_t key_strid
 
 // kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel)
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
+// the log-sum-exp merge of a decode launch's split sequences alone (after a fused launch)
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t stream);
+// decode waves and prefill items in one launch; fp8: the decode waves read E4M3 pools (the
+// prefill items read the bf16 pools named in f.pre, the staging pool for fp8 batches)
+hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_t stream);
 
 // The decode's static scratch (pa_decode_static): its size, and its device address on the
 // current device (looked up once per device).

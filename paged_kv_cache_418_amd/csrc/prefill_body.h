@@ -1,0 +1,651 @@
+// Device code of the varlen prefill (included by the prefill kernels and by the fused
+// decode + prefill kernel).  What is computed and the tiling are described at the top of
+// prefill_kernels.hip.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+template <int D>
+struct PrefillShape {
+  static constexpr int kThreads = 512;                 // 8 waves x 32 rows = kPrefillRows rows
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kKeys = kPrefillKeys;           // keys per K/V tile
+  static constexpr int kRowBytes = D * 2;              // one key row of a tile
+  static constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row (the swizzle period)
+  static constexpr int kTileBytes = kKeys * kRowBytes; // one tensor of one tile
+  static constexpr int kKSlots = 4;                    // K ring: K(t+3) is copied at step t
+  static constexpr int kVSlots = 3;                    // row-major V ring: V(t+3) copied at step t
+  static constexpr int kVtSlots = 3;                   // V^T ring (64 keys x D, 128-byte rows)
+  static constexpr int kVtRowBytes = kKeys * 2;        // one d row of a V^T tile
+  static constexpr int kTransposes = D / 32;           // 512-byte transposing reads per wave per tile
+  static constexpr int kLdsBytes = (kKSlots + kVSlots + kVtSlots) * kTileBytes;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;           // rows one wave-wide 1 KB copy fills
+  static constexpr int kCopies = kTileBytes / 1024 / kWaves;      // copies per wave per tensor per tile
+  static constexpr int kKSteps = D / 16;               // 32x32x16 MFMAs over d
+  static constexpr int kDTiles = D / 32;               // 32-wide d tiles of O^T
+};
+
+__device__ __forceinline__ bf16x8 u4_to_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float max_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+#define PA_LDS __attribute__((address_space(3)))
+#define PA_GLOBAL __attribute__((address_space(1)))
+
+// Waits until at most n vector-memory instructions of this wave are outstanding
+// (s_waitcnt with only the vmcnt field active; gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Same, and also waits for all of this wave's LDS (and scalar-memory) operations.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// WINDOW: a lower edge on the visible keys as well -- a sliding window (p.window > 0: the
+// row at p sees p-window+1 .. p) or chunked local attention (p.chunk > 0: C*(p div C) .. p)
+// -- a variant of its own so that the plain causal kernel keeps its register budget.
+// One work item of a prefill launch: item item_idx (its bits as in PrefillParams) for kv head
+// kvh, by a work-group of PrefillShape<D>::kThreads threads with smem =
+// PrefillShape<D>::kLdsBytes bytes of LDS.
+template <int D, bool WINDOW>
+__device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned char* smem, int item_idx, int kvh) {
+  using Sh = PrefillShape<D>;
+
+  // ---- work item
+  const uint64_t item = p.items[item_idx];
+  const int s = (int)(item & 0x7FFFu);
+  const bool whole = (item >> 15) & 1u;
+  const int rt = (int)((item >> 16) & 0xFFFFu);
+  const int kt0 = (int)((item >> 32) & 0xFFFFu), kt1 = (int)(item >> 48);
+  const int G = p.group;
+  const int P = p.tile_positions;         // positions per row tile (rows = P * G <= 256)
+  const int q0 = p.qsl[s];
+  const int q_len = p.qsl[s + 1] - q0;
+  const int L = p.seq_lens[s];
+  const int c = L - q_len;
+  const int pos0 = rt * P;
+  const int pos_end = min(q_len, pos0 + P);  // positions of this tile: pos0 .. pos_end-1
+  const int kv_end = c + pos_end;            // keys the last row sees (exclusive)
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, rl = lane & 31;
+
+  // ---- the lane's row: R = 32*wave + rl -> (position pos0 + R / G, q head kvh*G + R % G)
+  const int R = 32 * wave + rl;
+  const bool row_ok = R < P * G && pos0 + R / G < pos_end;
+  const int row_pos = c + pos0 + R / G;  // absolute position: keys <= it are visible
+  // smallest and largest row position of the wave (masking and skipping whole tiles)
+  const int wave_first = c + pos0 + (32 * wave) / G;
+  const int wave_last = c + min(pos_end - 1, pos0 + (32 * wave + 31) / G);
+  const bool wave_live = 32 * wave < P * G && pos0 + (32 * wave) / G < pos_end;
+  // WINDOW: first visible key of the row at position q (non-decreasing in q)
+  auto first_visible = [&](int q) { return p.chunk > 0 ? q - q % p.chunk : q - p.window + 1; };
+  const uint32_t row_span = WINDOW ? (uint32_t)(row_pos - first_visible(row_pos) + 1) : 0u;  // keys the row sees
+  const int wave_lo_max = WINDOW ? first_visible(wave_last) : 0;  // largest first visible key of the wave
+
+  // ---- copy role: each wave copies kCopies 1 KB slabs of K and of V per tile.  Slab
+  // kCopies*wave + i holds rows kRowsPerCopy*(kCopies*wave + i) ...; lane = (row in slab,
+  // physical chunk); the chunk it fetches is the logical chunk stored in that slot,
+  // physical ^ (row % kChunks).  All rows of a wave's slabs lie in one paged block.
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
+  const size_t tok_stride = (size_t)p.num_kv_heads * D * 2;
+  const int lanes_per_row = Sh::kChunks;
+  const int copy_row0 = Sh::kRowsPerCopy * Sh::kCopies * wave;  // first row of this wave's slabs
+  // Keys no row of the tile sees are not read from the pool: those past the last visible
+  // key and, with a sliding window, those before the first row's first visible key (their
+  // blocks may have been given up).  Their rows copy a filler key that is always written
+  // and finite -- key 0, or with a window the last visible key -- and their scores are
+  // masked, so the probabilities that meet the filler are 0.
+  const int fill_key = WINDOW ? kv_end - 1 : 0;
+  const int key_first = WINDOW ? first_visible(c + pos0) : 0;
+  const int bt_fill = min(max(bt[fill_key >> 4], 0), p.num_blocks - 1);
+  // Physical block of this wave's rows of a tile.  The load is unconditional (a key past
+  // the last visible one reads the last visible key's entry; any entry read is clamped
+  // into the pool), so the compiler can count it among the loads in flight.
+  auto block_of = [&](int tile) { return bt[min(tile * Sh::kKeys + copy_row0, kv_end - 1) >> 4]; };
+  // Slab i (0 .. kCopies-1) of this wave's part of one tensor of a tile.
+  auto copy_slab = [&](const uint8_t* base, int tile, int phys, unsigned char* st, int i) {
+    phys = min(max(phys, 0), p.num_blocks - 1);
+    const int row = copy_row0 + Sh::kRowsPerCopy * i + lane / lanes_per_row;
+    const int slot = lane % lanes_per_row;
+    const int chunk = slot ^ (row % Sh::kChunks);
+    const int key = tile * Sh::kKeys + row;
+    const bool live = key < kv_end && (!WINDOW || key >= key_first);
+    const int ph = live ? phys : bt_fill;
+    const size_t off = ((size_t)ph * 16 + ((live ? key : fill_key) & 15)) * tok_stride + (size_t)kvh * D * 2 +
+                       chunk * 16;
+    unsigned char* dst = st + (copy_row0 + Sh::kRowsPerCopy * i) * Sh::kRowBytes;
+    __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(base + off), (void PA_LDS*)dst, 16, 0, 0);
+  };
+  auto copy_rows = [&](const uint8_t* base, int tile, int phys, unsigned char* st) {
+#pragma unroll
+    for (int i = 0; i < Sh::kCopies; ++i) copy_slab(base, tile, phys, st, i);
+  };
+  // LDS: a ring of four K tiles (tile t in slot (t - kt0) % 4), a ring of three row-major
+  // V tiles and a ring of three transposed V tiles (tile t in slot (t - kt0) % 3).
+  auto k_stage = [&](int tile) { return smem + ((tile - kt0) & 3) * Sh::kTileBytes; };
+  auto v_stage = [&](int tile) { return smem + (Sh::kKSlots + (tile - kt0) % 3) * Sh::kTileBytes; };
+  auto k_addr = [&](int tile) { return (uint32_t)(uintptr_t)k_stage(tile); };
+  auto v_addr = [&](int tile) { return (uint32_t)(uintptr_t)v_stage(tile); };
+  auto vt_addr = [&](int tile) {
+    return (uint32_t)(uintptr_t)(smem + (Sh::kKSlots + Sh::kVSlots + (tile - kt0) % 3) * Sh::kTileBytes);
+  };
+
+  // block ids of the first four tiles, read before Q so the first copies wait only for them
+  const int ph0 = block_of(kt0), ph1 = block_of(kt0 + 1), ph2 = block_of(kt0 + 2);
+  int phys_next = block_of(kt0 + 3);
+
+  // ---- Q^T operand: lane holds q[row rl][16*kk + 8*half .. +7].  A lane without a row
+  // (past the tile's last position) reads the sequence's first row instead; its results
+  // are never stored.  The loads are unconditional so that the wait below can count them.
+  bf16x8 qf[Sh::kKSteps];
+  {
+    const int h = kvh * G + (R % G);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.query) +
+                                                     ((size_t)(q0 + (row_ok ? pos0 + R / G : 0)) * p.num_q_heads +
+                                                      (row_ok ? h : 0)) * D + 8 * half);
+#pragma unroll
+    for (int kk = 0; kk < Sh::kKSteps; ++kk) qf[kk] = u4_to_bf16x8(qp[2 * kk]);
+  }
+
+  f32x16 acc[Sh::kDTiles];
+#pragma unroll
+  for (int n = 0; n < Sh::kDTiles; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
+  float m_ref = -INFINITY, lsum = 0.f;
+  // the score scale, waited for here so that no wait inside the tile loop is attributed to it
+  float scale_log2 = p.scale_log2;
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(scale_log2));
+
+  // S^T for both 32-key halves of a tile from a K slot: two independent MFMA chains.  The
+  // lane's K row (key kt*32 + rl) is read in 16-byte chunks 2*kk + half, stored at chunk
+  // (2*kk + half) ^ (rl % kChunks) (32 % kChunks == 0).  Operands are read two k-steps
+  // before their MFMAs so the LDS latency hides behind the matrix cores; the reads are
+  // issued and waited for from asm, like the V reads below.
+  uint32_t koff[Sh::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < Sh::kKSteps; ++kk)
+    koff[kk] = (uint32_t)(rl * Sh::kRowBytes + (((2 * kk + half) ^ (rl % Sh::kChunks)) << 4));
+  auto k_issue = [&](u32x4 (&x)[2], uint32_t base, auto kk_c) {
+    constexpr int KK = decltype(kk_c)::value;
+    const uint32_t a = base + koff[KK];
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:%3"
+        : "=&v"(x[0]), "=&v"(x[1])
+        : "v"(a), "i"(32 * Sh::kRowBytes)
+        : "memory");
+  };
+  // waits until at most N LDS reads issued after x's are in flight (reads return in order)
+  auto op_wait = [&](u32x4& x, auto n_c) {
+    constexpr int N = decltype(n_c)::value;
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N) : "memory");
+  };
+  auto scores = [&](f32x16 (&sacc)[2], uint32_t kbase_lds) {
+    constexpr int kAhead = 2;
+    u32x4 kb[kAhead + 1][2];
+    static_for<0, kAhead>([&](auto kk_c) { k_issue(kb[decltype(kk_c)::value], kbase_lds, kk_c); });
+    static_for<0, Sh::kKSteps>([&](auto kk_c) {
+      constexpr int kk = decltype(kk_c)::value;
+      constexpr int nxt = kk + kAhead;
+      if constexpr (nxt < Sh::kKSteps) k_issue(kb[nxt % (kAhead + 1)], kbase_lds, std::integral_constant<int, nxt>{});
+      // reads issued after this k-step's two: the next steps' (at most kAhead of them)
+      constexpr int kLater = 2 * (nxt < Sh::kKSteps ? kAhead : Sh::kKSteps - 1 - kk);
+      // each MFMA waits for its own operand only
+      static_for<0, 2>([&](auto kt_c) {
+        constexpr int kt = decltype(kt_c)::value;
+        op_wait(kb[kk % (kAhead + 1)][kt], std::integral_constant<int, kLater + 1 - kt>{});
+        const f32x16 c = kk == 0 ? f32x16{} : sacc[kt];
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(kb[kk % (kAhead + 1)][kt]), qf[kk], c, 0, 0, 0);
+      });
+    });
+  };
+
+  // ---- V^T tiles.  PV needs, per lane, 8 keys of one d in one register quad, while the
+  // pool (and the copied tile) holds rows of d for one key.  Each tile is transposed once
+  // in LDS: wave w turns kTransposes 16(d) x 16(key) blocks of the row-major tile into V^T
+  // rows with ds_read_b64_tr_b16 (in each 16-lane group, output lane i element k is
+  // element i%4 of the 8 bytes addressed by lane 4k + i/4: lane 4k + q addresses key
+  // kb + k at d d0 + 4q, so lane i receives keys kb..kb+3 of d d0 + i) and ds_write_b64.
+  // A V^T row (d) holds the 64 keys in 16-byte chunks 2*ch + h = keys ch*16 + 8*(j/4) +
+  // 4h + j%4, j = 0..7: the order in which the probabilities sit in the S^T registers, so
+  // the operand of chunk ch is one ds_read_b128.  Chunk c of row d is stored at c ^
+  // ((d >> 1) & 7) (rows are half a bank line: reads and writes are conflict-free).
+  constexpr int kTileQuad = Sh::kDTiles;  // V^T operand reads per chunk (one per 32-wide d tile)
+  uint32_t tr_src[Sh::kTransposes], tr_dst[Sh::kTransposes];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int j = 0; j < Sh::kTransposes; ++j) {
+      const int blk = wave * Sh::kTransposes + j;  // (d block, key chunk) of the tile
+      const int dblk = blk >> 2, ch = blk & 3;
+      const int key = ch * 16 + 4 * g + (i >> 2);  // the key this lane addresses
+      const int byte = (16 * dblk + 4 * (i & 3)) * 2;
+      tr_src[j] = (uint32_t)(key * Sh::kRowBytes + ((((byte >> 4) ^ (key % Sh::kChunks)) << 4) | (byte & 15)));
+      const int d = 16 * dblk + i;  // the row this lane writes: keys ch*16 + 4g .. +3
+      tr_dst[j] = (uint32_t)(d * Sh::kVtRowBytes + ((((2 * ch + (g & 1)) ^ ((d >> 1) & 7))) << 4) + 8 * (g >> 1));
+    }
+  }
+  auto tr_addrs = [&](uint32_t (&a)[Sh::kTransposes], uint32_t base, const uint32_t (&off)[Sh::kTransposes]) {
+#pragma unroll
+    for (int j = 0; j < Sh::kTransposes; ++j) a[j] = base + off[j];
+  };
+  // writes the transposed rows (the registers hold landed data)
+  auto tr_write = [&](const u32x2 (&x)[Sh::kTransposes], uint32_t dst) {
+    uint32_t w[Sh::kTransposes];
+    tr_addrs(w, dst, tr_dst);
+    if constexpr (Sh::kTransposes == 4) {
+      asm volatile(
+          "ds_write_b64 %0, %4\n\t"
+          "ds_write_b64 %1, %5\n\t"
+          "ds_write_b64 %2, %6\n\t"
+          "ds_write_b64 %3, %7"
+          :
+          : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3])
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_write_b64 %0, %2\n\t"
+          "ds_write_b64 %1, %3"
+          :
+          : "v"(w[0]), "v"(w[1]), "v"(x[0]), "v"(x[1])
+          : "memory");
+    }
+  };
+  // the whole transposition of this wave's blocks of a tile, reads waited for at once
+  auto transpose = [&](uint32_t src, uint32_t dst) {
+    u32x2 x[Sh::kTransposes];
+    uint32_t a[Sh::kTransposes];
+    tr_addrs(a, src, tr_src);
+    if constexpr (Sh::kTransposes == 4) {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4\n\t"
+          "ds_read_b64_tr_b16 %1, %5\n\t"
+          "ds_read_b64_tr_b16 %2, %6\n\t"
+          "ds_read_b64_tr_b16 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %2\n\t"
+          "ds_read_b64_tr_b16 %1, %3\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1])
+          : "v"(a[0]), "v"(a[1])
+          : "memory");
+    }
+    tr_write(x, dst);
+  };
+  // lane (d = 32n + rl, h = half) reads chunk 2*ch + h of V^T row d: offset vt_off[ch] + n*32 rows
+  uint32_t vt_off[4];
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch)
+    vt_off[ch] = (uint32_t)(rl * Sh::kVtRowBytes + (((2 * ch + half) ^ ((rl >> 1) & 7)) << 4));
+  // issue (no wait) the V^T operand reads of one chunk; op_wait waits for each of them and
+  // hands the register on.  Issued from asm: the compiler would otherwise wait for every LDS copy in
+  // flight before an LDS read it cannot tell apart from them.
+  auto vt_issue = [&](u32x4 (&x)[kTileQuad], uint32_t base) {
+    constexpr int kRows32 = 32 * Sh::kVtRowBytes;
+    if constexpr (kTileQuad == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:%5\n\t"
+          "ds_read_b128 %2, %4 offset:%6\n\t"
+          "ds_read_b128 %3, %4 offset:%7"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+          : "v"(base), "i"(kRows32), "i"(2 * kRows32), "i"(3 * kRows32)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b128 %1, %2 offset:%3"
+          : "=&v"(x[0]), "=&v"(x[1])
+          : "v"(base), "i"(kRows32)
+          : "memory");
+    }
+  };
+  // the V^T reads of the last chunk plus this wave's transposing reads of the next tile
+  auto vt_issue_tr = [&](u32x4 (&x)[kTileQuad], uint32_t base, u32x2 (&t)[Sh::kTransposes], uint32_t src) {
+    constexpr int kRows32 = 32 * Sh::kVtRowBytes;
+    uint32_t a[Sh::kTransposes];
+    tr_addrs(a, src, tr_src);
+    if constexpr (kTileQuad == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %8 offset:%13\n\t"
+          "ds_read_b128 %2, %8 offset:%14\n\t"
+          "ds_read_b128 %3, %8 offset:%15\n\t"
+          "ds_read_b64_tr_b16 %4, %9\n\t"
+          "ds_read_b64_tr_b16 %5, %10\n\t"
+          "ds_read_b64_tr_b16 %6, %11\n\t"
+          "ds_read_b64_tr_b16 %7, %12"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+          : "v"(base), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(kRows32), "i"(2 * kRows32), "i"(3 * kRows32)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:%7\n\t"
+          "ds_read_b64_tr_b16 %2, %5\n\t"
+          "ds_read_b64_tr_b16 %3, %6"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(t[0]), "=&v"(t[1])
+          : "v"(base), "v"(a[0]), "v"(a[1]), "i"(kRows32)
+          : "memory");
+    }
+  };
+  // waits for this wave's transposing reads (the last LDS reads it issued)
+  auto tr_wait = [&](u32x2 (&t)[Sh::kTransposes]) {
+    if constexpr (Sh::kTransposes == 4) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]) : : "memory");
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]) : : "memory");
+    }
+  };
+
+  // Online softmax of one tile's scores: P = exp2(s*scale - m) packed to bf16 in pw[chunk]
+  // (16-key chunk ch = 2*half32 + cc), l and the reference maximum m updated.
+  auto softmax = [&](f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4]) {
+    // lane's entries: key key0 + kt*32 + 8*(r/4) + 4*half + r%4 of row rl.  Raw scores are
+    // masked and maximised; the scale (> 0) is applied inside exp2(fma(s, scale, -m)).
+    // a tile needs masking if it reaches past some row's position, or (WINDOW) below some
+    // row's first visible key
+    if constexpr (WINDOW) {
+      if (key0 + Sh::kKeys - 1 > wave_first || key0 < wave_lo_max) {
+        // visible: 0 <= row_pos - key < row_span, one unsigned comparison
+        const uint32_t rel = (uint32_t)(row_pos - key0 - 4 * half);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t dist = rel - (uint32_t)(kt * 32 + 8 * (r >> 2) + (r & 3));
+            sacc[kt][r] = dist < row_span ? sacc[kt][r] : -INFINITY;
+          }
+      }
+    } else if (key0 + Sh::kKeys - 1 > wave_first) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          sacc[kt][r] = key <= row_pos ? sacc[kt][r] : -INFINITY;
+        }
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sacc[kt][r]);
+    bmax = max_halves(bmax) * scale_log2;
+    // move the reference maximum only when it is exceeded by more than 8 (log2 units)
+    const bool need = bmax > m_ref + 8.f;
+    if (__any(need)) {
+      const float mnew = need ? bmax : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int n = 0; n < Sh::kDTiles; ++n) acc[n] *= alpha;
+      m_ref = mnew;
+    }
+    const float msub = m_ref == -INFINITY ? 0.f : m_ref;
+    float ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kt][8 * cc + 2 * j], scale_log2, -msub));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kt][8 * cc + 2 * j + 1], scale_log2, -msub));
+          ps += p0 + p1;
+          pw[2 * kt + cc][j] = pack_bf16x2(p0, p1);
+        }
+    lsum += ps;
+  };
+
+  // O^T += V^T P^T for one tile, V^T from the slot at byte address vtbase.  The reads of
+  // chunk ch+1 are in flight while the MFMAs of chunk ch run; between(ch) is called after
+  // they are issued (the copies of the step go there, spread over the matrix-core work
+  // instead of stalling the wave at once).  The wave's share of the transposition of the
+  // next tile (row-major slot tr_from -> V^T slot tr_to) rides along: its reads are issued
+  // with the last chunk's and its rows written after the last MFMAs.
+  auto pv = [&](const u32x4 (&pw)[4], uint32_t vtbase, auto&& between, uint32_t tr_from, uint32_t tr_to) {
+    u32x4 vb[2][kTileQuad];
+    u32x2 tx[Sh::kTransposes];
+    vt_issue(vb[0], vtbase + vt_off[0]);
+    static_for<0, 4>([&](auto ch_c) {
+      constexpr int ch = decltype(ch_c)::value;
+      if constexpr (ch + 2 < 4) {
+        vt_issue(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1]);
+      } else if constexpr (ch + 1 < 4) {
+        vt_issue_tr(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1], tx, tr_from);
+      }
+      // reads issued after this chunk's: the next chunk's operands and (from chunk 2 on) the
+      // transposing reads; the last chunk's operands were read before the transposing reads,
+      // so its MFMAs wait only for them, the transposed rows after.  Each MFMA waits for its
+      // own operand only.
+      constexpr int kLater = ch < 2 ? kTileQuad : ch == 2 ? kTileQuad + Sh::kTransposes : Sh::kTransposes;
+      const bf16x8 pb = u4_to_bf16x8(pw[ch]);
+      static_for<0, kTileQuad>([&](auto n_c) {
+        constexpr int n = decltype(n_c)::value;
+        op_wait(vb[ch & 1][n], std::integral_constant<int, kLater + kTileQuad - 1 - n>{});
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(vb[ch & 1][n]), pb, acc[n], 0, 0, 0);
+        if constexpr (n == 0) between(ch);  // the step's copy of this chunk, beside the first MFMA
+      });
+    });
+    tr_wait(tx);
+    tr_write(tx, tr_to);
+  };
+
+  // Pipeline over the item's key tiles t = kt0 .. kt1-1, one step per tile between
+  // work-group barriers.  Per tile a wave has a matrix-core part (S = K Q^T and
+  // O += V P, 32 MFMAs) and a vector part (the softmax), about equally long.  The waves
+  // are in two groups, one wave of each on every SIMD, that run the parts in opposite
+  // order, so one group's exponentials issue while the other group's MFMAs run:
+  //   leading group   (waves 0-3): O += V P(t-1), S(t)  | softmax(t) -> P(t)
+  //   following group (waves 4-7): softmax(t) -> P(t)   | O += V P(t), S(t+1)
+  // and every wave transposes its share of V(t+1) into V^T(t+1) during its O += V P.
+  // Step t also reads the block id of tile t+4 and starts the copies of K(t+3) and
+  // V(t+3) (spread over the matrix-core part).  K slot (t+3)%4 last held K(t-1), read at
+  // step t-1; V slot (t+3)%3 last held V(t), transposed at step t-1; V^T slot (t+1)%3
+  // last held V^T(t-2), read at step t-1.  Before the barrier a wave waits for its V^T
+  // writes and for everything older than this step's copies (vector-memory instructions
+  // retire in order and the copies are the last loads of a step: vmcnt <= 2*kCopies),
+  // which covers K(t+2) and V(t+2), the newest tiles step t+1 reads.  Block ids are read
+  // before the copies of their step, so consuming one never waits on copies in flight.
+  // Tiles past the item's range are copied too (valid rows, never used) so that every
+  // step is alike.
+  constexpr int kStepLoads = 2 * Sh::kCopies;
+  const int wave_tiles_end = min(kt1, wave_last / Sh::kKeys + 1);  // tiles this wave computes
+  // (a sliding window's lower edge is left to the item's key range and to masking: a wave
+  // that also skipped its own leading tiles would need registers the kernel does not have)
+  const bool leading = wave < Sh::kWaves / 2;
+  auto computes = [&](int tile) { return wave_live && tile < wave_tiles_end; };
+  {
+    wait_vmcnt<Sh::kKSteps>();  // the block ids have landed; Q may still be in flight
+    copy_rows(kbase, kt0, ph0, k_stage(kt0));
+    copy_rows(vbase, kt0, ph0, v_stage(kt0));
+    copy_rows(kbase, kt0 + 1, ph1, k_stage(kt0 + 1));
+    copy_rows(vbase, kt0 + 1, ph1, v_stage(kt0 + 1));
+    copy_rows(kbase, kt0 + 2, ph2, k_stage(kt0 + 2));
+    copy_rows(vbase, kt0 + 2, ph2, v_stage(kt0 + 2));
+    wait_vmcnt<2 * Sh::kCopies>();  // Q and tiles kt0, kt0+1 have landed
+    __builtin_amdgcn_s_barrier();
+    transpose(v_addr(kt0), vt_addr(kt0));
+    wait_vmcnt_lgkm0<2 * Sh::kCopies>();
+    __builtin_amdgcn_s_barrier();
+
+    f32x16 sc[2];  // scores of the tile the wave softmaxes next
+    u32x4 pw[4];   // its probabilities, bf16
+    if (!leading && computes(kt0)) scores(sc, k_addr(kt0));
+    for (int tile = kt0; tile < kt1; ++tile) {
+      const int phys_new = block_of(tile + 4);
+      // this step's copies: K(t+3) and V(t+3), kCopies slabs each
+      const int phys = phys_next;
+      unsigned char* const k_dst = k_stage(tile + 3);
+      unsigned char* const v_dst = v_stage(tile + 3);
+      auto copy_part = [&](int part) {
+        if (part < Sh::kCopies)
+          copy_slab(kbase, tile + 3, phys, k_dst, part);
+        else if (part < 2 * Sh::kCopies)
+          copy_slab(vbase, tile + 3, phys, v_dst, part - Sh::kCopies);
+      };
+      auto copy_all = [&]() {
+#pragma unroll
+        for (int part = 0; part < 2 * Sh::kCopies; ++part) copy_part(part);
+      };
+      phys_next = phys_new;
+      if (!leading && computes(tile)) softmax(sc, tile * Sh::kKeys, pw);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      // V(t+1) -> V^T(t+1) by every wave (inside its O += V P when it has one); tiles past
+      // the range hold valid rows too, so the transposition is unconditional
+      const uint32_t tr_from = v_addr(tile + 1), tr_to = vt_addr(tile + 1);
+      if (leading) {
+        if (tile > kt0 && computes(tile - 1)) {
+          pv(pw, vt_addr(tile - 1), copy_part, tr_from, tr_to);
+        } else {
+          copy_all();
+          transpose(tr_from, tr_to);
+        }
+        if (computes(tile)) scores(sc, k_addr(tile));
+      } else {
+        if (computes(tile)) {
+          pv(pw, vt_addr(tile), copy_part, tr_from, tr_to);
+        } else {
+          copy_all();
+          transpose(tr_from, tr_to);
+        }
+        if (computes(tile + 1)) scores(sc, k_addr(tile + 1));
+      }
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (leading && computes(tile)) softmax(sc, tile * Sh::kKeys, pw);
+      wait_vmcnt_lgkm0<kStepLoads>();
+      __builtin_amdgcn_s_barrier();
+    }
+    // the last O += V P of the leading group; V^T(kt1-1)'s slot is not refilled.  (Its
+    // transposition rides along into the slot of V^T(kt1+1), which nothing reads.)
+    if (leading && computes(kt1 - 1)) pv(pw, vt_addr(kt1 - 1), [](int) {}, v_addr(kt1 + 1), vt_addr(kt1 + 1));
+    wait_vmcnt<0>();  // no copy may still be writing LDS when the work-group ends
+  }
+
+  // ---- epilogue.  The lane's outputs (d = n*32 + 8*(r/4) + 4*half + r%4 of row rl) are
+  // scattered pieces of 32 rows; stored as they are, every store instruction would touch 32
+  // lines.  Each wave stages its 32 rows in LDS (free now; 16-byte chunks XOR-swizzled by
+  // row so that the writes spread over the banks) and stores whole rows from there, 16
+  // bytes per lane.  A whole row tile stores bf16 outputs; a split piece stores O / l in
+  // fp16 with a per-row scale (below), its reference maximum m and weight sum l, for the
+  // merge.
+  __syncthreads();  // every wave is done with the rings
+  if (!wave_live) return;
+  const float l = sum_halves(lsum);
+  const float inv = whole ? p.v_scale / l : (l > 0.f ? 1.f / l : 0.f);  // a row that saw no key stores 0
+  const size_t slot_row0 = ((size_t)(p.item_base + item_idx) * p.num_kv_heads + kvh) * kPrefillRows + 32 * wave;
+  if (whole) {
+    unsigned char* const stage = smem + wave * 32 * Sh::kRowBytes;
+#pragma unroll
+    for (int n = 0; n < Sh::kDTiles; ++n)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int chunk = (n * 4 + rq) ^ (rl % Sh::kChunks);
+        const float a0 = acc[n][4 * rq] * inv, a1 = acc[n][4 * rq + 1] * inv;
+        const float a2 = acc[n][4 * rq + 2] * inv, a3 = acc[n][4 * rq + 3] * inv;
+        *reinterpret_cast<u32x2*>(stage + rl * Sh::kRowBytes + chunk * 16 + half * 8) =
+            u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int kRowsPerStore = 64 / Sh::kChunks;
+    const int sc_chunk = lane % Sh::kChunks;
+#pragma unroll
+    for (int it = 0; it < 32 / kRowsPerStore; ++it) {
+      const int row = it * kRowsPerStore + lane / Sh::kChunks;
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(stage + row * Sh::kRowBytes + ((sc_chunk ^ (row % Sh::kChunks)) << 4));
+      const int Rw = 32 * wave + row;
+      if (Rw >= P * G || pos0 + Rw / G >= pos_end) continue;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) +
+                      ((size_t)(q0 + pos0 + Rw / G) * p.num_q_heads + kvh * G + Rw % G) * D;
+      *reinterpret_cast<u32x4*>(dst + sc_chunk * 8) = v;
+    }
+    return;
+  }
+  // split piece: O / l in fp16 scaled by a per-row power of two sigma = 2^(E-15), where
+  // 2^(E-1) <= the row's largest |O / l| < 2^E, so every stored value is below 2^15 (fp16
+  // holds up to 65504) and the rounding error is at most 2^-11 of that largest magnitude,
+  // whatever the range of V.  sigma goes to the merge beside m and l.
+  float amax = 0.f;
+#pragma unroll
+  for (int n = 0; n < Sh::kDTiles; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[n][r]));
+  amax = max_halves(amax) * inv;  // the row's two lanes hold its D values between them
+  int e2 = 0;
+  (void)frexpf(amax, &e2);  // amax = f * 2^e2, f in [0.5, 1) (e2 = 0 for amax = 0)
+  const float sigma = ldexpf(1.f, e2 - 15);
+  const float mul = inv * ldexpf(1.f, 15 - e2);
+  unsigned char* const stage = smem + wave * 32 * Sh::kRowBytes;
+#pragma unroll
+  for (int n = 0; n < Sh::kDTiles; ++n)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int chunk = (n * 4 + rq) ^ (rl % Sh::kChunks);
+      const float a0 = acc[n][4 * rq] * mul, a1 = acc[n][4 * rq + 1] * mul;
+      const float a2 = acc[n][4 * rq + 2] * mul, a3 = acc[n][4 * rq + 3] * mul;
+      *reinterpret_cast<u32x2*>(stage + rl * Sh::kRowBytes + chunk * 16 + half * 8) =
+          u32x2{pack_f16x2(a0, a1), pack_f16x2(a2, a3)};
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kRowsPerStore = 64 / Sh::kChunks;
+  const int sc_chunk = lane % Sh::kChunks;
+#pragma unroll
+  for (int it = 0; it < 32 / kRowsPerStore; ++it) {
+    const int row = it * kRowsPerStore + lane / Sh::kChunks;
+    const u32x4 v =
+        *reinterpret_cast<const u32x4*>(stage + row * Sh::kRowBytes + ((sc_chunk ^ (row % Sh::kChunks)) << 4));
+    const int Rw = 32 * wave + row;
+    if (Rw >= P * G || pos0 + Rw / G >= pos_end) continue;
+    *reinterpret_cast<u32x4*>(p.part_o + (slot_row0 + row) * D + sc_chunk * 8) = v;
+  }
+  if (half == 0 && row_ok) {
+    p.part_m[slot_row0 + rl] = m_ref;
+    p.part_l[slot_row0 + rl] = l;
+    p.part_s[slot_row0 + rl] = sigma;
+  }
+}
+
+}  // namespace
+
+}  // namespace pa

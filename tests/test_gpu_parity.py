@@ -510,6 +510,81 @@ def test_mixed_step_full():
     assert err <= TOL["bf16"]
 
 
+# ---- decode rows and chunks in one launch (pa_set_fused) or in two
+
+@pytest.fixture
+def fused_mode():
+    """Sets the library's fused-launch mode for one test and restores the default afterwards."""
+    def set_mode(mode):
+        pk.set_fused(mode)
+    yield set_mode
+    pk.set_fused(-1)
+
+
+def _mixed_case(seed, heads, kv, num_seqs=10):
+    """A random batch with several decode rows and several chunks (both parts of a fused launch)."""
+    Hq, Hkv, D = heads
+    rng = np.random.default_rng(seed)
+    q_lens = [1 if i % 2 == 0 else int(rng.integers(2, 300)) for i in range(num_seqs)]
+    ctx = [int(q + rng.integers(0, 1500)) for q in q_lens]
+    scales = dict(k_scale=0.05, v_scale=0.04) if kv == "fp8" else {}
+    return wl.build(f"mixed_{seed}", seed=seed, ctx_lens=ctx, q_lens=q_lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                    head_dim=D, q_dtype="bf16", kv_dtype=kv, **scales)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("seed,heads", [(481, (32, 8, 128)), (482, (8, 2, 64)), (483, (48, 1, 128)),
+                                        (484, (12, 4, 128))])
+def test_mixed_batch_fused_and_separate_launches(fused_mode, mode, kv, seed, heads):
+    """Decode rows and chunks of one batch: in one launch (mode 2: decode work-groups beside the prefill items) and
+    in two (mode 0), each against the oracle."""
+    fused_mode(mode)
+    w = _mixed_case(seed, heads, kv)
+    say("mixed batch", "fused" if mode == 2 else "separate", kv, seed, heads, list(w.q_lens))
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    out = d.prefill()
+    torch.cuda.synchronize()
+    err = max_err(out, oracle.attention_for(w, pools=oracle.written_pools(w)))
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL[kv]
+
+
+@pytest.mark.parametrize("mask", ["window", "local"])
+def test_mixed_batch_fused_window_and_local(fused_mode, mask):
+    fused_mode(2)
+    w = _mixed_case(491, (32, 8, 128), "bf16")
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    say("mixed batch fused", mask)
+    if mask == "window":
+        out = d.prefill_window(200)
+        ref = oracle.attention_for(w, pools=oracle.written_pools(w), window=200)
+    else:
+        out = d.prefill_local(256)
+        ref = oracle.attention_for(w, pools=oracle.written_pools(w), chunk=256)
+    torch.cuda.synchronize()
+    err = max_err(out, ref)
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_mixed_step_full_fused_forced_and_separate(fused_mode):
+    """The full mixed continuous-batching step in one launch and in two: both match the oracle element by element."""
+    w = wl.mixed_step_bf16()
+    d = DevWorkload(w)
+    d.write_new_tokens()
+    ref = oracle.attention_for(w, pools=oracle.written_pools(w))
+    for mode in (2, 0):
+        fused_mode(mode)
+        out = d.prefill()
+        torch.cuda.synchronize()
+        err = max_err(out, ref)
+        say(f"mixed step full, mode {mode}: max_abs_err={err:.3e}")
+        assert err <= TOL["bf16"]
+
+
 def test_prefill_whole_prompt_equals_chunks_and_decode():
     L = 1024
     w = wl.random_case(421, num_seqs=1, ctx_range=(L, L), q_lens=[L], num_q_heads=8, num_kv_heads=2,
