@@ -58,8 +58,12 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_418_amd", "csrc")
 COPY_BYTES = 1 << 30
 SCRATCH_BYTES = 512 << 20       # written between the cold-cache steps of C5 (twice the 256 MB MALL)
 TOL = {"f32": 2e-3, "bf16": 1.5e-2, "fp8": 6e-2}
-DECODE_SOURCES = ["decode_kernels.hip", "pa_device.h", "pa_internal.h", "abi.cpp"]  # abi.cpp: launch shape
-PREFILL_SOURCES = ["prefill_kernels.hip", "pa_device.h", "pa_internal.h", "abi.cpp"]
+# the sources a kernel's measured counters depend on (a profile taken on other sources is stale)
+DECODE_SOURCES = ["decode_kernels.hip", "decode_body.h", "pa_device.h", "pa_internal.h",
+                  "abi.cpp"]  # abi.cpp: launch shape
+PREFILL_SOURCES = ["prefill_kernels.hip", "prefill_body.h", "pa_device.h", "pa_internal.h", "abi.cpp"]
+# the cascade launch holds the decode body and the prefill body (its prefix tiles)
+CASCADE_SOURCES = DECODE_SOURCES + ["prefill_body.h", "prefill_kernels.hip", "fused_kernels.hip"]
 
 
 def _log(*a):
@@ -564,14 +568,15 @@ def bench_cascade(args, result):
     for name, cascade in (("plain", False), ("cascade", True)):
         st = Step(w, cascade=cascade)
         ms, _, per = time_steps(st, args.steps, args.warmup)
-        kt = kernel_times(st, args.steps, ["decode", "decode_merge"])
+        kt = kernel_times(st, args.steps, ["decode", "decode_merge", "stage_fp8"])
         cms, _, cper = time_steps(st, args.steps, args.warmup, between=flush)
-        ktc = kernel_times(st, args.steps, ["decode", "decode_merge"], between=flush)
+        ktc = kernel_times(st, args.steps, ["decode", "decode_merge", "stage_fp8"], between=flush)
         d = kmean(kt, "decode")
         out[name] = {"ms_per_step": round(ms, 5), "step_ms": per, "logical_gbps": round(logical / (ms * 1e-3) / 1e9, 1),
                      "unique_gbps": round(unique / (ms * 1e-3) / 1e9, 1),
                      "decode_kernel_ms": round(d, 5), "decode_kernel": kt["decode"],
                      "merge_kernel_ms": kmean(kt, "decode_merge"),
+                     "stage_kernel_ms": kmean(kt, "stage_fp8"),
                      "kernel_unique_gbps": round(unique / (d * 1e-3) / 1e9, 1),
                      "kernel_unique_frac_hbm": round(unique / (d * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "cold": {"note": "512 MB scratch write before every step, outside the timed region",
@@ -584,7 +589,7 @@ def bench_cascade(args, result):
     out["speedup"] = round(out["plain"]["ms_per_step"] / out["cascade"]["ms_per_step"], 3)
     del scratch
     result["cascade_step"] = out
-    traffic = read_traffic("cascade_fp8_prefix_shared_traffic", DECODE_SOURCES)
+    traffic = read_traffic("cascade_fp8_prefix_shared_traffic", CASCADE_SOURCES)
     rec, par = (None, None)
     if not args.no_cpu:
         rows = decode_rows_sample(w, 8)

@@ -285,8 +285,12 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
  * [A]'s attention-backend table).  The result is pa_decode's: the keys of the
  * shared prefix and of each sequence's own suffix are attended separately
  * and combined with the log-sum-exp rule ([B] tutorial 7), so only the order
- * of fp32 sums differs.  The prefix is read once per group of 16/G sequences
- * (G = num_q_heads / num_kv_heads <= 16) instead of once per sequence.
+ * of fp32 sums differs.  The prefix is attended as dense matrix-core tiles:
+ * for each kv head, all num_seqs x G query rows (G = num_q_heads /
+ * num_kv_heads <= 16) against the prefix blocks, each block read once per 256
+ * rows, in one launch with the suffixes' shares; fp8 pools stage the prefix
+ * as bf16 first (one more launch).  With fp32 queries (pa_decode_cascade_fp8)
+ * the prefix is read once per group of 16/G sequences by decode waves instead.
  * Requirements: prefix_blocks >= 1; every seq_lens[s] >= prefix_blocks *
  * block_size; block_tables[s][j] the same for every s and j < prefix_blocks
  * (checked under PA_VALIDATE=1, trusted otherwise).  dtype: PA_BF16.
@@ -527,11 +531,11 @@ int32_t pa_pool_free_queue(const pa_block_pool_t* pool, int32_t* out, int32_t ma
 typedef enum pa_kernel {
   PA_K_SLOT_MAPPING = 0,    /* pa_slot_mapping */
   PA_K_RESHAPE_AND_CACHE = 1, /* pa_reshape_and_cache, pa_reshape_and_cache_fp8 */
-  PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode(_fp8), pa_decode_cascade(_fp8), decode rows of pa_prefill_varlen) */
+  PA_K_DECODE = 2,          /* the paged decode kernel (pa_decode(_fp8), decode rows of pa_prefill_varlen), and the prefix-tile + suffix launch of pa_decode_cascade(_fp8) */
   PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
   PA_K_PREFILL = 4,         /* the varlen prefill kernel */
   PA_K_PREFILL_MERGE = 5,   /* the log-sum-exp merge of split prefill row tiles */
-  PA_K_STAGE_FP8 = 6,       /* the fp8 -> bf16 staging of chunk sequences in pa_prefill_varlen_fp8 */
+  PA_K_STAGE_FP8 = 6,       /* the fp8 -> bf16 staging of chunk sequences (pa_prefill_varlen_fp8) and of a cascade's prefix */
   PA_K_FUSED = 7            /* decode rows and prefill chunks of a mixed batch in one launch (pa_prefill_varlen*) */
 } pa_kernel_t;
 

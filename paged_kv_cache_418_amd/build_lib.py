@@ -40,7 +40,9 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    # PA_EXTRA_CFLAGS: extra compiler flags (e.g. -D switches of a variant being measured)
+    extra = os.environ.get("PA_EXTRA_CFLAGS", "").split()
+    cmd = [_hipcc(), *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -97,6 +97,7 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n) {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr int kFusedDecodeWaves = 8;  // decode waves per work-group of a fused launch
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -679,6 +680,194 @@ pa_status_t check_cascade(const int32_t* block_tables, int32_t bt_stride, const 
 
 }  // namespace
 
+namespace {
+
+// Cascade prefix as dense matrix-core tiles ("vLLM 架构概述" §2: blocks shared by several
+// requests are stored once; cascade attention in the backend table of §6).  For each kv
+// head the num_seqs query rows x its G q heads are rows of the prefill kernel's 256-row
+// tiles (256 / G sequences each), attended against the shared prefix, whose key tiles are
+// cut into `shares` key ranges: one work item per (kv head, row tile, share).  The items run
+// in one launch with the suffix shares of the split decode (launch_fused: the decode
+// work-groups first, eight decode waves each, then the items, one work-group per compute
+// unit), each item leaves an unnormalised partial per (share, sequence, head), and the
+// decode merge folds them with the suffix pieces.  fp8 pools: the prefix blocks are first
+// staged as the exact bf16 values of their codes (the tiles read bf16 operands).
+//
+// The split between the two parts uses the fused launch's host estimate (PA_FUSED_TILE_NS
+// per 64-key tile of a 256-row item plus 5 us; PA_FUSED_CU_GBPS per decode compute unit up
+// to PA_FUSED_DECODE_GBPS in all).  The host does not see seq_lens here, so the suffix bytes
+// are estimated as if suffix lengths were spread evenly up to max_seq_len - prefix.  The
+// share count minimises the larger of the item time and the suffix time.
+struct CascadeTilePlan {
+  bool ok = false;
+  int positions = 0;     // sequences per row tile: 256 / G
+  int row_tiles = 0;
+  int key_tiles = 0;     // 64-key tiles of the prefix
+  int tps = 0;           // key tiles per share
+  int shares = 0;
+  int n_decode_wgs = 0;  // compute units the estimate gives the suffix
+  int n_splits = 0;      // suffix shares per kv head
+  size_t dec_bytes = 0, pre_o_bytes = 0, pre_m_bytes = 0, table_bytes = 0, stage_bytes = 0, total = 0;
+};
+
+bool cascade_tiles_enabled() {
+  static const int on = env_int("PA_CASCADE_TILES", 1, 0, 1);
+  return on != 0;
+}
+
+CascadeTilePlan plan_cascade_tiles(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                                   int prefix_blocks, int num_splits, int kv_elem) {
+  CascadeTilePlan cp;
+  const int G = num_q_heads / std::max(1, num_kv_heads);
+  if (num_seqs < 1 || G < 1 || G > pa::kMaxGroup) return cp;
+  cp.positions = pa::kPrefillRows / G;
+  cp.row_tiles = ceil_div(num_seqs, cp.positions);
+  const int prefix_len = prefix_blocks * pa::kBlockSize;
+  cp.key_tiles = ceil_div(prefix_len, pa::kPrefillKeys);
+  static const double tile_s = env_int("PA_FUSED_TILE_NS", 2200, 100, 1000000) * 1e-9;
+  static const double bw = env_int("PA_FUSED_DECODE_GBPS", 6000, 100, 100000) * 1e9;
+  static const double bw_cu = env_int("PA_FUSED_CU_GBPS", 29, 1, 100000) * 1e9;
+  // an fp8 block is half the bytes for the same work per block: fewer bytes per compute unit
+  // (measured on the prefix-shared fp8 step: 18 GB/s per decode compute unit)
+  static const double bw_cu8 = env_int("PA_FUSED_CU_GBPS_FP8", 18, 1, 100000) * 1e9;
+  const double item_s = 5e-6;
+  const int C = device_cu_count();
+  const double cu_rate = kv_elem == 1 ? bw_cu8 : bw_cu;
+  const double dec_bytes =
+      2.0 * num_seqs * 0.5 * std::max(0, max_seq_len - prefix_len) * num_kv_heads * head_dim * kv_elem;
+  double best = 1e30;
+  static const int forced = env_int("PA_CASCADE_SHARES", 0, 0, 1 << 16);  // measurement: fix the share count
+  for (int want = 1; want <= cp.key_tiles; ++want) {
+    const int tps = ceil_div(cp.key_tiles, want);  // near-equal key ranges
+    const int shares = ceil_div(cp.key_tiles, tps);
+    if (shares != want) continue;
+    const int items = cp.row_tiles * shares;
+    if (items > pa::kMaxPrefillItems) break;
+    const int q = C - items * num_kv_heads;
+    if (q < 8) break;
+    if (forced > 0 && shares != forced) continue;
+    const double t = std::max(tps * tile_s + item_s, dec_bytes / std::min(bw, cu_rate * q));
+    if (t < best) {
+      best = t;
+      cp.tps = tps;
+      cp.shares = shares;
+      cp.n_decode_wgs = q;
+    }
+  }
+  if (cp.tps == 0) return cp;
+  // suffix shares: eight decode waves on each compute unit of the estimate (or num_splits),
+  // never more than the blocks there can be
+  const int64_t max_blocks = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
+  int64_t ns = num_splits > 0 ? num_splits : (int64_t)cp.n_decode_wgs * kFusedDecodeWaves / num_kv_heads;
+  ns = std::min<int64_t>(std::max<int64_t>(ns, 1), std::max<int64_t>(max_blocks, 1));
+  cp.n_splits = (int)ns;
+  cp.n_decode_wgs = ceil_div((int64_t)cp.n_splits * num_kv_heads, kFusedDecodeWaves);
+  cp.dec_bytes = align_up(decode_layout(num_seqs, num_q_heads, cp.n_splits, head_dim).total);
+  const size_t rows = (size_t)cp.shares * num_seqs * num_q_heads;
+  cp.pre_o_bytes = align_up(rows * head_dim * sizeof(float));
+  cp.pre_m_bytes = align_up(rows * sizeof(float));
+  // fp8 pools: the prefix staged in bf16, K and V, with its table (always counted: the size
+  // query takes no dtype)
+  cp.table_bytes = align_up((size_t)prefix_blocks * sizeof(int32_t));
+  cp.stage_bytes = align_up((size_t)prefix_blocks * pa::kBlockSize * num_kv_heads * head_dim * 2);
+  cp.total = cp.dec_bytes + cp.pre_o_bytes + 2 * cp.pre_m_bytes + cp.table_bytes + 2 * cp.stage_bytes;
+  cp.ok = true;
+  return cp;
+}
+
+pa_status_t run_cascade_tiles(const CascadeTilePlan& cp, void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
+                              float k_scale, float v_scale, void* workspace, hipStream_t stream,
+                              int32_t prefix_blocks) {
+  auto* base = static_cast<unsigned char*>(workspace);
+  // the suffix: the split decode's shares over each sequence's own blocks, every piece partial
+  pa::FusedParams f{};
+  pa::DecodeParams& d = f.dec;
+  d = make_decode_params(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, scale, kv_kind, 0, k_scale,
+                         v_scale, cp.n_splits, workspace, 0, 0, 0);
+  d.num_blocks = num_blocks;
+  d.n_splits = cp.n_splits;
+  const DecodeLayout lay = decode_layout(num_seqs, num_q_heads, cp.n_splits, head_dim);
+  d.part_o = reinterpret_cast<float*>(base);
+  d.part_m = reinterpret_cast<float*>(base + lay.o_bytes);
+  d.part_l = reinterpret_cast<float*>(base + lay.o_bytes + lay.m_bytes);
+  d.piece_first = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes);
+  d.piece_last = reinterpret_cast<int32_t*>(base + lay.o_bytes + 2 * lay.m_bytes + lay.idx_bytes);
+  unsigned char* pre = base + cp.dec_bytes;
+  d.pre_o = reinterpret_cast<float*>(pre);
+  d.pre_m = reinterpret_cast<float*>(pre + cp.pre_o_bytes);
+  d.pre_l = reinterpret_cast<float*>(pre + cp.pre_o_bytes + cp.pre_m_bytes);
+  d.skip_blocks = prefix_blocks;
+  d.force_partial = 1;
+  d.prefix_blocks = prefix_blocks;
+  d.prefix_shares = 0;  // in the launch: no decode wave takes prefix pieces
+  d.prefix_waves = 0;
+  // the prefix tiles, over a bf16 copy of the prefix for fp8 pools (staged just before)
+  const void* pk = key_cache;
+  const void* pv = value_cache;
+  const int32_t* ptab = block_tables;
+  int pblocks = num_blocks;
+  if (kv_kind == pa::kFP8) {
+    unsigned char* sb = pre + cp.pre_o_bytes + 2 * cp.pre_m_bytes;
+    auto* st_table = reinterpret_cast<int32_t*>(sb);
+    auto* st_k = reinterpret_cast<uint16_t*>(sb + cp.table_bytes);
+    auto* st_v = reinterpret_cast<uint16_t*>(sb + cp.table_bytes + cp.stage_bytes);
+    pa_status_t st = hip_status(
+        pa::launch_stage_prefix_fp8(static_cast<const uint8_t*>(key_cache), static_cast<const uint8_t*>(value_cache),
+                                    block_tables, prefix_blocks, num_kv_heads, head_dim, num_blocks, st_k, st_v,
+                                    st_table, stream),
+        "cascade prefix staging launch");
+    if (st != PA_OK) return st;
+    pk = st_k;
+    pv = st_v;
+    ptab = st_table;
+    pblocks = prefix_blocks;
+  }
+  pa::PrefillParams& pp = f.pre;
+  pp.out = out;
+  pp.query = query;
+  pp.key_cache = pk;
+  pp.value_cache = pv;
+  pp.block_tables = ptab;
+  pp.seq_lens = seq_lens;
+  pp.bt_stride = bt_stride;
+  pp.num_tokens = num_seqs;
+  pp.num_q_heads = num_q_heads;
+  pp.num_kv_heads = num_kv_heads;
+  pp.group = num_q_heads / num_kv_heads;
+  pp.num_blocks = pblocks;
+  pp.tile_positions = cp.positions;
+  pp.scale_log2 = d.scale_log2;
+  pp.v_scale = 1.f;
+  pp.prefix_rows = num_seqs;
+  pp.prefix_keys = prefix_blocks * pa::kBlockSize;
+  pp.prefix_share_tiles = cp.tps;
+  pp.pre_o = d.pre_o;
+  pp.pre_m = d.pre_m;
+  pp.pre_l = d.pre_l;
+  int n = 0;
+  for (int rt = 0; rt < cp.row_tiles; ++rt)
+    for (int j = 0; j < cp.shares; ++j) {
+      const uint64_t kt0 = (uint64_t)j * cp.tps, kt1 = std::min<uint64_t>(kt0 + cp.tps, cp.key_tiles);
+      pp.items[n++] = ((uint64_t)rt << 16) | (kt0 << 32) | (kt1 << 48);
+    }
+  pp.n_items = n;
+  f.decode_waves_per_wg = kFusedDecodeWaves;
+  f.decode_waves = d.n_splits * num_kv_heads;
+  f.n_decode_wgs = ceil_div(f.decode_waves, kFusedDecodeWaves);
+  pa_status_t st = hip_status(pa::launch_fused(f, head_dim, kv_kind == pa::kFP8, stream, pa::kKDecode),
+                              "cascade prefix tiles + suffix launch");
+  if (st != PA_OK) return st;
+  pa::DecodeParams m = d;
+  m.prefix_shares = cp.shares;
+  return hip_status(pa::launch_decode_merge(m, head_dim, stream), "cascade merge launch");
+}
+
+}  // namespace
+
 size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_seq_len, int32_t prefix_blocks,
                                          int32_t num_splits) {
@@ -686,7 +875,14 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
       (head_dim != 64 && head_dim != 128) || num_splits < 0 || prefix_blocks < 1 ||
       (int64_t)prefix_blocks * pa::kBlockSize > max_seq_len || num_q_heads / num_kv_heads > pa::kMaxGroup)
     return 0;
-  return cascade_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits).total;
+  size_t need = cascade_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits).total;
+  if (cascade_tiles_enabled())
+    for (const int elem : {1, 2}) {  // the size query takes no dtype: room for either plan
+      const CascadeTilePlan cp = plan_cascade_tiles(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                    prefix_blocks, num_splits, elem);
+      if (cp.ok) need = std::max(need, cp.total);
+    }
+  return need;
 }
 
 pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -709,6 +905,14 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
   if (validate_enabled()) {
     st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
     if (st != PA_OK) return st;
+  }
+  if (cascade_tiles_enabled()) {
+    const CascadeTilePlan cp =
+        plan_cascade_tiles(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits, 2);
+    if (cp.ok)
+      return run_cascade_tiles(cp, out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                               num_q_heads, num_kv_heads, head_dim, num_blocks, max_seq_len, scale, pa::kBF16, 1.f,
+                               1.f, workspace, static_cast<hipStream_t>(stream), prefix_blocks);
   }
   return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
@@ -738,6 +942,15 @@ pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const uint8_t* k
   if (validate_enabled()) {
     st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
     if (st != PA_OK) return st;
+  }
+  // the tiles read bf16 queries; fp32 queries take the decode waves' path
+  if (q_dtype == PA_BF16 && cascade_tiles_enabled()) {
+    const CascadeTilePlan cp =
+        plan_cascade_tiles(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits, 1);
+    if (cp.ok)
+      return run_cascade_tiles(cp, out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                               num_q_heads, num_kv_heads, head_dim, num_blocks, max_seq_len, scale, pa::kFP8, k_scale,
+                               v_scale, workspace, static_cast<hipStream_t>(stream), prefix_blocks);
   }
   return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
@@ -894,7 +1107,6 @@ struct StepPlan {
   int decode_splits = 0;  // decode shares per column of the fused launch
 };
 
-constexpr int kFusedDecodeWaves = 8;  // decode waves per work-group of a fused launch
 
 pa_status_t plan_step(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_tokens, int bt_stride,
                       int num_q_heads, int num_kv_heads, int head_dim, int kv_elem, int window, int chunk,

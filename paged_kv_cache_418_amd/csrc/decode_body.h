@@ -177,17 +177,23 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
 // blocks it holds (a share holding only the start units of s has no piece of it).
 // Shares are consecutive, so a wave visits its sequences in increasing order and the
 // pieces of a sequence come from consecutive shares.  All arguments are wave-uniform.
+// (wave-uniform values pass through readfirstlane: the compiler cannot see that a shuffle
+// reduction or a ballot loop ends alike in every lane, and would otherwise keep the piece
+// bounds, and every loop over blocks after them, in vector registers and divergent branches)
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <typename Fn>
 __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int split, Fn&& piece) {
   const int lane = threadIdx.x & 63;
   const int c = p.piece_cost;
-  int tot = 0;
+  int tot = 0, nb_first = 0;
   for (int base = 0; base < p.num_seqs; base += 64) {
     const int s = base + lane;
     const int nb = s < p.num_seqs ? decode_blocks(p, s) : 0;
+    if (base == 0) nb_first = nb;  // kept: the first 64 sequences are not loaded twice
     tot += nb > 0 ? nb + c : 0;
   }
-  const long long T = wave_sum_i32(tot);
+  const long long T = wave_uniform(wave_sum_i32(tot));
   // never more shares than units, so no share is empty
   const long long n = min((long long)p.n_splits, T);
   if (split >= n) return;
@@ -195,18 +201,21 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int split,
   int carry = 0;
   for (int base = 0; base < p.num_seqs && carry < hi; base += 64) {
     const int s = base + lane;
-    const int nb = s < p.num_seqs ? decode_blocks(p, s) : 0;
+    const int nb = base == 0 ? nb_first : (s < p.num_seqs ? decode_blocks(p, s) : 0);
     const int w = nb > 0 ? nb + c : 0;
     const int incl = wave_incl_scan_i32(w, lane);
     const int start = carry + incl - w + c;  // units before block 0 of s
-    unsigned long long hits = __ballot(nb > 0 && start < hi && start + nb > lo);
+    const unsigned long long hits0 = __ballot(nb > 0 && start < hi && start + nb > lo);
+    unsigned long long hits = ((unsigned long long)(unsigned)wave_uniform((int)(hits0 >> 32)) << 32) |
+                              (unsigned)wave_uniform((int)hits0);
     while (hits) {
-      const int ln = __ffsll((long long)hits) - 1;
+      const int ln = wave_uniform(__ffsll((long long)hits) - 1);
       hits &= hits - 1;
-      const int bs = __builtin_amdgcn_readlane(start, ln), nbs = __builtin_amdgcn_readlane(nb, ln);
-      piece(base + ln, max(lo - bs, 0), min(hi - bs, nbs), nbs);
+      const int bs = wave_uniform(__builtin_amdgcn_readlane(start, ln));
+      const int nbs = wave_uniform(__builtin_amdgcn_readlane(nb, ln));
+      piece(base + ln, wave_uniform(max(lo - bs, 0)), wave_uniform(min(hi - bs, nbs)), nbs);
     }
-    carry += __builtin_amdgcn_readlane(incl, 63);
+    carry = wave_uniform(carry + __builtin_amdgcn_readlane(incl, 63));
   }
 }
 
@@ -219,224 +228,106 @@ __device__ __forceinline__ void note_piece(const DecodeParams& p, int split, int
   if (b1 == nb) p.piece_last[s] = split;
 }
 
-// One wave per (share, kv head).  Per 16-token block of each piece:
-//   S[tok][g] = K[tok][:] . Q[g][:]     v_mfma_f32_16x16x32_bf16, K through a swizzled LDS tile
-//   O^T[d][g] += V^T[d][tok] P^T[tok][g] v_mfma_f32_16x16x16_bf16, V straight from registers
-// The K tile rows are read in the order sigma(m) = m/4 + 4*(m%4), so score
-// element r of lane (a, g) belongs to token a + 4r: exactly the four tokens
-// whose V slices the same lane loaded.  P therefore never leaves its lane,
-// and the V^T operand of MFMA j (d = VEC*m + j) is two byte permutes of the
-// lane's own V words.  Two blocks are in flight while one is computed.
-// Blocks [b0, b1) of sequence s (nb blocks in all) for q heads 16*hg .. 16*hg+15 of kv
-// head kvh (all of them when the kv head has at most 16; more take one wave per group
-// of 16, each reading the blocks).
-//
-// GROUP (cascade prefix): the 16 columns are 16/G sequences x G heads instead of the G
-// heads of one sequence, so each block of the shared prefix feeds 16/G sequences at
-// once; s is the group's first sequence, split the prefix share, [b0, b1) blocks of
-// the prefix (whole blocks, every key visible).  Otherwise the piece covers blocks
-// [b0, b1) of sequence s after its skip_blocks shared blocks.
-template <int D, bool FP8, bool GROUP = false>
-__device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned char* k_lds, int split, int kvh, int s,
-                                             int b0, int b1, int nb, int hg = 0) {
+// One 16-token block of a piece for the wave's 16 matrix-core columns:
+//   S[tok][col] = K[tok][:] . Q[col][:]     v_mfma_f32_16x16x32_bf16, K through a swizzled LDS tile
+//   O^T[d][col] += V^T[d][tok] P^T[tok][col] v_mfma_f32_16x16x16_bf16, V straight from registers
+// The K tile rows are read in the order sigma(m) = m/4 + 4*(m%4), so score element r of
+// lane (a, c) belongs to token a + 4r: exactly the four tokens whose V slices the same lane
+// loaded.  P therefore never leaves its lane, and the V^T operand of MFMA j (d = VEC*m + j)
+// is two byte permutes of the lane's own V words.  Tokens outside [key_lo, tok1) are
+// masked by selection; V rows at or past tok1 are zeroed (never multiplied: NaN-safe).
+template <int D, bool FP8>
+__device__ __forceinline__ void block_step(const DecodeParams& p, const BlockRegs<D, FP8>& r, unsigned char* kl,
+                                           int blk_tok, int tok1, int key_lo,
+                                           const bf16x8 (&qf)[DecodeShape<D, FP8>::kKSteps], float& m, float& l,
+                                           f32x4 (&acc)[DecodeShape<D, FP8>::kVec]) {
   using Sh = DecodeShape<D, FP8>;
   constexpr int VEC = Sh::kVec, W = Sh::kWords;
-  const int row = p.qsl ? p.qsl[s] : s;
-  const int L = GROUP ? p.prefix_blocks * 16 : min(p.seq_lens[s], p.max_seq_len);
-  const int skip = GROUP ? 0 : decode_skip(p, L);
-  const int key_lo = GROUP ? 0 : decode_first_key(p, L);  // keys below it are outside the window
-  const int tok0 = (skip + b0) * 16;
-  const int tok1 = min(L, (skip + b1) * 16);
-  const int nblk = b1 - b0;
-  const bool whole = !GROUP && b0 == 0 && b1 == nb && !p.force_partial;
-
   const int lane = threadIdx.x & 63;
-  const int a = lane >> 4, c = lane & 15;  // row group / column within the row group
-  const int G = p.group;
-  // the lane's column: q head g of query row col_row (col_ok: a real column)
-  const int g = GROUP ? c % G : 16 * hg + c;
-  const int col_seq = GROUP ? s + c / G : s;
-  const bool col_ok = GROUP ? (c < (16 / G) * G && col_seq < p.num_seqs) : g < G;
-  const int col_row = GROUP ? col_seq : row;
-
-  // Q^T operand of MFMA kk: lane (a, column c) holds q[column][8*(a + 4*kk) .. +7]
-  bf16x8 qf[Sh::kKSteps];
-  {
-    if (col_ok) {
-      const size_t qoff = ((size_t)col_row * p.num_q_heads + kvh * G + g) * D;
-#pragma unroll
-      for (int kk = 0; kk < Sh::kKSteps; ++kk) {
-        const int d0 = 8 * (a + 4 * kk);
-        u32x4 t;
-        if (p.q_f32) {
-          const float* qp = reinterpret_cast<const float*>(p.query) + qoff + d0;
-          t = u32x4{pack_bf16x2(qp[0], qp[1]), pack_bf16x2(qp[2], qp[3]), pack_bf16x2(qp[4], qp[5]),
-                    pack_bf16x2(qp[6], qp[7])};
-        } else {
-          t = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.query) + qoff + d0);
-        }
-        qf[kk] = __builtin_bit_cast(bf16x8, t);
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < Sh::kKSteps; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
-  }
-
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int kElem = FP8 ? 1 : 2;
-  const size_t row_stride = (size_t)p.num_kv_heads * D * kElem;  // bytes between token rows of a block
-  const size_t block_bytes = row_stride * 16;
-  // byte offsets of this lane's four rows inside a block (a block of one pool is < 4 GB)
-  uint32_t roff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    roff[i] = (uint32_t)((a + 4 * i) * row_stride) + (uint32_t)(kvh * D * kElem) + (uint32_t)(c * Sh::kLoadBytes);
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
-  // Physical block ids of the partition, 64 at a time in one VGPR (lane i holds block
-  // win0 + i); a wave-uniform block id is then one v_readlane away.
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + skip + b0;
-  int win0 = 0;
-  int bt_win = lane < nblk ? bt[lane] : 0;
-
-  // Loads of block b of the partition.  Indices past the end re-read the last
-  // block (cache-resident, no HBM traffic) so that the loop is branch-free and
-  // the order of outstanding loads never depends on the data.
-  auto issue = [&](BlockRegs<D, FP8>& r, int b) {
-    b = min(b, nblk - 1);
-    if (b >= win0 + 64) {
-      win0 += 64;
-      bt_win = win0 + lane < nblk ? bt[win0 + lane] : 0;
-    }
-    int phys = __builtin_amdgcn_readlane(bt_win, b - win0);
-    phys = min(max(phys, 0), p.num_blocks - 1);
-    const uint8_t* kb = kbase + (size_t)phys * block_bytes;  // wave-uniform
-    const uint8_t* vb = vbase + (size_t)phys * block_bytes;
-    // a sequence's own blocks are streamed once; the shared prefix of a cascade is re-read by
-    // every group of sequences and is left to the caches
-    if constexpr (GROUP) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) load_raw(r.k[i], kb + roff[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) load_raw(r.v[i], vb + roff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) load_raw_stream(r.k[i], kb + roff[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) load_raw_stream(r.v[i], vb + roff[i]);
-    }
-  };
-
-  // LDS addresses: K row t, logical 16-byte chunk x lives at chunk x ^ (t % kChunks)
-  unsigned char* const kl = k_lds;
+  const int a = lane >> 4, c = lane & 15;
   const int m_row = (c >> 2) + 4 * (c & 3);  // sigma(c): the token row this lane feeds into the MFMA
-
-  auto compute = [&](BlockRegs<D, FP8>& r, int b, BlockRegs<D, FP8>& refill, int b_refill) {
-    const int blk_tok = tok0 + b * 16;
-    const bool partial = blk_tok + 16 > tok1;
-    // K slices -> LDS (bf16, swizzled)
+  const bool partial = blk_tok + 16 > tok1;
+  // K slices -> LDS (bf16, swizzled: row t, logical 16-byte chunk x lives at chunk x ^ (t % kChunks))
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w[W];
-      raw_to_words<D, FP8>(r.k[i], w);
-      const int t = a + 4 * i;
-      const int byte = c * VEC * 2;
-      unsigned char* dst = kl + t * Sh::kRowBytes + (((byte >> 4) ^ (t % Sh::kChunks)) << 4) + (byte & 15);
-      if constexpr (W == 4)
-        *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
-      else
-        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-    }
-    // V slices -> bf16 words, rows past the sequence end zeroed (never multiplied: NaN-safe)
-    uint32_t vw[4][W];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      raw_to_words<D, FP8>(r.v[i], vw[i]);
-      if (partial && blk_tok + a + 4 * i >= tok1) {
-#pragma unroll
-        for (int x = 0; x < W; ++x) vw[i][x] = 0u;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < Sh::kKSteps; ++kk) {
-      const int x = a + 4 * kk;
-      const u32x4 kw =
-          *reinterpret_cast<const u32x4*>(kl + m_row * Sh::kRowBytes + ((x ^ (m_row % Sh::kChunks)) << 4));
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[kk], sacc, 0, 0, 0);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // online softmax over the block: element r of this lane is token a + 4r of head g = c
-    float z[4];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = blk_tok + a + 4 * i;
-      const bool live = tok < tok1 && tok >= key_lo;
-      z[i] = live ? sacc[i] * p.scale_log2 : -INFINITY;
-      bmax = fmaxf(bmax, z[i]);
-    }
-    bmax = max_across_rows(bmax);
-    const float mnew = fmaxf(m, bmax);
-    const float alpha = fast_exp2(m - mnew);
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(z[i] - mnew);
-    l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = mnew;
-    i16x4 pb;
-    {
-      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-      pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
-    }
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t lo = __builtin_amdgcn_perm(vw[1][j >> 1], vw[0][j >> 1], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(vw[3][j >> 1], vw[2][j >> 1], sel);
-      const i16x4 va = __builtin_bit_cast(i16x4, u32x2{lo, hi});
-      acc[j] *= alpha;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[j], 0, 0, 0);
-    }
-    // this block's registers are consumed: refill them with a later block
-    issue(refill, b_refill);
-  };
-
-  // Blocks rotate through kInFlight register sets (loads of the others in flight while one
-  // is computed); blocks past the piece's end are fully masked copies of its last block
-  // (no effect on m, l or the output).  Measured on the Llama-3-8B layer at one wave per
-  // SIMD: 2 sets 89 us, 3 sets 92, 4 sets 94 (1 set 88 with more waves): the memory
-  // system, not the wave's latency, is the limit.
-  constexpr int kSets = kInFlight<FP8>;
-  BlockRegs<D, FP8> rs[kSets];
-  static_for<0, kSets>([&](auto i_c) {
-    issue(rs[decltype(i_c)::value], decltype(i_c)::value);
-    __builtin_amdgcn_sched_barrier(0);
-  });
-  for (int b = 0; b < nblk; b += kSets) {
-    static_for<0, kSets>([&](auto i_c) {
-      constexpr int i = decltype(i_c)::value;
-      compute(rs[i], b + i, rs[i], b + i + kSets);
-    });
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w[W];
+    raw_to_words<D, FP8>(r.k[i], w);
+    const int t = a + 4 * i;
+    const int byte = c * VEC * 2;
+    unsigned char* dst = kl + t * Sh::kRowBytes + (((byte >> 4) ^ (t % Sh::kChunks)) << 4) + (byte & 15);
+    if constexpr (W == 4)
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    else
+      *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
   }
+  // V slices -> bf16 words, rows past the sequence end zeroed
+  uint32_t vw[4][W];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    raw_to_words<D, FP8>(r.v[i], vw[i]);
+    if (partial && blk_tok + a + 4 * i >= tok1) {
+#pragma unroll
+      for (int x = 0; x < W; ++x) vw[i][x] = 0u;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < Sh::kKSteps; ++kk) {
+    const int x = a + 4 * kk;
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(kl + m_row * Sh::kRowBytes + ((x ^ (m_row % Sh::kChunks)) << 4));
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[kk], sacc, 0, 0, 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // the four row groups hold partial sums over different tokens of the same head
-  l = sum_across_rows(l);
+  // online softmax over the block: element r of this lane is token a + 4r of column c
+  float z[4];
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = blk_tok + a + 4 * i;
+    const bool live = tok < tok1 && tok >= key_lo;
+    z[i] = live ? sacc[i] * p.scale_log2 : -INFINITY;
+    bmax = fmaxf(bmax, z[i]);
+  }
+  bmax = max_across_rows(bmax);
+  const float mnew = fmaxf(m, bmax);
+  const float alpha = fast_exp2(m - mnew);
+  float pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(z[i] - mnew);
+  l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+  m = mnew;
+  i16x4 pb;
+  {
+    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+    pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t lo = __builtin_amdgcn_perm(vw[1][j >> 1], vw[0][j >> 1], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(vw[3][j >> 1], vw[2][j >> 1], sel);
+    const i16x4 va = __builtin_bit_cast(i16x4, u32x2{lo, hi});
+    acc[j] *= alpha;
+    acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[j], 0, 0, 0);
+  }
+}
 
-  if (!col_ok) return;
-  const int h = kvh * G + g;
-  // lane (a, column) holds O[column][VEC*(4a + r) + j] in acc[j][r]: 4*VEC consecutive d
+// Writes a finished piece of q head h (lane (a, column) holds O[column][VEC*(4a + r) + j] in
+// acc[j][r]: 4*VEC consecutive d; l already summed over the four row groups).  GROUP: the
+// cascade prefix partial of (prefix share split, sequence col_seq); whole: the normalised
+// output row; else the partial of piece id split + s (unique: shares and sequences are both
+// visited in increasing order).
+template <int D, bool GROUP>
+__device__ __forceinline__ void piece_output(const DecodeParams& p, const f32x4 (&acc)[D / 16], float m, float l,
+                                             int h, int split, int s, int row, int col_seq, bool whole) {
+  constexpr int VEC = D / 16;
+  const int a = (threadIdx.x & 63) >> 4;
   const int d0 = 4 * VEC * a;
   if constexpr (GROUP) {
     const size_t pi = ((size_t)split * p.num_seqs + col_seq) * p.num_q_heads + h;
@@ -471,7 +362,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
                                                               pack_bf16x2(acc[j + 2][r] * inv, acc[j + 3][r] * inv)};
     }
   } else {
-    const size_t pi = (size_t)(split + s) * p.num_q_heads + h;  // piece id split + s is unique
+    const size_t pi = (size_t)(split + s) * p.num_q_heads + h;
     float* po = p.part_o + pi * D + d0;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -483,6 +374,135 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
       p.part_l[pi] = l;
     }
   }
+}
+
+// Q^T operand words of MFMA kk for lane (a, column): q[row][head][8*(a + 4*kk) .. +7] as bf16.
+template <int D>
+__device__ __forceinline__ u32x4 q_words(const DecodeParams& p, size_t qoff, int a, int kk) {
+  const int d0 = 8 * (a + 4 * kk);
+  if (p.q_f32) {
+    const float* qp = reinterpret_cast<const float*>(p.query) + qoff + d0;
+    return u32x4{pack_bf16x2(qp[0], qp[1]), pack_bf16x2(qp[2], qp[3]), pack_bf16x2(qp[4], qp[5]),
+                 pack_bf16x2(qp[6], qp[7])};
+  }
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.query) + qoff + d0);
+}
+
+// One wave, one piece: blocks [b0, b1) of sequence s (nb blocks in all) for q heads
+// 16*hg .. 16*hg+15 of kv head kvh (all of them when the kv head has at most 16; more take
+// one wave per group of 16, each reading the blocks), kInFlight blocks in flight while one
+// is computed.
+//
+// GROUP (cascade prefix): the 16 columns are 16/G sequences x G heads instead of the G
+// heads of one sequence, so each block of the shared prefix feeds 16/G sequences at
+// once; s is the group's first sequence, split the prefix share, [b0, b1) blocks of
+// the prefix (whole blocks, every key visible).  Otherwise the piece covers blocks
+// [b0, b1) of sequence s after its skip_blocks shared blocks.
+template <int D, bool FP8, bool GROUP = false>
+__device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned char* k_lds, int split, int kvh, int s,
+                                             int b0, int b1, int nb, int hg = 0) {
+  using Sh = DecodeShape<D, FP8>;
+  constexpr int VEC = Sh::kVec;
+  const int row = p.qsl ? p.qsl[s] : s;
+  const int L = GROUP ? p.prefix_blocks * 16 : min(p.seq_lens[s], p.max_seq_len);
+  const int skip = GROUP ? 0 : decode_skip(p, L);
+  const int key_lo = GROUP ? 0 : decode_first_key(p, L);  // keys below it are outside the window
+  const int tok0 = (skip + b0) * 16;
+  const int tok1 = min(L, (skip + b1) * 16);
+  const int nblk = b1 - b0;
+  const bool whole = !GROUP && b0 == 0 && b1 == nb && !p.force_partial;
+
+  const int lane = threadIdx.x & 63;
+  const int a = lane >> 4, c = lane & 15;  // row group / column within the row group
+  const int G = p.group;
+  // the lane's column: q head g of query row col_row (col_ok: a real column)
+  const int g = GROUP ? c % G : 16 * hg + c;
+  const int col_seq = GROUP ? s + c / G : s;
+  const bool col_ok = GROUP ? (c < (16 / G) * G && col_seq < p.num_seqs) : g < G;
+  const int col_row = GROUP ? col_seq : row;
+
+  bf16x8 qf[Sh::kKSteps];
+  {
+    const size_t qoff = ((size_t)col_row * p.num_q_heads + kvh * G + g) * D;
+#pragma unroll
+    for (int kk = 0; kk < Sh::kKSteps; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, col_ok ? q_words<D>(p, qoff, a, kk) : u32x4{0u, 0u, 0u, 0u});
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int kElem = FP8 ? 1 : 2;
+  const size_t row_stride = (size_t)p.num_kv_heads * D * kElem;  // bytes between token rows of a block
+  const size_t block_bytes = row_stride * 16;
+  // byte offsets of this lane's four rows inside a block (a block of one pool is < 4 GB)
+  uint32_t roff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    roff[i] = (uint32_t)((a + 4 * i) * row_stride) + (uint32_t)(kvh * D * kElem) + (uint32_t)(c * Sh::kLoadBytes);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
+  // Physical block ids of the partition, 64 at a time in one VGPR (lane i holds block
+  // win0 + i); a wave-uniform block id is then one v_readlane away.  (Loading the next 64
+  // one issue ahead, so that a crossing never waits for the table, measured slower:
+  // Llama-3-8B layer 89.0 against 87.2 us, 70B long context 363 against 352.)
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + skip + b0;
+  int win0 = 0;
+  int bt_win = lane < nblk ? bt[lane] : 0;
+
+  // Loads of block b of the partition.  Indices past the end re-read the last
+  // block (cache-resident, no HBM traffic) so that the loop is branch-free and
+  // the order of outstanding loads never depends on the data.
+  auto issue = [&](BlockRegs<D, FP8>& r, int b) {
+    b = min(b, nblk - 1);
+    if (b >= win0 + 64) {
+      win0 += 64;
+      bt_win = win0 + lane < nblk ? bt[win0 + lane] : 0;
+    }
+    int phys = __builtin_amdgcn_readlane(bt_win, b - win0);
+    phys = min(max(phys, 0), p.num_blocks - 1);
+    const uint8_t* kb = kbase + (size_t)phys * block_bytes;  // wave-uniform
+    const uint8_t* vb = vbase + (size_t)phys * block_bytes;
+    // a sequence's own blocks are streamed once; the shared prefix of a cascade is re-read by
+    // every group of sequences and is left to the caches
+    if constexpr (GROUP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_raw(r.k[i], kb + roff[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_raw(r.v[i], vb + roff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_raw_stream(r.k[i], kb + roff[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_raw_stream(r.v[i], vb + roff[i]);
+    }
+  };
+
+  // Blocks rotate through kInFlight register sets (loads of the others in flight while one
+  // is computed); blocks past the piece's end are fully masked copies of its last block
+  // (no effect on m, l or the output).  Measured on the Llama-3-8B layer at one wave per
+  // SIMD: 2 sets 89 us, 3 sets 92, 4 sets 94 (1 set 88 with more waves): the memory
+  // system, not the wave's latency, is the limit.
+  constexpr int kSets = kInFlight<FP8>;
+  BlockRegs<D, FP8> rs[kSets];
+  static_for<0, kSets>([&](auto i_c) {
+    issue(rs[decltype(i_c)::value], decltype(i_c)::value);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  for (int b = 0; b < nblk; b += kSets) {
+    static_for<0, kSets>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      block_step<D, FP8>(p, rs[i], k_lds, tok0 + (b + i) * 16, tok1, key_lo, qf, m, l, acc);
+      // this block's registers are consumed: refill them with a later block
+      issue(rs[i], b + i + kSets);
+    });
+  }
+
+  // the four row groups hold partial sums over different tokens of the same head
+  l = sum_across_rows(l);
+  if (col_ok) piece_output<D, GROUP>(p, acc, m, l, kvh * G + g, split, s, row, col_seq, whole);
 }
 
 // With a cascade, the first groups * prefix_shares work-groups of each kv head take the

@@ -10,6 +10,8 @@
 // work-groups are dispatched first and keep their compute units streaming K/V from HBM while
 // the prefill items run on the others.  The host plan sizes the two parts so that they end
 // together; the decode merge and the prefill merge follow as in the separate launches.
+#include <type_traits>
+
 #include "decode_body.h"
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -19,7 +21,7 @@ namespace pa {
 
 namespace {
 
-template <int D, bool WINDOW, bool FP8>
+template <int D, bool WINDOW, bool FP8, bool PREFIX>
 __global__ void __launch_bounds__(512) fused_kernel(FusedParams f) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wg = blockIdx.x;
@@ -33,35 +35,41 @@ __global__ void __launch_bounds__(512) fused_kernel(FusedParams f) {
   }
   // prefill items in the order of the prefill kernel's grid (kv heads fastest)
   const int w = wg - f.n_decode_wgs;
-  prefill_body<D, WINDOW>(f.pre, smem, w / f.pre.num_kv_heads, w % f.pre.num_kv_heads);
+  prefill_body<D, WINDOW, PREFIX>(f.pre, smem, w / f.pre.num_kv_heads, w % f.pre.num_kv_heads);
 }
 
 }  // namespace
 
 size_t prefill_lds_bytes(int head_dim);
 
-hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_t stream) {
+hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_t stream, int timing_id) {
   const bool win = f.pre.window > 0 || f.pre.chunk > 0;
+  const bool prefix = f.pre.prefix_keys > 0;  // cascade prefix tiles (never with a window)
   const dim3 grid(f.n_decode_wgs + f.pre.n_items * f.pre.num_kv_heads);
   const size_t lds = prefill_lds_bytes(head_dim);
-  timing_mark(kKFused, true, stream);
+  timing_mark(timing_id, true, stream);
   auto launch = [&](auto kernel) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
     hipLaunchKernelGGL(kernel, grid, dim3(512), lds, stream, f);
   };
-  if (head_dim == 128) {
-    if (fp8)
-      win ? launch(&fused_kernel<128, true, true>) : launch(&fused_kernel<128, false, true>);
+  auto pick = [&](auto d_c, auto fp8_c) {
+    constexpr int D = decltype(d_c)::value;
+    constexpr bool F = decltype(fp8_c)::value;
+    if (prefix)
+      launch(&fused_kernel<D, false, F, true>);
+    else if (win)
+      launch(&fused_kernel<D, true, F, false>);
     else
-      win ? launch(&fused_kernel<128, true, false>) : launch(&fused_kernel<128, false, false>);
-  } else {
-    if (fp8)
-      win ? launch(&fused_kernel<64, true, true>) : launch(&fused_kernel<64, false, true>);
-    else
-      win ? launch(&fused_kernel<64, true, false>) : launch(&fused_kernel<64, false, false>);
-  }
-  timing_mark(kKFused, false, stream);
+      launch(&fused_kernel<D, false, F, false>);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (head_dim == 128)
+    fp8 ? pick(std::integral_constant<int, 128>{}, T{}) : pick(std::integral_constant<int, 128>{}, F{});
+  else
+    fp8 ? pick(std::integral_constant<int, 64>{}, T{}) : pick(std::integral_constant<int, 64>{}, F{});
+  timing_mark(timing_id, false, stream);
   return hipGetLastError();
 }
 

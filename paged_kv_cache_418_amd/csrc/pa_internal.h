@@ -98,6 +98,15 @@ struct PrefillParams {
   float v_scale;             // 1, or the fp8 value scale (pools staged as the codes' exact values)
   int window;                // sliding window (> 0): the row at position p sees keys p-window+1 .. p
   int chunk;                 // chunked local attention (> 0): the row at position p sees keys C*(p div C) .. p
+  // cascade prefix tiles (prefill_body's PREFIX form): the rows of a kv head are the
+  // prefix_rows query rows x its G q heads, each sees keys 0 .. prefix_keys-1 of table
+  // row 0, and an item's unnormalised partial goes to pre_* at share kt0 / prefix_share_tiles
+  int prefix_rows;
+  int prefix_keys;
+  int prefix_share_tiles;
+  float* pre_o;              // [shares][prefix_rows][num_q_heads][D]
+  float* pre_m;              // [shares][prefix_rows][num_q_heads] (log2 units)
+  float* pre_l;              // [shares][prefix_rows][num_q_heads]
   int n_items;
   uint64_t items[kMaxPrefillItems];
 };
@@ -179,7 +188,14 @@ hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t stream);
 // decode waves and prefill items in one launch; fp8: the decode waves read E4M3 pools (the
 // prefill items read the bf16 pools named in f.pre, the staging pool for fp8 batches)
-hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_t stream);
+// (timing_id: the kernel id the launch is timed under -- kKFused for a mixed batch, kKDecode
+// for a cascade, whose prefix tiles and suffix shares share the launch)
+hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_t stream, int timing_id = kKFused);
+// Cascade prefix over fp8 pools: the prefix_blocks blocks of table row 0 copied, as the exact
+// bf16 values of their codes, to staging blocks 0 .. prefix_blocks-1, with their table.
+hipError_t launch_stage_prefix_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
+                                   int prefix_blocks, int num_kv_heads, int head_dim, int num_blocks,
+                                   uint16_t* stage_k, uint16_t* stage_v, int32_t* stage_table, hipStream_t stream);
 
 // The decode's static scratch (pa_decode_static): its size, and its device address on the
 // current device (looked up once per device).

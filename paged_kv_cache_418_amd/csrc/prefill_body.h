@@ -70,9 +70,15 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // One work item of a prefill launch: item item_idx (its bits as in PrefillParams) for kv head
 // kvh, by a work-group of PrefillShape<D>::kThreads threads with smem =
 // PrefillShape<D>::kLdsBytes bytes of LDS.
-template <int D, bool WINDOW>
+//
+// PREFIX (cascade prefix tiles, without WINDOW): the "positions" of the item are query rows
+// 0 .. p.prefix_rows-1 of the batch, each one query of its own sequence, and every row sees
+// all of keys 0 .. p.prefix_keys-1 (the blocks that every sequence's table begins with,
+// read through table row s = 0); the item leaves its unnormalised partial in pre_*.
+template <int D, bool WINDOW, bool PREFIX = false>
 __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned char* smem, int item_idx, int kvh) {
   using Sh = PrefillShape<D>;
+  static_assert(!(PREFIX && WINDOW), "prefix tiles see the whole prefix");
 
   // ---- work item
   const uint64_t item = p.items[item_idx];
@@ -82,13 +88,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   const int kt0 = (int)((item >> 32) & 0xFFFFu), kt1 = (int)(item >> 48);
   const int G = p.group;
   const int P = p.tile_positions;         // positions per row tile (rows = P * G <= 256)
-  const int q0 = p.qsl[s];
-  const int q_len = p.qsl[s + 1] - q0;
-  const int L = p.seq_lens[s];
-  const int c = L - q_len;
+  const int q0 = PREFIX ? 0 : p.qsl[s];
+  const int q_len = PREFIX ? p.prefix_rows : p.qsl[s + 1] - q0;
+  const int L = PREFIX ? p.prefix_keys : p.seq_lens[s];
+  // every position of a prefix tile sits at L - 1 (all of the prefix visible)
+  const int c = PREFIX ? 0 : L - q_len;
   const int pos0 = rt * P;
   const int pos_end = min(q_len, pos0 + P);  // positions of this tile: pos0 .. pos_end-1
-  const int kv_end = c + pos_end;            // keys the last row sees (exclusive)
+  const int kv_end = PREFIX ? L : c + pos_end;  // keys the last row sees (exclusive)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -97,10 +104,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // ---- the lane's row: R = 32*wave + rl -> (position pos0 + R / G, q head kvh*G + R % G)
   const int R = 32 * wave + rl;
   const bool row_ok = R < P * G && pos0 + R / G < pos_end;
-  const int row_pos = c + pos0 + R / G;  // absolute position: keys <= it are visible
+  const int row_pos = PREFIX ? L - 1 : c + pos0 + R / G;  // absolute position: keys <= it are visible
   // smallest and largest row position of the wave (masking and skipping whole tiles)
-  const int wave_first = c + pos0 + (32 * wave) / G;
-  const int wave_last = c + min(pos_end - 1, pos0 + (32 * wave + 31) / G);
+  const int wave_first = PREFIX ? L - 1 : c + pos0 + (32 * wave) / G;
+  const int wave_last = PREFIX ? L - 1 : c + min(pos_end - 1, pos0 + (32 * wave + 31) / G);
   const bool wave_live = 32 * wave < P * G && pos0 + (32 * wave) / G < pos_end;
   // WINDOW: first visible key of the row at position q (non-decreasing in q)
   auto first_visible = [&](int q) { return p.chunk > 0 ? q - q % p.chunk : q - p.window + 1; };
@@ -568,6 +575,26 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   __syncthreads();  // every wave is done with the rings
   if (!wave_live) return;
   const float l = sum_halves(lsum);
+  if constexpr (PREFIX) {
+    // unnormalised O, the reference maximum and the weight sum of (sequence pos0 + R / G,
+    // q head kvh*G + R % G) for the prefix share of this item's keys; lane (rl, half) holds
+    // d = 32n + 8*(r/4) + 4*half + r%4, four consecutive d per (n, r/4)
+    if (!row_ok) return;
+    const size_t pi = ((size_t)(kt0 / p.prefix_share_tiles) * p.prefix_rows + pos0 + R / G) * p.num_q_heads +
+                      kvh * G + R % G;
+    float* po = p.pre_o + pi * D + 4 * half;
+#pragma unroll
+    for (int n = 0; n < Sh::kDTiles; ++n)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<f32x4*>(po + 32 * n + 8 * rq) =
+            f32x4{acc[n][4 * rq], acc[n][4 * rq + 1], acc[n][4 * rq + 2], acc[n][4 * rq + 3]};
+    if (half == 0) {
+      p.pre_m[pi] = m_ref;
+      p.pre_l[pi] = l;
+    }
+    return;
+  }
   const float inv = whole ? p.v_scale / l : (l > 0.f ? 1.f / l : 0.f);  // a row that saw no key stores 0
   const size_t slot_row0 = ((size_t)(p.item_base + item_idx) * p.num_kv_heads + kvh) * kPrefillRows + 32 * wave;
   if (whole) {

@@ -161,7 +161,49 @@ __global__ void __launch_bounds__(256) stage_fp8_kernel(const uint8_t* key_cache
   }
 }
 
+// Cascade prefix over fp8 pools: work-group (j, q) copies quarter q of block j of table row 0
+// -- the prefix every sequence's table begins with -- to staging block j as the exact bf16
+// values of its codes (16 codes per thread: one load of K and one of V each), and (q = 0)
+// writes staging table entry j = j.
+__global__ void __launch_bounds__(256) stage_prefix_fp8_kernel(const uint8_t* key_cache, const uint8_t* value_cache,
+                                                                const int32_t* block_tables, int row_bytes,
+                                                                int num_blocks, uint16_t* stage_k, uint16_t* stage_v,
+                                                                int32_t* stage_table) {
+  const int j = blockIdx.x;
+  const int phys = min(max(block_tables[j], 0), num_blocks - 1);
+  if (threadIdx.x == 0 && blockIdx.y == 0) stage_table[j] = j;
+  const int block_bytes = 16 * row_bytes;
+  const uint8_t* ks = key_cache + (size_t)phys * block_bytes;
+  const uint8_t* vs = value_cache + (size_t)phys * block_bytes;
+  uint16_t* kd = stage_k + (size_t)j * block_bytes;
+  uint16_t* vd = stage_v + (size_t)j * block_bytes;
+  for (int e = (blockIdx.y * 256 + threadIdx.x) * 16; e < block_bytes; e += gridDim.y * 256 * 16) {
+    const u32x4 kc = *reinterpret_cast<const u32x4*>(ks + e);
+    const u32x4 vc = *reinterpret_cast<const u32x4*>(vs + e);
+    const u32x2 k0 = e4m3x4_to_bf16x4(kc.x), k1 = e4m3x4_to_bf16x4(kc.y), k2 = e4m3x4_to_bf16x4(kc.z),
+                k3 = e4m3x4_to_bf16x4(kc.w);
+    const u32x2 v0 = e4m3x4_to_bf16x4(vc.x), v1 = e4m3x4_to_bf16x4(vc.y), v2 = e4m3x4_to_bf16x4(vc.z),
+                v3 = e4m3x4_to_bf16x4(vc.w);
+    *reinterpret_cast<u32x4*>(kd + e) = u32x4{k0.x, k0.y, k1.x, k1.y};
+    *reinterpret_cast<u32x4*>(kd + e + 8) = u32x4{k2.x, k2.y, k3.x, k3.y};
+    *reinterpret_cast<u32x4*>(vd + e) = u32x4{v0.x, v0.y, v1.x, v1.y};
+    *reinterpret_cast<u32x4*>(vd + e + 8) = u32x4{v2.x, v2.y, v3.x, v3.y};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stage_prefix_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
+                                   int prefix_blocks, int num_kv_heads, int head_dim, int num_blocks,
+                                   uint16_t* stage_k, uint16_t* stage_v, int32_t* stage_table, hipStream_t stream) {
+  // one 16-code chunk per thread: 256 threads x 16 codes per work-group along y
+  const int parts = (16 * num_kv_heads * head_dim + 256 * 16 - 1) / (256 * 16);
+  timing_mark(kKStageFp8, true, stream);
+  hipLaunchKernelGGL(stage_prefix_fp8_kernel, dim3(prefix_blocks, parts), dim3(256), 0, stream, key_cache, value_cache,
+                     block_tables, num_kv_heads * head_dim, num_blocks, stage_k, stage_v, stage_table);
+  timing_mark(kKStageFp8, false, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
                             int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int max_blocks,
