@@ -216,8 +216,9 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache, const
  * fixing where the window starts; this library takes the W most recent
  * positions, the current one included.  Table entries wholly before the
  * window are not read (a caller may have given those blocks up; PA_VALIDATE=1
- * still checks every entry).  dtype: PA_BF16.
- * sliding_window >= 1 (a window of at least seq_lens[s] is pa_decode).
+ * still checks every entry).  dtype: PA_BF16, or PA_F32 (fp32 pools and
+ * queries, the vector-ALU kernel).  sliding_window >= 1 (a window of at
+ * least seq_lens[s] is pa_decode).
  * workspace: pa_decode_workspace_bytes(...) with the same max_seq_len.
  * Other arguments as pa_decode.
  */
@@ -235,7 +236,7 @@ pa_status_t pa_decode_window(void* out, const void* query, const void* key_cache
  * chunk_size tokens, 0 .. C-1, C .. 2C-1, ..., and a row sees the keys of its
  * own chunk up to itself).  The query of sequence s (at position L-1) attends
  * to positions C*((L-1) div C) .. L-1.  Table entries wholly before that
- * chunk are not read.  dtype: PA_BF16; chunk_size >= 1.  workspace:
+ * chunk are not read.  dtype: PA_BF16 or PA_F32; chunk_size >= 1.  workspace:
  * pa_decode_workspace_bytes(...) with the same max_seq_len.  Other arguments
  * as pa_decode.
  */
@@ -293,7 +294,9 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
  * the prefix is read once per group of 16/G sequences by decode waves instead.
  * Requirements: prefix_blocks >= 1; every seq_lens[s] >= prefix_blocks *
  * block_size; block_tables[s][j] the same for every s and j < prefix_blocks
- * (checked under PA_VALIDATE=1, trusted otherwise).  dtype: PA_BF16.
+ * (checked under PA_VALIDATE=1, trusted otherwise).  dtype: PA_BF16, or
+ * PA_F32 (fp32 pools and queries: the plain fp32 decode over each whole
+ * sequence, the same attention without the shared grouping).
  * workspace: pa_decode_cascade_workspace_bytes(...) bytes (always needed).
  * num_splits: waves per kv head for the suffixes, as in pa_decode.  Other
  * arguments as pa_decode.
@@ -334,8 +337,12 @@ size_t pa_prefill_varlen_workspace_bytes(const int32_t* query_start_loc_host, co
  * [B] tutorials 5 (chunked prefill) and 7.
  * For row t of sequence s (new row i, c = seq_lens[s]-q_len cached tokens):
  * out[t][h][:] = sum_{j <= c+i} softmax_j(scale * q[t][h] . K_j) V_j.
- * query/out: [num_tokens][num_q_heads][head_dim]; dtype PA_BF16 (PA_F32 is
- * accepted for batches whose q_len are all 1).  The host copies of
+ * query/out: [num_tokens][num_q_heads][head_dim]; dtype PA_BF16 (the
+ * matrix-core kernel) or PA_F32 (fp32 pools and activations: decode rows on
+ * the vector-ALU decode kernel, and a batch with chunks runs every token as a
+ * decode row of its own, which sees exactly the keys of its position -- one
+ * decode launch, no matrix cores; the workspace sizes below count it).  The
+ * host copies of
  * query_start_loc and seq_lens plan the work (the control plane is on the
  * CPU) and must equal the device arrays.  scale must be positive and finite
  * (PA_ERR_SHAPE otherwise; the same holds for every pa_prefill_varlen*
@@ -357,8 +364,8 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
  * positions max(0, p-sliding_window+1) .. p.  No pool data is read from the
  * blocks wholly before the window of a sequence's first new row (their table
  * entries may name any block; PA_VALIDATE=1 still checks them), and 64-key
- * tiles wholly before it are not computed.  dtype: PA_BF16 (activations and
- * pools); sliding_window >= 1.  workspace:
+ * tiles wholly before it are not computed.  dtype: PA_BF16 or PA_F32 (as
+ * pa_prefill_varlen); sliding_window >= 1.  workspace:
  * pa_prefill_varlen_window_workspace_bytes(...) with the same window (the
  * work split depends on it; returns 0 on invalid input).  Other arguments as
  * pa_prefill_varlen.
@@ -379,7 +386,7 @@ pa_status_t pa_prefill_varlen_window(void* out, const void* query, const void* k
  * (the reading of pa_decode_local): the row at position p attends to
  * positions C*(p div C) .. p, C = chunk_size >= 1.  No pool data is read from
  * the blocks wholly before the chunk of a sequence's first new row.  dtype:
- * PA_BF16.  workspace: pa_prefill_varlen_local_workspace_bytes(...) with the
+ * PA_BF16 or PA_F32.  workspace: pa_prefill_varlen_local_workspace_bytes(...) with the
  * same chunk_size (0 on invalid input).  Other arguments as
  * pa_prefill_varlen.
  */
@@ -403,8 +410,10 @@ pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* ke
  * codes, into a staging pool in the workspace (its size depends on the
  * chunk sequences' lengths and on bt_stride), then attended by the bf16
  * matrix-core kernel with k_scale folded into the score scale and v_scale
- * into the output.  q_dtype (= out dtype): PA_BF16 (PA_F32 for batches whose
- * q_len are all 1).  Other arguments as pa_prefill_varlen.
+ * into the output.  q_dtype (= out dtype): PA_BF16, or PA_F32 (decode rows
+ * as pa_decode_fp8 with fp32 queries; a batch with chunks runs every token as
+ * a decode row of its own on the fp8 decode kernel, as pa_prefill_varlen does
+ * for PA_F32).  Other arguments as pa_prefill_varlen.
  */
 size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
                                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -416,6 +425,58 @@ pa_status_t pa_prefill_varlen_fp8(void* out, const void* query, const uint8_t* k
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                   int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale, float v_scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_window_fp8, pa_decode_local_fp8 -- pa_decode_window and
+ * pa_decode_local over E4M3FN pools, with the scales and q_dtype of
+ * pa_decode_fp8 ([A] §5.1; [B] tutorial 6).  workspace:
+ * pa_decode_workspace_bytes(...) with the same max_seq_len.  Other arguments
+ * as pa_decode_fp8 and pa_decode_window / pa_decode_local.
+ */
+pa_status_t pa_decode_window_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                 const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                 pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t sliding_window,
+                                 int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+pa_status_t pa_decode_local_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t chunk_size,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_varlen_window_fp8, pa_prefill_varlen_local_fp8 --
+ * pa_prefill_varlen_window and pa_prefill_varlen_local over E4M3FN pools,
+ * with the scales, q_dtype and staging of pa_prefill_varlen_fp8 ([A] §5.1;
+ * [B] tutorials 5 and 6).  workspace: the matching *_workspace_bytes(...)
+ * with the same bt_stride and window or chunk size (0 on invalid input).
+ */
+size_t pa_prefill_varlen_window_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t head_dim, int32_t bt_stride, int32_t sliding_window);
+pa_status_t pa_prefill_varlen_window_fp8(void* out, const void* query, const uint8_t* key_cache,
+                                         const uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                         const int32_t* seq_lens, const int32_t* query_start_loc,
+                                         const int32_t* seq_lens_host, const int32_t* query_start_loc_host,
+                                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                         int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale,
+                                         float v_scale, int32_t sliding_window, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+size_t pa_prefill_varlen_local_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t bt_stride, int32_t chunk_size);
+pa_status_t pa_prefill_varlen_local_fp8(void* out, const void* query, const uint8_t* key_cache,
+                                        const uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* seq_lens, const int32_t* query_start_loc,
+                                        const int32_t* seq_lens_host, const int32_t* query_start_loc_host,
+                                        int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale,
+                                        float v_scale, int32_t chunk_size, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /*
  * Host block pool -- the control plane that hands out the physical blocks

@@ -5,11 +5,11 @@ functions re-exported here are its ctypes binding and take GPU torch tensors.
 ``workloads`` holds the seeded synthetic inputs.
 """
 from ._binding import (  # noqa: F401
-    BlockPool, pool_hash_blocks, PA_BF16, PA_F32, PA_FP8_E4M3, PAError, abi_version, header_symbols, load, pa_decode, pa_decode_cascade,
-    pa_decode_cascade_fp8, pa_decode_cascade_workspace_bytes, pa_decode_fp8, pa_decode_local, pa_decode_static, pa_decode_window,
+    BlockPool, pool_hash_blocks, PA_BF16, PA_F32, PA_FP8_E4M3, PAError, abi_version, header_symbols, load,
+    pa_decode, pa_decode_cascade, pa_decode_cascade_fp8, pa_decode_cascade_workspace_bytes, pa_decode_fp8,
+    pa_decode_local, pa_decode_local_fp8, pa_decode_static, pa_decode_window, pa_decode_window_fp8,
     pa_decode_workspace_bytes, pa_prefill_varlen, pa_prefill_varlen_fp8, pa_prefill_varlen_fp8_workspace_bytes,
-    pa_prefill_varlen_local, pa_prefill_varlen_local_workspace_bytes, pa_prefill_varlen_window,
-    pa_prefill_varlen_window_workspace_bytes, pa_prefill_varlen_workspace_bytes,
-    pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_write_kv, set_fused, set_validate,
-    timing_enable,
-    timing_read, timing_reset)
+    pa_prefill_varlen_local, pa_prefill_varlen_local_fp8, pa_prefill_varlen_local_workspace_bytes,
+    pa_prefill_varlen_window, pa_prefill_varlen_window_fp8, pa_prefill_varlen_window_workspace_bytes,
+    pa_prefill_varlen_workspace_bytes, pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_write_kv,
+    set_fused, set_validate, timing_enable, timing_read, timing_reset)

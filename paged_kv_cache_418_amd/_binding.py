@@ -96,6 +96,16 @@ def load() -> ctypes.CDLL:
             "pa_prefill_varlen_local_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
             "pa_prefill_varlen_local": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                          ctypes.c_int, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_window_fp8": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                                      f32, f32, i32, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_local_fp8": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                                     f32, f32, i32, i32, P, sz, P], ctypes.c_int),
+            "pa_prefill_varlen_window_fp8_workspace_bytes": ([P, P, i32, i32, i32, i32, i32, i32], sz),
+            "pa_prefill_varlen_window_fp8": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                              ctypes.c_int, f32, f32, i32, P, sz, P], ctypes.c_int),
+            "pa_prefill_varlen_local_fp8_workspace_bytes": ([P, P, i32, i32, i32, i32, i32, i32], sz),
+            "pa_prefill_varlen_local_fp8": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                             ctypes.c_int, f32, f32, i32, P, sz, P], ctypes.c_int),
             "pa_pool_create": ([i32, i32, ctypes.POINTER(P)], ctypes.c_int),
             "pa_pool_destroy": ([P], None),
             "pa_pool_num_free": ([P], i32),
@@ -527,6 +537,75 @@ def pa_prefill_varlen_fp8(query, key_cache, value_cache, block_tables, seq_lens,
         sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), float(k_scale), float(v_scale),
         None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
+
+
+def _decode_fp8_masked(name, query, key_cache, value_cache, block_tables, seq_lens, scale, k_scale, v_scale,
+                       max_seq_len, size, num_splits, out, workspace):
+    lib = load()
+    S, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    out = torch.empty_like(query) if out is None else out
+    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, num_splits), query.device, workspace)
+    _check(name, getattr(lib, name)(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B, NB, max_seq_len, float(scale), _dtype_code(query),
+        float(k_scale), float(v_scale), size, num_splits, None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
+def pa_decode_window_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: float, k_scale: float,
+                         v_scale: float, max_seq_len: int, sliding_window: int, num_splits: int = 0, out=None,
+                         workspace=None):
+    """pa_decode_window over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
+    return _decode_fp8_masked("pa_decode_window_fp8", query, key_cache, value_cache, block_tables, seq_lens, scale,
+                              k_scale, v_scale, max_seq_len, sliding_window, num_splits, out, workspace)
+
+
+def pa_decode_local_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: float, k_scale: float,
+                        v_scale: float, max_seq_len: int, chunk_size: int, num_splits: int = 0, out=None,
+                        workspace=None):
+    """pa_decode_local over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
+    return _decode_fp8_masked("pa_decode_local_fp8", query, key_cache, value_cache, block_tables, seq_lens, scale,
+                              k_scale, v_scale, max_seq_len, chunk_size, num_splits, out, workspace)
+
+
+def _prefill_fp8_masked(name, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, seq_lens_host,
+                        query_start_loc_host, scale, k_scale, v_scale, size, out, workspace):
+    lib = load()
+    T, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    qh = _i32_host(query_start_loc_host)
+    sh = _i32_host(seq_lens_host)
+    out = torch.empty_like(query) if out is None else out
+    need = int(getattr(lib, name + "_workspace_bytes")(qh.data_ptr(), sh.data_ptr(), sh.numel(), Hq, Hkv, D,
+                                                       block_tables.shape[1], size))
+    ws, wsb = _workspace(need, query.device, workspace)
+    _check(name, getattr(lib, name)(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(),
+        sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), float(k_scale), float(v_scale), size,
+        None if ws is None else ws.data_ptr(), wsb, _stream()))
+    return out
+
+
+def pa_prefill_varlen_window_fp8(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc,
+                                 seq_lens_host, query_start_loc_host, scale: float, k_scale: float, v_scale: float,
+                                 sliding_window: int, out=None, workspace=None):
+    """pa_prefill_varlen_window over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
+    return _prefill_fp8_masked("pa_prefill_varlen_window_fp8", query, key_cache, value_cache, block_tables, seq_lens,
+                               query_start_loc, seq_lens_host, query_start_loc_host, scale, k_scale, v_scale,
+                               sliding_window, out, workspace)
+
+
+def pa_prefill_varlen_local_fp8(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc,
+                                seq_lens_host, query_start_loc_host, scale: float, k_scale: float, v_scale: float,
+                                chunk_size: int, out=None, workspace=None):
+    """pa_prefill_varlen_local over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
+    return _prefill_fp8_masked("pa_prefill_varlen_local_fp8", query, key_cache, value_cache, block_tables, seq_lens,
+                               query_start_loc, seq_lens_host, query_start_loc_host, scale, k_scale, v_scale,
+                               chunk_size, out, workspace)
 
 
 # ---- host block pool (pa_pool_*)

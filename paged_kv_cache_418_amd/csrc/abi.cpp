@@ -882,7 +882,9 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
                                                     prefix_blocks, num_splits, elem);
       if (cp.ok) need = std::max(need, cp.total);
     }
-  return need;
+  // fp32 pools run the plain decode
+  return std::max(need, pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                  num_splits));
 }
 
 pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -891,7 +893,7 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
                               int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
                               pa_dtype_t dtype, int32_t prefix_blocks, int32_t num_splits, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "cascade decode: dtype must be PA_BF16");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
   const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                                                         prefix_blocks, num_splits);
   pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
@@ -906,6 +908,12 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
     st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
     if (st != PA_OK) return st;
   }
+  // fp32 pools: the plain fp32 decode over each whole sequence (the same attention; only the
+  // grouping of keys, and so the order of fp32 sums, would differ)
+  if (dtype == PA_F32)
+    return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                      pa::kF32, 1, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
   if (cascade_tiles_enabled()) {
     const CascadeTilePlan cp =
         plan_cascade_tiles(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits, 2);
@@ -1239,13 +1247,13 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
                  head_dim, kv_kind == pa::kFP8 ? 1 : 2, sliding_window, local_chunk, sp);
   if (st != PA_OK) return st;
   const VarlenPlan& plan = sp.plan;
-  if (dtype == PA_F32 && !plan.items.empty())
-    return fail(PA_ERR_DTYPE, "fp32 is supported only for decode rows (q_len == 1); chunks need PA_BF16");
+  // chunks of fp32 pools, or of fp32 queries over fp8 pools: every token on its own, no scratch
+  const bool rows = dtype == PA_F32 && !plan.items.empty();
   const StageLayout stage = kv_kind == pa::kFP8 ? stage_layout(query_start_loc_host, seq_lens_host, num_seqs, bt_stride,
                                                                 num_kv_heads, head_dim)
                                                    : StageLayout{};
   const size_t base_need = varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
-  const size_t need = plan.items.empty() ? base_need : align_up(base_need) + stage.total;
+  const size_t need = rows ? 0 : plan.items.empty() ? base_need : align_up(base_need) + stage.total;
   if (need && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
@@ -1265,6 +1273,17 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int dec_kind = kv_kind == pa::kFP8 ? pa::kFP8 : (dtype == PA_F32 ? pa::kF32 : pa::kBF16);
+  if (rows) {
+    int max_len = 1;
+    for (int s = 0; s < num_seqs; ++s) max_len = std::max(max_len, (int)seq_lens_host[s]);
+    pa::DecodeParams p = make_decode_params(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens,
+                                            query_start_loc, num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                                            head_dim, max_len, scale, dec_kind, 1, k_scale, v_scale, 1, nullptr, 0,
+                                            sliding_window, local_chunk);
+    p.num_blocks = num_blocks;
+    return hip_status(pa::launch_rows_f32(p, dec_kind, head_dim, num_tokens, hs), "fp32 rows launch");
+  }
+
   if (plan.any_decode && !sp.fused) {
     st = run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc, num_seqs,
                     num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, plan.max_decode_len, scale,
@@ -1405,13 +1424,13 @@ pa_status_t pa_decode_window(void* out, const void* query, const void* key_cache
                              int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype,
                              int32_t sliding_window, int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "sliding-window decode: dtype must be PA_BF16");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
   if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
   pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                                      num_splits, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (num_q_heads / num_kv_heads > pa::kMaxGqa)
+  if (dtype == PA_BF16 && num_q_heads / num_kv_heads > pa::kMaxGqa)
     return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGqa);
   if (num_seqs == 0) return ok();
   if (validate_enabled()) {
@@ -1420,8 +1439,8 @@ pa_status_t pa_decode_window(void* out, const void* query, const void* key_cache
   }
   return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                    pa::kBF16, 0, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
-                    0, sliding_window);
+                    dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype == PA_F32, 1.f, 1.f, num_splits, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream), 0, sliding_window);
 }
 
 pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -1431,7 +1450,7 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               int32_t num_blocks, float scale, pa_dtype_t dtype, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_BF16 (or PA_F32 for decode rows)");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
   return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
                     seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                     block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream);
@@ -1444,7 +1463,7 @@ pa_status_t pa_prefill_varlen_window(void* out, const void* query, const void* k
                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                      int32_t num_blocks, float scale, pa_dtype_t dtype, int32_t sliding_window,
                                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "sliding-window prefill: dtype must be PA_BF16");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
   if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
   return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
                     seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
@@ -1468,13 +1487,13 @@ pa_status_t pa_decode_local(void* out, const void* query, const void* key_cache,
                             int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype,
                             int32_t chunk_size, int32_t num_splits, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "chunked local decode: dtype must be PA_BF16");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
   if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
   pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                                      num_splits, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (num_q_heads / num_kv_heads > pa::kMaxGqa)
+  if (dtype == PA_BF16 && num_q_heads / num_kv_heads > pa::kMaxGqa)
     return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to %d q heads per kv head", pa::kMaxGqa);
   if (num_seqs == 0) return ok();
   if (validate_enabled()) {
@@ -1483,8 +1502,8 @@ pa_status_t pa_decode_local(void* out, const void* query, const void* key_cache,
   }
   return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                    pa::kBF16, 0, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
-                    0, 0, chunk_size);
+                    dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype == PA_F32, 1.f, 1.f, num_splits, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream), 0, 0, chunk_size);
 }
 
 pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -1494,7 +1513,7 @@ pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* ke
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                     int32_t num_blocks, float scale, pa_dtype_t dtype, int32_t chunk_size,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (dtype != PA_BF16) return fail(PA_ERR_DTYPE, "chunked local prefill: dtype must be PA_BF16");
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
   if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
   return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
                     seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
@@ -1502,17 +1521,28 @@ pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* ke
                     chunk_size);
 }
 
+namespace {
+
+// pa_prefill_varlen(_window|_local)_fp8_workspace_bytes without the argument checks: the
+// plan's workspace (or the virtual rows'), then the bf16 staging of the chunk sequences.
+size_t varlen_fp8_workspace_bytes(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int bt_stride, int window, int chunk) {
+  const size_t base =
+      varlen_workspace_bytes(qsl, sl, num_seqs, num_q_heads, num_kv_heads, head_dim, window, chunk, /*kv_elem=*/1);
+  const StageLayout stage = stage_layout(qsl, sl, num_seqs, bt_stride, num_kv_heads, head_dim);
+  return stage.total ? align_up(base) + stage.total : base;
+}
+
+}  // namespace
+
 size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
                                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                              int32_t head_dim, int32_t bt_stride) {
   if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
       head_dim < 1 || bt_stride < 1 || num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa)
     return 0;
-  const size_t base = varlen_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
-                                             head_dim, 0, 0, /*kv_elem=*/1);
-  const StageLayout stage = stage_layout(query_start_loc_host, seq_lens_host, num_seqs, bt_stride, num_kv_heads,
-                                         head_dim);
-  return stage.total ? align_up(base) + stage.total : base;
+  return varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim, bt_stride, 0, 0);
 }
 
 pa_status_t pa_prefill_varlen_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
@@ -1522,14 +1552,130 @@ pa_status_t pa_prefill_varlen_fp8(void* out, const void* query, const uint8_t* k
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                   int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale, float v_scale,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  if (q_dtype != PA_F32 && q_dtype != PA_BF16)
-    return fail(PA_ERR_DTYPE, "q_dtype must be PA_BF16 (or PA_F32 for decode rows)");
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
   return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
                     seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                     block_size, num_blocks, scale, q_dtype, pa::kFP8, k_scale, v_scale, workspace, workspace_bytes,
                     stream);
+}
+
+
+size_t pa_prefill_varlen_window_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t head_dim, int32_t bt_stride, int32_t sliding_window) {
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      head_dim < 1 || bt_stride < 1 || num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa ||
+      sliding_window < 1)
+    return 0;
+  return varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim, bt_stride, sliding_window, 0);
+}
+
+size_t pa_prefill_varlen_local_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t bt_stride, int32_t chunk_size) {
+  if (!query_start_loc_host || !seq_lens_host || num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      head_dim < 1 || bt_stride < 1 || num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa ||
+      chunk_size < 1)
+    return 0;
+  return varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim, bt_stride, 0, chunk_size);
+}
+
+namespace {
+
+// pa_decode_fp8 with a sliding window or local chunks (exactly one of them > 0).
+pa_status_t decode_fp8_masked(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                              const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                              pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t sliding_window,
+                              int32_t local_chunk, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  if (num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "fp8 decode supports up to %d q heads per kv head", pa::kMaxGqa);
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, pa::kFP8,
+                    q_dtype == PA_F32, k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream), 0, sliding_window, local_chunk);
+}
+
+}  // namespace
+
+pa_status_t pa_decode_window_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                 const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                 pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t sliding_window,
+                                 int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
+  return decode_fp8_masked(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, q_dtype,
+                           k_scale, v_scale, sliding_window, 0, num_splits, workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_local_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t chunk_size,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
+  return decode_fp8_masked(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, q_dtype,
+                           k_scale, v_scale, 0, chunk_size, num_splits, workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_prefill_varlen_window_fp8(void* out, const void* query, const uint8_t* key_cache,
+                                         const uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                         const int32_t* seq_lens, const int32_t* query_start_loc,
+                                         const int32_t* seq_lens_host, const int32_t* query_start_loc_host,
+                                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                         int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale,
+                                         float v_scale, int32_t sliding_window, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
+  return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
+                    seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, scale, q_dtype, pa::kFP8, k_scale, v_scale, workspace, workspace_bytes,
+                    stream, sliding_window);
+}
+
+pa_status_t pa_prefill_varlen_local_fp8(void* out, const void* query, const uint8_t* key_cache,
+                                        const uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* seq_lens, const int32_t* query_start_loc,
+                                        const int32_t* seq_lens_host, const int32_t* query_start_loc_host,
+                                        int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, float scale, pa_dtype_t q_dtype, float k_scale,
+                                        float v_scale, int32_t chunk_size, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
+  return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
+                    seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, scale, q_dtype, pa::kFP8, k_scale, v_scale, workspace, workspace_bytes,
+                    stream, 0, chunk_size);
 }
 
 }  // extern "C"

@@ -53,8 +53,10 @@ __device__ __forceinline__ void decode_f32_piece(const DecodeParams& p, int spli
   constexpr int QD = D / 4;
   const int row = p.qsl ? p.qsl[s] : s;
   const int L = min(p.seq_lens[s], p.max_seq_len);
-  const int tok0 = b0 * 16;
-  const int tok1 = min(L, b1 * 16);
+  const int skip = decode_skip(p, L);        // blocks wholly before a window / local chunk
+  const int key_lo = decode_first_key(p, L);  // keys below it are not visible
+  const int tok0 = (skip + b0) * 16;
+  const int tok1 = min(L, (skip + b1) * 16);
   const int nblk = b1 - b0;
   const int lane = threadIdx.x;
   const int t = lane & 15, quarter = lane >> 4;
@@ -68,7 +70,7 @@ __device__ __forceinline__ void decode_f32_piece(const DecodeParams& p, int spli
 #pragma unroll
   for (int i = 0; i < QD; ++i) o[i] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + b0;  // no cascade for fp32 pools
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + skip + b0;
   const float* kc = reinterpret_cast<const float*>(p.key_cache);
   const float* vc = reinterpret_cast<const float*>(p.value_cache);
 
@@ -76,7 +78,7 @@ __device__ __forceinline__ void decode_f32_piece(const DecodeParams& p, int spli
     int phys = bt[b];
     phys = min(max(phys, 0), p.num_blocks - 1);
     const int pos = tok0 + b * 16 + t;
-    const bool live = pos < tok1;
+    const bool live = pos < tok1 && pos >= key_lo;
     const size_t off = (((size_t)phys * 16 + t) * p.num_kv_heads + kvh) * D + quarter * QD;
     float dot = 0.f;
     if (live) {
@@ -243,6 +245,119 @@ hipError_t static_scratch(void** ptr) {
   }
   *ptr = addr[dev];
   return hipSuccess;
+}
+
+namespace {
+
+// One wave per (token t, q head h) of a flattened batch, fp32 queries and output; fp32 pools or
+// E4M3 codes (exact in fp32; k_scale is in scale_log2, v_scale applied at the end).  Lane =
+// (key t16 = lane % 16 of a block, quarter = lane / 16 holding D/4 elements of a row), as in
+// the fp32 decode.  The token finds its sequence by binary search over query_start_loc.
+template <int D, bool FP8>
+__global__ void __launch_bounds__(64) rows_f32_kernel(DecodeParams p) {
+  constexpr int QD = D / 4;
+  const int t = blockIdx.x, h = blockIdx.y;
+  int lo = 0, hi = p.num_seqs - 1;  // the last sequence s with qsl[s] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  const int q_len = p.qsl[s + 1] - p.qsl[s];
+  const int L = p.seq_lens[s] - q_len + (t - p.qsl[s]) + 1;  // keys 0 .. L-1 (causal)
+  const int skip = decode_skip(p, L);
+  const int key_lo = decode_first_key(p, L);
+  const int nblk = (L + 15) / 16 - skip;
+  const int lane = threadIdx.x;
+  const int t16 = lane & 15, quarter = lane >> 4;
+  const int kvh = h / p.group;
+
+  float q[QD];
+  const float* qp = reinterpret_cast<const float*>(p.query) + ((size_t)t * p.num_q_heads + h) * D + quarter * QD;
+#pragma unroll
+  for (int i = 0; i < QD; ++i) q[i] = qp[i];
+  float o[QD];
+#pragma unroll
+  for (int i = 0; i < QD; ++i) o[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int* bt = p.block_tables + (size_t)s * p.bt_stride + skip;
+  for (int b = 0; b < nblk; ++b) {
+    const int phys = min(max(bt[b], 0), p.num_blocks - 1);
+    const int pos = (skip + b) * 16 + t16;
+    const bool live = pos < L && pos >= key_lo;
+    const size_t off = (((size_t)phys * 16 + t16) * p.num_kv_heads + kvh) * D + quarter * QD;
+    float k[QD], v[QD];
+    if constexpr (FP8) {
+      const uint32_t* kc = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(p.key_cache) + off);
+      const uint32_t* vc = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(p.value_cache) + off);
+#pragma unroll
+      for (int i = 0; i < QD / 4; ++i) {
+        const u32x2 kw = e4m3x4_to_bf16x4(live ? kc[i] : 0u), vw = e4m3x4_to_bf16x4(live ? vc[i] : 0u);
+        k[4 * i] = __uint_as_float(kw.x << 16);
+        k[4 * i + 1] = __uint_as_float(kw.x & 0xFFFF0000u);
+        k[4 * i + 2] = __uint_as_float(kw.y << 16);
+        k[4 * i + 3] = __uint_as_float(kw.y & 0xFFFF0000u);
+        v[4 * i] = __uint_as_float(vw.x << 16);
+        v[4 * i + 1] = __uint_as_float(vw.x & 0xFFFF0000u);
+        v[4 * i + 2] = __uint_as_float(vw.y << 16);
+        v[4 * i + 3] = __uint_as_float(vw.y & 0xFFFF0000u);
+      }
+    } else {
+      const float* kc = reinterpret_cast<const float*>(p.key_cache) + off;
+      const float* vc = reinterpret_cast<const float*>(p.value_cache) + off;
+#pragma unroll
+      for (int i = 0; i < QD; ++i) {
+        k[i] = live ? kc[i] : 0.f;
+        v[i] = live ? vc[i] : 0.f;
+      }
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < QD; ++i) dot += q[i] * k[i];
+    dot += shfl_xor(dot, 16);
+    dot += shfl_xor(dot, 32);
+    const float z = live ? dot * p.scale_log2 : -INFINITY;
+    float bmax = z;
+#pragma unroll
+    for (int msk = 1; msk < 16; msk <<= 1) bmax = fmaxf(bmax, shfl_xor(bmax, msk));
+    const float mnew = fmaxf(m, bmax);
+    const float alpha = fast_exp2(m - mnew);
+    const float pr = fast_exp2(z - mnew);
+    l = l * alpha + pr;
+    m = mnew;
+#pragma unroll
+    for (int i = 0; i < QD; ++i) o[i] = o[i] * alpha + pr * v[i];
+  }
+#pragma unroll
+  for (int msk = 1; msk < 16; msk <<= 1) {
+    l += shfl_xor(l, msk);
+#pragma unroll
+    for (int i = 0; i < QD; ++i) o[i] += shfl_xor(o[i], msk);
+  }
+  if (t16 == 0) {
+    const float inv = p.v_scale / l;
+    float* op = reinterpret_cast<float*>(p.out) + ((size_t)t * p.num_q_heads + h) * D + quarter * QD;
+#pragma unroll
+    for (int i = 0; i < QD; ++i) op[i] = o[i] * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rows_f32(const DecodeParams& p, int kv, int head_dim, int num_tokens, hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const dim3 grid(num_tokens, p.num_q_heads);
+  timing_mark(kKDecode, true, stream);
+  if (head_dim == 128 && kv == kFP8)
+    hipLaunchKernelGGL((rows_f32_kernel<128, true>), grid, dim3(64), 0, stream, p);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((rows_f32_kernel<128, false>), grid, dim3(64), 0, stream, p);
+  else if (kv == kFP8)
+    hipLaunchKernelGGL((rows_f32_kernel<64, true>), grid, dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((rows_f32_kernel<64, false>), grid, dim3(64), 0, stream, p);
+  timing_mark(kKDecode, false, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream) {

@@ -208,6 +208,13 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
 // fp8 prefill: the blocks of every sequence with q_len > 1 copied, as the exact bf16
 // values of their codes, into a compact staging pool (sequence s's blocks from the sum
 // of the block counts of the chunk sequences before it), with its staging table row.
+// Every query token of a flattened batch attended on its own by one wave per (token, q head),
+// on the vector ALU, without scratch: the chunks of pools or queries the prefill kernel does
+// not take (fp32 pools and activations; fp32 queries over fp8 pools).  Token t of sequence s
+// sits at position c_s + i (c_s = seq_lens[s] - q_len_s, i = t - qsl[s]) and sees the keys a
+// decode query of a sequence of length c_s + i + 1 sees (p.window / p.chunk apply).  p: the
+// decode parameters of the batch (qsl, seq_lens over num_seqs, q_f32 = 1); out is fp32.
+hipError_t launch_rows_f32(const DecodeParams& p, int kv, int head_dim, int num_tokens, hipStream_t stream);
 hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
                             int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
                             int max_blocks, int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k,

@@ -61,21 +61,37 @@ class DevWorkload:
 
     def decode_window(self, window, num_splits=0, out=None):
         w = self.w
+        if w.kv_dtype == "fp8":
+            return pk.pa_decode_window_fp8(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                           w.scale, w.k_scale, w.v_scale, self.max_seq_len(), window, num_splits,
+                                           out=out)
         return pk.pa_decode_window(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
                                    self.max_seq_len(), window, num_splits, out=out)
 
     def prefill_window(self, window, out=None):
         w = self.w
+        if w.kv_dtype == "fp8":
+            return pk.pa_prefill_varlen_window_fp8(self.query, self.k_cache, self.v_cache, self.block_tables,
+                                                   self.seq_lens, self.qsl, w.seq_lens, w.query_start_loc, w.scale,
+                                                   w.k_scale, w.v_scale, window, out=out)
         return pk.pa_prefill_varlen_window(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
                                            self.qsl, w.seq_lens, w.query_start_loc, w.scale, window, out=out)
 
     def decode_local(self, chunk, num_splits=0, out=None):
         w = self.w
+        if w.kv_dtype == "fp8":
+            return pk.pa_decode_local_fp8(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                          w.scale, w.k_scale, w.v_scale, self.max_seq_len(), chunk, num_splits,
+                                          out=out)
         return pk.pa_decode_local(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.scale,
                                   self.max_seq_len(), chunk, num_splits, out=out)
 
     def prefill_local(self, chunk, out=None):
         w = self.w
+        if w.kv_dtype == "fp8":
+            return pk.pa_prefill_varlen_local_fp8(self.query, self.k_cache, self.v_cache, self.block_tables,
+                                                  self.seq_lens, self.qsl, w.seq_lens, w.query_start_loc, w.scale,
+                                                  w.k_scale, w.v_scale, chunk, out=out)
         return pk.pa_prefill_varlen_local(self.query, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
                                           self.qsl, w.seq_lens, w.query_start_loc, w.scale, chunk, out=out)
 

@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 44
+    assert len(syms) == 50
     assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
@@ -124,7 +124,9 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, [1, 5, 9], [10, 10]) == 2            # does not start at 0
     assert _prefill(lib, [0, 5, 9], [3, 10]) == 2             # seq_len < q_len
     assert _prefill(lib, [0, 5, 9], [10, 10], T=8) == 2       # num_tokens mismatch
-    assert _prefill(lib, [0, 5, 9], [10, 10], dtype=b.PA_F32) == 3  # chunks need bf16
+    assert _prefill(lib, [0, 5, 9], [10, 10], dtype=b.PA_FP8_E4M3) == 3  # fp8 pools have their own entry point
+    # fp32 chunks (every token on its own) need no scratch: only the launch, which fails without a GPU
+    assert _prefill(lib, [0, 5, 9], [10, 10], dtype=b.PA_F32, ws=None, wsb=0) == 6
     assert _prefill(lib, [0, 1, 2], [3000, 10], ws=None, bt_stride=256) == 4  # decode rows over 512 need scratch
     assert _prefill(lib, [0, 5, 9], [2000, 10], bt_stride=64) == 2  # more blocks than table columns
     assert _prefill(lib, [0, 5, 9], [10, 10], scale=0.0) == 2       # the scale must be positive
@@ -241,7 +243,7 @@ def test_cascade_workspace_and_argument_checks(lib):
     assert pk.pa_decode_cascade_workspace_bytes(4, 64, 2, 128, 3072, 8, 0) == 0
     # entry points reject bad arguments before touching the device
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 4, 32, 8, 128, 16, 1000, 3072, 0.088]
-    assert lib.pa_decode_cascade(*args, b.PA_F32, 8, 0, FAKE, 1 << 30, None) == 3          # dtype
+    assert lib.pa_decode_cascade(*args, b.PA_FP8_E4M3, 8, 0, FAKE, 1 << 30, None) == 3    # dtype (fp8: _fp8 call)
     assert lib.pa_decode_cascade(*args, b.PA_BF16, 0, 0, FAKE, 1 << 30, None) == 2         # no prefix
     assert lib.pa_decode_cascade(*args, b.PA_BF16, 8, 0, FAKE, 16, None) == 4              # workspace too small
     assert lib.pa_decode_cascade_fp8(*args, b.PA_BF16, 0.05, -1.0, 8, 0, FAKE, 1 << 30, None) == 2  # v_scale
@@ -275,11 +277,11 @@ def test_window_workspace_and_argument_checks(lib):
     assert lib.pa_prefill_varlen_window_workspace_bytes(*args, 0) == 0
     assert lib.pa_prefill_varlen_window_workspace_bytes(*args, 64) >= 0
     dec = [FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 4, 32, 8, 128, 16, 1000, 3072, 0.088]
-    assert lib.pa_decode_window(*dec, b.PA_F32, 128, 0, FAKE, 1 << 30, None) == 3      # dtype
+    assert lib.pa_decode_window(*dec, b.PA_FP8_E4M3, 128, 0, FAKE, 1 << 30, None) == 3  # dtype (fp8: _fp8 call)
     assert lib.pa_decode_window(*dec, b.PA_BF16, 0, 0, FAKE, 1 << 30, None) == 2      # window
     pre = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, ctypes.addressof(s), ctypes.addressof(q), 3, 341, 32, 8,
            128, 16, 1000, 0.088]
-    assert lib.pa_prefill_varlen_window(*pre, b.PA_F32, 128, FAKE, 1 << 30, None) == 3  # dtype
+    assert lib.pa_prefill_varlen_window(*pre, b.PA_FP8_E4M3, 128, FAKE, 1 << 30, None) == 3  # dtype
     assert lib.pa_prefill_varlen_window(*pre, b.PA_BF16, -5, FAKE, 1 << 30, None) == 2  # window
 
 
@@ -290,11 +292,11 @@ def test_local_workspace_and_argument_checks(lib):
     assert lib.pa_prefill_varlen_local_workspace_bytes(*args, 5000) == base  # one chunk: causal work
     assert lib.pa_prefill_varlen_local_workspace_bytes(*args, 0) == 0
     dec = [FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 4, 32, 8, 128, 16, 1000, 3072, 0.088]
-    assert lib.pa_decode_local(*dec, b.PA_F32, 128, 0, FAKE, 1 << 30, None) == 3       # dtype
+    assert lib.pa_decode_local(*dec, b.PA_FP8_E4M3, 128, 0, FAKE, 1 << 30, None) == 3  # dtype
     assert lib.pa_decode_local(*dec, b.PA_BF16, 0, 0, FAKE, 1 << 30, None) == 2       # chunk
     pre = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, ctypes.addressof(s), ctypes.addressof(q), 3, 341, 32, 8,
            128, 16, 1000, 0.088]
-    assert lib.pa_prefill_varlen_local(*pre, b.PA_F32, 128, FAKE, 1 << 30, None) == 3  # dtype
+    assert lib.pa_prefill_varlen_local(*pre, b.PA_FP8_E4M3, 128, FAKE, 1 << 30, None) == 3  # dtype
     assert lib.pa_prefill_varlen_local(*pre, b.PA_BF16, 0, FAKE, 1 << 30, None) == 2   # chunk
 
 
@@ -330,3 +332,26 @@ def test_empty_batches_return_ok_without_touching_memory(lib):
     assert lib.pa_reshape_and_cache(FAKE, FAKE, 1024, 1024, FAKE, FAKE, FAKE, 0, 8, 128, 16, 100, b.PA_BF16, None) == 0
     assert lib.pa_write_kv(FAKE, FAKE, 1024, 1024, FAKE, FAKE, None, FAKE, 64, FAKE, FAKE, 0, 0, 0, 8, 128, 16, 100,
                            b.PA_BF16, None) == 0
+
+
+def test_fp8_window_and_local_argument_checks(lib):
+    """The sliding-window and chunked-local entry points over fp8 pools refuse what pa_decode_fp8 and
+    pa_prefill_varlen_fp8 refuse, and a window or chunk below 1, before anything is launched."""
+    q, s = _host_i32([0, 40, 41, 341]), _host_i32([100, 5000, 900])
+    args = (ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128, 400)
+    for size_fn in (lib.pa_prefill_varlen_window_fp8_workspace_bytes, lib.pa_prefill_varlen_local_fp8_workspace_bytes):
+        assert size_fn(*args, 64) > 0
+        assert size_fn(*args, 0) == 0                      # window / chunk below 1
+        assert size_fn(*args[:6], 0, 64) == 0              # bt_stride below 1
+    dec = [FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 4, 32, 8, 128, 16, 1000, 3072, 0.088]
+    for fn in (lib.pa_decode_window_fp8, lib.pa_decode_local_fp8):
+        assert fn(*dec, b.PA_FP8_E4M3, 0.05, 0.04, 128, 0, FAKE, 1 << 30, None) == 3   # q dtype
+        assert fn(*dec, b.PA_BF16, 0.0, 0.04, 128, 0, FAKE, 1 << 30, None) == 2        # k_scale
+        assert fn(*dec, b.PA_BF16, 0.05, -1.0, 128, 0, FAKE, 1 << 30, None) == 2       # v_scale
+        assert fn(*dec, b.PA_BF16, 0.05, 0.04, 0, 0, FAKE, 1 << 30, None) == 2         # window / chunk
+    pre = [FAKE, FAKE, FAKE, FAKE, FAKE, 400, FAKE, FAKE, ctypes.addressof(s), ctypes.addressof(q), 3, 341, 32, 8,
+           128, 16, 1000, 0.088]
+    for fn in (lib.pa_prefill_varlen_window_fp8, lib.pa_prefill_varlen_local_fp8):
+        assert fn(*pre, b.PA_FP8_E4M3, 0.05, 0.04, 128, FAKE, 1 << 30, None) == 3      # q dtype
+        assert fn(*pre, b.PA_BF16, float("nan"), 0.04, 128, FAKE, 1 << 30, None) == 2  # k_scale
+        assert fn(*pre, b.PA_BF16, 0.05, 0.04, 0, FAKE, 1 << 30, None) == 2            # window / chunk
