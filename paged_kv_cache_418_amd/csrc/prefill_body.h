@@ -340,32 +340,25 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
           : "memory");
     }
   };
-  // the V^T reads of the last chunk plus this wave's transposing reads of the next tile
-  auto vt_issue_tr = [&](u32x4 (&x)[kTileQuad], uint32_t base, u32x2 (&t)[Sh::kTransposes], uint32_t src) {
-    constexpr int kRows32 = 32 * Sh::kVtRowBytes;
+  // issues (no wait) this wave's transposing reads of a tile
+  auto tr_issue = [&](u32x2 (&t)[Sh::kTransposes], uint32_t src) {
     uint32_t a[Sh::kTransposes];
     tr_addrs(a, src, tr_src);
-    if constexpr (kTileQuad == 4) {
+    if constexpr (Sh::kTransposes == 4) {
       asm volatile(
-          "ds_read_b128 %0, %8\n\t"
-          "ds_read_b128 %1, %8 offset:%13\n\t"
-          "ds_read_b128 %2, %8 offset:%14\n\t"
-          "ds_read_b128 %3, %8 offset:%15\n\t"
-          "ds_read_b64_tr_b16 %4, %9\n\t"
-          "ds_read_b64_tr_b16 %5, %10\n\t"
-          "ds_read_b64_tr_b16 %6, %11\n\t"
-          "ds_read_b64_tr_b16 %7, %12"
-          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
-          : "v"(base), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(kRows32), "i"(2 * kRows32), "i"(3 * kRows32)
+          "ds_read_b64_tr_b16 %0, %4\n\t"
+          "ds_read_b64_tr_b16 %1, %5\n\t"
+          "ds_read_b64_tr_b16 %2, %6\n\t"
+          "ds_read_b64_tr_b16 %3, %7"
+          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
           : "memory");
     } else {
       asm volatile(
-          "ds_read_b128 %0, %4\n\t"
-          "ds_read_b128 %1, %4 offset:%7\n\t"
-          "ds_read_b64_tr_b16 %2, %5\n\t"
-          "ds_read_b64_tr_b16 %3, %6"
-          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(t[0]), "=&v"(t[1])
-          : "v"(base), "v"(a[0]), "v"(a[1]), "i"(kRows32)
+          "ds_read_b64_tr_b16 %0, %2\n\t"
+          "ds_read_b64_tr_b16 %1, %3"
+          : "=&v"(t[0]), "=&v"(t[1])
+          : "v"(a[0]), "v"(a[1])
           : "memory");
     }
   };
@@ -441,25 +434,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // O^T += V^T P^T for one tile, V^T from the slot at byte address vtbase.  The reads of
   // chunk ch+1 are in flight while the MFMAs of chunk ch run; between(ch) is called after
   // they are issued (the copies of the step go there, spread over the matrix-core work
-  // instead of stalling the wave at once).  The wave's share of the transposition of the
-  // next tile (row-major slot tr_from -> V^T slot tr_to) rides along: its reads are issued
-  // with the last chunk's and its rows written after the last MFMAs.
-  auto pv = [&](const u32x4 (&pw)[4], uint32_t vtbase, auto&& between, uint32_t tr_from, uint32_t tr_to) {
+  // instead of stalling the wave at once).
+  auto pv = [&](const u32x4 (&pw)[4], uint32_t vtbase, auto&& between) {
     u32x4 vb[2][kTileQuad];
-    u32x2 tx[Sh::kTransposes];
     vt_issue(vb[0], vtbase + vt_off[0]);
     static_for<0, 4>([&](auto ch_c) {
       constexpr int ch = decltype(ch_c)::value;
-      if constexpr (ch + 2 < 4) {
-        vt_issue(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1]);
-      } else if constexpr (ch + 1 < 4) {
-        vt_issue_tr(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1], tx, tr_from);
-      }
-      // reads issued after this chunk's: the next chunk's operands and (from chunk 2 on) the
-      // transposing reads; the last chunk's operands were read before the transposing reads,
-      // so its MFMAs wait only for them, the transposed rows after.  Each MFMA waits for its
-      // own operand only.
-      constexpr int kLater = ch < 2 ? kTileQuad : ch == 2 ? kTileQuad + Sh::kTransposes : Sh::kTransposes;
+      if constexpr (ch + 1 < 4) vt_issue(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1]);
+      constexpr int kLater = ch + 1 < 4 ? kTileQuad : 0;
       const bf16x8 pb = u4_to_bf16x8(pw[ch]);
       static_for<0, kTileQuad>([&](auto n_c) {
         constexpr int n = decltype(n_c)::value;
@@ -468,6 +450,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
         if constexpr (n == 0) between(ch);  // the step's copy of this chunk, beside the first MFMA
       });
     });
+  };
+  // the softmax phase of a step with this wave's share of the transposition V(t+1) -> V^T(t+1):
+  // its reads issued first, its rows written after the exponentials
+  auto softmax_tr = [&](bool comp, f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4], uint32_t tr_from, uint32_t tr_to) {
+    u32x2 tx[Sh::kTransposes];
+    tr_issue(tx, tr_from);
+    if (comp) softmax(sacc, key0, pw);
     tr_wait(tx);
     tr_write(tx, tr_to);
   };
@@ -479,7 +468,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // order, so one group's exponentials issue while the other group's MFMAs run:
   //   leading group   (waves 0-3): O += V P(t-1), S(t)  | softmax(t) -> P(t)
   //   following group (waves 4-7): softmax(t) -> P(t)   | O += V P(t), S(t+1)
-  // and every wave transposes its share of V(t+1) into V^T(t+1) during its O += V P.
+  // and every wave transposes its share of V(t+1) into V^T(t+1) in its softmax part (its
+  // transposing reads are in flight during the exponentials, off the matrix-core part).
   // Step t also reads the block id of tile t+4 and starts the copies of K(t+3) and
   // V(t+3) (spread over the matrix-core part).  K slot (t+3)%4 last held K(t-1), read at
   // step t-1; V slot (t+3)%3 last held V(t), transposed at step t-1; V^T slot (t+1)%3
@@ -530,38 +520,36 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
         for (int part = 0; part < 2 * Sh::kCopies; ++part) copy_part(part);
       };
       phys_next = phys_new;
-      if (!leading && computes(tile)) softmax(sc, tile * Sh::kKeys, pw);
+      // V(t+1) -> V^T(t+1) by every wave; tiles past the range hold valid rows too, so the
+      // transposition is unconditional
+      const uint32_t tr_from = v_addr(tile + 1), tr_to = vt_addr(tile + 1);
+      if (!leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
-      // V(t+1) -> V^T(t+1) by every wave (inside its O += V P when it has one); tiles past
-      // the range hold valid rows too, so the transposition is unconditional
-      const uint32_t tr_from = v_addr(tile + 1), tr_to = vt_addr(tile + 1);
       if (leading) {
         if (tile > kt0 && computes(tile - 1)) {
-          pv(pw, vt_addr(tile - 1), copy_part, tr_from, tr_to);
+          pv(pw, vt_addr(tile - 1), copy_part);
         } else {
           copy_all();
-          transpose(tr_from, tr_to);
         }
         if (computes(tile)) scores(sc, k_addr(tile));
       } else {
         if (computes(tile)) {
-          pv(pw, vt_addr(tile), copy_part, tr_from, tr_to);
+          pv(pw, vt_addr(tile), copy_part);
         } else {
           copy_all();
-          transpose(tr_from, tr_to);
         }
         if (computes(tile + 1)) scores(sc, k_addr(tile + 1));
       }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      if (leading && computes(tile)) softmax(sc, tile * Sh::kKeys, pw);
+      if (leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to);
       wait_vmcnt_lgkm0<kStepLoads>();
       __builtin_amdgcn_s_barrier();
     }
-    // the last O += V P of the leading group; V^T(kt1-1)'s slot is not refilled.  (Its
-    // transposition rides along into the slot of V^T(kt1+1), which nothing reads.)
-    if (leading && computes(kt1 - 1)) pv(pw, vt_addr(kt1 - 1), [](int) {}, v_addr(kt1 + 1), vt_addr(kt1 + 1));
+    // the last O += V P of the leading group (the last step transposed V(kt1) into a slot
+    // that nothing reads: tiles past the range hold valid rows)
+    if (leading && computes(kt1 - 1)) pv(pw, vt_addr(kt1 - 1), [](int) {});
     wait_vmcnt<0>();  // no copy may still be writing LDS when the work-group ends
   }
 
