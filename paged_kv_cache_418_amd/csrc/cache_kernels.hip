@@ -55,6 +55,28 @@ __device__ __forceinline__ void copy_token(const uint8_t* key, const uint8_t* va
   }
 }
 
+// Elements e .. e+7 of a bf16 or fp32 row (element offset e of the row at src).
+template <bool SRC_F32>
+__device__ __forceinline__ void load8(const void* src, int64_t e, float (&x)[8]) {
+  if constexpr (SRC_F32) {
+    const float* s = reinterpret_cast<const float*>(src) + e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = s[j];
+  } else {
+    const uint16_t* s = reinterpret_cast<const uint16_t*>(src) + e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(s[j]);
+  }
+}
+
+// The E4M3 codes of x / scale, one 8-byte store.
+__device__ __forceinline__ void store_e4m3x8(uint8_t* dst, const float (&x)[8], float scale) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j >> 2] |= (uint32_t)f32_to_e4m3(__fdiv_rn(x[j], scale)) << (8 * (j & 3));
+  *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+}
+
 // fp8: each thread quantises 8 consecutive elements of token t (one 8-byte store per pool).
 template <bool SRC_F32>
 __device__ __forceinline__ void quantize_token(const void* key, const void* value, int64_t key_stride,
@@ -62,31 +84,10 @@ __device__ __forceinline__ void quantize_token(const void* key, const void* valu
                                                int slot, int row_elems, float k_scale, float v_scale) {
   for (int c = threadIdx.x; c < row_elems / 8; c += blockDim.x) {
     float xk[8], xv[8];
-    if constexpr (SRC_F32) {
-      const float* ks = reinterpret_cast<const float*>(key) + (int64_t)t * key_stride + c * 8;
-      const float* vs = reinterpret_cast<const float*>(value) + (int64_t)t * value_stride + c * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xk[j] = ks[j];
-        xv[j] = vs[j];
-      }
-    } else {
-      const uint16_t* ks = reinterpret_cast<const uint16_t*>(key) + (int64_t)t * key_stride + c * 8;
-      const uint16_t* vs = reinterpret_cast<const uint16_t*>(value) + (int64_t)t * value_stride + c * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xk[j] = bf16_to_f32(ks[j]);
-        xv[j] = bf16_to_f32(vs[j]);
-      }
-    }
-    uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      kw[j >> 2] |= (uint32_t)f32_to_e4m3(__fdiv_rn(xk[j], k_scale)) << (8 * (j & 3));
-      vw[j >> 2] |= (uint32_t)f32_to_e4m3(__fdiv_rn(xv[j], v_scale)) << (8 * (j & 3));
-    }
-    *reinterpret_cast<u32x2*>(key_cache + (int64_t)slot * row_elems + c * 8) = u32x2{kw[0], kw[1]};
-    *reinterpret_cast<u32x2*>(value_cache + (int64_t)slot * row_elems + c * 8) = u32x2{vw[0], vw[1]};
+    load8<SRC_F32>(key, (int64_t)t * key_stride + c * 8, xk);
+    load8<SRC_F32>(value, (int64_t)t * value_stride + c * 8, xv);
+    store_e4m3x8(key_cache + (int64_t)slot * row_elems + c * 8, xk, k_scale);
+    store_e4m3x8(value_cache + (int64_t)slot * row_elems + c * 8, xv, v_scale);
   }
 }
 
@@ -115,10 +116,58 @@ __global__ void __launch_bounds__(256) reshape_fp8_kernel(const void* key, const
 
 // Slot mapping and KV write in one launch: grid (num_seqs, min(ceil(max_q_len / kWriteTokens),
 // 65535)); work-group (s, g) takes the groups of kWriteTokens new rows g, g + gridDim.y, ... of
-// sequence s, computes each row's slot
-// as slot_mapping_kernel does (stored when slots_out is given), and writes the row as the
-// reshape kernels do (skipped for slots outside the pool).
+// sequence s, computes each row's slot as slot_mapping_kernel does (stored when slots_out is
+// given), and writes the rows as the reshape kernels do (skipped for slots outside the pool).
+// A group's table reads are issued together, then every load of its rows before any store, so
+// the rows' memory round trips overlap instead of following one another.
 constexpr int kWriteTokens = 4;
+
+// Copies rows tok[j] -> slots slot[j] (slot < 0: no row) in VecT chunks.
+template <typename VecT>
+__device__ __forceinline__ void copy_rows(const uint8_t* key, const uint8_t* value, int64_t key_stride_b,
+                                          int64_t value_stride_b, uint8_t* key_cache, uint8_t* value_cache,
+                                          const int (&tok)[kWriteTokens], const int (&slot)[kWriteTokens],
+                                          int row_bytes) {
+  const int n = row_bytes / (int)sizeof(VecT);
+  for (int c = threadIdx.x; c < n; c += blockDim.x) {
+    VecT kx[kWriteTokens], vx[kWriteTokens];
+#pragma unroll
+    for (int j = 0; j < kWriteTokens; ++j)
+      if (slot[j] >= 0) {
+        kx[j] = reinterpret_cast<const VecT*>(key + (int64_t)tok[j] * key_stride_b)[c];
+        vx[j] = reinterpret_cast<const VecT*>(value + (int64_t)tok[j] * value_stride_b)[c];
+      }
+#pragma unroll
+    for (int j = 0; j < kWriteTokens; ++j)
+      if (slot[j] >= 0) {
+        reinterpret_cast<VecT*>(key_cache + (int64_t)slot[j] * row_bytes)[c] = kx[j];
+        reinterpret_cast<VecT*>(value_cache + (int64_t)slot[j] * row_bytes)[c] = vx[j];
+      }
+  }
+}
+
+// Quantises rows tok[j] into slots slot[j] (slot < 0: no row), 8 elements per thread and row.
+template <bool SRC_F32>
+__device__ __forceinline__ void quantize_rows(const void* key, const void* value, int64_t key_stride,
+                                              int64_t value_stride, uint8_t* key_cache, uint8_t* value_cache,
+                                              const int (&tok)[kWriteTokens], const int (&slot)[kWriteTokens],
+                                              int row_elems, float k_scale, float v_scale) {
+  for (int c = threadIdx.x; c < row_elems / 8; c += blockDim.x) {
+    float xk[kWriteTokens][8], xv[kWriteTokens][8];
+#pragma unroll
+    for (int j = 0; j < kWriteTokens; ++j)
+      if (slot[j] >= 0) {
+        load8<SRC_F32>(key, (int64_t)tok[j] * key_stride + c * 8, xk[j]);
+        load8<SRC_F32>(value, (int64_t)tok[j] * value_stride + c * 8, xv[j]);
+      }
+#pragma unroll
+    for (int j = 0; j < kWriteTokens; ++j)
+      if (slot[j] >= 0) {
+        store_e4m3x8(key_cache + (int64_t)slot[j] * row_elems + c * 8, xk[j], k_scale);
+        store_e4m3x8(value_cache + (int64_t)slot[j] * row_elems + c * 8, xv[j], v_scale);
+      }
+  }
+}
 
 template <typename VecT, int KIND>  // KIND 0: copy; 1: fp8 from bf16; 2: fp8 from fp32
 __global__ void __launch_bounds__(128) write_kv_kernel(const void* key, const void* value, int64_t key_stride,
@@ -133,20 +182,22 @@ __global__ void __launch_bounds__(128) write_kv_kernel(const void* key, const vo
   const int* bt = block_tables + (size_t)s * bt_stride;
   // row groups blockIdx.y, blockIdx.y + gridDim.y, ... of kWriteTokens rows (the grid's y extent is capped)
   for (int g0 = blockIdx.y * kWriteTokens; g0 < q_len; g0 += gridDim.y * kWriteTokens) {
-    const int i1 = min(q_len, g0 + kWriteTokens);
-    for (int i = g0; i < i1; ++i) {
-      const int t = q0 + i;
-      if (t < 0 || t >= num_tokens) continue;
-      const int slot = row_slot(bt, bt_stride, cached, i, block_size);
-      if (slots_out && threadIdx.x == 0) slots_out[t] = slot;
-      if (slot < 0 || slot >= num_slots) continue;
-      if constexpr (KIND == 0)  // key_stride / value_stride in bytes, row in bytes
-        copy_token<VecT>(reinterpret_cast<const uint8_t*>(key), reinterpret_cast<const uint8_t*>(value), key_stride,
-                         value_stride, key_cache, value_cache, t, slot, row);
-      else  // strides in elements, row in elements
-        quantize_token<KIND == 2>(key, value, key_stride, value_stride, key_cache, value_cache, t, slot, row, k_scale,
-                                  v_scale);
+    int tok[kWriteTokens], slot[kWriteTokens];
+#pragma unroll
+    for (int j = 0; j < kWriteTokens; ++j) {
+      const int i = g0 + j, t = q0 + i;
+      const bool row_ok = i < q_len && t >= 0 && t < num_tokens;
+      tok[j] = t;
+      slot[j] = row_ok ? row_slot(bt, bt_stride, cached, i, block_size) : -1;
+      if (row_ok && slots_out && threadIdx.x == 0) slots_out[t] = slot[j];
+      if (slot[j] >= num_slots) slot[j] = -1;  // outside the pool: not written
     }
+    if constexpr (KIND == 0)  // key_stride / value_stride in bytes, row in bytes
+      copy_rows<VecT>(reinterpret_cast<const uint8_t*>(key), reinterpret_cast<const uint8_t*>(value), key_stride,
+                      value_stride, key_cache, value_cache, tok, slot, row);
+    else  // strides in elements, row in elements
+      quantize_rows<KIND == 2>(key, value, key_stride, value_stride, key_cache, value_cache, tok, slot, row, k_scale,
+                               v_scale);
   }
 }
 

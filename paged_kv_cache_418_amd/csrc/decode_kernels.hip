@@ -147,9 +147,12 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + wave, s = blockIdx.x;  // sequences on x: no 65535 limit on the batch
   if (h >= p.num_q_heads) return;
+  // the piece range is read beside the length (one memory round trip, not two); it is only
+  // meaningful when the sequence has pieces of its own
+  const int pf = p.piece_first[s], pl = p.piece_last[s];
   const bool own = decode_blocks(p, s) > 0;  // the sequence has pieces of its own
   if (!own && p.prefix_shares == 0) return;
-  const int first = own ? p.piece_first[s] : 0, last = own ? p.piece_last[s] : -1;
+  const int first = own ? pf : 0, last = own ? pl : -1;
   if (first >= last && !p.force_partial) return;  // finished in place
   const int row = p.qsl ? p.qsl[s] : s;
   const size_t step = (size_t)p.num_q_heads;
