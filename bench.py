@@ -493,6 +493,8 @@ def bench_mixed(args, result):
     counters = read_profile("prefill_bf16_d128_counters", PREFILL_SOURCES)
     mfma_busy = {"chunks": float(counters["mfma_busy_chunks"]), "long": float(counters["mfma_busy_long"])} \
         if counters["valid"] and "mfma_busy_chunks" in counters else None
+    # the shader clock the counters saw under the long prompts (the published peak assumes 2.4 GHz)
+    clock_long = float(counters["clock_ghz_long"]) if counters["valid"] and "clock_ghz_long" in counters else None
     chunk_fetch = float(counters["fetch_bytes_chunks"]) if counters["valid"] and "fetch_bytes_chunks" in counters \
         else None
     mixed = {"workload": "mixed_step_bf16", "ms_per_step": round(ms, 5), "step_ms": per,
@@ -523,7 +525,9 @@ def bench_mixed(args, result):
                               "call_frac_of_peak": round(long_flops / (long_call_ms * 1e-3) / 1e12 /
                                                          BF16_MFMA_PEAK_TFLOPS, 4),
                               "call_frac_of_measured_peak": round(long_flops / (long_call_ms * 1e-3) / 1e12 /
-                                                                  mfma_peak, 4)},
+                                                                  mfma_peak, 4),
+                              "counters_clock_ghz": clock_long,
+                              "counters_mfma_busy": mfma_busy["long"] if mfma_busy else None},
              "mfma_measured_peak_tflops": round(mfma_peak, 1),
              "prefill_fp8": {"call_ms": round(pre8_call_ms, 5), "kernel_ms": kmean(kt8, "prefill"),
                              "staging_ms": kmean(kt8, "stage_fp8"),
@@ -590,6 +594,9 @@ def bench_cascade(args, result):
     del scratch
     result["cascade_step"] = out
     traffic = read_traffic("cascade_fp8_prefix_shared_traffic", CASCADE_SOURCES)
+    if traffic.get("fetch_bytes") is not None:  # the cascade launch's HBM reads against the unique KV bytes
+        out["cascade"]["kernel_fetch_bytes"] = traffic["fetch_bytes"]
+        out["cascade"]["kernel_fetch_over_unique"] = round(traffic["fetch_bytes"] / unique, 4)
     rec, par = (None, None)
     if not args.no_cpu:
         rows = decode_rows_sample(w, 8)
