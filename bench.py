@@ -470,11 +470,11 @@ def bench_mixed(args, result):
     kt = kernel_times(cs.attend_next, args.steps, ["prefill", "prefill_merge"])
     pre_ms = kmean(kt, "prefill")
     del cs
-    # the same two chunks over fp8 pools: staging + bf16 kernel + merge
+    # the same two chunks over fp8 pools (the kernel converts the codes itself) + merge
     w8 = wl.mixed_step_bf16(kv_dtype="fp8")
     cs8 = Step(_sub(w8, list(range(48, 50))), copies=1)
     pre8_call_ms, _, _ = time_steps(cs8.attend_next, args.steps, args.warmup)
-    kt8 = kernel_times(cs8.attend_next, args.steps, ["prefill", "stage_fp8"])
+    kt8 = kernel_times(cs8.attend_next, args.steps, ["prefill"])
     del cs8, w8
     # steady state: long prompts, where launch, first tiles and tail are small next to the tile loop
     lw = wl.long_prefill_bf16()
@@ -530,7 +530,6 @@ def bench_mixed(args, result):
                               "counters_mfma_busy": mfma_busy["long"] if mfma_busy else None},
              "mfma_measured_peak_tflops": round(mfma_peak, 1),
              "prefill_fp8": {"call_ms": round(pre8_call_ms, 5), "kernel_ms": kmean(kt8, "prefill"),
-                             "staging_ms": kmean(kt8, "stage_fp8"),
                              "call_tflops": round(flops / (pre8_call_ms * 1e-3) / 1e12, 2)},
              "decode_part_gbps": round(dec_bytes / (dms * 1e-3) / 1e9, 2),
              "decode_part_ms": round(dms, 5)}
@@ -572,15 +571,14 @@ def bench_cascade(args, result):
     for name, cascade in (("plain", False), ("cascade", True)):
         st = Step(w, cascade=cascade)
         ms, _, per = time_steps(st, args.steps, args.warmup)
-        kt = kernel_times(st, args.steps, ["decode", "decode_merge", "stage_fp8"])
+        kt = kernel_times(st, args.steps, ["decode", "decode_merge"])
         cms, _, cper = time_steps(st, args.steps, args.warmup, between=flush)
-        ktc = kernel_times(st, args.steps, ["decode", "decode_merge", "stage_fp8"], between=flush)
+        ktc = kernel_times(st, args.steps, ["decode", "decode_merge"], between=flush)
         d = kmean(kt, "decode")
         out[name] = {"ms_per_step": round(ms, 5), "step_ms": per, "logical_gbps": round(logical / (ms * 1e-3) / 1e9, 1),
                      "unique_gbps": round(unique / (ms * 1e-3) / 1e9, 1),
                      "decode_kernel_ms": round(d, 5), "decode_kernel": kt["decode"],
                      "merge_kernel_ms": kmean(kt, "decode_merge"),
-                     "stage_kernel_ms": kmean(kt, "stage_fp8"),
                      "kernel_unique_gbps": round(unique / (d * 1e-3) / 1e9, 1),
                      "kernel_unique_frac_hbm": round(unique / (d * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "cold": {"note": "512 MB scratch write before every step, outside the timed region",

@@ -289,8 +289,8 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
  * of fp32 sums differs.  The prefix is attended as dense matrix-core tiles:
  * for each kv head, all num_seqs x G query rows (G = num_q_heads /
  * num_kv_heads <= 16) against the prefix blocks, each block read once per 256
- * rows, in one launch with the suffixes' shares; fp8 pools stage the prefix
- * as bf16 first (one more launch).  With fp32 queries (pa_decode_cascade_fp8)
+ * rows, in one launch with the suffixes' shares (fp8 pools: the tiles convert
+ * the codes to bf16 themselves).  With fp32 queries (pa_decode_cascade_fp8)
  * the prefix is read once per group of 16/G sequences by decode waves instead.
  * Requirements: prefix_blocks >= 1; every seq_lens[s] >= prefix_blocks *
  * block_size; block_tables[s][j] the same for every s and j < prefix_blocks
@@ -405,12 +405,12 @@ pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* ke
  * pa_prefill_varlen_fp8 -- pa_prefill_varlen over E4M3FN pools (uint8 codes)
  * with per-tensor scales.  [B] tutorials 5 and 6, [C] core point 2.
  * K_j = decode(code) * k_scale, V_j = decode(code) * v_scale.  Decode rows
- * (q_len == 1) read the codes directly as in pa_decode_fp8; the blocks of
- * the chunk sequences are first copied, as the exact bf16 values of their
- * codes, into a staging pool in the workspace (its size depends on the
- * chunk sequences' lengths and on bt_stride), then attended by the bf16
- * matrix-core kernel with k_scale folded into the score scale and v_scale
- * into the output.  q_dtype (= out dtype): PA_BF16, or PA_F32 (decode rows
+ * (q_len == 1) read the codes directly as in pa_decode_fp8; the chunks'
+ * K/V tiles are copied as codes and converted to their exact bf16 values
+ * inside the matrix-core kernel, with k_scale folded into the score scale
+ * and v_scale into the output (nothing is staged: the workspace is the
+ * plan's, as for pa_prefill_varlen; bt_stride is checked, >= 1, and does not
+ * change the size).  q_dtype (= out dtype): PA_BF16, or PA_F32 (decode rows
  * as pa_decode_fp8 with fp32 queries; a batch with chunks runs every token as
  * a decode row of its own on the fp8 decode kernel, as pa_prefill_varlen does
  * for PA_F32).  Other arguments as pa_prefill_varlen.
@@ -449,7 +449,7 @@ pa_status_t pa_decode_local_fp8(void* out, const void* query, const uint8_t* key
 /*
  * pa_prefill_varlen_window_fp8, pa_prefill_varlen_local_fp8 --
  * pa_prefill_varlen_window and pa_prefill_varlen_local over E4M3FN pools,
- * with the scales, q_dtype and staging of pa_prefill_varlen_fp8 ([A] §5.1;
+ * with the scales, q_dtype and in-kernel conversion of pa_prefill_varlen_fp8 ([A] §5.1;
  * [B] tutorials 5 and 6).  workspace: the matching *_workspace_bytes(...)
  * with the same bt_stride and window or chunk size (0 on invalid input).
  */
@@ -596,7 +596,7 @@ typedef enum pa_kernel {
   PA_K_DECODE_MERGE = 3,    /* the log-sum-exp merge of split sequences */
   PA_K_PREFILL = 4,         /* the varlen prefill kernel */
   PA_K_PREFILL_MERGE = 5,   /* the log-sum-exp merge of split prefill row tiles */
-  PA_K_STAGE_FP8 = 6,       /* the fp8 -> bf16 staging of chunk sequences (pa_prefill_varlen_fp8) and of a cascade's prefix */
+  PA_K_STAGE_FP8 = 6,       /* no launch is timed under it (fp8 tiles are converted inside the kernels) */
   PA_K_FUSED = 7            /* decode rows and prefill chunks of a mixed batch in one launch (pa_prefill_varlen*) */
 } pa_kernel_t;
 

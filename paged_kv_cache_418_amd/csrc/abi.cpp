@@ -707,7 +707,7 @@ struct CascadeTilePlan {
   int shares = 0;
   int n_decode_wgs = 0;  // compute units the estimate gives the suffix
   int n_splits = 0;      // suffix shares per kv head
-  size_t dec_bytes = 0, pre_o_bytes = 0, pre_m_bytes = 0, table_bytes = 0, stage_bytes = 0, total = 0;
+  size_t dec_bytes = 0, pre_o_bytes = 0, pre_m_bytes = 0, total = 0;
 };
 
 bool cascade_tiles_enabled() {
@@ -766,11 +766,7 @@ CascadeTilePlan plan_cascade_tiles(int num_seqs, int num_q_heads, int num_kv_hea
   const size_t rows = (size_t)cp.shares * num_seqs * num_q_heads;
   cp.pre_o_bytes = align_up(rows * head_dim * sizeof(float));
   cp.pre_m_bytes = align_up(rows * sizeof(float));
-  // fp8 pools: the prefix staged in bf16, K and V, with its table (always counted: the size
-  // query takes no dtype)
-  cp.table_bytes = align_up((size_t)prefix_blocks * sizeof(int32_t));
-  cp.stage_bytes = align_up((size_t)prefix_blocks * pa::kBlockSize * num_kv_heads * head_dim * 2);
-  cp.total = cp.dec_bytes + cp.pre_o_bytes + 2 * cp.pre_m_bytes + cp.table_bytes + 2 * cp.stage_bytes;
+  cp.total = cp.dec_bytes + cp.pre_o_bytes + 2 * cp.pre_m_bytes;
   cp.ok = true;
   return cp;
 }
@@ -805,40 +801,21 @@ pa_status_t run_cascade_tiles(const CascadeTilePlan& cp, void* out, const void* 
   d.prefix_blocks = prefix_blocks;
   d.prefix_shares = 0;  // in the launch: no decode wave takes prefix pieces
   d.prefix_waves = 0;
-  // the prefix tiles, over a bf16 copy of the prefix for fp8 pools (staged just before)
-  const void* pk = key_cache;
-  const void* pv = value_cache;
-  const int32_t* ptab = block_tables;
-  int pblocks = num_blocks;
-  if (kv_kind == pa::kFP8) {
-    unsigned char* sb = pre + cp.pre_o_bytes + 2 * cp.pre_m_bytes;
-    auto* st_table = reinterpret_cast<int32_t*>(sb);
-    auto* st_k = reinterpret_cast<uint16_t*>(sb + cp.table_bytes);
-    auto* st_v = reinterpret_cast<uint16_t*>(sb + cp.table_bytes + cp.stage_bytes);
-    pa_status_t st = hip_status(
-        pa::launch_stage_prefix_fp8(static_cast<const uint8_t*>(key_cache), static_cast<const uint8_t*>(value_cache),
-                                    block_tables, prefix_blocks, num_kv_heads, head_dim, num_blocks, st_k, st_v,
-                                    st_table, stream),
-        "cascade prefix staging launch");
-    if (st != PA_OK) return st;
-    pk = st_k;
-    pv = st_v;
-    ptab = st_table;
-    pblocks = prefix_blocks;
-  }
+  // the prefix tiles, over the pools themselves (fp8: converted in the kernel)
   pa::PrefillParams& pp = f.pre;
   pp.out = out;
   pp.query = query;
-  pp.key_cache = pk;
-  pp.value_cache = pv;
-  pp.block_tables = ptab;
+  pp.key_cache = key_cache;
+  pp.value_cache = value_cache;
+  pp.block_tables = block_tables;
   pp.seq_lens = seq_lens;
   pp.bt_stride = bt_stride;
   pp.num_tokens = num_seqs;
   pp.num_q_heads = num_q_heads;
   pp.num_kv_heads = num_kv_heads;
   pp.group = num_q_heads / num_kv_heads;
-  pp.num_blocks = pblocks;
+  pp.num_blocks = num_blocks;
+  pp.kv_fp8 = kv_kind == pa::kFP8;
   pp.tile_positions = cp.positions;
   pp.scale_log2 = d.scale_log2;
   pp.v_scale = 1.f;
@@ -1195,33 +1172,8 @@ size_t varlen_workspace_bytes(const int32_t* qsl, const int32_t* sl, int num_seq
   return varlen_workspace(sp.plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
 }
 
-// fp8 prefill staging: bf16 copies of the blocks of every chunk sequence (q_len > 1), then
-// their table rows (same stride as the caller's tables).
-struct StageLayout {
-  int blocks = 0, max_blocks = 0;
-  size_t tables_bytes = 0, pool_bytes = 0, total = 0;
-};
-
-StageLayout stage_layout(const int32_t* qsl, const int32_t* sl, int num_seqs, int bt_stride, int num_kv_heads,
-                         int head_dim) {
-  StageLayout L;
-  int64_t blocks = 0;
-  for (int s = 0; s < num_seqs; ++s)
-    if (qsl[s + 1] - qsl[s] > 1) {
-      const int nb = ceil_div(std::max(sl[s], 0), pa::kBlockSize);
-      blocks += nb;
-      L.max_blocks = std::max(L.max_blocks, nb);
-    }
-  L.blocks = (int)std::min<int64_t>(blocks, INT32_MAX);
-  L.tables_bytes = align_up((size_t)num_seqs * bt_stride * sizeof(int32_t));
-  L.pool_bytes = align_up((size_t)blocks * pa::kBlockSize * num_kv_heads * head_dim * sizeof(uint16_t));
-  L.total = blocks ? L.tables_bytes + 2 * L.pool_bytes : 0;
-  return L;
-}
-
 // The varlen call for bf16 pools (kv_kind kBF16; dtype PA_F32 allowed for decode-only
-// batches) and for fp8 pools (kFP8: decode rows read the codes directly; the chunk
-// sequences' blocks are first staged as exact bf16 values, see launch_stage_fp8).
+// batches) and for fp8 pools (kFP8: decode rows and chunks read the codes directly).
 pa_status_t run_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
                        const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                        const int32_t* query_start_loc, const int32_t* seq_lens_host,
@@ -1249,11 +1201,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   const VarlenPlan& plan = sp.plan;
   // chunks of fp32 pools, or of fp32 queries over fp8 pools: every token on its own, no scratch
   const bool rows = dtype == PA_F32 && !plan.items.empty();
-  const StageLayout stage = kv_kind == pa::kFP8 ? stage_layout(query_start_loc_host, seq_lens_host, num_seqs, bt_stride,
-                                                                num_kv_heads, head_dim)
-                                                   : StageLayout{};
-  const size_t base_need = varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
-  const size_t need = rows ? 0 : plan.items.empty() ? base_need : align_up(base_need) + stage.total;
+  const size_t need = rows ? 0 : varlen_workspace(plan, num_seqs, num_q_heads, num_kv_heads, head_dim);
   if (need && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if (need && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
@@ -1301,32 +1249,12 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   float* part_l = plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + lay.m_bytes) : nullptr;
   float* part_s =
       plan.n_split_items ? reinterpret_cast<float*>(ws + dec_bytes + lay.o_bytes + 2 * lay.m_bytes) : nullptr;
-  // fp8: stage the chunk sequences' blocks, then run the bf16 kernel on the staging pool
-  const void* pk_cache = key_cache;
-  const void* pv_cache = value_cache;
-  const int32_t* p_tables = block_tables;
-  int p_num_blocks = num_blocks;
-  if (kv_kind == pa::kFP8 && !plan.items.empty()) {
-    unsigned char* sbase = ws + align_up(base_need);
-    auto* st_tables = reinterpret_cast<int32_t*>(sbase);
-    auto* st_k = reinterpret_cast<uint16_t*>(sbase + stage.tables_bytes);
-    auto* st_v = reinterpret_cast<uint16_t*>(sbase + stage.tables_bytes + stage.pool_bytes);
-    st = hip_status(pa::launch_stage_fp8(static_cast<const uint8_t*>(key_cache), static_cast<const uint8_t*>(value_cache),
-                                         block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, stage.max_blocks,
-                                         num_kv_heads, head_dim, num_blocks, st_k, st_v, st_tables, hs),
-                    "fp8 staging launch");
-    if (st != PA_OK) return st;
-    pk_cache = st_k;
-    pv_cache = st_v;
-    p_tables = st_tables;
-    p_num_blocks = stage.blocks;
-  }
   auto prefill_params = [&](size_t i0, pa::PrefillParams& p) {
     p.out = out;
     p.query = query;
-    p.key_cache = pk_cache;
-    p.value_cache = pv_cache;
-    p.block_tables = p_tables;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
     p.seq_lens = seq_lens;
     p.qsl = query_start_loc;
     p.part_o = part_o;
@@ -1338,7 +1266,8 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     p.num_q_heads = num_q_heads;
     p.num_kv_heads = num_kv_heads;
     p.group = num_q_heads / num_kv_heads;
-    p.num_blocks = p_num_blocks;
+    p.num_blocks = num_blocks;
+    p.kv_fp8 = kv_kind == pa::kFP8;
     p.tile_positions = plan.tile_positions;
     p.item_base = (int)i0;
     p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
@@ -1524,13 +1453,11 @@ pa_status_t pa_prefill_varlen_local(void* out, const void* query, const void* ke
 namespace {
 
 // pa_prefill_varlen(_window|_local)_fp8_workspace_bytes without the argument checks: the
-// plan's workspace (or the virtual rows'), then the bf16 staging of the chunk sequences.
+// plan's workspace (the kernels read the codes themselves, nothing is staged).
 size_t varlen_fp8_workspace_bytes(const int32_t* qsl, const int32_t* sl, int num_seqs, int num_q_heads,
-                                  int num_kv_heads, int head_dim, int bt_stride, int window, int chunk) {
-  const size_t base =
-      varlen_workspace_bytes(qsl, sl, num_seqs, num_q_heads, num_kv_heads, head_dim, window, chunk, /*kv_elem=*/1);
-  const StageLayout stage = stage_layout(qsl, sl, num_seqs, bt_stride, num_kv_heads, head_dim);
-  return stage.total ? align_up(base) + stage.total : base;
+                                  int num_kv_heads, int head_dim, int window, int chunk) {
+  return varlen_workspace_bytes(qsl, sl, num_seqs, num_q_heads, num_kv_heads, head_dim, window, chunk,
+                                /*kv_elem=*/1);
 }
 
 }  // namespace
@@ -1542,7 +1469,7 @@ size_t pa_prefill_varlen_fp8_workspace_bytes(const int32_t* query_start_loc_host
       head_dim < 1 || bt_stride < 1 || num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > pa::kMaxGqa)
     return 0;
   return varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
-                                    head_dim, bt_stride, 0, 0);
+                                    head_dim, 0, 0);
 }
 
 pa_status_t pa_prefill_varlen_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
@@ -1570,7 +1497,7 @@ size_t pa_prefill_varlen_window_fp8_workspace_bytes(const int32_t* query_start_l
       sliding_window < 1)
     return 0;
   return varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
-                                    head_dim, bt_stride, sliding_window, 0);
+                                    head_dim, sliding_window, 0);
 }
 
 size_t pa_prefill_varlen_local_fp8_workspace_bytes(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
@@ -1581,7 +1508,7 @@ size_t pa_prefill_varlen_local_fp8_workspace_bytes(const int32_t* query_start_lo
       chunk_size < 1)
     return 0;
   return varlen_fp8_workspace_bytes(query_start_loc_host, seq_lens_host, num_seqs, num_q_heads, num_kv_heads,
-                                    head_dim, bt_stride, 0, chunk_size);
+                                    head_dim, 0, chunk_size);
 }
 
 namespace {

@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(512) fused_kernel(FusedParams f) {
   }
   // prefill items in the order of the prefill kernel's grid (kv heads fastest)
   const int w = wg - f.n_decode_wgs;
-  prefill_body<D, WINDOW, PREFIX>(f.pre, smem, w / f.pre.num_kv_heads, w % f.pre.num_kv_heads);
+  prefill_body<D, WINDOW, PREFIX, FP8>(f.pre, smem, w / f.pre.num_kv_heads, w % f.pre.num_kv_heads);
 }
 
 }  // namespace

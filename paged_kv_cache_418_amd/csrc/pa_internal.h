@@ -95,9 +95,10 @@ struct PrefillParams {
   int tile_positions;        // positions per row tile: 256 / group
   int item_base;
   float scale_log2;
-  float v_scale;             // 1, or the fp8 value scale (pools staged as the codes' exact values)
+  float v_scale;             // 1, or the fp8 value scale (the tiles hold the codes' exact values)
   int window;                // sliding window (> 0): the row at position p sees keys p-window+1 .. p
   int chunk;                 // chunked local attention (> 0): the row at position p sees keys C*(p div C) .. p
+  int kv_fp8;                // the pools hold E4M3 codes (k_scale folded into scale_log2)
   // cascade prefix tiles (prefill_body's PREFIX form): the rows of a kv head are the
   // prefix_rows query rows x its G q heads, each sees keys 0 .. prefix_keys-1 of table
   // row 0, and an item's unnormalised partial goes to pre_* at share kt0 / prefix_share_tiles
@@ -152,7 +153,7 @@ enum KernelId {
   kKDecodeMerge = 3,
   kKPrefill = 4,
   kKPrefillMerge = 5,
-  kKStageFp8 = 6,
+  kKStageFp8 = 6,            // no launch is timed under it (the id keeps the others fixed)
   kKFused = 7,
   kNumKernelIds = 8
 };
@@ -186,16 +187,10 @@ hipError_t launch_write_kv(const void* key, const void* value, int64_t key_strid
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
 // the log-sum-exp merge of a decode launch's split sequences alone (after a fused launch)
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t stream);
-// decode waves and prefill items in one launch; fp8: the decode waves read E4M3 pools (the
-// prefill items read the bf16 pools named in f.pre, the staging pool for fp8 batches)
+// decode waves and prefill items in one launch; fp8: both read the E4M3 pools (f.pre.kv_fp8 set)
 // (timing_id: the kernel id the launch is timed under -- kKFused for a mixed batch, kKDecode
 // for a cascade, whose prefix tiles and suffix shares share the launch)
 hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_t stream, int timing_id = kKFused);
-// Cascade prefix over fp8 pools: the prefix_blocks blocks of table row 0 copied, as the exact
-// bf16 values of their codes, to staging blocks 0 .. prefix_blocks-1, with their table.
-hipError_t launch_stage_prefix_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
-                                   int prefix_blocks, int num_kv_heads, int head_dim, int num_blocks,
-                                   uint16_t* stage_k, uint16_t* stage_v, int32_t* stage_table, hipStream_t stream);
 
 // The decode's static scratch (pa_decode_static): its size, and its device address on the
 // current device (looked up once per device).
@@ -204,10 +199,8 @@ constexpr int kMaxDevices = 64;
 hipError_t static_scratch(void** ptr);
 
 
+// the prefill kernel over bf16 pools, or over E4M3 pools when p.kv_fp8 is set
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream);
-// fp8 prefill: the blocks of every sequence with q_len > 1 copied, as the exact bf16
-// values of their codes, into a compact staging pool (sequence s's blocks from the sum
-// of the block counts of the chunk sequences before it), with its staging table row.
 // Every query token of a flattened batch attended on its own by one wave per (token, q head),
 // on the vector ALU, without scratch: the chunks of pools or queries the prefill kernel does
 // not take (fp32 pools and activations; fp32 queries over fp8 pools).  Token t of sequence s
@@ -215,10 +208,6 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stre
 // decode query of a sequence of length c_s + i + 1 sees (p.window / p.chunk apply).  p: the
 // decode parameters of the batch (qsl, seq_lens over num_seqs, q_f32 = 1); out is fp32.
 hipError_t launch_rows_f32(const DecodeParams& p, int kv, int head_dim, int num_tokens, hipStream_t stream);
-hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
-                            int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
-                            int max_blocks, int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k,
-                            uint16_t* stage_v, int32_t* stage_tables, hipStream_t stream);
 hipError_t launch_prefill_merge(const PrefillMergeParams& p, int head_dim, hipStream_t stream);
 // matrix-core peak probe (measurement only): blocks x 256 threads, 4 x iters MFMAs per wave
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t stream);

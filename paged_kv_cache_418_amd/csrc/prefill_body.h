@@ -28,6 +28,21 @@ struct PrefillShape {
   static constexpr int kCopies = kTileBytes / 1024 / kWaves;      // copies per wave per tensor per tile
   static constexpr int kKSteps = D / 16;               // 32x32x16 MFMAs over d
   static constexpr int kDTiles = D / 32;               // 32-wide d tiles of O^T
+  // fp8 pools: the copies fill raw tiles of E4M3 codes (one byte an element).  K operands
+  // are converted as they are read; V is converted into a bf16 row-major tile, which the
+  // transposition then turns into V^T as for bf16 pools.
+  static constexpr int kRawRowBytes = D;
+  static constexpr int kRawChunks = D / 16;            // 16-byte chunks per raw row (its swizzle period)
+  static constexpr int kRawTileBytes = kKeys * kRawRowBytes;
+  static constexpr int kRawKSlots = 4;                 // raw K ring: K(t+3) copied at step t
+  static constexpr int kRawVSlots = 3;                 // raw V ring: V(t+4) copied at step t, converted at step t+2
+  static constexpr int kVRowSlots8 = 2;                // bf16 V rows: V(t+2) converted at step t, transposed at t+1
+  static constexpr int kRawRowsPerWave = kKeys / kWaves;  // rows of a raw tile each wave copies and converts
+  static constexpr int kRawLanes = kRawRowsPerWave * kRawChunks;  // lanes that hold one 16-byte raw chunk
+  static constexpr int kLdsBytesF8 =
+      (kRawKSlots + kRawVSlots) * kRawTileBytes + (kVRowSlots8 + kVtSlots) * kTileBytes;
+  static_assert(kLdsBytesF8 <= kLdsBytes, "the fp8 rings fit the bf16 kernel's LDS");
+  static_assert(kRawLanes <= 64, "one raw slab per wave and tensor");
 };
 
 __device__ __forceinline__ bf16x8 u4_to_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -75,7 +90,11 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // 0 .. p.prefix_rows-1 of the batch, each one query of its own sequence, and every row sees
 // all of keys 0 .. p.prefix_keys-1 (the blocks that every sequence's table begins with,
 // read through table row s = 0); the item leaves its unnormalised partial in pre_*.
-template <int D, bool WINDOW, bool PREFIX = false>
+//
+// F8: the pools hold E4M3 codes (the k_scale is in p.scale_log2, the v_scale is applied to
+// the output or by the merge); the tiles are converted to their exact bf16 values in LDS
+// and in registers, so the matrix-core work is the bf16 kernel's.
+template <int D, bool WINDOW, bool PREFIX = false, bool F8 = false>
 __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned char* smem, int item_idx, int kvh) {
   using Sh = PrefillShape<D>;
   static_assert(!(PREFIX && WINDOW), "prefix tiles see the whole prefix");
@@ -121,7 +140,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   const int* bt = p.block_tables + (size_t)s * p.bt_stride;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
-  const size_t tok_stride = (size_t)p.num_kv_heads * D * 2;
+  const size_t tok_stride = (size_t)p.num_kv_heads * D * (F8 ? 1 : 2);
   const int lanes_per_row = Sh::kChunks;
   const int copy_row0 = Sh::kRowsPerCopy * Sh::kCopies * wave;  // first row of this wave's slabs
   // Keys no row of the tile sees are not read from the pool: those past the last visible
@@ -154,19 +173,44 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
 #pragma unroll
     for (int i = 0; i < Sh::kCopies; ++i) copy_slab(base, tile, phys, st, i);
   };
+  // fp8: this wave's kRawRowsPerWave rows of a raw tile (kRawChunks lanes a row, 16 codes a
+  // lane; physical chunk = logical ^ (row % kRawChunks)), one copy instruction
+  auto copy_raw = [&](const uint8_t* base, int tile, int phys, unsigned char* st) {
+    phys = min(max(phys, 0), p.num_blocks - 1);
+    const int row = Sh::kRawRowsPerWave * wave + lane / Sh::kRawChunks;
+    const int chunk = (lane % Sh::kRawChunks) ^ (row % Sh::kRawChunks);
+    const int key = tile * Sh::kKeys + row;
+    const bool live = key < kv_end && (!WINDOW || key >= key_first);
+    const int ph = live ? phys : bt_fill;
+    const size_t off = ((size_t)ph * 16 + ((live ? key : fill_key) & 15)) * tok_stride + (size_t)kvh * D + chunk * 16;
+    unsigned char* dst = st + Sh::kRawRowsPerWave * wave * Sh::kRawRowBytes;
+    if (lane < Sh::kRawLanes)
+      __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(base + off), (void PA_LDS*)dst, 16, 0, 0);
+  };
   // LDS: a ring of four K tiles (tile t in slot (t - kt0) % 4), a ring of three row-major
   // V tiles and a ring of three transposed V tiles (tile t in slot (t - kt0) % 3).
-  auto k_stage = [&](int tile) { return smem + ((tile - kt0) & 3) * Sh::kTileBytes; };
-  auto v_stage = [&](int tile) { return smem + (Sh::kKSlots + (tile - kt0) % 3) * Sh::kTileBytes; };
+  // fp8: four raw K tiles (slot (t - kt0) % 4), three raw V tiles (slot (t - kt0) % 3), two
+  // bf16 row-major V tiles (slot (t - kt0) % 2) and the three V^T tiles.
+  constexpr int kRawV0 = Sh::kRawKSlots * Sh::kRawTileBytes;        // fp8 layout offsets
+  constexpr int kVRow0 = kRawV0 + Sh::kRawVSlots * Sh::kRawTileBytes;
+  constexpr int kVt0 = F8 ? kVRow0 + Sh::kVRowSlots8 * Sh::kTileBytes : (Sh::kKSlots + Sh::kVSlots) * Sh::kTileBytes;
+  auto k_stage = [&](int tile) {
+    return smem + ((tile - kt0) & 3) * (F8 ? Sh::kRawTileBytes : Sh::kTileBytes);
+  };
+  auto v_stage = [&](int tile) {  // the row-major bf16 V tile the transposition reads
+    if constexpr (F8) return smem + kVRow0 + ((tile - kt0) & 1) * Sh::kTileBytes;
+    else return smem + (Sh::kKSlots + (tile - kt0) % 3) * Sh::kTileBytes;
+  };
+  auto vraw_stage = [&](int tile) { return smem + kRawV0 + ((tile - kt0) % 3) * Sh::kRawTileBytes; };
   auto k_addr = [&](int tile) { return (uint32_t)(uintptr_t)k_stage(tile); };
   auto v_addr = [&](int tile) { return (uint32_t)(uintptr_t)v_stage(tile); };
-  auto vt_addr = [&](int tile) {
-    return (uint32_t)(uintptr_t)(smem + (Sh::kKSlots + Sh::kVSlots + (tile - kt0) % 3) * Sh::kTileBytes);
-  };
+  auto vt_addr = [&](int tile) { return (uint32_t)(uintptr_t)(smem + kVt0 + ((tile - kt0) % 3) * Sh::kTileBytes); };
 
-  // block ids of the first four tiles, read before Q so the first copies wait only for them
+  // block ids of the first four tiles (fp8: five, V runs a tile further ahead), read before Q
+  // so the first copies wait only for them
   const int ph0 = block_of(kt0), ph1 = block_of(kt0 + 1), ph2 = block_of(kt0 + 2);
   int phys_next = block_of(kt0 + 3);
+  int phys_v_next = F8 ? block_of(kt0 + 4) : 0;
 
   // ---- Q^T operand: lane holds q[row rl][16*kk + 8*half .. +7].  A lane without a row
   // (past the tile's last position) reads the sequence's first row instead; its results
@@ -196,28 +240,50 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // (2*kk + half) ^ (rl % kChunks) (32 % kChunks == 0).  Operands are read two k-steps
   // before their MFMAs so the LDS latency hides behind the matrix cores; the reads are
   // issued and waited for from asm, like the V reads below.
+  // fp8: the same elements are bytes 16*kk + 8*half .. +7 of raw row rl (raw chunk kk, stored
+  // at kk ^ (rl % kRawChunks)), read as 8 bytes and converted to the bf16 operand in registers.
+  using KOp = std::conditional_t<F8, u32x2, u32x4>;
   uint32_t koff[Sh::kKSteps];
 #pragma unroll
   for (int kk = 0; kk < Sh::kKSteps; ++kk)
-    koff[kk] = (uint32_t)(rl * Sh::kRowBytes + (((2 * kk + half) ^ (rl % Sh::kChunks)) << 4));
-  auto k_issue = [&](u32x4 (&x)[2], uint32_t base, auto kk_c) {
+    koff[kk] = F8 ? (uint32_t)(rl * Sh::kRawRowBytes + ((kk ^ (rl % Sh::kRawChunks)) << 4) + 8 * half)
+                  : (uint32_t)(rl * Sh::kRowBytes + (((2 * kk + half) ^ (rl % Sh::kChunks)) << 4));
+  auto k_issue = [&](KOp (&x)[2], uint32_t base, auto kk_c) {
     constexpr int KK = decltype(kk_c)::value;
     const uint32_t a = base + koff[KK];
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %2 offset:%3"
-        : "=&v"(x[0]), "=&v"(x[1])
-        : "v"(a), "i"(32 * Sh::kRowBytes)
-        : "memory");
+    if constexpr (F8) {
+      asm volatile(
+          "ds_read_b64 %0, %2\n\t"
+          "ds_read_b64 %1, %2 offset:%3"
+          : "=&v"(x[0]), "=&v"(x[1])
+          : "v"(a), "i"(32 * Sh::kRawRowBytes)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b128 %1, %2 offset:%3"
+          : "=&v"(x[0]), "=&v"(x[1])
+          : "v"(a), "i"(32 * Sh::kRowBytes)
+          : "memory");
+    }
+  };
+  // the K operand of an MFMA from what k_issue read
+  auto k_operand = [&](const KOp& x) {
+    if constexpr (F8) {
+      const u32x2 lo = e4m3x4_to_bf16x4(x.x), hi = e4m3x4_to_bf16x4(x.y);
+      return u4_to_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+    } else {
+      return u4_to_bf16x8(x);
+    }
   };
   // waits until at most N LDS reads issued after x's are in flight (reads return in order)
-  auto op_wait = [&](u32x4& x, auto n_c) {
+  auto op_wait = [&](auto& x, auto n_c) {
     constexpr int N = decltype(n_c)::value;
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N) : "memory");
   };
   auto scores = [&](f32x16 (&sacc)[2], uint32_t kbase_lds) {
     constexpr int kAhead = 2;
-    u32x4 kb[kAhead + 1][2];
+    KOp kb[kAhead + 1][2];
     static_for<0, kAhead>([&](auto kk_c) { k_issue(kb[decltype(kk_c)::value], kbase_lds, kk_c); });
     static_for<0, Sh::kKSteps>([&](auto kk_c) {
       constexpr int kk = decltype(kk_c)::value;
@@ -230,7 +296,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
         constexpr int kt = decltype(kt_c)::value;
         op_wait(kb[kk % (kAhead + 1)][kt], std::integral_constant<int, kLater + 1 - kt>{});
         const f32x16 c = kk == 0 ? f32x16{} : sacc[kt];
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(kb[kk % (kAhead + 1)][kt]), qf[kk], c, 0, 0, 0);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kb[kk % (kAhead + 1)][kt]), qf[kk], c, 0, 0, 0);
       });
     });
   };
@@ -371,6 +437,38 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     }
   };
 
+  // fp8: this wave's rows of a raw V tile -> the bf16 row-major tile the transposition reads.
+  // Lane (row cv_row, logical raw chunk cv_cr) converts 16 codes (d = 16*cv_cr .. +15) into bf16
+  // chunks 2*cv_cr and 2*cv_cr+1 of the row, each stored at chunk ^ (row % kChunks).  With
+  // fewer rows' chunks than lanes (D = 64) the upper lanes repeat the lower ones' work.
+  const int cv_row = Sh::kRawRowsPerWave * wave + (lane % Sh::kRawLanes) / Sh::kRawChunks;
+  const int cv_cr = lane % Sh::kRawChunks;
+  const uint32_t cv_src = (uint32_t)(cv_row * Sh::kRawRowBytes + ((cv_cr ^ (cv_row % Sh::kRawChunks)) << 4));
+  const uint32_t cv_dst0 = (uint32_t)(cv_row * Sh::kRowBytes + (((2 * cv_cr) ^ (cv_row % Sh::kChunks)) << 4));
+  const uint32_t cv_dst1 = (uint32_t)(cv_row * Sh::kRowBytes + (((2 * cv_cr + 1) ^ (cv_row % Sh::kChunks)) << 4));
+  auto vraw_issue = [&](u32x4& x, uint32_t raw_base) {
+    asm volatile("ds_read_b128 %0, %1" : "=&v"(x) : "v"(raw_base + cv_src) : "memory");
+  };
+  // x holds landed codes (its read waited for, and x passed through a later asm statement)
+  auto vraw_write = [&](const u32x4& x, uint32_t row_base) {
+    const u32x2 a = e4m3x4_to_bf16x4(x.x), b = e4m3x4_to_bf16x4(x.y);
+    const u32x2 c2 = e4m3x4_to_bf16x4(x.z), d2 = e4m3x4_to_bf16x4(x.w);
+    const u32x4 lo = {a.x, a.y, b.x, b.y}, hi = {c2.x, c2.y, d2.x, d2.y};
+    asm volatile(
+        "ds_write_b128 %0, %2\n\t"
+        "ds_write_b128 %1, %3"
+        :
+        : "v"(row_base + cv_dst0), "v"(row_base + cv_dst1), "v"(lo), "v"(hi)
+        : "memory");
+  };
+  // the whole conversion of this wave's rows of one tile, its read waited for at once
+  auto vraw_convert = [&](uint32_t raw_base, uint32_t row_base) {
+    u32x4 x;
+    vraw_issue(x, raw_base);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x) : : "memory");
+    vraw_write(x, row_base);
+  };
+
   // Online softmax of one tile's scores: P = exp2(s*scale - m) packed to bf16 in pw[chunk]
   // (16-key chunk ch = 2*half32 + cc), l and the reference maximum m updated.
   auto softmax = [&](f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4]) {
@@ -453,12 +551,21 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   };
   // the softmax phase of a step with this wave's share of the transposition V(t+1) -> V^T(t+1):
   // its reads issued first, its rows written after the exponentials
-  auto softmax_tr = [&](bool comp, f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4], uint32_t tr_from, uint32_t tr_to) {
+  // (fp8: also this wave's share of the conversion of raw V(t+2) into bf16 rows, its read issued
+  // with the transposing reads and its rows written after them)
+  auto softmax_tr = [&](bool comp, f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4], uint32_t tr_from, uint32_t tr_to,
+                        uint32_t raw_from, uint32_t row_to) {
     u32x2 tx[Sh::kTransposes];
+    u32x4 vr;
+    if constexpr (F8) vraw_issue(vr, raw_from);
     tr_issue(tx, tr_from);
     if (comp) softmax(sacc, key0, pw);
     tr_wait(tx);
     tr_write(tx, tr_to);
+    if constexpr (F8) {
+      asm volatile("" : "+v"(vr) : : "memory");  // landed with the transposing reads (lgkmcnt(0) above)
+      vraw_write(vr, row_to);
+    }
   };
 
   // Pipeline over the item's key tiles t = kt0 .. kt1-1, one step per tile between
@@ -480,7 +587,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // before the copies of their step, so consuming one never waits on copies in flight.
   // Tiles past the item's range are copied too (valid rows, never used) so that every
   // step is alike.
-  constexpr int kStepLoads = 2 * Sh::kCopies;
+  // fp8: step t copies raw K(t+3) and raw V(t+4) (block ids of tiles t+4 and t+5 read), and
+  // every wave also converts its rows of raw V(t+2) into bf16 row slot t%2, which last held
+  // V(t), transposed at step t-1; the transposition of step t reads slot (t+1)%2, written at
+  // step t-1.  Raw V slot (t+4)%3 last held V(t+1), converted at step t-1; raw K slot
+  // (t+3)%4 last held K(t-1).  The end-of-step wait covers raw K(t+2) and raw V(t+3), the
+  // newest raw tiles step t+1 reads.
+  constexpr int kStepLoads = F8 ? 2 : 2 * Sh::kCopies;  // copy instructions per wave and step
   const int wave_tiles_end = min(kt1, wave_last / Sh::kKeys + 1);  // tiles this wave computes
   // (a sliding window's lower edge is left to the item's key range and to masking: a wave
   // that also skipped its own leading tiles would need registers the kernel does not have)
@@ -488,42 +601,75 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   auto computes = [&](int tile) { return wave_live && tile < wave_tiles_end; };
   {
     wait_vmcnt<Sh::kKSteps>();  // the block ids have landed; Q may still be in flight
-    copy_rows(kbase, kt0, ph0, k_stage(kt0));
-    copy_rows(vbase, kt0, ph0, v_stage(kt0));
-    copy_rows(kbase, kt0 + 1, ph1, k_stage(kt0 + 1));
-    copy_rows(vbase, kt0 + 1, ph1, v_stage(kt0 + 1));
-    copy_rows(kbase, kt0 + 2, ph2, k_stage(kt0 + 2));
-    copy_rows(vbase, kt0 + 2, ph2, v_stage(kt0 + 2));
-    wait_vmcnt<2 * Sh::kCopies>();  // Q and tiles kt0, kt0+1 have landed
-    __builtin_amdgcn_s_barrier();
-    transpose(v_addr(kt0), vt_addr(kt0));
-    wait_vmcnt_lgkm0<2 * Sh::kCopies>();
-    __builtin_amdgcn_s_barrier();
+    if constexpr (F8) {
+      // raw K and V of tiles kt0 .. kt0+2; V(kt0) and V(kt0+1) converted, V(kt0) transposed,
+      // and raw V(kt0+3) copied into the slot V(kt0) left, before the first step
+      copy_raw(kbase, kt0, ph0, k_stage(kt0));
+      copy_raw(vbase, kt0, ph0, vraw_stage(kt0));
+      copy_raw(kbase, kt0 + 1, ph1, k_stage(kt0 + 1));
+      copy_raw(vbase, kt0 + 1, ph1, vraw_stage(kt0 + 1));
+      copy_raw(kbase, kt0 + 2, ph2, k_stage(kt0 + 2));
+      copy_raw(vbase, kt0 + 2, ph2, vraw_stage(kt0 + 2));
+      wait_vmcnt<2>();  // Q and tiles kt0, kt0+1 have landed
+      __builtin_amdgcn_s_barrier();
+      vraw_convert((uint32_t)(uintptr_t)vraw_stage(kt0), v_addr(kt0));
+      vraw_convert((uint32_t)(uintptr_t)vraw_stage(kt0 + 1), v_addr(kt0 + 1));
+      wait_vmcnt_lgkm0<2>();
+      __builtin_amdgcn_s_barrier();
+      transpose(v_addr(kt0), vt_addr(kt0));
+      copy_raw(vbase, kt0 + 3, phys_next, vraw_stage(kt0 + 3));
+      wait_vmcnt_lgkm0<1>();  // tile kt0+2 has landed; raw V(kt0+3) may be in flight
+      __builtin_amdgcn_s_barrier();
+    } else {
+      copy_rows(kbase, kt0, ph0, k_stage(kt0));
+      copy_rows(vbase, kt0, ph0, v_stage(kt0));
+      copy_rows(kbase, kt0 + 1, ph1, k_stage(kt0 + 1));
+      copy_rows(vbase, kt0 + 1, ph1, v_stage(kt0 + 1));
+      copy_rows(kbase, kt0 + 2, ph2, k_stage(kt0 + 2));
+      copy_rows(vbase, kt0 + 2, ph2, v_stage(kt0 + 2));
+      wait_vmcnt<2 * Sh::kCopies>();  // Q and tiles kt0, kt0+1 have landed
+      __builtin_amdgcn_s_barrier();
+      transpose(v_addr(kt0), vt_addr(kt0));
+      wait_vmcnt_lgkm0<2 * Sh::kCopies>();
+      __builtin_amdgcn_s_barrier();
+    }
 
     f32x16 sc[2];  // scores of the tile the wave softmaxes next
     u32x4 pw[4];   // its probabilities, bf16
     if (!leading && computes(kt0)) scores(sc, k_addr(kt0));
     for (int tile = kt0; tile < kt1; ++tile) {
       const int phys_new = block_of(tile + 4);
-      // this step's copies: K(t+3) and V(t+3), kCopies slabs each
-      const int phys = phys_next;
+      const int phys_v_new = F8 ? block_of(tile + 5) : 0;
+      // this step's copies: K(t+3) and V(t+3), kCopies slabs each (fp8: raw K(t+3) and raw
+      // V(t+4), one slab each)
+      const int phys = phys_next, phys_v = phys_v_next;
       unsigned char* const k_dst = k_stage(tile + 3);
-      unsigned char* const v_dst = v_stage(tile + 3);
+      unsigned char* const v_dst = F8 ? vraw_stage(tile + 4) : v_stage(tile + 3);
       auto copy_part = [&](int part) {
-        if (part < Sh::kCopies)
-          copy_slab(kbase, tile + 3, phys, k_dst, part);
-        else if (part < 2 * Sh::kCopies)
-          copy_slab(vbase, tile + 3, phys, v_dst, part - Sh::kCopies);
+        if constexpr (F8) {
+          if (part == 0)
+            copy_raw(kbase, tile + 3, phys, k_dst);
+          else if (part == 1)
+            copy_raw(vbase, tile + 4, phys_v, v_dst);
+        } else {
+          if (part < Sh::kCopies)
+            copy_slab(kbase, tile + 3, phys, k_dst, part);
+          else if (part < 2 * Sh::kCopies)
+            copy_slab(vbase, tile + 3, phys, v_dst, part - Sh::kCopies);
+        }
       };
       auto copy_all = [&]() {
 #pragma unroll
-        for (int part = 0; part < 2 * Sh::kCopies; ++part) copy_part(part);
+        for (int part = 0; part < kStepLoads; ++part) copy_part(part);
       };
       phys_next = phys_new;
+      phys_v_next = phys_v_new;
       // V(t+1) -> V^T(t+1) by every wave; tiles past the range hold valid rows too, so the
-      // transposition is unconditional
+      // transposition is unconditional (fp8: and raw V(t+2) -> bf16 rows, into the slot V(t) left)
       const uint32_t tr_from = v_addr(tile + 1), tr_to = vt_addr(tile + 1);
-      if (!leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to);
+      const uint32_t raw_from = F8 ? (uint32_t)(uintptr_t)vraw_stage(tile + 2) : 0u;
+      const uint32_t row_to = F8 ? v_addr(tile + 2) : 0u;
+      if (!leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to, raw_from, row_to);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
       if (leading) {
@@ -543,7 +689,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
       }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      if (leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to);
+      if (leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to, raw_from, row_to);
       wait_vmcnt_lgkm0<kStepLoads>();
       __builtin_amdgcn_s_barrier();
     }

@@ -27,6 +27,11 @@
 // item may cover only a range of key tiles (a split of a long row tile); it
 // then leaves (O, m, l) for the merge kernel, which combines the splits with
 // the log-sum-exp rule.
+//
+// fp8 pools (tutorial 6 of the same page: E4M3 KV with a scale): the tiles are copied as
+// raw codes; K operands are converted to bf16 as they are read, and V is converted into a
+// bf16 row-major tile before its transposition, so the matrix cores see the codes' exact
+// bf16 values (the scales go to the score scale and the output).
 #include <type_traits>
 
 #include "pa_device.h"
@@ -37,13 +42,13 @@ namespace pa {
 
 namespace {
 
-template <int D, bool WINDOW>
+template <int D, bool WINDOW, bool F8>
 __global__ void __launch_bounds__(512) prefill_kernel(PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   // grid (kv heads, items): the dispatcher walks x fastest, so every kv head's item i
   // starts before any head's item i+1 -- with items listed longest first, the work-groups
   // start in longest-first order across the heads, and the short items fill the tail
-  prefill_body<D, WINDOW>(p, smem, blockIdx.y, blockIdx.x);
+  prefill_body<D, WINDOW, false, F8>(p, smem, blockIdx.y, blockIdx.x);
 }
 
 // Log-sum-exp merge of the splits of a row tile: grid (row tiles x 8 groups of 32 rows,
@@ -108,114 +113,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillMergeParams p
   }
 }
 
-// fp8 staging: one work-group of 256 threads per (sequence, block) -- blocks past the grid's
-// capped y extent (65535) go to work-group y, y + gridDim.y, ....  Sequence s's
-// first staging block is the sum of the block counts of the sequences before it that
-// have q_len > 1 (a block-wide sum over them; the batch's sequence count is small next
-// to the blocks moved).  Each thread turns 16 codes into 16 bf16 values per step.
-__global__ void __launch_bounds__(256) stage_fp8_kernel(const uint8_t* key_cache, const uint8_t* value_cache,
-                                                         const int32_t* block_tables, int bt_stride,
-                                                         const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
-                                                         int row_bytes, int num_blocks, uint16_t* stage_k,
-                                                         uint16_t* stage_v, int32_t* stage_tables) {
-  __shared__ int red[256];
-  const int s = blockIdx.x;
-  if (qsl[s + 1] - qsl[s] <= 1) return;
-  const int nb = (seq_lens[s] + 15) >> 4;
-  if ((int)blockIdx.y >= nb) return;
-  int acc = 0;
-  for (int t = threadIdx.x; t < s; t += 256) acc += qsl[t + 1] - qsl[t] > 1 ? (seq_lens[t] + 15) >> 4 : 0;
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  const int base = red[0];
-  const int block_bytes = 16 * row_bytes;  // codes per block (one byte each)
-  for (int j = blockIdx.y; j < nb; j += gridDim.y) {  // the grid's y extent is capped
-    const int phys = min(max(block_tables[(size_t)s * bt_stride + j], 0), num_blocks - 1);
-    const int dst = base + j;
-    if (threadIdx.x == 0) stage_tables[(size_t)s * bt_stride + j] = dst;
-    const uint8_t* ks = key_cache + (size_t)phys * block_bytes;
-    const uint8_t* vs = value_cache + (size_t)phys * block_bytes;
-    uint16_t* kd = stage_k + (size_t)dst * block_bytes;
-    uint16_t* vd = stage_v + (size_t)dst * block_bytes;
-    for (int e = threadIdx.x * 16; e < block_bytes; e += 256 * 16) {
-      const u32x4 kc = *reinterpret_cast<const u32x4*>(ks + e);
-      const u32x4 vc = *reinterpret_cast<const u32x4*>(vs + e);
-      u32x4 klo, khi, vlo, vhi;
-      const u32x2 k0 = e4m3x4_to_bf16x4(kc.x), k1 = e4m3x4_to_bf16x4(kc.y), k2 = e4m3x4_to_bf16x4(kc.z),
-                  k3 = e4m3x4_to_bf16x4(kc.w);
-      const u32x2 v0 = e4m3x4_to_bf16x4(vc.x), v1 = e4m3x4_to_bf16x4(vc.y), v2 = e4m3x4_to_bf16x4(vc.z),
-                  v3 = e4m3x4_to_bf16x4(vc.w);
-      klo = u32x4{k0.x, k0.y, k1.x, k1.y};
-      khi = u32x4{k2.x, k2.y, k3.x, k3.y};
-      vlo = u32x4{v0.x, v0.y, v1.x, v1.y};
-      vhi = u32x4{v2.x, v2.y, v3.x, v3.y};
-      *reinterpret_cast<u32x4*>(kd + e) = klo;
-      *reinterpret_cast<u32x4*>(kd + e + 8) = khi;
-      *reinterpret_cast<u32x4*>(vd + e) = vlo;
-      *reinterpret_cast<u32x4*>(vd + e + 8) = vhi;
-    }
-  }
-}
-
-// Cascade prefix over fp8 pools: work-group (j, q) copies quarter q of block j of table row 0
-// -- the prefix every sequence's table begins with -- to staging block j as the exact bf16
-// values of its codes (16 codes per thread: one load of K and one of V each), and (q = 0)
-// writes staging table entry j = j.
-__global__ void __launch_bounds__(256) stage_prefix_fp8_kernel(const uint8_t* key_cache, const uint8_t* value_cache,
-                                                                const int32_t* block_tables, int row_bytes,
-                                                                int num_blocks, uint16_t* stage_k, uint16_t* stage_v,
-                                                                int32_t* stage_table) {
-  const int j = blockIdx.x;
-  const int phys = min(max(block_tables[j], 0), num_blocks - 1);
-  if (threadIdx.x == 0 && blockIdx.y == 0) stage_table[j] = j;
-  const int block_bytes = 16 * row_bytes;
-  const uint8_t* ks = key_cache + (size_t)phys * block_bytes;
-  const uint8_t* vs = value_cache + (size_t)phys * block_bytes;
-  uint16_t* kd = stage_k + (size_t)j * block_bytes;
-  uint16_t* vd = stage_v + (size_t)j * block_bytes;
-  for (int e = (blockIdx.y * 256 + threadIdx.x) * 16; e < block_bytes; e += gridDim.y * 256 * 16) {
-    const u32x4 kc = *reinterpret_cast<const u32x4*>(ks + e);
-    const u32x4 vc = *reinterpret_cast<const u32x4*>(vs + e);
-    const u32x2 k0 = e4m3x4_to_bf16x4(kc.x), k1 = e4m3x4_to_bf16x4(kc.y), k2 = e4m3x4_to_bf16x4(kc.z),
-                k3 = e4m3x4_to_bf16x4(kc.w);
-    const u32x2 v0 = e4m3x4_to_bf16x4(vc.x), v1 = e4m3x4_to_bf16x4(vc.y), v2 = e4m3x4_to_bf16x4(vc.z),
-                v3 = e4m3x4_to_bf16x4(vc.w);
-    *reinterpret_cast<u32x4*>(kd + e) = u32x4{k0.x, k0.y, k1.x, k1.y};
-    *reinterpret_cast<u32x4*>(kd + e + 8) = u32x4{k2.x, k2.y, k3.x, k3.y};
-    *reinterpret_cast<u32x4*>(vd + e) = u32x4{v0.x, v0.y, v1.x, v1.y};
-    *reinterpret_cast<u32x4*>(vd + e + 8) = u32x4{v2.x, v2.y, v3.x, v3.y};
-  }
-}
-
 }  // namespace
-
-hipError_t launch_stage_prefix_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
-                                   int prefix_blocks, int num_kv_heads, int head_dim, int num_blocks,
-                                   uint16_t* stage_k, uint16_t* stage_v, int32_t* stage_table, hipStream_t stream) {
-  // one 16-code chunk per thread: 256 threads x 16 codes per work-group along y
-  const int parts = (16 * num_kv_heads * head_dim + 256 * 16 - 1) / (256 * 16);
-  timing_mark(kKStageFp8, true, stream);
-  hipLaunchKernelGGL(stage_prefix_fp8_kernel, dim3(prefix_blocks, parts), dim3(256), 0, stream, key_cache, value_cache,
-                     block_tables, num_kv_heads * head_dim, num_blocks, stage_k, stage_v, stage_table);
-  timing_mark(kKStageFp8, false, stream);
-  return hipGetLastError();
-}
-
-hipError_t launch_stage_fp8(const uint8_t* key_cache, const uint8_t* value_cache, const int32_t* block_tables,
-                            int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int max_blocks,
-                            int num_kv_heads, int head_dim, int num_blocks, uint16_t* stage_k, uint16_t* stage_v,
-                            int32_t* stage_tables, hipStream_t stream) {
-  const dim3 grid(num_seqs, std::min(max_blocks, 65535));
-  timing_mark(kKStageFp8, true, stream);
-  hipLaunchKernelGGL(stage_fp8_kernel, grid, dim3(256), 0, stream, key_cache, value_cache, block_tables, bt_stride,
-                     seq_lens, qsl, num_seqs, num_kv_heads * head_dim, num_blocks, stage_k, stage_v, stage_tables);
-  timing_mark(kKStageFp8, false, stream);
-  return hipGetLastError();
-}
 
 size_t prefill_lds_bytes(int head_dim) {
   return head_dim == 128 ? PrefillShape<128>::kLdsBytes : PrefillShape<64>::kLdsBytes;
@@ -224,23 +122,27 @@ size_t prefill_lds_bytes(int head_dim) {
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads, p.n_items);
   const size_t lds = prefill_lds_bytes(head_dim);
+  const bool win = p.window > 0 || p.chunk > 0;
   timing_mark(kKPrefill, true, stream);
-  auto launch = [&](auto kernel, int threads) {
+  auto launch = [&](auto kernel) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
-    hipLaunchKernelGGL(kernel, grid, dim3(threads), lds, stream, p);
+    hipLaunchKernelGGL(kernel, grid, dim3(512), lds, stream, p);
   };
-  if (head_dim == 128) {
-    if (p.window > 0 || p.chunk > 0)
-      launch(&prefill_kernel<128, true>, PrefillShape<128>::kThreads);
+  auto pick = [&](auto d_c, auto f8_c) {
+    constexpr int D = decltype(d_c)::value;
+    constexpr bool F8 = decltype(f8_c)::value;
+    if (win)
+      launch(&prefill_kernel<D, true, F8>);
     else
-      launch(&prefill_kernel<128, false>, PrefillShape<128>::kThreads);
-  } else {
-    if (p.window > 0 || p.chunk > 0)
-      launch(&prefill_kernel<64, true>, PrefillShape<64>::kThreads);
-    else
-      launch(&prefill_kernel<64, false>, PrefillShape<64>::kThreads);
-  }
+      launch(&prefill_kernel<D, false, F8>);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (head_dim == 128)
+    p.kv_fp8 ? pick(std::integral_constant<int, 128>{}, T{}) : pick(std::integral_constant<int, 128>{}, F{});
+  else
+    p.kv_fp8 ? pick(std::integral_constant<int, 64>{}, T{}) : pick(std::integral_constant<int, 64>{}, F{});
   timing_mark(kKPrefill, false, stream);
   return hipGetLastError();
 }

@@ -253,15 +253,15 @@ def _align(x):
     return (x + 255) // 256 * 256
 
 
-def test_prefill_fp8_workspace_adds_staging(lib):
-    # chunks of 40 and 300 tokens on 100- and 900-token contexts: staging = ceil(100/16) + ceil(900/16) = 7 + 57
-    # blocks, bf16 K and V of 16 x 8 x 128 each, plus the staging table rows (3 sequences x 64 columns)
+def test_prefill_fp8_workspace_is_the_plans(lib):
+    # chunks of 40 and 300 tokens on 100- and 900-token contexts and one decode row: the fp8 kernels convert the
+    # codes themselves, so nothing is staged and the size is the plan's, for any table stride
     q, s = _host_i32([0, 40, 41, 341]), _host_i32([100, 5000, 900])
     base = lib.pa_prefill_varlen_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128)
-    got = lib.pa_prefill_varlen_fp8_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128, 400)
-    pool = _align((7 + 57) * 16 * 8 * 128 * 2)
-    assert got == _align(base) + _align(3 * 400 * 4) + 2 * pool
-    # decode rows only: no staging
+    for bt_stride in (64, 400):
+        assert lib.pa_prefill_varlen_fp8_workspace_bytes(ctypes.addressof(q), ctypes.addressof(s), 3, 32, 8, 128,
+                                                         bt_stride) == base > 0
+    # decode rows only
     q1, s1 = _host_i32([0, 1, 2]), _host_i32([1000, 10])
     assert lib.pa_prefill_varlen_fp8_workspace_bytes(ctypes.addressof(q1), ctypes.addressof(s1), 2, 32, 8, 128,
                                                      100) == \
