@@ -97,7 +97,6 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n) {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-constexpr int kFusedDecodeWaves = 8;  // decode waves per work-group of a fused launch
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -124,6 +123,16 @@ int env_int(const char* name, int dflt, int lo, int hi) {
   return x >= lo && x <= hi ? x : dflt;
 }
 
+// The decode scratch of a varlen call is sized for kFusedSplitsFactor waves per SIMD (eight
+// decode waves per compute unit of a fused launch); the fused launch never takes more shares.
+constexpr int kFusedSplitsFactor = 2;
+
+// decode waves per work-group of a fused launch (PA_FUSED_DECODE_WAVES, 1..8; measurement)
+int fused_decode_waves() {
+  static const int w = env_int("PA_FUSED_DECODE_WAVES", 8, 1, 8);
+  return w;
+}
+
 // Compute units of the current device (cached per device; 256 when no device is visible).
 int device_cu_count() {
   static std::atomic<int> cache[64];
@@ -137,17 +146,18 @@ int device_cu_count() {
 }
 
 // Decode waves per SIMD the automatic split aims at: PA_DECODE_WAVES_PER_SIMD when set, else
-// one for bf16/fp32 pools (with streaming loads one wave per SIMD, two blocks in flight each,
-// beat two on a Llama-3-8B layer, 89 against 96 us) and two for fp8 pools (a block is half the
-// bytes for the same per-block work: on the same layer with E4M3 pools 53 us at two waves, 60
-// at one, 54 at three, 63 at four).
+// one, for every pool type.  With streaming loads, one wave per SIMD with two blocks in flight
+// beat two waves on a Llama-3-8B layer (89 against 96 us), and with E4M3 pools as well once the
+// block ids came through the scalar cache (48.4-48.9 against 51.3-51.6 us; three, four or six
+// register sets at one wave: 51.3, 51.5, 54.2 us).
 int decode_waves_per_simd(bool fp8) {
+  (void)fp8;
   static const int env = [] {
     const char* v = std::getenv("PA_DECODE_WAVES_PER_SIMD");
     const int x = v ? std::atoi(v) : 0;
     return x >= 1 && x <= 16 ? x : 0;
   }();
-  return env ? env : (fp8 ? 2 : 1);
+  return env ? env : 1;
 }
 
 // Blocks' worth of time a decode piece costs to start (PA_DECODE_PIECE_COST): the share
@@ -558,9 +568,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || max_seq_len < 1 || num_splits < 0)
     return 0;
   if (num_q_heads % num_kv_heads) return 0;
-  // sized for the larger automatic share count (fp8 pools); a bf16 or fp32 call uses part of it
-  const int n_splits =
-      resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), max_seq_len, 1, true);
+  // sized for two waves per SIMD: the decode part of a fused decode + prefill launch runs up
+  // to eight decode waves per compute unit (an automatic plain decode uses half of it)
+  const int n_splits = resolve_splits(num_splits, num_seqs, decode_columns(num_q_heads, num_kv_heads), max_seq_len,
+                                      kFusedSplitsFactor);
   if (n_splits <= 1) return 0;
   return decode_layout(num_seqs, num_q_heads, n_splits, head_dim).total;
 }
@@ -758,10 +769,10 @@ CascadeTilePlan plan_cascade_tiles(int num_seqs, int num_q_heads, int num_kv_hea
   // suffix shares: eight decode waves on each compute unit of the estimate (or num_splits),
   // never more than the blocks there can be
   const int64_t max_blocks = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
-  int64_t ns = num_splits > 0 ? num_splits : (int64_t)cp.n_decode_wgs * kFusedDecodeWaves / num_kv_heads;
+  int64_t ns = num_splits > 0 ? num_splits : (int64_t)cp.n_decode_wgs * fused_decode_waves() / num_kv_heads;
   ns = std::min<int64_t>(std::max<int64_t>(ns, 1), std::max<int64_t>(max_blocks, 1));
   cp.n_splits = (int)ns;
-  cp.n_decode_wgs = ceil_div((int64_t)cp.n_splits * num_kv_heads, kFusedDecodeWaves);
+  cp.n_decode_wgs = ceil_div((int64_t)cp.n_splits * num_kv_heads, fused_decode_waves());
   cp.dec_bytes = align_up(decode_layout(num_seqs, num_q_heads, cp.n_splits, head_dim).total);
   const size_t rows = (size_t)cp.shares * num_seqs * num_q_heads;
   cp.pre_o_bytes = align_up(rows * head_dim * sizeof(float));
@@ -832,9 +843,9 @@ pa_status_t run_cascade_tiles(const CascadeTilePlan& cp, void* out, const void* 
       pp.items[n++] = ((uint64_t)rt << 16) | (kt0 << 32) | (kt1 << 48);
     }
   pp.n_items = n;
-  f.decode_waves_per_wg = kFusedDecodeWaves;
+  f.decode_waves_per_wg = fused_decode_waves();
   f.decode_waves = d.n_splits * num_kv_heads;
-  f.n_decode_wgs = ceil_div(f.decode_waves, kFusedDecodeWaves);
+  f.n_decode_wgs = ceil_div(f.decode_waves, fused_decode_waves());
   pa_status_t st = hip_status(pa::launch_fused(f, head_dim, kv_kind == pa::kFP8, stream, pa::kKDecode),
                               "cascade prefix tiles + suffix launch");
   if (st != PA_OK) return st;
@@ -1156,7 +1167,7 @@ pa_status_t plan_step(const int32_t* qsl, const int32_t* sl, int num_seqs, int n
   sp.fused = true;
   sp.plan = std::move(best_plan);
   sp.n_decode_wgs = best_q;
-  sp.decode_splits = std::max(1, best_q * kFusedDecodeWaves / decode_columns(num_q_heads, num_kv_heads));
+  sp.decode_splits = std::max(1, best_q * fused_decode_waves() / decode_columns(num_q_heads, num_kv_heads));
   return PA_OK;
 }
 
@@ -1279,16 +1290,19 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
     std::memcpy(p.items, plan.items.data() + i0, n * sizeof(uint64_t));
   };
   if (sp.fused) {  // decode waves and prefill items in one launch (plan_step keeps the items to one launch)
+    // never more shares than the decode scratch of the workspace was sized for
+    const int ws_splits = resolve_splits(0, num_seqs, decode_columns(num_q_heads, num_kv_heads),
+                                         plan.max_decode_len, kFusedSplitsFactor);
     pa::FusedParams f{};
     f.dec = make_decode_params(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens,
                                query_start_loc, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                                plan.max_decode_len, scale, dec_kind, dtype == PA_F32, k_scale, v_scale,
-                               sp.decode_splits, workspace, 0, sliding_window, local_chunk);
+                               std::min(sp.decode_splits, ws_splits), workspace, 0, sliding_window, local_chunk);
     f.dec.num_blocks = num_blocks;
     prefill_params(0, f.pre);
-    f.decode_waves_per_wg = kFusedDecodeWaves;
+    f.decode_waves_per_wg = fused_decode_waves();
     f.decode_waves = (f.dec.prefix_waves + f.dec.n_splits) * decode_columns(num_q_heads, num_kv_heads);
-    f.n_decode_wgs = (f.decode_waves + kFusedDecodeWaves - 1) / kFusedDecodeWaves;
+    f.n_decode_wgs = (f.decode_waves + fused_decode_waves() - 1) / fused_decode_waves();
     st = hip_status(pa::launch_fused(f, head_dim, kv_kind == pa::kFP8, hs), "fused decode + prefill launch");
     if (st != PA_OK) return st;
     st = hip_status(pa::launch_decode_merge(f.dec, head_dim, hs), "decode merge launch");

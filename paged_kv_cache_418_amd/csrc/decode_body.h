@@ -47,6 +47,10 @@ struct BlockRegs {
   RawVec<Sh::kLoadBytes> k[4], v[4];
 };
 
+// pointers into the constant address space: loads through them from wave-uniform addresses
+// become scalar loads
+#define PA_CONST_AS __attribute__((address_space(4)))
+
 #ifndef PA_DECODE_IN_FLIGHT
 #define PA_DECODE_IN_FLIGHT 2
 #endif
@@ -444,24 +448,22 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
     roff[i] = (uint32_t)((a + 4 * i) * row_stride) + (uint32_t)(kvh * D * kElem) + (uint32_t)(c * Sh::kLoadBytes);
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
-  // Physical block ids of the partition, 64 at a time in one VGPR (lane i holds block
-  // win0 + i); a wave-uniform block id is then one v_readlane away.  (Loading the next 64
-  // one issue ahead, so that a crossing never waits for the table, measured slower:
-  // Llama-3-8B layer 89.0 against 87.2 us, 70B long context 363 against 352.)
-  const int* bt = p.block_tables + (size_t)s * p.bt_stride + skip + b0;
-  int win0 = 0;
-  int bt_win = lane < nblk ? bt[lane] : 0;
+  // Physical block ids of the piece come through the scalar cache (wave-uniform addresses),
+  // each read one issue before the loads that use it.  A vector load of the ids (a window of
+  // 64 in a VGPR, reloaded when a piece crosses it) made the compiler wait for every vector
+  // load in flight before each issue -- the reload might still be pending -- which drained
+  // the blocks being prefetched.
+  const int PA_CONST_AS* bt =
+      (const int PA_CONST_AS*)(uintptr_t)(p.block_tables + (size_t)s * p.bt_stride + skip + b0);
+  int phys_next = bt[0];
 
   // Loads of block b of the partition.  Indices past the end re-read the last
   // block (cache-resident, no HBM traffic) so that the loop is branch-free and
   // the order of outstanding loads never depends on the data.
   auto issue = [&](BlockRegs<D, FP8>& r, int b) {
-    b = min(b, nblk - 1);
-    if (b >= win0 + 64) {
-      win0 += 64;
-      bt_win = win0 + lane < nblk ? bt[win0 + lane] : 0;
-    }
-    int phys = __builtin_amdgcn_readlane(bt_win, b - win0);
+    // issues come for b = 0, 1, 2, ... in turn: this one's id was read by the previous one
+    int phys = phys_next;
+    phys_next = bt[min(b + 1, nblk - 1)];
     phys = min(max(phys, 0), p.num_blocks - 1);
     const uint8_t* kb = kbase + (size_t)phys * block_bytes;  // wave-uniform
     const uint8_t* vb = vbase + (size_t)phys * block_bytes;

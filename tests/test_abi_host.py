@@ -43,6 +43,12 @@ def test_decode_workspace_arithmetic(lib):
     assert pk.pa_decode_workspace_bytes(1, 4, 2, 64, 16, 0) == 0               # a single block
     assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, -1) == 0         # invalid share count
     assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) > 0           # automatic
+    # the automatic size holds the shares of eight decode waves per compute unit (256 of them without a GPU):
+    # what the decode part of a fused decode + prefill launch may take
+    assert pk.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) == pk.pa_decode_workspace_bytes(64, 32, 8, 128,
+                                                                                                 4096, 256)
+    assert pk.pa_decode_workspace_bytes(8, 8, 2, 64, 1800, 0) == pk.pa_decode_workspace_bytes(8, 8, 2, 64, 1800,
+                                                                                              8 * 113)
     # a kv head with 32 q heads takes two waves per share (16 matrix-core columns each): the automatic plan of
     # 32 q heads over 1 kv head is that of 32 over 2
     assert pk.pa_decode_workspace_bytes(64, 32, 1, 128, 4096, 0) == pk.pa_decode_workspace_bytes(64, 32, 2, 128, 4096, 0)
