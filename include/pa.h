@@ -172,9 +172,9 @@ pa_status_t pa_write_kv_fp8(const void* key, const void* value, int64_t key_tok_
  * pa_decode_workspace_bytes -- scratch pa_decode / pa_decode_fp8 need.
  * The blocks of all sequences, laid end to end, are cut into num_splits
  * equal shares per kv head (0 = automatic: about one wave per SIMD of the
- * current device for bf16/fp32 pools and two for fp8 pools, whose blocks are
- * half the bytes; PA_DECODE_WAVES_PER_SIMD overrides both, and the size
- * returned covers the larger count); a sequence
+ * current device for every pool type; PA_DECODE_WAVES_PER_SIMD overrides it;
+ * the size returned covers twice that count, the share count of the decode
+ * part of a fused decode + prefill launch of pa_prefill_varlen*); a sequence
  * split across shares gets partial results that are merged with the
  * log-sum-exp rule ([B] tutorial 7).  The count is capped at
  * num_seqs * ceil(max_seq_len / 16).  Returns 0 when a single share is used
