@@ -280,6 +280,53 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_write -- one decode step's KV write and attention in one call:
+ * the result, and every byte of both pools, are those of pa_write_kv (one
+ * new row per sequence: query_start_loc = 0, 1, ..., num_seqs, max_q_len 1)
+ * followed by pa_decode.  [A] §3 (the new token's K/V are stored into its
+ * slot, then attention reads the cache through the block table), [B]
+ * tutorial 3 (slot of position p: block_tables[s][p / block_size] *
+ * block_size + p % block_size).  key/value: [num_seqs][num_kv_heads]
+ * [head_dim] rows of dtype, row s the K/V of sequence s's position
+ * seq_lens[s] - 1, heads and head_dim contiguous, key_tok_stride /
+ * value_tok_stride elements between rows.  With bf16 pools and every
+ * kv-head slice 16-byte aligned (key, value and both strides in bytes
+ * multiples of 16), the decode launch stores the rows itself and attends
+ * them from registers; otherwise (fp32 pools, other alignments) the write
+ * runs as its own launch first.  Conditions on the batch, beyond
+ * pa_decode's: the block holding a sequence's new row is read by no other
+ * sequence of the batch (a block manager shares only full blocks); a
+ * sequence with seq_lens[s] > max_seq_len is cut as in pa_decode and its row
+ * is not stored; a row whose table entry lies outside the pool is not stored
+ * (as pa_write_kv) but still attended.  dtype: PA_F32 or PA_BF16, for the
+ * pools, query/out and key/value.  Other arguments, workspace and errors as
+ * pa_decode.
+ */
+pa_status_t pa_decode_write(void* out, const void* query, const void* key, const void* value,
+                            int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache, void* value_cache,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                            pa_dtype_t dtype, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * pa_decode_write_fp8 -- pa_decode_write over E4M3FN pools ([B] tutorial 6):
+ * the stored codes are pa_write_kv_fp8's (of x / k_scale and x / v_scale),
+ * the attention pa_decode_fp8's.  dtype (PA_F32 or PA_BF16) is that of
+ * query/out and of key/value; the decode launch stores the rows itself when
+ * every kv-head slice is 16-byte aligned.  Other arguments as
+ * pa_decode_write and pa_decode_fp8.
+ */
+pa_status_t pa_decode_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_seq_len, float scale, pa_dtype_t dtype, float k_scale, float v_scale,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_cascade -- pa_decode for a batch whose sequences all begin with
  * the same prefix_blocks physical blocks (prefix sharing: [A] §2, two
  * requests' tables pointing at the same blocks; cascade attention is named in

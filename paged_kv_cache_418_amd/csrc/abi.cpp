@@ -344,18 +344,36 @@ pa::DecodeParams make_decode_params(void* out, const void* query, const void* ke
   return p;
 }
 
+// The step's new K/V rows for a decode launch that stores them itself (row s: sequence s).
+struct NewRows {
+  const void* key;
+  const void* value;
+  int64_t key_stride, value_stride;  // elements
+  int src_f32;
+  float k_scale, v_scale;            // fp8 pools, else 1
+};
+
 pa_status_t run_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                        const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, const int32_t* qsl,
                        int32_t num_seqs, int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
                        int q_f32, float k_scale, float v_scale, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, hipStream_t stream, int32_t prefix_blocks = 0,
-                       int32_t sliding_window = 0, int32_t local_chunk = 0) {
+                       int32_t sliding_window = 0, int32_t local_chunk = 0, const NewRows* rows = nullptr) {
   pa::DecodeParams p = make_decode_params(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, qsl,
                                           num_seqs, num_rows, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                                           scale, kv_kind, q_f32, k_scale, v_scale, num_splits, workspace,
                                           prefix_blocks, sliding_window, local_chunk);
   p.num_blocks = num_blocks;
+  if (rows) {
+    p.new_k = rows->key;
+    p.new_v = rows->value;
+    p.new_k_stride = rows->key_stride;
+    p.new_v_stride = rows->value_stride;
+    p.new_f32 = rows->src_f32;
+    p.new_k_scale = rows->k_scale;
+    p.new_v_scale = rows->v_scale;
+  }
   (void)workspace_bytes;
   (void)block_size;
   return hip_status(pa::launch_decode(p, kv_kind, head_dim, stream), "decode launch");
@@ -664,6 +682,85 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache
 
 namespace {
 
+// pa_decode_write / pa_decode_write_fp8: the decode launch stores the new rows itself when the
+// pools are bf16 or fp8 and each kv-head slice of a row is 16-byte aligned; otherwise (fp32
+// pools, other alignments) the KV write runs first as its own launch.  Both give the same bytes.
+pa_status_t decode_write(void* out, const void* query, const void* key, const void* value, int64_t key_tok_stride,
+                         int64_t value_tok_stride, void* key_cache, void* value_cache, const int32_t* block_tables,
+                         int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_seq_len, float scale, int kv_kind, pa_dtype_t dtype, float k_scale,
+                         float v_scale, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (kv_kind != pa::kF32 && num_q_heads / num_kv_heads > pa::kMaxGqa)
+    return fail(PA_ERR_UNSUPPORTED, "decode supports up to %d q heads per kv head", pa::kMaxGqa);
+  if (num_seqs > 0 && (!key || !value)) return fail(PA_ERR_NULL, "key or value is NULL");
+  if (key_tok_stride < (int64_t)num_kv_heads * head_dim || value_tok_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "token stride smaller than num_kv_heads * head_dim");
+  if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_SHAPE, "pool has more than 2^31 slots");
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  const int src_f32 = dtype == PA_F32;
+  const int64_t elem = src_f32 ? 4 : 2;
+  const uintptr_t align = (uintptr_t)key | (uintptr_t)value | (uintptr_t)(key_tok_stride * elem) |
+                          (uintptr_t)(value_tok_stride * elem);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kv_kind != pa::kF32 && (align & 15u) == 0) {
+    const NewRows rows{key, value, key_tok_stride, value_tok_stride, src_f32, k_scale, v_scale};
+    return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                      kv_kind, src_f32, k_scale, v_scale, num_splits, workspace, workspace_bytes, s, 0, 0, 0, &rows);
+  }
+  const int write_kind = kv_kind == pa::kFP8 ? (src_f32 ? pa::kFP8 + 1 : pa::kFP8) : kv_kind;
+  st = hip_status(pa::launch_write_kv(key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, nullptr,
+                                      block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_seqs, 1, num_kv_heads,
+                                      head_dim, block_size, num_blocks, write_kind, k_scale, v_scale, s),
+                  "write_kv launch");
+  if (st != PA_OK) return st;
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_seqs,
+                    num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, kv_kind, src_f32,
+                    k_scale, v_scale, num_splits, workspace, workspace_bytes, s);
+}
+
+}  // namespace
+
+pa_status_t pa_decode_write(void* out, const void* query, const void* key, const void* value, int64_t key_tok_stride,
+                            int64_t value_tok_stride, void* key_cache, void* value_cache, const int32_t* block_tables,
+                            int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  return decode_write(out, query, key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                      bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_seq_len, scale, dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype, 1.f, 1.f, num_splits,
+                      workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                                float scale, pa_dtype_t dtype, float k_scale, float v_scale, int32_t num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  return decode_write(out, query, key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                      bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_seq_len, scale, pa::kFP8, dtype, k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                      stream);
+}
+
+namespace {
+
 // Arguments of a cascade call on top of the decode checks: a prefix of whole blocks
 // inside every sequence, a group of at most 16 q heads, and (PA_VALIDATE=1) tables
 // that really share it.
@@ -701,8 +798,8 @@ namespace {
 // in one launch with the suffix shares of the split decode (launch_fused: the decode
 // work-groups first, eight decode waves each, then the items, one work-group per compute
 // unit), each item leaves an unnormalised partial per (share, sequence, head), and the
-// decode merge folds them with the suffix pieces.  fp8 pools: the prefix blocks are first
-// staged as the exact bf16 values of their codes (the tiles read bf16 operands).
+// decode merge folds them with the suffix pieces.  fp8 pools: the tiles copy the codes and
+// convert them to their exact bf16 values in the kernel, on the way to the matrix cores.
 //
 // The split between the two parts uses the fused launch's host estimate (PA_FUSED_TILE_NS
 // per 64-key tile of a 256-row item plus 5 us; PA_FUSED_CU_GBPS per decode compute unit up

@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(128) write_kv_kernel(const void* key, const vo
                                                        int block_size, int num_slots, int row, float k_scale,
                                                        float v_scale) {
   const int s = blockIdx.x;
-  const int q0 = qsl[s], q_len = qsl[s + 1] - q0;
+  const int q0 = qsl ? qsl[s] : s, q_len = qsl ? qsl[s + 1] - q0 : 1;  // no qsl: one row per sequence
   const int cached = seq_lens[s] - q_len;
   const int* bt = block_tables + (size_t)s * bt_stride;
   // row groups blockIdx.y, blockIdx.y + gridDim.y, ... of kWriteTokens rows (the grid's y extent is capped)

@@ -73,6 +73,29 @@ __device__ __forceinline__ void load_raw(RawVec<N>& r, const uint8_t* p) {
   else r.v = *reinterpret_cast<const uint32_t*>(p);
 }
 
+template <int N>
+__device__ __forceinline__ void store_raw(uint8_t* p, const RawVec<N>& r) {
+  if constexpr (N == 16) *reinterpret_cast<u32x4*>(p) = r.v;
+  else if constexpr (N == 8) *reinterpret_cast<u32x2*>(p) = r.v;
+  else *reinterpret_cast<uint32_t*>(p) = r.v;
+}
+
+// r = x where take (per lane)
+template <int N>
+__device__ __forceinline__ void select_raw(RawVec<N>& r, const RawVec<N>& x, bool take) {
+  if constexpr (N == 16) {
+    r.v.x = take ? x.v.x : r.v.x;
+    r.v.y = take ? x.v.y : r.v.y;
+    r.v.z = take ? x.v.z : r.v.z;
+    r.v.w = take ? x.v.w : r.v.w;
+  } else if constexpr (N == 8) {
+    r.v.x = take ? x.v.x : r.v.x;
+    r.v.y = take ? x.v.y : r.v.y;
+  } else {
+    r.v = take ? x.v : r.v;
+  }
+}
+
 // The same as a non-temporal load: KV that one wave streams once is not kept in the
 // caches (measured: the decode kernel of a Llama-3-8B layer 103 -> 96 us, the 70B
 // long-context one 394 -> 356 us, with less L2/last-level-cache churn).
@@ -137,6 +160,92 @@ __device__ __forceinline__ float sum_across_rows(float x) {
   const uint32_t v = __float_as_uint(x);
   auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
+// A new K/V row's slice of kv head kvh as loaded (row `row` of the input, 16-byte aligned slices,
+// checked by the caller).  bf16 pools: lane (a, c) loads elements c*VEC .. c*VEC+VEC-1 of K and
+// of V, the pool-format slice it substitutes.  fp8 pools: the quantisation is spread over the
+// whole wave -- lane l loads elements (l % 32)*D/32 .. +D/32-1 of K (l < 32) or V (l >= 32), fp32
+// or bf16 -- and the codes reach the lanes that substitute them through cross-lane reads.
+template <int D>
+struct NewRowSrc {
+  uint32_t w[D / 32];
+};
+
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t* w, const void* p) {
+  if constexpr (N == 4) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(p);
+    w[0] = t.x;
+    w[1] = t.y;
+    w[2] = t.z;
+    w[3] = t.w;
+  } else if constexpr (N == 2) {
+    const u32x2 t = *reinterpret_cast<const u32x2*>(p);
+    w[0] = t.x;
+    w[1] = t.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void load_new_row(const DecodeParams& p, NewRowSrc<D>& k, NewRowSrc<D>& v, int row,
+                                             int kvh, int lane) {
+  constexpr int VEC = D / 16;
+  if constexpr (!FP8) {
+    const int64_t e = kvh * D + (lane & 15) * VEC;
+    load_words<VEC / 2>(k.w, reinterpret_cast<const uint16_t*>(p.new_k) + (int64_t)row * p.new_k_stride + e);
+    load_words<VEC / 2>(v.w, reinterpret_cast<const uint16_t*>(p.new_v) + (int64_t)row * p.new_v_stride + e);
+  } else {
+    constexpr int N = D / 32;  // elements of this lane
+    const bool is_v = lane >= 32;
+    const void* src = is_v ? p.new_v : p.new_k;
+    const int64_t e = (int64_t)row * (is_v ? p.new_v_stride : p.new_k_stride) + kvh * D + (lane & 31) * N;
+    if (p.new_f32) load_words<N>(k.w, reinterpret_cast<const float*>(src) + e);
+    else load_words<N / 2>(k.w, reinterpret_cast<const uint16_t*>(src) + e);
+  }
+}
+
+// The substituting lane's slices in the pool's format: the bf16 values themselves, or for an
+// fp8 pool the E4M3 codes of x / scale -- the codes the KV write stores (round to nearest even,
+// saturating).  fp8: every lane of the wave takes part (cross-lane reads).
+template <int D, bool FP8>
+__device__ __forceinline__ void new_row_raw(const DecodeParams& p, const NewRowSrc<D>& k, const NewRowSrc<D>& v,
+                                            RawVec<DecodeShape<D, FP8>::kLoadBytes>& nk,
+                                            RawVec<DecodeShape<D, FP8>::kLoadBytes>& nv, int lane) {
+  constexpr int VEC = D / 16;
+  if constexpr (!FP8) {
+    if constexpr (VEC == 8) {
+      nk.v = u32x4{k.w[0], k.w[1], k.w[2], k.w[3]};
+      nv.v = u32x4{v.w[0], v.w[1], v.w[2], v.w[3]};
+    } else {
+      nk.v = u32x2{k.w[0], k.w[1]};
+      nv.v = u32x2{v.w[0], v.w[1]};
+    }
+  } else {
+    constexpr int N = D / 32;
+    const float scale = lane >= 32 ? p.new_v_scale : p.new_k_scale;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float x = p.new_f32 ? __uint_as_float(k.w[j])
+                                : __uint_as_float((j & 1) ? (k.w[j >> 1] & 0xFFFF0000u) : (k.w[j >> 1] << 16));
+      codes |= (uint32_t)f32_to_e4m3(__fdiv_rn(x, scale)) << (8 * j);
+    }
+    // lane (a, c) substitutes elements c*VEC .. c*VEC+VEC-1: N codes each from lanes 2c, 2c+1
+    // (K) and 32+2c, 33+2c (V)
+    const int c = lane & 15;
+    const uint32_t k0 = __shfl((int)codes, 2 * c, 64), k1 = __shfl((int)codes, 2 * c + 1, 64);
+    const uint32_t v0 = __shfl((int)codes, 32 + 2 * c, 64), v1 = __shfl((int)codes, 33 + 2 * c, 64);
+    if constexpr (N == 4) {
+      nk.v = u32x2{k0, k1};
+      nv.v = u32x2{v0, v1};
+    } else {
+      nk.v = (k0 & 0xFFFFu) | (k1 << 16);
+      nv.v = (v0 & 0xFFFFu) | (v1 << 16);
+    }
+  }
 }
 
 // Blocks of sequence s the decode attends: ceil(seq_len / 16), or 0 when s
@@ -243,11 +352,16 @@ __device__ __forceinline__ void note_piece(const DecodeParams& p, int split, int
 // loaded.  P therefore never leaves its lane, and the V^T operand of MFMA j (d = VEC*m + j)
 // is two byte permutes of the lane's own V words.  Tokens outside [key_lo, tok1) are
 // masked by selection; V rows at or past tok1 are zeroed (never multiplied: NaN-safe).
-template <int D, bool FP8>
+// SUB: row sub_i of this lane's four (-1: none) takes the slices nk / nv in place of what was
+// loaded, each at the point its row is consumed (the loads are waited for row by row as usual).
+template <int D, bool FP8, bool SUB = false>
 __device__ __forceinline__ void block_step(const DecodeParams& p, const BlockRegs<D, FP8>& r, unsigned char* kl,
                                            int blk_tok, int tok1, int key_lo,
                                            const bf16x8 (&qf)[DecodeShape<D, FP8>::kKSteps], float& m, float& l,
-                                           f32x4 (&acc)[DecodeShape<D, FP8>::kVec]) {
+                                           f32x4 (&acc)[DecodeShape<D, FP8>::kVec],
+                                           const RawVec<DecodeShape<D, FP8>::kLoadBytes>* nk = nullptr,
+                                           const RawVec<DecodeShape<D, FP8>::kLoadBytes>* nv = nullptr,
+                                           int sub_i = -1) {
   using Sh = DecodeShape<D, FP8>;
   constexpr int VEC = Sh::kVec, W = Sh::kWords;
   const int lane = threadIdx.x & 63;
@@ -258,7 +372,9 @@ __device__ __forceinline__ void block_step(const DecodeParams& p, const BlockReg
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t w[W];
-    raw_to_words<D, FP8>(r.k[i], w);
+    RawVec<Sh::kLoadBytes> kr = r.k[i];
+    if constexpr (SUB) select_raw(kr, *nk, i == sub_i);
+    raw_to_words<D, FP8>(kr, w);
     const int t = a + 4 * i;
     const int byte = c * VEC * 2;
     unsigned char* dst = kl + t * Sh::kRowBytes + (((byte >> 4) ^ (t % Sh::kChunks)) << 4) + (byte & 15);
@@ -271,7 +387,9 @@ __device__ __forceinline__ void block_step(const DecodeParams& p, const BlockReg
   uint32_t vw[4][W];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    raw_to_words<D, FP8>(r.v[i], vw[i]);
+    RawVec<Sh::kLoadBytes> vr = r.v[i];
+    if constexpr (SUB) select_raw(vr, *nv, i == sub_i);
+    raw_to_words<D, FP8>(vr, vw[i]);
     if (partial && blk_tok + a + 4 * i >= tok1) {
 #pragma unroll
       for (int x = 0; x < W; ++x) vw[i][x] = 0u;
@@ -405,9 +523,17 @@ __device__ __forceinline__ u32x4 q_words(const DecodeParams& p, size_t qoff, int
 // once; s is the group's first sequence, split the prefix share, [b0, b1) blocks of
 // the prefix (whole blocks, every key visible).  Otherwise the piece covers blocks
 // [b0, b1) of sequence s after its skip_blocks shared blocks.
-template <int D, bool FP8, bool GROUP = false>
+//
+// WRITE (the decode that also writes the step's K/V): position seq_lens[s] - 1 holds the new
+// row of s (row s of new_k / new_v).  The piece whose blocks hold it takes the row's slices
+// in place of what the loads of that block return (the pool may still hold an older row
+// there), and the waves of the first q-head group store them to the pool, at the slot the KV
+// write uses.  Nobody else in the launch reads those bytes: the waves of the other q-head
+// groups substitute the row as well, and other kv heads read other bytes of the token.
+template <int D, bool FP8, bool GROUP = false, bool WRITE = false>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned char* k_lds, int split, int kvh, int s,
                                              int b0, int b1, int nb, int hg = 0) {
+  static_assert(!(GROUP && WRITE), "the cascade prefix holds no new rows");
   using Sh = DecodeShape<D, FP8>;
   constexpr int VEC = Sh::kVec;
   const int row = p.qsl ? p.qsl[s] : s;
@@ -460,6 +586,27 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
       (const int PA_CONST_AS*)(uintptr_t)(p.block_tables + (size_t)s * p.bt_stride + skip + b0);
   int phys_next = bt[0];
 
+  // WRITE: block sub_blk of the piece (-1: none) holds the new row, at row sub_t of the block;
+  // lanes of row group sub_t % 4 hold its slices
+  // WRITE: block sub_blk of the piece (-1: none) holds the new row, at row sub_t of the block;
+  // lanes of row group sub_t % 4 hold its slices.  The new row is the sequence's last position,
+  // so sub_blk is the piece's last block when the piece holds it.
+  int sub_blk = -1, sub_t = 0;
+  NewRowSrc<D> ksrc{}, vsrc{};
+  RawVec<Sh::kLoadBytes> nk{}, nv{};
+  if constexpr (WRITE) {
+    const int Lt = p.seq_lens[s];  // a sequence cut to max_seq_len has its new row outside the attended keys
+    const int rel = ((Lt - 1) >> 4) - skip - b0;
+    if (Lt >= 1 && Lt <= p.max_seq_len && rel == nblk - 1) {
+      sub_blk = rel;
+      sub_t = (Lt - 1) & 15;
+    }
+    sub_blk = wave_uniform(sub_blk);
+    sub_t = wave_uniform(sub_t);
+    // only loaded here: converted after the first blocks' loads are issued, so the wave does not
+    // wait for this row before it starts streaming
+    if (sub_blk >= 0 && (FP8 || a == (sub_t & 3))) load_new_row<D, FP8>(p, ksrc, vsrc, row, kvh, lane);
+  }
   // Loads of block b of the partition.  Indices past the end re-read the last
   // block (cache-resident, no HBM traffic) so that the loop is branch-free and
   // the order of outstanding loads never depends on the data.
@@ -490,16 +637,26 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
   // (no effect on m, l or the output).  Measured on the Llama-3-8B layer at one wave per
   // SIMD: 2 sets 89 us, 3 sets 92, 4 sets 94 (1 set 88 with more waves): the memory
   // system, not the wave's latency, is the limit.
+  //
+  // WRITE: the loop streams the blocks before the new row's block, which it sees fully masked
+  // (its loads are the past-the-end re-reads); that block is attended after the loop, from a set
+  // holding it, with the new row in place.  The hot loop stays the plain one, and the real
+  // blocks are folded in the same order as without the write.
   constexpr int kSets = kInFlight<FP8>;
+  const int nloop = sub_blk >= 0 ? sub_blk : nblk;
+  const int tok1_loop = sub_blk >= 0 ? tok0 + sub_blk * 16 : tok1;
   BlockRegs<D, FP8> rs[kSets];
   static_for<0, kSets>([&](auto i_c) {
     issue(rs[decltype(i_c)::value], decltype(i_c)::value);
     __builtin_amdgcn_sched_barrier(0);
   });
-  for (int b = 0; b < nblk; b += kSets) {
+  if constexpr (WRITE) {
+    if (sub_blk >= 0) new_row_raw<D, FP8>(p, ksrc, vsrc, nk, nv, lane);
+  }
+  for (int b = 0; b < nloop; b += kSets) {
     static_for<0, kSets>([&](auto i_c) {
       constexpr int i = decltype(i_c)::value;
-      block_step<D, FP8>(p, rs[i], k_lds, tok0 + (b + i) * 16, tok1, key_lo, qf, m, l, acc);
+      block_step<D, FP8>(p, rs[i], k_lds, tok0 + (b + i) * 16, tok1_loop, key_lo, qf, m, l, acc);
       // bf16: a refill waits until the other sets have landed, so a wave streams about one
       // block ahead rather than kSets (the Llama-3-8B layer, 1024 waves: 87.7-87.9 us against
       // 88.8-89.7 with both 8 KB sets always in flight -- the memory system is already full);
@@ -508,6 +665,23 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, unsigned cha
       // this block's registers are consumed: refill them with a later block
       issue(rs[i], b + i + kSets);
     });
+  }
+
+  // WRITE: the new row's block (every set holds it: the loop's last issues were past its end), then
+  // the waves of the first q-head group store the row, at the slot the KV write uses
+  if constexpr (WRITE) {
+    if (sub_blk >= 0)
+      block_step<D, FP8, true>(p, rs[0], k_lds, tok0 + sub_blk * 16, tok1, key_lo, qf, m, l, acc, &nk, &nv,
+                               a == (sub_t & 3) ? sub_t >> 2 : -1);
+    if (sub_blk >= 0 && hg == 0) {
+      const int phys = bt[sub_blk];
+      if (a == (sub_t & 3) && phys >= 0 && phys < p.num_blocks) {
+        const size_t off = (size_t)phys * block_bytes + (size_t)sub_t * row_stride + (size_t)kvh * D * kElem +
+                           (size_t)c * Sh::kLoadBytes;
+        store_raw(const_cast<uint8_t*>(kbase) + off, nk);
+        store_raw(const_cast<uint8_t*>(vbase) + off, nv);
+      }
+    }
   }
 
   // the four row groups hold partial sums over different tokens of the same head
@@ -534,14 +708,17 @@ __device__ __forceinline__ bool prefix_piece(const DecodeParams& p, unsigned cha
 // One decode wave: share x (the first prefix_waves ids take the cascade's shared prefix)
 // of kv head y / head_groups, q-head group y % head_groups.  k_lds: this wave's 16 rows of
 // K (DecodeShape::kLdsBytes).
-template <int D, bool FP8>
+// WRITE: the waves also store the step's new K/V rows (no cascade).
+template <int D, bool FP8, bool WRITE = false>
 __device__ __forceinline__ void decode_wave(const DecodeParams& p, unsigned char* k_lds, int x, int y) {
   const int kvh = y / p.head_groups, hg = y % p.head_groups;
-  if (prefix_piece<D, FP8>(p, k_lds, x, kvh)) return;
+  if constexpr (!WRITE) {
+    if (prefix_piece<D, FP8>(p, k_lds, x, kvh)) return;
+  }
   const int split = x - p.prefix_waves;
   for_each_piece(p, split, [&](int s, int b0, int b1, int nb) {
     if (y == 0 && (threadIdx.x & 63) == 0) note_piece(p, split, s, b0, b1, nb);
-    decode_piece<D, FP8>(p, k_lds, split, kvh, s, b0, b1, nb, hg);
+    decode_piece<D, FP8, false, WRITE>(p, k_lds, split, kvh, s, b0, b1, nb, hg);
   });
 }
 

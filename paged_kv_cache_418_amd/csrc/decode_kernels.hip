@@ -38,11 +38,12 @@ namespace pa {
 
 namespace {
 
-template <int D, bool FP8>
+// WRITE: the decode that also stores the step's new K/V rows (p.new_k / p.new_v)
+template <int D, bool FP8, bool WRITE>
 __global__ void __launch_bounds__(64) decode_mfma_kernel(DecodeParams p) {
   __shared__ __align__(16) unsigned char k_lds[DecodeShape<D, FP8>::kLdsBytes];
   // grid y: (kv head, group of 16 of its q heads); a cascade has one group per kv head
-  decode_wave<D, FP8>(p, k_lds, blockIdx.x, blockIdx.y);
+  decode_wave<D, FP8, WRITE>(p, k_lds, blockIdx.x, blockIdx.y);
 }
 
 // fp32 pools and queries: vector-ALU kernel, one wave per (share, q head).
@@ -208,12 +209,16 @@ hipError_t launch_decode_d(const DecodeParams& p, int kv, hipStream_t stream) {
   timing_mark(kKDecode, true, stream);
   if (kv == kF32) {
     hipLaunchKernelGGL(decode_f32_kernel<D>, dim3(p.n_splits, p.num_q_heads), dim3(64), 0, stream, p);
-  } else if (kv == kFP8) {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, true>), dim3(p.prefix_waves + p.n_splits, p.num_kv_heads * p.head_groups),
-                       dim3(64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, false>),
-                       dim3(p.prefix_waves + p.n_splits, p.num_kv_heads * p.head_groups), dim3(64), 0, stream, p);
+    const dim3 grid(p.prefix_waves + p.n_splits, p.num_kv_heads * p.head_groups);
+    if (kv == kFP8 && p.new_k)
+      hipLaunchKernelGGL((decode_mfma_kernel<D, true, true>), grid, dim3(64), 0, stream, p);
+    else if (kv == kFP8)
+      hipLaunchKernelGGL((decode_mfma_kernel<D, true, false>), grid, dim3(64), 0, stream, p);
+    else if (p.new_k)
+      hipLaunchKernelGGL((decode_mfma_kernel<D, false, true>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<D, false, false>), grid, dim3(64), 0, stream, p);
   }
   timing_mark(kKDecode, false, stream);
   hipError_t e = hipGetLastError();

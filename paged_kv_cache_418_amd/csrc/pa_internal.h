@@ -68,6 +68,15 @@ struct DecodeParams {
   float scale_log2;          // softmax scale * log2(e) (* k_scale for fp8 pools)
   float v_scale;             // 1, or the fp8 value scale
   int q_f32;                 // query / output are fp32 (else bf16)
+  // decode that also writes the step's K/V (the kernels' write_new variant, else unused): row s of
+  // new_k / new_v is the K/V of position seq_lens[s] - 1 of sequence s, all kv heads
+  const void* new_k;
+  const void* new_v;
+  int64_t new_k_stride;      // elements between the rows of new_k
+  int64_t new_v_stride;
+  int new_f32;               // the rows are fp32 (else bf16; bf16 pools take bf16 rows)
+  float new_k_scale;         // fp8 pools: the stored codes are those of x / scale
+  float new_v_scale;
 };
 
 // One prefill launch: grid (num_kv_heads, n_items).  Item bits: sequence (15),
@@ -176,14 +185,16 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, int6
 
 // Slot mapping and KV write in one launch.  kind: kF32 / kBF16 (plain copy, strides in
 // elements of that type), kFP8 (E4M3 pools from a bf16 source) or kFP8 + 1 (from fp32);
-// slots_out optional.  Work-groups: num_seqs x ceil(max_q_len / 4).
+// slots_out optional; qsl NULL: one new row per sequence, row s of key/value (a decode step).
+// Work-groups: num_seqs x ceil(max_q_len / 4).
 hipError_t launch_write_kv(const void* key, const void* value, int64_t key_stride, int64_t value_stride,
                            void* key_cache, void* value_cache, int32_t* slots_out, const int32_t* block_tables,
                            int bt_stride, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, int num_tokens,
                            int max_q_len, int num_kv_heads, int head_dim, int block_size, int num_blocks, int kind,
                            float k_scale, float v_scale, hipStream_t stream);
 
-// kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel)
+// kv: kF32 (VALU kernel), kBF16 or kFP8 (matrix-core kernel); p.new_k set (kBF16 / kFP8 only):
+// the matrix-core kernel also stores the step's new K/V rows and attends them from registers
 hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_t stream);
 // the log-sum-exp merge of a decode launch's split sequences alone (after a fused launch)
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t stream);

@@ -329,6 +329,12 @@ def decode_alg_bytes(w: Workload) -> int:
     return decode_kv_bytes(w) + qo + 4 * nblk + 4 * w.num_seqs
 
 
+def decode_write_alg_bytes(w: Workload) -> int:
+    """decode_alg_bytes plus the step's new K/V rows, read from the input and stored into the pools."""
+    row = w.num_tokens * w.num_kv_heads * w.head_dim
+    return decode_alg_bytes(w) + 2 * row * (w.q_elem_bytes + w.kv_elem_bytes)
+
+
 def unique_kv_bytes(w: Workload) -> int:
     """KV bytes of distinct cached positions (shared prefix blocks counted once)."""
     B = w.block_size

@@ -18,8 +18,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 50
-    assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes"} <= set(syms)
+    assert len(syms) == 52
+    assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes", "pa_decode_write",
+            "pa_decode_write_fp8"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -361,3 +362,27 @@ def test_fp8_window_and_local_argument_checks(lib):
         assert fn(*pre, b.PA_FP8_E4M3, 0.05, 0.04, 128, FAKE, 1 << 30, None) == 3      # q dtype
         assert fn(*pre, b.PA_BF16, float("nan"), 0.04, 128, FAKE, 1 << 30, None) == 2  # k_scale
         assert fn(*pre, b.PA_BF16, 0.05, 0.04, 0, FAKE, 1 << 30, None) == 2            # window / chunk
+
+
+def test_decode_write_argument_checks(lib):
+    """pa_decode_write / pa_decode_write_fp8 refuse what pa_decode refuses, a missing or too narrow new K/V row and
+    bad fp8 scales, before anything is launched; an empty batch is PA_OK without touching memory."""
+    D, Hkv = 128, 8
+
+    def call(fp8=False, key=FAKE, ks=Hkv * D, S=4, Hq=32, dtype=b.PA_BF16, k_scale=0.05, ws=FAKE, wsb=1 << 30):
+        args = [FAKE, FAKE, key, FAKE, ks, Hkv * D, FAKE, FAKE, FAKE, 256, FAKE, S, Hq, Hkv, D, 16, 100, 1000, 0.088,
+                dtype]
+        if fp8:
+            return lib.pa_decode_write_fp8(*args, k_scale, 0.04, 0, ws, wsb, None)
+        return lib.pa_decode_write(*args, 0, ws, wsb, None)
+
+    for fp8 in (False, True):
+        assert call(fp8, dtype=b.PA_FP8_E4M3) == 3
+        assert call(fp8, key=None) == 1
+        assert call(fp8, ks=Hkv * D - 1) == 2
+        assert call(fp8, ws=None) == 4
+        assert call(fp8, Hq=Hkv * 257) == 5
+        assert lib.pa_last_error().decode()
+        assert call(fp8, S=0, ws=None, wsb=0) == 0
+    assert call(True, k_scale=0.0) == 2
+    assert call(True, k_scale=float("nan")) == 2
