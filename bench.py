@@ -91,7 +91,7 @@ class Step:
         self.cascade = cascade
         self.window = window
         # a decode step as one call that also stores the new K/V (pa_decode_write*)
-        self.fused_write = fused_write and w.is_decode and not cascade and not window
+        self.fused_write = fused_write and w.is_decode and not window
         dev = "cuda"
         self.pools = [(w.k_cache.to(dev), w.v_cache.to(dev))]
         for _ in range(copies - 1):
@@ -158,9 +158,13 @@ class Step:
                                  out=self.out, workspace=self.ws)
 
     def write_and_attend(self, kc, vc):
-        """The decode step as one call: pa_decode_write stores the new K/V and attends."""
+        """The decode step as one call: pa_decode_write (pa_decode_cascade_write) stores the new K/V and attends."""
         w, pk = self.w, self.pk
-        if w.kv_dtype == "fp8":
+        if self.cascade:
+            pk.pa_decode_cascade_write_fp8(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, w.scale, w.k_scale,
+                                           w.v_scale, self.max_len, w.shared_prefix_blocks, out=self.out,
+                                           workspace=self.ws)
+        elif w.kv_dtype == "fp8":
             pk.pa_decode_write_fp8(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, w.scale, w.k_scale, w.v_scale,
                                    self.max_len, out=self.out, workspace=self.ws)
         else:
@@ -598,7 +602,8 @@ def bench_mixed(args, result):
 
 def bench_cascade(args, result):
     """C5: prefix-shared fp8 decode (128 requests, a 2048-token shared prefix, suffixes U[128,1024]): whole steps
-    with the plain decode and with the cascade decode; logical KV bytes (each request's whole context) and unique
+    with the plain decode and with the cascade decode, each one call that also stores the new K/V
+    (pa_decode_write_fp8, pa_decode_cascade_write_fp8; step_two_calls_ms: the KV write's launch, then the decode); logical KV bytes (each request's whole context) and unique
     bytes (the prefix once) per second, warm and with a 512 MB scratch write before every step (so no step finds
     the previous step's KV in the 256 MB MALL)."""
     from paged_kv_cache_418_amd import workloads as wl
@@ -614,13 +619,15 @@ def bench_cascade(args, result):
     flush = lambda: scratch.fill_(7)  # noqa: E731  (a plain fill kernel: 512 MB written)
     casc_out = None
     for name, cascade in (("plain", False), ("cascade", True)):
-        st = Step(w, cascade=cascade)
+        st = Step(w, cascade=cascade, fused_write=True)
         ms, _, per = time_steps(st, args.steps, args.warmup)
         kt = kernel_times(st, args.steps, ["decode", "decode_merge"])
+        _, _, per2 = time_steps(st.two_calls, args.steps, args.warmup)
         cms, _, cper = time_steps(st, args.steps, args.warmup, between=flush)
         ktc = kernel_times(st, args.steps, ["decode", "decode_merge"], between=flush)
         d = kmean(kt, "decode")
-        out[name] = {"ms_per_step": round(ms, 5), "step_ms": per, "logical_gbps": round(logical / (ms * 1e-3) / 1e9, 1),
+        out[name] = {"ms_per_step": round(ms, 5), "step_ms": per, "step_two_calls_ms": per2,
+                     "logical_gbps": round(logical / (ms * 1e-3) / 1e9, 1),
                      "unique_gbps": round(unique / (ms * 1e-3) / 1e9, 1),
                      "decode_kernel_ms": round(d, 5), "decode_kernel": kt["decode"],
                      "merge_kernel_ms": kmean(kt, "decode_merge"),

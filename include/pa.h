@@ -24,7 +24,8 @@
  *    physical block holding positions j*block_size .. j*block_size+block_size-1
  *    of sequence s.  Only the first ceil(seq_len/block_size) entries are read.
  *  - seq_lens[s]: tokens of sequence s INCLUDING the new tokens of this step
- *    (they must have been written into the pool first).
+ *    (they must have been written into the pool first; the *_write decode
+ *    entry points store them themselves).
  *  - query_start_loc: device int32 [num_seqs+1], prefix sums of the new-token
  *    counts; the new tokens of all sequences form one flattened array of
  *    num_tokens = query_start_loc[num_seqs] rows.  Sequence s has
@@ -344,7 +345,8 @@ pa_status_t pa_decode_write_fp8(void* out, const void* query, const void* key, c
  * (checked under PA_VALIDATE=1, trusted otherwise).  dtype: PA_BF16, or
  * PA_F32 (fp32 pools and queries: the plain fp32 decode over each whole
  * sequence, the same attention without the shared grouping).
- * workspace: pa_decode_cascade_workspace_bytes(...) bytes (always needed).
+ * workspace: pa_decode_cascade_workspace_bytes(...) bytes (needed for every
+ * non-empty batch; 0 when num_seqs is 0, and for invalid arguments).
  * num_splits: waves per kv head for the suffixes, as in pa_decode.  Other
  * arguments as pa_decode.
  */
@@ -368,6 +370,41 @@ pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const uint8_t* k
                                   int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
                                   pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t prefix_blocks,
                                   int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_cascade_write -- one decode step of a prefix-shared batch: the
+ * result, and every byte of both pools, are those of pa_write_kv (one new row
+ * per sequence) followed by pa_decode_cascade.  [A] §2-§3, [B] tutorial 3.
+ * key/value, strides, dtype and the conditions on the new rows as
+ * pa_decode_write; besides, every new row lies after the shared prefix
+ * (seq_lens[s] > prefix_blocks * block_size, checked under PA_VALIDATE=1): the
+ * shared blocks are never written.  When the prefix is attended as tiles and
+ * every kv-head slice is 16-byte aligned, the suffix waves of the tiles'
+ * launch store the rows and attend them from registers; otherwise the write
+ * runs as its own launch first.  Workspace: pa_decode_cascade_workspace_bytes.
+ * Other arguments and errors as pa_decode_cascade.
+ */
+pa_status_t pa_decode_cascade_write(void* out, const void* query, const void* key, const void* value,
+                                    int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache,
+                                    void* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t prefix_blocks,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_cascade_write_fp8 -- pa_decode_cascade_write over E4M3FN pools:
+ * the codes of pa_write_kv_fp8, the attention of pa_decode_cascade_fp8.
+ * dtype (PA_F32 or PA_BF16): query/out and key/value.  [B] tutorial 6.
+ */
+pa_status_t pa_decode_cascade_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                        int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                        uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype,
+                                        float k_scale, float v_scale, int32_t prefix_blocks, int32_t num_splits,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_prefill_varlen_workspace_bytes -- scratch pa_prefill_varlen needs for

@@ -79,6 +79,10 @@ def load() -> ctypes.CDLL:
                                  ctypes.c_int, i32, P, sz, P], ctypes.c_int),
             "pa_decode_write_fp8": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                      ctypes.c_int, f32, f32, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_cascade_write": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
+                                         f32, ctypes.c_int, i32, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_cascade_write_fp8": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
+                                             i32, f32, ctypes.c_int, f32, f32, i32, i32, P, sz, P], ctypes.c_int),
             "pa_decode_cascade_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
             "pa_decode_cascade": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32, ctypes.c_int, i32,
                                    i32, P, sz, P], ctypes.c_int),
@@ -316,7 +320,7 @@ def pa_decode_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: 
 
 
 def _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens, max_seq_len, num_splits,
-                       out, workspace):
+                       out, workspace, prefix_blocks=None):
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D):
@@ -326,7 +330,9 @@ def _decode_write_args(query, key, value, key_cache, value_cache, block_tables, 
     if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
         raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
     out = torch.empty_like(query) if out is None else out
-    ws, wsb = _workspace(pa_decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, num_splits), query.device, workspace)
+    nbytes = (pa_decode_workspace_bytes(S, Hq, Hkv, D, max_seq_len, num_splits) if prefix_blocks is None else
+              pa_decode_cascade_workspace_bytes(S, Hq, Hkv, D, max_seq_len, prefix_blocks, num_splits))
+    ws, wsb = _workspace(nbytes, query.device, workspace)
     head = (_dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key, "key"), _dev(value, "value"),
             key.stride(0), value.stride(0), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
             _dev(block_tables, "block_tables"), block_tables.shape[1], _dev(seq_lens, "seq_lens"), S, Hq, Hkv, D, B,
@@ -355,6 +361,30 @@ def pa_decode_write_fp8(query, key, value, key_cache, value_cache, block_tables,
                                               max_seq_len, num_splits, out, workspace)
     _check("pa_decode_write_fp8", lib.pa_decode_write_fp8(*head, float(scale), _dtype_code(query), float(k_scale),
                                                           float(v_scale), num_splits, ws, wsb, _stream()))
+    return out
+
+
+def pa_decode_cascade_write(query, key, value, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                            max_seq_len: int, prefix_blocks: int, num_splits: int = 0, out=None, workspace=None):
+    """pa_decode_write for a batch whose tables begin with the same prefix_blocks blocks (pa_decode_cascade)."""
+    lib = load()
+    out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
+                                              max_seq_len, num_splits, out, workspace, prefix_blocks)
+    _check("pa_decode_cascade_write", lib.pa_decode_cascade_write(*head, float(scale), _dtype_code(key_cache),
+                                                                  prefix_blocks, num_splits, ws, wsb, _stream()))
+    return out
+
+
+def pa_decode_cascade_write_fp8(query, key, value, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                                k_scale: float, v_scale: float, max_seq_len: int, prefix_blocks: int,
+                                num_splits: int = 0, out=None, workspace=None):
+    """pa_decode_cascade_write over fp8 E4M3 pools (uint8 codes of x / scale)."""
+    lib = load()
+    out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
+                                              max_seq_len, num_splits, out, workspace, prefix_blocks)
+    _check("pa_decode_cascade_write_fp8",
+           lib.pa_decode_cascade_write_fp8(*head, float(scale), _dtype_code(query), float(k_scale), float(v_scale),
+                                           prefix_blocks, num_splits, ws, wsb, _stream()))
     return out
 
 

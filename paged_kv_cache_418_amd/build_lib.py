@@ -61,7 +61,9 @@ def build(verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    # only the pa_* entry points of include/pa.h are exported
+    cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", f"-Wl,--version-script={os.path.join(CSRC, 'libpa.map')}",
+           "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -764,9 +764,10 @@ namespace {
 // Arguments of a cascade call on top of the decode checks: a prefix of whole blocks
 // inside every sequence, a group of at most 16 q heads, and (PA_VALIDATE=1) tables
 // that really share it.
+// writes: the step's new rows are stored as well, so each must lie after the shared prefix.
 pa_status_t check_cascade(const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t block_size, int32_t max_seq_len,
-                          int32_t prefix_blocks) {
+                          int32_t prefix_blocks, bool writes = false) {
   if (prefix_blocks < 1) return fail(PA_ERR_SHAPE, "prefix_blocks %d < 1", prefix_blocks);
   if ((int64_t)prefix_blocks * block_size > max_seq_len)
     return fail(PA_ERR_SHAPE, "prefix of %d blocks longer than max_seq_len %d", prefix_blocks, max_seq_len);
@@ -779,6 +780,8 @@ pa_status_t check_cascade(const int32_t* block_tables, int32_t bt_stride, const 
   for (int s = 0; s < num_seqs; ++s) {
     if (sl[s] < prefix_blocks * block_size)
       return fail(PA_ERR_SHAPE, "PA_VALIDATE: seq_lens[%d] = %d shorter than the shared prefix", s, sl[s]);
+    if (writes && sl[s] <= prefix_blocks * block_size)
+      return fail(PA_ERR_SHAPE, "PA_VALIDATE: the new row of sequence %d would be stored inside the shared prefix", s);
     for (int j = 0; j < prefix_blocks; ++j)
       if (bt[(size_t)s * bt_stride + j] != bt[j])
         return fail(PA_ERR_SHAPE, "PA_VALIDATE: block_tables[%d][%d] differs from sequence 0's", s, j);
@@ -884,7 +887,7 @@ pa_status_t run_cascade_tiles(const CascadeTilePlan& cp, void* out, const void* 
                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind,
                               float k_scale, float v_scale, void* workspace, hipStream_t stream,
-                              int32_t prefix_blocks) {
+                              int32_t prefix_blocks, const NewRows* rows = nullptr) {
   auto* base = static_cast<unsigned char*>(workspace);
   // the suffix: the split decode's shares over each sequence's own blocks, every piece partial
   pa::FusedParams f{};
@@ -909,6 +912,15 @@ pa_status_t run_cascade_tiles(const CascadeTilePlan& cp, void* out, const void* 
   d.prefix_blocks = prefix_blocks;
   d.prefix_shares = 0;  // in the launch: no decode wave takes prefix pieces
   d.prefix_waves = 0;
+  if (rows) {  // the suffix waves store the new rows (each in its sequence's own blocks)
+    d.new_k = rows->key;
+    d.new_v = rows->value;
+    d.new_k_stride = rows->key_stride;
+    d.new_v_stride = rows->value_stride;
+    d.new_f32 = rows->src_f32;
+    d.new_k_scale = rows->k_scale;
+    d.new_v_scale = rows->v_scale;
+  }
   // the prefix tiles, over the pools themselves (fp8: converted in the kernel)
   pa::PrefillParams& pp = f.pre;
   pp.out = out;
@@ -960,6 +972,7 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
       (head_dim != 64 && head_dim != 128) || num_splits < 0 || prefix_blocks < 1 ||
       (int64_t)prefix_blocks * pa::kBlockSize > max_seq_len || num_q_heads / num_kv_heads > pa::kMaxGroup)
     return 0;
+  if (num_seqs == 0) return 0;  // an empty batch needs no scratch (as pa_decode_workspace_bytes)
   size_t need = cascade_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits).total;
   if (cascade_tiles_enabled())
     for (const int elem : {1, 2}) {  // the size query takes no dtype: room for either plan
@@ -972,6 +985,80 @@ size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
                                                   num_splits));
 }
 
+namespace {
+
+// The cascade decode (pa_decode_cascade*), and with rows the decode step that also stores the new
+// K/V (pa_decode_cascade_write*): the suffix waves of the tiles' launch store them when the pools
+// are bf16 or fp8 and every kv-head slice is 16-byte aligned; otherwise the KV write runs first as
+// its own launch.  kv_kind: the pools (kF32 pools take the plain fp32 decode over whole sequences).
+pa_status_t cascade_call(void* out, const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t max_seq_len, float scale, int kv_kind, int q_f32, float k_scale,
+                         float v_scale, int32_t prefix_blocks, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, const NewRows* rows) {
+  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                        prefix_blocks, num_splits);
+  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                                     num_splits, workspace, workspace_bytes, need);
+  if (st != PA_OK) return st;
+  if (kv_kind == pa::kFP8 &&
+      (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  st = check_cascade(block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, block_size, max_seq_len,
+                     prefix_blocks, rows != nullptr);
+  if (st != PA_OK) return st;
+  if (rows) {
+    if (num_seqs > 0 && (!rows->key || !rows->value)) return fail(PA_ERR_NULL, "key or value is NULL");
+    if (rows->key_stride < (int64_t)num_kv_heads * head_dim || rows->value_stride < (int64_t)num_kv_heads * head_dim)
+      return fail(PA_ERR_SHAPE, "token stride smaller than num_kv_heads * head_dim");
+    if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_SHAPE, "pool has more than 2^31 slots");
+  }
+  if (num_seqs == 0) return ok();
+  if (validate_enabled()) {
+    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
+    if (st != PA_OK) return st;
+  }
+  // the tiles read bf16 queries; fp32 queries take the decode waves' path
+  CascadeTilePlan cp;
+  if (kv_kind != pa::kF32 && !q_f32 && cascade_tiles_enabled())
+    cp = plan_cascade_tiles(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits,
+                            kv_kind == pa::kFP8 ? 1 : 2);
+  if (rows) {
+    const int64_t elem = rows->src_f32 ? 4 : 2;
+    const uintptr_t align = (uintptr_t)rows->key | (uintptr_t)rows->value | (uintptr_t)(rows->key_stride * elem) |
+                            (uintptr_t)(rows->value_stride * elem);
+    if (cp.ok && (align & 15u) == 0)
+      return run_cascade_tiles(cp, out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                               num_q_heads, num_kv_heads, head_dim, num_blocks, max_seq_len, scale, kv_kind, k_scale,
+                               v_scale, workspace, stream, prefix_blocks, rows);
+    const int write_kind = kv_kind == pa::kFP8 ? (rows->src_f32 ? pa::kFP8 + 1 : pa::kFP8) : kv_kind;
+    st = hip_status(pa::launch_write_kv(rows->key, rows->value, rows->key_stride, rows->value_stride,
+                                        const_cast<void*>(key_cache), const_cast<void*>(value_cache), nullptr,
+                                        block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_seqs, 1,
+                                        num_kv_heads, head_dim, block_size, num_blocks, write_kind, k_scale, v_scale,
+                                        stream),
+                    "write_kv launch");
+    if (st != PA_OK) return st;
+  }
+  // fp32 pools: the plain fp32 decode over each whole sequence (the same attention; only the
+  // grouping of keys, and so the order of fp32 sums, would differ)
+  if (kv_kind == pa::kF32)
+    return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                      pa::kF32, 1, 1.f, 1.f, num_splits, workspace, workspace_bytes, stream);
+  if (cp.ok)
+    return run_cascade_tiles(cp, out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, num_blocks, max_seq_len, scale, kv_kind, k_scale,
+                             v_scale, workspace, stream, prefix_blocks);
+  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, kv_kind,
+                    q_f32, k_scale, v_scale, num_splits, workspace, workspace_bytes, stream, prefix_blocks);
+}
+
+}  // namespace
+
 pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache, const void* value_cache,
                               const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -979,38 +1066,10 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
                               pa_dtype_t dtype, int32_t prefix_blocks, int32_t num_splits, void* workspace,
                               size_t workspace_bytes, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
-  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                                        prefix_blocks, num_splits);
-  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
-                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                                     num_splits, workspace, workspace_bytes, need);
-  if (st != PA_OK) return st;
-  st = check_cascade(block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, block_size, max_seq_len,
-                     prefix_blocks);
-  if (st != PA_OK) return st;
-  if (num_seqs == 0) return ok();
-  if (validate_enabled()) {
-    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
-    if (st != PA_OK) return st;
-  }
-  // fp32 pools: the plain fp32 decode over each whole sequence (the same attention; only the
-  // grouping of keys, and so the order of fp32 sums, would differ)
-  if (dtype == PA_F32)
-    return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
-                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                      pa::kF32, 1, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
-  if (cascade_tiles_enabled()) {
-    const CascadeTilePlan cp =
-        plan_cascade_tiles(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits, 2);
-    if (cp.ok)
-      return run_cascade_tiles(cp, out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
-                               num_q_heads, num_kv_heads, head_dim, num_blocks, max_seq_len, scale, pa::kBF16, 1.f,
-                               1.f, workspace, static_cast<hipStream_t>(stream), prefix_blocks);
-  }
-  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
-                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                    pa::kBF16, 0, 1.f, 1.f, num_splits, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
-                    prefix_blocks);
+  return cascade_call(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                      dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype == PA_F32, 1.f, 1.f, prefix_blocks, num_splits,
+                      workspace, workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
 }
 
 pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
@@ -1020,35 +1079,41 @@ pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const uint8_t* k
                                   pa_dtype_t q_dtype, float k_scale, float v_scale, int32_t prefix_blocks,
                                   int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q_dtype must be PA_F32 or PA_BF16");
-  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                                        prefix_blocks, num_splits);
-  pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
-                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                                     num_splits, workspace, workspace_bytes, need);
-  if (st != PA_OK) return st;
-  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
-    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
-  st = check_cascade(block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, block_size, max_seq_len,
-                     prefix_blocks);
-  if (st != PA_OK) return st;
-  if (num_seqs == 0) return ok();
-  if (validate_enabled()) {
-    st = validate_tables(block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_blocks, max_seq_len, block_size);
-    if (st != PA_OK) return st;
-  }
-  // the tiles read bf16 queries; fp32 queries take the decode waves' path
-  if (q_dtype == PA_BF16 && cascade_tiles_enabled()) {
-    const CascadeTilePlan cp =
-        plan_cascade_tiles(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, prefix_blocks, num_splits, 1);
-    if (cp.ok)
-      return run_cascade_tiles(cp, out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
-                               num_q_heads, num_kv_heads, head_dim, num_blocks, max_seq_len, scale, pa::kFP8, k_scale,
-                               v_scale, workspace, static_cast<hipStream_t>(stream), prefix_blocks);
-  }
-  return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
-                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                    pa::kFP8, q_dtype == PA_F32, k_scale, v_scale, num_splits, workspace, workspace_bytes,
-                    static_cast<hipStream_t>(stream), prefix_blocks);
+  return cascade_call(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, pa::kFP8,
+                      q_dtype == PA_F32, k_scale, v_scale, prefix_blocks, num_splits, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream), nullptr);
+}
+
+pa_status_t pa_decode_cascade_write(void* out, const void* query, const void* key, const void* value,
+                                    int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache,
+                                    void* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t prefix_blocks,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  const NewRows rows{key, value, key_tok_stride, value_tok_stride, dtype == PA_F32, 1.f, 1.f};
+  return cascade_call(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
+                      dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype == PA_F32, 1.f, 1.f, prefix_blocks, num_splits,
+                      workspace, workspace_bytes, static_cast<hipStream_t>(stream), &rows);
+}
+
+pa_status_t pa_decode_cascade_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                        int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                        uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, int32_t max_seq_len, float scale, pa_dtype_t dtype,
+                                        float k_scale, float v_scale, int32_t prefix_blocks, int32_t num_splits,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  const NewRows rows{key, value, key_tok_stride, value_tok_stride, dtype == PA_F32, k_scale, v_scale};
+  return cascade_call(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, pa::kFP8, dtype == PA_F32,
+                      k_scale, v_scale, prefix_blocks, num_splits, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream), &rows);
 }
 
 namespace {

@@ -21,7 +21,9 @@ namespace pa {
 
 namespace {
 
-template <int D, bool WINDOW, bool FP8, bool PREFIX>
+// WRITE (cascade only): the decode waves also store the step's new K/V rows (f.dec.new_k / new_v),
+// which lie in each sequence's own blocks, never in the shared prefix the tiles read
+template <int D, bool WINDOW, bool FP8, bool PREFIX, bool WRITE = false>
 __global__ void __launch_bounds__(512) fused_kernel(FusedParams f) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wg = blockIdx.x;
@@ -30,7 +32,7 @@ __global__ void __launch_bounds__(512) fused_kernel(FusedParams f) {
     const int g = wg * f.decode_waves_per_wg + wave;  // decode wave: share g / Y of column g % Y
     if (wave >= f.decode_waves_per_wg || g >= f.decode_waves) return;
     const int Y = f.dec.num_kv_heads * f.dec.head_groups;
-    decode_wave<D, FP8>(f.dec, smem + wave * DecodeShape<D, FP8>::kLdsBytes, g / Y, g % Y);
+    decode_wave<D, FP8, WRITE>(f.dec, smem + wave * DecodeShape<D, FP8>::kLdsBytes, g / Y, g % Y);
     return;
   }
   // prefill items in the order of the prefill kernel's grid (kv heads fastest)
@@ -56,7 +58,9 @@ hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_
   auto pick = [&](auto d_c, auto fp8_c) {
     constexpr int D = decltype(d_c)::value;
     constexpr bool F = decltype(fp8_c)::value;
-    if (prefix)
+    if (prefix && f.dec.new_k)
+      launch(&fused_kernel<D, false, F, true, true>);
+    else if (prefix)
       launch(&fused_kernel<D, false, F, true>);
     else if (win)
       launch(&fused_kernel<D, true, F, false>);

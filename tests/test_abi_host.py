@@ -18,9 +18,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 52
+    assert len(syms) == 54
     assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes", "pa_decode_write",
-            "pa_decode_write_fp8"} <= set(syms)
+            "pa_decode_write_fp8", "pa_decode_cascade_write", "pa_decode_cascade_write_fp8"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -386,3 +386,29 @@ def test_decode_write_argument_checks(lib):
         assert call(fp8, S=0, ws=None, wsb=0) == 0
     assert call(True, k_scale=0.0) == 2
     assert call(True, k_scale=float("nan")) == 2
+
+
+def test_cascade_write_argument_checks(lib):
+    """pa_decode_cascade_write / _fp8 refuse what pa_decode_cascade refuses and a missing or too narrow new K/V row,
+    before anything is launched; an empty batch is PA_OK without touching memory."""
+    D, Hkv = 128, 8
+
+    def call(fp8=False, key=FAKE, ks=Hkv * D, S=4, Hq=32, dtype=b.PA_BF16, prefix=8, k_scale=0.05, ws=FAKE,
+             wsb=1 << 30):
+        args = [FAKE, FAKE, key, FAKE, ks, Hkv * D, FAKE, FAKE, FAKE, 256, FAKE, S, Hq, Hkv, D, 16, 100, 1000, 0.088,
+                dtype]
+        if fp8:
+            return lib.pa_decode_cascade_write_fp8(*args, k_scale, 0.04, prefix, 0, ws, wsb, None)
+        return lib.pa_decode_cascade_write(*args, prefix, 0, ws, wsb, None)
+
+    for fp8 in (False, True):
+        assert call(fp8, dtype=b.PA_FP8_E4M3) == 3
+        assert call(fp8, key=None) == 1
+        assert call(fp8, ks=Hkv * D - 1) == 2
+        assert call(fp8, prefix=0) == 2
+        assert call(fp8, prefix=63) == 2  # 63 blocks = 1008 positions > max_seq_len 1000
+        assert call(fp8, Hq=Hkv * 17) == 5
+        assert call(fp8, ws=None) == 4
+        assert lib.pa_last_error().decode()
+        assert call(fp8, S=0, ws=None, wsb=0) == 0
+    assert call(True, k_scale=-1.0) == 2

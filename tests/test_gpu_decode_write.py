@@ -21,8 +21,9 @@ pytestmark = pytest.mark.gpu
 class Step:
     """Device copies of a decode workload; run(fused) returns (out, key pool, value pool)."""
 
-    def __init__(self, w, key=None, value=None, seq_lens=None, max_len=None):
+    def __init__(self, w, key=None, value=None, seq_lens=None, max_len=None, prefix=0):
         self.w = w
+        self.prefix = prefix  # > 0: the cascade entry points over this many shared blocks
         self.kc = w.k_cache.cuda()
         self.vc = w.v_cache.cuda()
         self.bt = torch.from_numpy(w.block_tables).cuda()
@@ -38,6 +39,8 @@ class Step:
         kc, vc = self.kc.clone(), self.vc.clone()
         out = torch.zeros_like(self.q)  # rows of empty sequences are left as they are
         fp8 = w.kv_dtype == "fp8"
+        if self.prefix:
+            return self._run_cascade(fused, num_splits, kc, vc, out)
         if fused:
             if fp8:
                 pk.pa_decode_write_fp8(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, w.scale, w.k_scale,
@@ -53,6 +56,27 @@ class Step:
                                  num_splits, out=out)
             else:
                 pk.pa_decode(self.q, kc, vc, self.bt, self.sl, w.scale, self.max_len, num_splits, out=out)
+        torch.cuda.synchronize()
+        return out, kc, vc
+
+    def _run_cascade(self, fused, num_splits, kc, vc, out):
+        w, P = self.w, self.prefix
+        fp8 = w.kv_dtype == "fp8"
+        if fused:
+            if fp8:
+                pk.pa_decode_cascade_write_fp8(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, w.scale, w.k_scale,
+                                               w.v_scale, self.max_len, P, num_splits, out=out)
+            else:
+                pk.pa_decode_cascade_write(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, w.scale, self.max_len,
+                                           P, num_splits, out=out)
+        else:
+            scales = dict(k_scale=w.k_scale, v_scale=w.v_scale) if fp8 else {}
+            pk.pa_write_kv(self.nk, self.nv, kc, vc, self.bt, self.sl, self.qsl, 1, **scales)
+            if fp8:
+                pk.pa_decode_cascade_fp8(self.q, kc, vc, self.bt, self.sl, w.scale, w.k_scale, w.v_scale,
+                                         self.max_len, P, num_splits, out=out)
+            else:
+                pk.pa_decode_cascade(self.q, kc, vc, self.bt, self.sl, w.scale, self.max_len, P, num_splits, out=out)
         torch.cuda.synchronize()
         return out, kc, vc
 
@@ -178,3 +202,28 @@ def test_decode_write_repeats_bit_identical():
     step.kc, step.vc = first[1], first[2]
     second = step.run(True)
     assert _same(first, second)
+
+
+# ---- the cascade decode step (pa_decode_cascade_write*): the same contract over a batch whose tables begin with
+# the same physical blocks; the suffix waves of the prefix tiles' launch store the rows (bf16 queries over bf16 or
+# fp8 pools), the other paths run the write first
+
+@pytest.mark.parametrize("kinds", [("bf16", "bf16"), ("bf16", "fp8"), ("f32", "fp8"), ("f32", "f32")])
+@pytest.mark.parametrize("heads", [(32, 8, 128), (4, 2, 64), (16, 1, 128)])
+@pytest.mark.parametrize("num_splits", [0, 7])
+def test_cascade_write_equals_write_then_cascade(kinds, heads, num_splits):
+    """Shared prefixes of 3 blocks, suffixes 1..300 tokens (new rows at every block offset)."""
+    Hq, Hkv, D = heads
+    seed = 980 + Hq + 3 * Hkv + D + num_splits + len(kinds[0]) + 7 * len(kinds[1])
+    w = wl.random_case(seed, num_seqs=9, ctx_range=(49, 348), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                       q_dtype=kinds[0], kv_dtype=kinds[1], k_scale=0.05, v_scale=0.04, shared_prefix_tokens=48)
+    say("cascade_write", kinds, heads, num_splits, "seq_lens", w.seq_lens.tolist())
+    _check(w, Step(w, prefix=3), num_splits)
+
+
+def test_cascade_write_prefix_shared_fp8_full():
+    """The bench's prefix-shared batch at full size (128 requests, a 2048-token shared prefix, suffixes
+    U[128,1024], E4M3 pools): bit-identical to the two calls; oracle at the parity tolerance."""
+    w = wl.prefix_shared_fp8_decode()
+    say("cascade_write full", w.name)
+    _check(w, Step(w, prefix=w.shared_prefix_blocks))
