@@ -90,8 +90,9 @@ class Step:
         self.w = w
         self.cascade = cascade
         self.window = window
-        # a decode step as one call that also stores the new K/V (pa_decode_write*)
-        self.fused_write = fused_write and w.is_decode and not window
+        # a step as one call that also stores the new K/V (pa_decode_write*, pa_decode_cascade_write_fp8,
+        # pa_prefill_varlen_write over bf16 pools)
+        self.fused_write = fused_write and not window and (w.is_decode or cascade or w.kv_dtype != "fp8")
         dev = "cuda"
         self.pools = [(w.k_cache.to(dev), w.v_cache.to(dev))]
         for _ in range(copies - 1):
@@ -158,12 +159,16 @@ class Step:
                                  out=self.out, workspace=self.ws)
 
     def write_and_attend(self, kc, vc):
-        """The decode step as one call: pa_decode_write (pa_decode_cascade_write) stores the new K/V and attends."""
+        """The step as one call that stores the new K/V and attends (pa_decode_write, pa_decode_cascade_write_fp8,
+        pa_prefill_varlen_write)."""
         w, pk = self.w, self.pk
         if self.cascade:
             pk.pa_decode_cascade_write_fp8(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, w.scale, w.k_scale,
                                            w.v_scale, self.max_len, w.shared_prefix_blocks, out=self.out,
                                            workspace=self.ws)
+        elif not w.is_decode:
+            pk.pa_prefill_varlen_write(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, self.qsl, w.seq_lens,
+                                       w.query_start_loc, w.scale, out=self.out, workspace=self.ws)
         elif w.kv_dtype == "fp8":
             pk.pa_decode_write_fp8(self.q, self.nk, self.nv, kc, vc, self.bt, self.sl, w.scale, w.k_scale, w.v_scale,
                                    self.max_len, out=self.out, workspace=self.ws)
@@ -498,10 +503,12 @@ def bench_mixed(args, result):
     from paged_kv_cache_418_amd import workloads as wl
     _log("generating mixed_step_bf16 ...")
     w = wl.mixed_step_bf16()
-    st = Step(w)
+    st = Step(w, fused_write=True)
     ms, _, per = time_steps(st, args.steps, args.warmup)
     kt_step = kernel_times(st, args.steps, ["reshape_and_cache", "decode", "decode_merge", "prefill",
                                             "prefill_merge", "fused"])
+    # the same step as two calls (the KV write's own launch, then pa_prefill_varlen), for reference
+    _, _, per_two = time_steps(st.two_calls, args.steps, args.warmup)
     flops = wl.prefill_flops(w)
     rec, par = (None, None)
     if not args.no_cpu:
@@ -546,7 +553,7 @@ def bench_mixed(args, result):
     clock_long = float(counters["clock_ghz_long"]) if counters["valid"] and "clock_ghz_long" in counters else None
     chunk_fetch = float(counters["fetch_bytes_chunks"]) if counters["valid"] and "fetch_bytes_chunks" in counters \
         else None
-    mixed = {"workload": "mixed_step_bf16", "ms_per_step": round(ms, 5), "step_ms": per,
+    mixed = {"workload": "mixed_step_bf16", "ms_per_step": round(ms, 5), "step_ms": per, "step_two_calls_ms": per_two,
              "step_kernels_ms": {k: (v["mean"] if v else None) for k, v in kt_step.items()},
              "prefill_gflop": round(flops / 1e9, 3),
              "prefill_kernel_ms": round(pre_ms, 5), "prefill_kernel": kt["prefill"],

@@ -442,6 +442,32 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
                               size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill_varlen_write -- one step of a flattened batch that also stores
+ * its new K/V: the result, and every byte of both pools, are those of
+ * pa_write_kv (max_q_len: the longest q_len) followed by pa_prefill_varlen.
+ * [A] §3 (the new tokens' K/V go into their slots, then attention reads the
+ * cache), [C] core point 2.  key/value: [num_tokens][num_kv_heads][head_dim]
+ * of dtype, row t the K/V of the batch's new row t, heads and head_dim
+ * contiguous, key_tok_stride / value_tok_stride elements between rows.  When
+ * the step runs as one fused launch of decode rows and chunks (bf16, every
+ * kv-head slice 16-byte aligned), that launch stores the rows: the decode
+ * waves as pa_decode_write does, and the chunks' tiles read their new keys
+ * from key/value while one work item per row tile stores them.  Otherwise
+ * the write runs as its own launch first.  Condition beyond
+ * pa_prefill_varlen's: a block that holds new rows of one sequence is read by
+ * no other sequence of the batch.  Workspace: pa_prefill_varlen_workspace_bytes.
+ * Other arguments and errors as pa_prefill_varlen.
+ */
+pa_status_t pa_prefill_varlen_write(void* out, const void* query, const void* key, const void* value,
+                                    int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache,
+                                    void* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* seq_lens, const int32_t* query_start_loc,
+                                    const int32_t* seq_lens_host, const int32_t* query_start_loc_host,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                    pa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_varlen_window -- pa_prefill_varlen with sliding-window
  * attention ([A] §5.1, [B] tutorial 1; the window's start is this library's
  * reading, as in pa_decode_window): the row at position p attends to

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     pa_decode_local, pa_decode_local_fp8, pa_decode_static, pa_decode_window, pa_decode_window_fp8, pa_decode_write,
     pa_decode_write_fp8,
     pa_decode_workspace_bytes, pa_prefill_varlen, pa_prefill_varlen_fp8, pa_prefill_varlen_fp8_workspace_bytes,
+    pa_prefill_varlen_write,
     pa_prefill_varlen_local, pa_prefill_varlen_local_fp8, pa_prefill_varlen_local_workspace_bytes,
     pa_prefill_varlen_window, pa_prefill_varlen_window_fp8, pa_prefill_varlen_window_workspace_bytes,
     pa_prefill_varlen_workspace_bytes, pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_write_kv,

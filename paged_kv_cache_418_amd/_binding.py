@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
             "pa_prefill_varlen_workspace_bytes": ([P, P, i32, i32, i32, i32], sz),
             "pa_prefill_varlen": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                    ctypes.c_int, P, sz, P], ctypes.c_int),
+            "pa_prefill_varlen_write": ([P, P, P, P, i64, i64, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                         i32, f32, ctypes.c_int, P, sz, P], ctypes.c_int),
             "pa_prefill_varlen_fp8_workspace_bytes": ([P, P, i32, i32, i32, i32, i32], sz),
             "pa_prefill_varlen_fp8": ([P, P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                        ctypes.c_int, f32, f32, P, sz, P], ctypes.c_int),
@@ -487,6 +489,33 @@ def pa_prefill_varlen(query, key_cache, value_cache, block_tables, seq_lens, que
         _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(),
         sh.numel(), T, Hq, Hkv, D, B, NB, float(scale), _dtype_code(query), None if ws is None else ws.data_ptr(),
         wsb, _stream()))
+    return out
+
+
+def pa_prefill_varlen_write(query, key, value, key_cache, value_cache, block_tables, seq_lens, query_start_loc,
+                            seq_lens_host, query_start_loc_host, scale: float, out=None, workspace=None):
+    """One step of a flattened batch that also stores its new K/V: key/value [T, Hkv, D] (row t: the K/V of the
+    batch's new row t), the bytes of pa_write_kv followed by pa_prefill_varlen."""
+    lib = load()
+    T, Hq, D = query.shape
+    NB, B, Hkv, _ = key_cache.shape
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise ValueError(f"key/value must be [{T}, {Hkv}, {D}] (one row per new token)")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise ValueError("key/value must have the query's dtype")
+    if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
+        raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
+    qh = _i32_host(query_start_loc_host)
+    sh = _i32_host(seq_lens_host)
+    out = torch.empty_like(query) if out is None else out
+    need = int(lib.pa_prefill_varlen_workspace_bytes(qh.data_ptr(), sh.data_ptr(), sh.numel(), Hq, Hkv, D))
+    ws, wsb = _workspace(need, query.device, workspace)
+    _check("pa_prefill_varlen_write", lib.pa_prefill_varlen_write(
+        _dev(out, "out"), _dev(_contig(query, "query"), "query"), _dev(key, "key"), _dev(value, "value"),
+        key.stride(0), value.stride(0), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables"), block_tables.shape[1], _dev(seq_lens, "seq_lens"),
+        _dev(query_start_loc, "query_start_loc"), sh.data_ptr(), qh.data_ptr(), sh.numel(), T, Hq, Hkv, D, B, NB,
+        float(scale), _dtype_code(query), None if ws is None else ws.data_ptr(), wsb, _stream()))
     return out
 
 

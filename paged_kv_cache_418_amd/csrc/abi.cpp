@@ -1354,7 +1354,7 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, float scale, pa_dtype_t dtype, int kv_kind, float k_scale, float v_scale,
                        void* workspace, size_t workspace_bytes, void* stream, int32_t sliding_window = 0,
-                       int32_t local_chunk = 0) {
+                       int32_t local_chunk = 0, const NewRows* fresh = nullptr) {
   if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_SHAPE, "negative num_seqs or num_tokens");
   if (num_seqs == 0) return num_tokens == 0 ? ok() : fail(PA_ERR_SHAPE, "num_tokens > 0 with no sequences");
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start_loc ||
@@ -1394,6 +1394,28 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int dec_kind = kv_kind == pa::kFP8 ? pa::kFP8 : (dtype == PA_F32 ? pa::kF32 : pa::kBF16);
+  if (fresh) {
+    // the step's new rows: stored by the fused launch itself (bf16 pools and rows, no window,
+    // 16-byte aligned kv-head slices), else by the KV write's launch first
+    const int64_t elem = fresh->src_f32 ? 4 : 2;
+    const uintptr_t align = (uintptr_t)fresh->key | (uintptr_t)fresh->value | (uintptr_t)(fresh->key_stride * elem) |
+                            (uintptr_t)(fresh->value_stride * elem);
+    const bool in_launch = sp.fused && !rows && kv_kind == pa::kBF16 && dtype == PA_BF16 && sliding_window <= 0 &&
+                           local_chunk <= 0 && (align & 15u) == 0;
+    if (!in_launch) {
+      int max_q = 0;
+      for (int s = 0; s < num_seqs; ++s) max_q = std::max(max_q, query_start_loc_host[s + 1] - query_start_loc_host[s]);
+      const int write_kind = kv_kind == pa::kFP8 ? (fresh->src_f32 ? pa::kFP8 + 1 : pa::kFP8) : dec_kind;
+      st = hip_status(pa::launch_write_kv(fresh->key, fresh->value, fresh->key_stride, fresh->value_stride,
+                                          const_cast<void*>(key_cache), const_cast<void*>(value_cache), nullptr,
+                                          block_tables, bt_stride, seq_lens, query_start_loc, num_seqs, num_tokens,
+                                          max_q, num_kv_heads, head_dim, block_size, num_blocks, write_kind,
+                                          k_scale, v_scale, hs),
+                      "write_kv launch");
+      if (st != PA_OK) return st;
+      fresh = nullptr;
+    }
+  }
   if (rows) {
     int max_len = 1;
     for (int s = 0; s < num_seqs; ++s) max_len = std::max(max_len, (int)seq_lens_host[s]);
@@ -1462,6 +1484,15 @@ pa_status_t run_varlen(void* out, const void* query, const void* key_cache, cons
                                std::min(sp.decode_splits, ws_splits), workspace, 0, sliding_window, local_chunk);
     f.dec.num_blocks = num_blocks;
     prefill_params(0, f.pre);
+    if (fresh) {  // the decode waves and the prefill items store the new rows themselves
+      f.dec.new_k = f.pre.new_k = fresh->key;
+      f.dec.new_v = f.pre.new_v = fresh->value;
+      f.dec.new_k_stride = f.pre.new_k_stride = fresh->key_stride;
+      f.dec.new_v_stride = f.pre.new_v_stride = fresh->value_stride;
+      f.dec.new_f32 = 0;
+      f.dec.new_k_scale = f.dec.new_v_scale = 1.f;
+      f.dec.store_chunk_rows = 1;  // the chunks' rows: stored by the merge launch below
+    }
     f.decode_waves_per_wg = fused_decode_waves();
     f.decode_waves = (f.dec.prefix_waves + f.dec.n_splits) * decode_columns(num_q_heads, num_kv_heads);
     f.n_decode_wgs = (f.decode_waves + fused_decode_waves() - 1) / fused_decode_waves();
@@ -1559,6 +1590,26 @@ pa_status_t pa_prefill_varlen(void* out, const void* query, const void* key_cach
   return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
                     seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                     block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_prefill_varlen_write(void* out, const void* query, const void* key, const void* value,
+                                    int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache,
+                                    void* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* seq_lens, const int32_t* query_start_loc,
+                                    const int32_t* seq_lens_host, const int32_t* query_start_loc_host,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                    pa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  if (num_tokens > 0 && (!key || !value)) return fail(PA_ERR_NULL, "key or value is NULL");
+  if (key_tok_stride < (int64_t)num_kv_heads * head_dim || value_tok_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "token stride smaller than num_kv_heads * head_dim");
+  if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_SHAPE, "pool has more than 2^31 slots");
+  const NewRows rows{key, value, key_tok_stride, value_tok_stride, dtype == PA_F32, 1.f, 1.f};
+  return run_varlen(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, query_start_loc,
+                    seq_lens_host, query_start_loc_host, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, num_blocks, scale, dtype, pa::kBF16, 1.f, 1.f, workspace, workspace_bytes, stream, 0,
+                    0, &rows);
 }
 
 pa_status_t pa_prefill_varlen_window(void* out, const void* query, const void* key_cache, const void* value_cache,

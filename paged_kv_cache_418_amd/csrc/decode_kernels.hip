@@ -142,9 +142,44 @@ __global__ void __launch_bounds__(64) decode_f32_kernel(DecodeParams p) {
 // them (running maximum, weight sum and output), so the loads of later pieces
 // do not wait for earlier ones.  Sequences held by a single share were
 // finished in place.
+// Store role of the merge launch (p.store_chunk_rows, a mixed step that also stores its new K/V):
+// work-group x (past the merge's num_seqs) stores new rows 8x .. 8x+7 of the flattened batch at
+// their slots, as the KV write does, for the rows of sequences with q_len > 1 (the decode waves
+// stored the others); kv heads y, y + gridDim.y, ...  Every reader of those rows in the launch
+// before took them from the input rows.  Lane (row j = tid / 32, tensor tid / 16 % 2, chunk tid % 16).
+template <int D>
+__device__ __forceinline__ void store_chunk_rows(const DecodeParams& p, int x) {
+  constexpr int kRowChunks = D * 2 / 16;
+  const int tid = threadIdx.x;
+  const int t = 8 * x + (tid >> 5), chunk = tid & 15;
+  const bool is_v = (tid >> 4) & 1;
+  if (t >= p.num_rows || chunk >= kRowChunks) return;
+  int lo = 0, hi = p.num_seqs - 1;  // the last sequence s with qsl[s] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo, q0 = p.qsl[s], q_len = p.qsl[s + 1] - q0;
+  if (q_len <= 1) return;
+  const int pos = p.seq_lens[s] - q_len + (t - q0);
+  const int phys = p.block_tables[(size_t)s * p.bt_stride + (pos >> 4)];
+  if (phys < 0 || phys >= p.num_blocks) return;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(is_v ? p.new_v : p.new_k) +
+                       (size_t)t * (is_v ? p.new_v_stride : p.new_k_stride) * 2 + chunk * 16;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(const_cast<void*>(is_v ? p.value_cache : p.key_cache)) +
+                 ((size_t)phys * 16 + (pos & 15)) * p.num_kv_heads * D * 2 + chunk * 16;
+  for (int kvh = blockIdx.y; kvh < p.num_kv_heads; kvh += gridDim.y)
+    *reinterpret_cast<u32x4*>(dst + (size_t)kvh * D * 2) = *reinterpret_cast<const u32x4*>(src + (size_t)kvh * D * 2);
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
   constexpr int PER_LANE = D / 64;
+  if ((int)blockIdx.x >= p.num_seqs) {
+    store_chunk_rows<D>(p, blockIdx.x - p.num_seqs);
+    return;
+  }
+  if (p.n_splits <= 1 && !p.force_partial) return;  // a launch for the stores alone
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + wave, s = blockIdx.x;  // sequences on x: no 65535 limit on the batch
   if (h >= p.num_q_heads) return;
@@ -199,7 +234,9 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
 template <int D>
 hipError_t launch_merge_d(const DecodeParams& p, hipStream_t stream) {
   timing_mark(kKDecodeMerge, true, stream);
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.num_seqs, (p.num_q_heads + 3) / 4), dim3(256), 0, stream, p);
+  const int store_wgs = p.store_chunk_rows ? (p.num_rows + 7) / 8 : 0;
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(p.num_seqs + store_wgs, (p.num_q_heads + 3) / 4), dim3(256), 0,
+                     stream, p);
   timing_mark(kKDecodeMerge, false, stream);
   return hipGetLastError();
 }
@@ -374,7 +411,7 @@ hipError_t launch_decode(const DecodeParams& p, int kv, int head_dim, hipStream_
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if ((p.n_splits <= 1 && !p.force_partial) || p.num_seqs == 0) return hipSuccess;
+  if (((p.n_splits <= 1 && !p.force_partial) && !p.store_chunk_rows) || p.num_seqs == 0) return hipSuccess;
   if (head_dim == 128) return launch_merge_d<128>(p, stream);
   return launch_merge_d<64>(p, stream);
 }

@@ -21,8 +21,11 @@ namespace pa {
 
 namespace {
 
-// WRITE (cascade only): the decode waves also store the step's new K/V rows (f.dec.new_k / new_v),
-// which lie in each sequence's own blocks, never in the shared prefix the tiles read
+// WRITE: the launch also stores the step's new K/V rows.  The decode waves store and attend their
+// rows as the decode that writes does (f.dec.new_k / new_v); with a cascade those lie in each
+// sequence's own blocks, never in the shared prefix the tiles read.  Without one (bf16 pools, no
+// window) the prefill items take their chunks' new keys from the input rows (prefill_body's FRESH
+// form) and the decode merge launch that follows stores them.
 template <int D, bool WINDOW, bool FP8, bool PREFIX, bool WRITE = false>
 __global__ void __launch_bounds__(512) fused_kernel(FusedParams f) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -37,7 +40,7 @@ __global__ void __launch_bounds__(512) fused_kernel(FusedParams f) {
   }
   // prefill items in the order of the prefill kernel's grid (kv heads fastest)
   const int w = wg - f.n_decode_wgs;
-  prefill_body<D, WINDOW, PREFIX, FP8>(f.pre, smem, w / f.pre.num_kv_heads, w % f.pre.num_kv_heads);
+  prefill_body<D, WINDOW, PREFIX, FP8, WRITE && !PREFIX>(f.pre, smem, w / f.pre.num_kv_heads, w % f.pre.num_kv_heads);
 }
 
 }  // namespace
@@ -62,6 +65,8 @@ hipError_t launch_fused(const FusedParams& f, int head_dim, bool fp8, hipStream_
       launch(&fused_kernel<D, false, F, true, true>);
     else if (prefix)
       launch(&fused_kernel<D, false, F, true>);
+    else if (!F && !win && f.dec.new_k)  // the caller checks: fresh rows only over bf16 pools, no window
+      launch(&fused_kernel<D, false, false, false, true>);
     else if (win)
       launch(&fused_kernel<D, true, F, false>);
     else

@@ -77,6 +77,7 @@ struct DecodeParams {
   int new_f32;               // the rows are fp32 (else bf16; bf16 pools take bf16 rows)
   float new_k_scale;         // fp8 pools: the stored codes are those of x / scale
   float new_v_scale;
+  int store_chunk_rows;      // the merge launch also stores the new rows of sequences with q_len > 1
 };
 
 // One prefill launch: grid (num_kv_heads, n_items).  Item bits: sequence (15),
@@ -117,6 +118,13 @@ struct PrefillParams {
   float* pre_o;              // [shares][prefix_rows][num_q_heads][D]
   float* pre_m;              // [shares][prefix_rows][num_q_heads] (log2 units)
   float* pre_l;              // [shares][prefix_rows][num_q_heads]
+  // fresh rows (the prefill body's FRESH form, a mixed step that also stores its new K/V, bf16
+  // pools): keys at or past a chunk's cached length come from row qsl[s] + (key - cached) of
+  // new_k / new_v instead of the pool (the decode merge launch after stores them)
+  const void* new_k;
+  const void* new_v;
+  int64_t new_k_stride;      // elements between the rows of new_k
+  int64_t new_v_stride;
   int n_items;
   uint64_t items[kMaxPrefillItems];
 };

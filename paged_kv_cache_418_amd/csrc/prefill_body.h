@@ -94,10 +94,15 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // F8: the pools hold E4M3 codes (the k_scale is in p.scale_log2, the v_scale is applied to
 // the output or by the merge); the tiles are converted to their exact bf16 values in LDS
 // and in registers, so the matrix-core work is the bf16 kernel's.
-template <int D, bool WINDOW, bool PREFIX = false, bool F8 = false>
+//
+// FRESH (a mixed step that also stores its new K/V, bf16 pools): keys at or past the chunk's cached
+// length are copied from the input rows p.new_k / p.new_v (row qsl[s] + key - cached, the pool's
+// row layout) instead of the pool; the launch after this one stores them there.
+template <int D, bool WINDOW, bool PREFIX = false, bool F8 = false, bool FRESH = false>
 __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned char* smem, int item_idx, int kvh) {
   using Sh = PrefillShape<D>;
   static_assert(!(PREFIX && WINDOW), "prefix tiles see the whole prefix");
+  static_assert(!(FRESH && (WINDOW || PREFIX || F8)), "fresh rows: plain causal tiles over bf16 pools");
 
   // ---- work item
   const uint64_t item = p.items[item_idx];
@@ -166,8 +171,16 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     const int ph = live ? phys : bt_fill;
     const size_t off = ((size_t)ph * 16 + ((live ? key : fill_key) & 15)) * tok_stride + (size_t)kvh * D * 2 +
                        chunk * 16;
+    const uint8_t* src = base + off;
+    if constexpr (FRESH) {  // a new row (the filler too): from the input rows
+      const int kk = live ? key : fill_key;
+      const bool is_v = base == vbase;
+      const uint8_t* nb = reinterpret_cast<const uint8_t*>(is_v ? p.new_v : p.new_k);
+      const size_t nrow = (size_t)(is_v ? p.new_v_stride : p.new_k_stride) * 2;
+      if (kk >= c) src = nb + (size_t)(q0 + kk - c) * nrow + (size_t)kvh * D * 2 + chunk * 16;
+    }
     unsigned char* dst = st + (copy_row0 + Sh::kRowsPerCopy * i) * Sh::kRowBytes;
-    __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(base + off), (void PA_LDS*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)src, (void PA_LDS*)dst, 16, 0, 0);
   };
   auto copy_rows = [&](const uint8_t* base, int tile, int phys, unsigned char* st) {
 #pragma unroll
@@ -698,6 +711,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     if (leading && computes(kt1 - 1)) pv(pw, vt_addr(kt1 - 1), [](int) {});
     wait_vmcnt<0>();  // no copy may still be writing LDS when the work-group ends
   }
+
 
   // ---- epilogue.  The lane's outputs (d = n*32 + 8*(r/4) + 4*half + r%4 of row rl) are
   // scattered pieces of 32 rows; stored as they are, every store instruction would touch 32

@@ -227,3 +227,98 @@ def test_cascade_write_prefix_shared_fp8_full():
     w = wl.prefix_shared_fp8_decode()
     say("cascade_write full", w.name)
     _check(w, Step(w, prefix=w.shared_prefix_blocks))
+
+
+# ---- the mixed step (pa_prefill_varlen_write): decode rows and chunked-prefill chunks in one flattened batch;
+# in one fused launch the decode waves store their rows and the chunks' tiles read their new keys from the input
+# rows while one item per row tile stores them; otherwise the write runs first
+
+def _varlen_check(w, key=None, value=None):
+    kc0, vc0 = w.k_cache.cuda(), w.v_cache.cuda()
+    bt = torch.from_numpy(w.block_tables).cuda()
+    sl = torch.from_numpy(w.seq_lens).cuda()
+    qsl = torch.from_numpy(w.query_start_loc).cuda()
+    q = w.query.cuda()
+    nk = w.new_k.cuda() if key is None else key
+    nv = w.new_v.cuda() if value is None else value
+    res = []
+    for fused in (True, False):
+        kc, vc = kc0.clone(), vc0.clone()
+        out = torch.zeros_like(q)
+        if fused:
+            pk.pa_prefill_varlen_write(q, nk, nv, kc, vc, bt, sl, qsl, w.seq_lens, w.query_start_loc, w.scale,
+                                       out=out)
+        else:
+            pk.pa_write_kv(nk, nv, kc, vc, bt, sl, qsl, int(w.q_lens.max()))
+            pk.pa_prefill_varlen(q, kc, vc, bt, sl, qsl, w.seq_lens, w.query_start_loc, w.scale, out=out)
+        torch.cuda.synchronize()
+        res.append((out, kc, vc))
+    (out, kc, vc), (rout, rkc, rvc) = res
+    assert torch.equal(_bytes(kc), _bytes(rkc)), "key pool differs from pa_write_kv's"
+    assert torch.equal(_bytes(vc), _bytes(rvc)), "value pool differs from pa_write_kv's"
+    assert torch.equal(_bytes(out), _bytes(rout)), "output differs from pa_prefill_varlen's after the write"
+    return out
+
+
+def _mixed(seed, heads, num_seqs=10, q_dtype="bf16", kv="bf16"):
+    Hq, Hkv, D = heads
+    rng = np.random.default_rng(seed)
+    q_lens = [1 if i % 2 == 0 else int(rng.integers(2, 300)) for i in range(num_seqs)]
+    ctx = [int(q + rng.integers(0, 1500)) for q in q_lens]
+    ctx[1] = q_lens[1]  # one chunk from an empty cache: its filler key is a new row
+    return wl.build(f"mixed_write_{seed}", seed=seed, ctx_lens=ctx, q_lens=q_lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                    head_dim=D, q_dtype=q_dtype, kv_dtype=kv)
+
+
+@pytest.fixture
+def fused_mode():
+    def set_mode(mode):
+        pk.set_fused(mode)
+    yield set_mode
+    pk.set_fused(-1)
+
+
+@pytest.mark.parametrize("mode", [2, 0])
+@pytest.mark.parametrize("seed,heads", [(991, (32, 8, 128)), (992, (8, 2, 64)), (993, (48, 1, 128)),
+                                        (994, (12, 4, 128))])
+def test_varlen_write_equals_write_then_prefill(fused_mode, mode, seed, heads):
+    """Mixed batches (decode rows, chunks with and without cached tokens, partly filled blocks at both ends of a
+    chunk) with the fused launch forced on (the rows stored inside it) and off (the write's own launch)."""
+    fused_mode(mode)
+    w = _mixed(seed, heads)
+    say("varlen_write", mode, heads, "q_lens", w.q_lens.tolist())
+    out = _varlen_check(w)
+    want = oracle.attention_for(w, pools=oracle.written_pools(w))
+    err = max_err(out, want)
+    say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_varlen_write_fp32_takes_the_separate_write(fused_mode):
+    """fp32 pools and activations (every chunk token a decode row of its own): the write runs first."""
+    fused_mode(2)
+    w = _mixed(995, (8, 2, 128), q_dtype="f32", kv="f32")
+    say("varlen_write fp32")
+    _varlen_check(w)
+
+
+def test_varlen_write_unaligned_rows(fused_mode):
+    """Rows 2 bytes off 16-byte alignment: the write runs as its own launch."""
+    fused_mode(2)
+    w = _mixed(996, (8, 2, 64))
+    T, H, D = w.new_k.shape
+    buf = torch.empty(2, T * H * D + 8, dtype=torch.bfloat16, device="cuda")
+    key = buf[0, 1:1 + T * H * D].view(T, H, D)
+    value = buf[1, 1:1 + T * H * D].view(T, H, D)
+    key.copy_(w.new_k.cuda())
+    value.copy_(w.new_v.cuda())
+    _varlen_check(w, key, value)
+
+
+def test_varlen_write_mixed_step_full(fused_mode):
+    """The bench's mixed step at full size (48 decode rows + two 512-token chunks at 0 and 1536 cached tokens),
+    fused launch forced: bit-identical to the two calls."""
+    fused_mode(2)
+    w = wl.mixed_step_bf16()
+    say("varlen_write mixed step full")
+    _varlen_check(w)
