@@ -219,6 +219,16 @@ def _check_kv_write(key, value, key_cache, value_cache, fp8: bool) -> None:
                          "bfloat16")
 
 
+def _check_pools(query, key_cache, value_cache, fp8: bool) -> None:
+    """The attention calls read the pools in the query's dtype (bf16 or fp32 pools) or as E4M3 codes (fp8)."""
+    if key_cache.dtype != value_cache.dtype or key_cache.shape != value_cache.shape:
+        raise ValueError("key_cache and value_cache must have the same dtype and shape")
+    if fp8 and key_cache.dtype != torch.uint8:
+        raise ValueError("fp8 pools are uint8 E4M3 codes")
+    if not fp8 and key_cache.dtype != query.dtype:
+        raise ValueError(f"the pools ({key_cache.dtype}) must have the query's dtype ({query.dtype})")
+
+
 def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
     """Writes key/value [T, Hkv, D] (token stride may exceed Hkv*D) into the pools."""
     lib = load()
@@ -278,6 +288,7 @@ def pa_decode(query, key_cache, value_cache, block_tables, seq_lens, scale: floa
               num_splits: int = 0, out=None, workspace=None):
     """One new token per sequence: query [S, Hq, D] -> out [S, Hq, D] (fp32 or bf16 pools)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
@@ -294,6 +305,7 @@ def pa_decode_static(query, key_cache, value_cache, block_tables, seq_lens, scal
                      num_splits: int = 0, out=None):
     """pa_decode with the library's static scratch (no workspace, no allocation by the library)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
@@ -309,6 +321,7 @@ def pa_decode_fp8(query, key_cache, value_cache, block_tables, seq_lens, scale: 
                   v_scale: float, max_seq_len: int, num_splits: int = 0, out=None, workspace=None):
     """pa_decode over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
@@ -329,6 +342,7 @@ def _decode_write_args(query, key, value, key_cache, value_cache, block_tables, 
         raise ValueError(f"key/value must be [{S}, {Hkv}, {D}] (one new row per sequence)")
     if key.dtype != query.dtype or value.dtype != query.dtype:
         raise ValueError("key/value must have the query's dtype")
+    _check_kv_write(key, value, key_cache, value_cache, fp8=key_cache.dtype == torch.uint8)
     if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
         raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
     out = torch.empty_like(query) if out is None else out
@@ -347,6 +361,7 @@ def pa_decode_write(query, key, value, key_cache, value_cache, block_tables, seq
     """One decode step: stores key/value [S, Hkv, D] (row s: position seq_lens[s] - 1 of sequence s) into the
     pools and attends query [S, Hq, D] over the cache with them (fp32 or bf16 pools) -> out [S, Hq, D]."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
                                               max_seq_len, num_splits, out, workspace)
     _check("pa_decode_write", lib.pa_decode_write(*head, float(scale), _dtype_code(key_cache), num_splits, ws, wsb,
@@ -359,6 +374,7 @@ def pa_decode_write_fp8(query, key, value, key_cache, value_cache, block_tables,
                         workspace=None):
     """pa_decode_write over fp8 E4M3 pools (uint8 codes of x / scale) with per-tensor scales."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
     out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
                                               max_seq_len, num_splits, out, workspace)
     _check("pa_decode_write_fp8", lib.pa_decode_write_fp8(*head, float(scale), _dtype_code(query), float(k_scale),
@@ -370,6 +386,7 @@ def pa_decode_cascade_write(query, key, value, key_cache, value_cache, block_tab
                             max_seq_len: int, prefix_blocks: int, num_splits: int = 0, out=None, workspace=None):
     """pa_decode_write for a batch whose tables begin with the same prefix_blocks blocks (pa_decode_cascade)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
                                               max_seq_len, num_splits, out, workspace, prefix_blocks)
     _check("pa_decode_cascade_write", lib.pa_decode_cascade_write(*head, float(scale), _dtype_code(key_cache),
@@ -382,6 +399,7 @@ def pa_decode_cascade_write_fp8(query, key, value, key_cache, value_cache, block
                                 num_splits: int = 0, out=None, workspace=None):
     """pa_decode_cascade_write over fp8 E4M3 pools (uint8 codes of x / scale)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
     out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
                                               max_seq_len, num_splits, out, workspace, prefix_blocks)
     _check("pa_decode_cascade_write_fp8",
@@ -394,6 +412,7 @@ def pa_decode_window(query, key_cache, value_cache, block_tables, seq_lens, scal
                      sliding_window: int, num_splits: int = 0, out=None, workspace=None):
     """pa_decode where each query sees only its sequence's last sliding_window positions (bf16 pools)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
@@ -410,6 +429,7 @@ def pa_decode_local(query, key_cache, value_cache, block_tables, seq_lens, scale
                     chunk_size: int, num_splits: int = 0, out=None, workspace=None):
     """pa_decode where each query sees only the keys of its own chunk of chunk_size positions (bf16 pools)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
@@ -432,6 +452,7 @@ def pa_decode_cascade(query, key_cache, value_cache, block_tables, seq_lens, sca
                       prefix_blocks: int, num_splits: int = 0, out=None, workspace=None):
     """pa_decode for sequences that all start with the same prefix_blocks physical blocks (bf16 pools)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
@@ -450,6 +471,7 @@ def pa_decode_cascade_fp8(query, key_cache, value_cache, block_tables, seq_lens,
                           workspace=None):
     """pa_decode_cascade over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
     S, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     out = torch.empty_like(query) if out is None else out
@@ -476,6 +498,7 @@ def pa_prefill_varlen(query, key_cache, value_cache, block_tables, seq_lens, que
                       query_start_loc_host, scale: float, out=None, workspace=None):
     """Causal attention over a flattened batch of decode rows and prefill chunks: query [T, Hq, D]."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     T, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     qh = _i32_host(query_start_loc_host)
@@ -497,12 +520,14 @@ def pa_prefill_varlen_write(query, key, value, key_cache, value_cache, block_tab
     """One step of a flattened batch that also stores its new K/V: key/value [T, Hkv, D] (row t: the K/V of the
     batch's new row t), the bytes of pa_write_kv followed by pa_prefill_varlen."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     T, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
         raise ValueError(f"key/value must be [{T}, {Hkv}, {D}] (one row per new token)")
     if key.dtype != query.dtype or value.dtype != query.dtype:
         raise ValueError("key/value must have the query's dtype")
+    _check_kv_write(key, value, key_cache, value_cache, fp8=key_cache.dtype == torch.uint8)
     if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
         raise ValueError("heads and head_dim of key/value must be contiguous inside a token")
     qh = _i32_host(query_start_loc_host)
@@ -531,6 +556,7 @@ def pa_prefill_varlen_window(query, key_cache, value_cache, block_tables, seq_le
                              query_start_loc_host, scale: float, sliding_window: int, out=None, workspace=None):
     """pa_prefill_varlen where the row at position p sees positions p-sliding_window+1 .. p (bf16)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     T, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     qh = _i32_host(query_start_loc_host)
@@ -560,6 +586,7 @@ def pa_prefill_varlen_local(query, key_cache, value_cache, block_tables, seq_len
                             query_start_loc_host, scale: float, chunk_size: int, out=None, workspace=None):
     """pa_prefill_varlen where the row at position p sees positions chunk_size*(p // chunk_size) .. p (bf16)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
     T, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     qh = _i32_host(query_start_loc_host)
@@ -628,6 +655,7 @@ def pa_prefill_varlen_fp8(query, key_cache, value_cache, block_tables, seq_lens,
                           workspace=None):
     """pa_prefill_varlen over fp8 E4M3 pools (uint8 codes) with per-tensor scales."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
     T, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     qh = _i32_host(query_start_loc_host)
@@ -679,6 +707,7 @@ def pa_decode_local_fp8(query, key_cache, value_cache, block_tables, seq_lens, s
 def _prefill_fp8_masked(name, query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, seq_lens_host,
                         query_start_loc_host, scale, k_scale, v_scale, size, out, workspace):
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
     T, Hq, D = query.shape
     NB, B, Hkv, _ = key_cache.shape
     qh = _i32_host(query_start_loc_host)
@@ -805,6 +834,7 @@ class BlockPool:
 def probe_mfma_peak(blocks: int = 512, iters: int = 20000, reps: int = 3) -> float:
     """Measured bf16 matrix-core rate (TFLOP/s) of v_mfma_f32_32x32x16_bf16 on this GPU (best of reps)."""
     lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     best = None
     for _ in range(reps + 1):

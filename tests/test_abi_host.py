@@ -412,3 +412,26 @@ def test_cascade_write_argument_checks(lib):
         assert lib.pa_last_error().decode()
         assert call(fp8, S=0, ws=None, wsb=0) == 0
     assert call(True, k_scale=-1.0) == 2
+
+
+def test_binding_refuses_pools_of_another_dtype():
+    """The attention calls read bf16 or fp32 pools in the query's dtype and fp8 pools as uint8 codes: a mismatch is
+    refused before any device call (host tensors; the dtype checks come first)."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(2, 32, 128, dtype=bf)
+    pool = torch.zeros(4, 16, 8, 128, dtype=bf)
+    bt, sl = torch.zeros(2, 4, dtype=torch.int32), torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="query's dtype"):
+        pk.pa_decode(q.float(), pool, pool, bt, sl, 0.088, 16)           # fp32 queries over bf16 pools
+    with pytest.raises(ValueError, match="query's dtype"):
+        pk.pa_decode_cascade(q, pool.float(), pool.float(), bt, sl, 0.088, 32, 1)
+    with pytest.raises(ValueError, match="uint8"):
+        pk.pa_decode_fp8(q, pool, pool, bt, sl, 0.088, 0.05, 0.04, 16)  # a bf16 pool through the fp8 call
+    with pytest.raises(ValueError, match="same dtype"):
+        pk.pa_decode(q, pool, pool.float(), bt, sl, 0.088, 16)
+    k = torch.zeros(2, 8, 128, dtype=bf)
+    with pytest.raises(ValueError, match="dtype"):
+        pk.pa_decode_write(q.float(), k.float(), k.float(), pool, pool, bt, sl, 0.088, 16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pk.pa_decode_write(q, k, k, pool, pool, bt, sl, 0.088, 16)  # consistent: only the host placement is refused
