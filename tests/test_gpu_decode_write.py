@@ -322,3 +322,17 @@ def test_varlen_write_mixed_step_full(fused_mode):
     w = wl.mixed_step_bf16()
     say("varlen_write mixed step full")
     _varlen_check(w)
+
+
+@pytest.mark.parametrize("shape", ["decode_rows_only", "chunks_only"])
+def test_varlen_write_batches_that_do_not_fuse(fused_mode, shape):
+    """A batch of decode rows only, and one of chunks only: no fused launch, so the write runs first; same bytes."""
+    fused_mode(2)
+    rng = np.random.default_rng(997)
+    n = 7
+    q_lens = [1] * n if shape == "decode_rows_only" else [int(rng.integers(2, 200)) for _ in range(n)]
+    ctx = [int(q + rng.integers(0, 900)) for q in q_lens]
+    w = wl.build(f"varlen_write_{shape}", seed=997, ctx_lens=ctx, q_lens=q_lens, num_q_heads=16, num_kv_heads=4,
+                 head_dim=128, q_dtype="bf16", kv_dtype="bf16")
+    say("varlen_write", shape)
+    _varlen_check(w)
