@@ -328,6 +328,46 @@ pa_status_t pa_decode_write_fp8(void* out, const void* query, const void* key, c
                                 int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_window_write, pa_decode_window_write_fp8, pa_decode_local_write,
+ * pa_decode_local_write_fp8 -- the decode step that stores its new K/V
+ * (pa_decode_write, pa_decode_write_fp8) with the mask of pa_decode_window
+ * (sliding_window >= 1) or pa_decode_local (chunk_size >= 1): the bytes of
+ * pa_write_kv (pa_write_kv_fp8) followed by the masked decode.  The new row,
+ * at position seq_lens[s] - 1, is always visible.  Arguments, conditions,
+ * workspace and errors as pa_decode_write and the masked decode.
+ */
+pa_status_t pa_decode_window_write(void* out, const void* query, const void* key, const void* value,
+                                   int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache,
+                                   void* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t sliding_window,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream);
+pa_status_t pa_decode_window_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                       int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                       uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_seq_len, float scale, pa_dtype_t dtype, float k_scale,
+                                       float v_scale, int32_t sliding_window, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+pa_status_t pa_decode_local_write(void* out, const void* query, const void* key, const void* value,
+                                  int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache, void* value_cache,
+                                  const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                  pa_dtype_t dtype, int32_t chunk_size, int32_t num_splits, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+pa_status_t pa_decode_local_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                      int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                      uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_seq_len, float scale, pa_dtype_t dtype, float k_scale,
+                                      float v_scale, int32_t chunk_size, int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_cascade -- pa_decode for a batch whose sequences all begin with
  * the same prefix_blocks physical blocks (prefix sharing: [A] §2, two
  * requests' tables pointing at the same blocks; cascade attention is named in

@@ -8,7 +8,8 @@ from ._binding import (  # noqa: F401
     BlockPool, pool_hash_blocks, PA_BF16, PA_F32, PA_FP8_E4M3, PAError, abi_version, header_symbols, load,
     pa_decode, pa_decode_cascade, pa_decode_cascade_fp8, pa_decode_cascade_workspace_bytes, pa_decode_cascade_write,
     pa_decode_cascade_write_fp8, pa_decode_fp8,
-    pa_decode_local, pa_decode_local_fp8, pa_decode_static, pa_decode_window, pa_decode_window_fp8, pa_decode_write,
+    pa_decode_local, pa_decode_local_fp8, pa_decode_local_write, pa_decode_local_write_fp8, pa_decode_static,
+    pa_decode_window, pa_decode_window_fp8, pa_decode_window_write, pa_decode_window_write_fp8, pa_decode_write,
     pa_decode_write_fp8,
     pa_decode_workspace_bytes, pa_prefill_varlen, pa_prefill_varlen_fp8, pa_prefill_varlen_fp8_workspace_bytes,
     pa_prefill_varlen_write,

@@ -79,6 +79,14 @@ def load() -> ctypes.CDLL:
                                  ctypes.c_int, i32, P, sz, P], ctypes.c_int),
             "pa_decode_write_fp8": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32,
                                      ctypes.c_int, f32, f32, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_window_write": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                        ctypes.c_int, i32, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_window_write_fp8": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
+                                            f32, ctypes.c_int, f32, f32, i32, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_local_write": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                       ctypes.c_int, i32, i32, P, sz, P], ctypes.c_int),
+            "pa_decode_local_write_fp8": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
+                                           f32, ctypes.c_int, f32, f32, i32, i32, P, sz, P], ctypes.c_int),
             "pa_decode_cascade_write": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                          f32, ctypes.c_int, i32, i32, P, sz, P], ctypes.c_int),
             "pa_decode_cascade_write_fp8": ([P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
@@ -379,6 +387,58 @@ def pa_decode_write_fp8(query, key, value, key_cache, value_cache, block_tables,
                                               max_seq_len, num_splits, out, workspace)
     _check("pa_decode_write_fp8", lib.pa_decode_write_fp8(*head, float(scale), _dtype_code(query), float(k_scale),
                                                           float(v_scale), num_splits, ws, wsb, _stream()))
+    return out
+
+
+def pa_decode_window_write(query, key, value, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                           max_seq_len: int, sliding_window: int, num_splits: int = 0, out=None, workspace=None):
+    """pa_decode_write where each query sees its sequence's last sliding_window positions (pa_decode_window)."""
+    lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
+    out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
+                                              max_seq_len, num_splits, out, workspace)
+    _check("pa_decode_window_write", lib.pa_decode_window_write(*head, float(scale), _dtype_code(key_cache),
+                                                                sliding_window, num_splits, ws, wsb, _stream()))
+    return out
+
+
+def pa_decode_window_write_fp8(query, key, value, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                               k_scale: float, v_scale: float, max_seq_len: int, sliding_window: int,
+                               num_splits: int = 0, out=None, workspace=None):
+    """pa_decode_window_write over fp8 E4M3 pools."""
+    lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
+    out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
+                                              max_seq_len, num_splits, out, workspace)
+    _check("pa_decode_window_write_fp8",
+           lib.pa_decode_window_write_fp8(*head, float(scale), _dtype_code(query), float(k_scale), float(v_scale),
+                                          sliding_window, num_splits, ws, wsb, _stream()))
+    return out
+
+
+def pa_decode_local_write(query, key, value, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                          max_seq_len: int, chunk_size: int, num_splits: int = 0, out=None, workspace=None):
+    """pa_decode_write where each query sees the keys of its own chunk of chunk_size positions (pa_decode_local)."""
+    lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=False)
+    out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
+                                              max_seq_len, num_splits, out, workspace)
+    _check("pa_decode_local_write", lib.pa_decode_local_write(*head, float(scale), _dtype_code(key_cache), chunk_size,
+                                                              num_splits, ws, wsb, _stream()))
+    return out
+
+
+def pa_decode_local_write_fp8(query, key, value, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                              k_scale: float, v_scale: float, max_seq_len: int, chunk_size: int,
+                              num_splits: int = 0, out=None, workspace=None):
+    """pa_decode_local_write over fp8 E4M3 pools."""
+    lib = load()
+    _check_pools(query, key_cache, value_cache, fp8=True)
+    out, head, (ws, wsb) = _decode_write_args(query, key, value, key_cache, value_cache, block_tables, seq_lens,
+                                              max_seq_len, num_splits, out, workspace)
+    _check("pa_decode_local_write_fp8",
+           lib.pa_decode_local_write_fp8(*head, float(scale), _dtype_code(query), float(k_scale), float(v_scale),
+                                         chunk_size, num_splits, ws, wsb, _stream()))
     return out
 
 

@@ -690,7 +690,8 @@ pa_status_t decode_write(void* out, const void* query, const void* key, const vo
                          int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                          int32_t max_seq_len, float scale, int kv_kind, pa_dtype_t dtype, float k_scale,
-                         float v_scale, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                         float v_scale, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream,
+                         int32_t sliding_window = 0, int32_t local_chunk = 0) {
   pa_status_t st = check_decode_args(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, num_seqs,
                                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
                                      num_splits, workspace, workspace_bytes);
@@ -715,7 +716,8 @@ pa_status_t decode_write(void* out, const void* query, const void* key, const vo
     const NewRows rows{key, value, key_tok_stride, value_tok_stride, src_f32, k_scale, v_scale};
     return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs,
                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale,
-                      kv_kind, src_f32, k_scale, v_scale, num_splits, workspace, workspace_bytes, s, 0, 0, 0, &rows);
+                      kv_kind, src_f32, k_scale, v_scale, num_splits, workspace, workspace_bytes, s, 0,
+                      sliding_window, local_chunk, &rows);
   }
   const int write_kind = kv_kind == pa::kFP8 ? (src_f32 ? pa::kFP8 + 1 : pa::kFP8) : kv_kind;
   st = hip_status(pa::launch_write_kv(key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, nullptr,
@@ -725,7 +727,7 @@ pa_status_t decode_write(void* out, const void* query, const void* key, const vo
   if (st != PA_OK) return st;
   return run_decode(out, query, key_cache, value_cache, block_tables, bt_stride, seq_lens, nullptr, num_seqs, num_seqs,
                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len, scale, kv_kind, src_f32,
-                    k_scale, v_scale, num_splits, workspace, workspace_bytes, s);
+                    k_scale, v_scale, num_splits, workspace, workspace_bytes, s, 0, sliding_window, local_chunk);
 }
 
 }  // namespace
@@ -757,6 +759,74 @@ pa_status_t pa_decode_write_fp8(void* out, const void* query, const void* key, c
                       bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_seq_len, scale, pa::kFP8, dtype, k_scale, v_scale, num_splits, workspace, workspace_bytes,
                       stream);
+}
+
+// the sliding-window and chunked-local decode steps that also store the new K/V: pa_decode_write's path with
+// the mask of pa_decode_window / pa_decode_local (the new row, at L - 1, is always visible)
+pa_status_t pa_decode_window_write(void* out, const void* query, const void* key, const void* value,
+                                   int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache,
+                                   void* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_seq_len, float scale, pa_dtype_t dtype, int32_t sliding_window,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
+  return decode_write(out, query, key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                      bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_seq_len, scale, dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype, 1.f, 1.f, num_splits,
+                      workspace, workspace_bytes, stream, sliding_window, 0);
+}
+
+pa_status_t pa_decode_window_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                       int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                       uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_seq_len, float scale, pa_dtype_t dtype, float k_scale,
+                                       float v_scale, int32_t sliding_window, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  if (sliding_window < 1) return fail(PA_ERR_SHAPE, "sliding_window %d < 1", sliding_window);
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  return decode_write(out, query, key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                      bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_seq_len, scale, pa::kFP8, dtype, k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                      stream, sliding_window, 0);
+}
+
+pa_status_t pa_decode_local_write(void* out, const void* query, const void* key, const void* value,
+                                  int64_t key_tok_stride, int64_t value_tok_stride, void* key_cache, void* value_cache,
+                                  const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                                  pa_dtype_t dtype, int32_t chunk_size, int32_t num_splits, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
+  return decode_write(out, query, key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                      bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_seq_len, scale, dtype == PA_F32 ? pa::kF32 : pa::kBF16, dtype, 1.f, 1.f, num_splits,
+                      workspace, workspace_bytes, stream, 0, chunk_size);
+}
+
+pa_status_t pa_decode_local_write_fp8(void* out, const void* query, const void* key, const void* value,
+                                      int64_t key_tok_stride, int64_t value_tok_stride, uint8_t* key_cache,
+                                      uint8_t* value_cache, const int32_t* block_tables, int32_t bt_stride,
+                                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_seq_len, float scale, pa_dtype_t dtype, float k_scale,
+                                      float v_scale, int32_t chunk_size, int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_DTYPE, "dtype must be PA_F32 or PA_BF16");
+  if (chunk_size < 1) return fail(PA_ERR_SHAPE, "chunk_size %d < 1", chunk_size);
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be positive and finite");
+  return decode_write(out, query, key, value, key_tok_stride, value_tok_stride, key_cache, value_cache, block_tables,
+                      bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_seq_len, scale, pa::kFP8, dtype, k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                      stream, 0, chunk_size);
 }
 
 namespace {

@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = pk.header_symbols()
-    assert len(syms) == 55
+    assert len(syms) == 59
     assert {"pa_decode_cascade", "pa_decode_cascade_fp8", "pa_decode_cascade_workspace_bytes", "pa_decode_write",
             "pa_decode_write_fp8", "pa_decode_cascade_write", "pa_decode_cascade_write_fp8"} <= set(syms)
     for s in syms:

@@ -336,3 +336,44 @@ def test_varlen_write_batches_that_do_not_fuse(fused_mode, shape):
                  head_dim=128, q_dtype="bf16", kv_dtype="bf16")
     say("varlen_write", shape)
     _varlen_check(w)
+
+
+# ---- the sliding-window and chunked-local decode steps (pa_decode_window_write*, pa_decode_local_write*)
+
+def _masked_run(w, mask, size, fused, num_splits):
+    kc, vc = w.k_cache.cuda(), w.v_cache.cuda()
+    bt = torch.from_numpy(w.block_tables).cuda()
+    sl = torch.from_numpy(w.seq_lens).cuda()
+    qsl = torch.from_numpy(w.query_start_loc).cuda()
+    q, nk, nv = w.query.cuda(), w.new_k.cuda(), w.new_v.cuda()
+    out = torch.zeros_like(q)
+    L = int(w.seq_lens.max())
+    fp8 = w.kv_dtype == "fp8"
+    sc = (w.k_scale, w.v_scale) if fp8 else ()
+    if fused:
+        fn = {("window", False): pk.pa_decode_window_write, ("window", True): pk.pa_decode_window_write_fp8,
+              ("local", False): pk.pa_decode_local_write, ("local", True): pk.pa_decode_local_write_fp8}[(mask, fp8)]
+        fn(q, nk, nv, kc, vc, bt, sl, w.scale, *sc, L, size, num_splits, out=out)
+    else:
+        scales = dict(k_scale=w.k_scale, v_scale=w.v_scale) if fp8 else {}
+        pk.pa_write_kv(nk, nv, kc, vc, bt, sl, qsl, 1, **scales)
+        fn = {("window", False): pk.pa_decode_window, ("window", True): pk.pa_decode_window_fp8,
+              ("local", False): pk.pa_decode_local, ("local", True): pk.pa_decode_local_fp8}[(mask, fp8)]
+        fn(q, kc, vc, bt, sl, w.scale, *sc, L, size, num_splits, out=out)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+@pytest.mark.parametrize("kinds", [("bf16", "bf16"), ("bf16", "fp8"), ("f32", "fp8"), ("f32", "f32")])
+@pytest.mark.parametrize("mask,size", [("window", 1), ("window", 37), ("window", 200), ("window", 100000),
+                                       ("local", 16), ("local", 100)])
+@pytest.mark.parametrize("num_splits", [0, 7])
+def test_masked_decode_write_equals_write_then_masked_decode(kinds, mask, size, num_splits):
+    seed = 1100 + size % 97 + num_splits + len(kinds[0]) + 3 * len(kinds[1]) + (50 if mask == "local" else 0)
+    w = wl.random_case(seed, num_seqs=7, ctx_range=(1, 700), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       q_dtype=kinds[0], kv_dtype=kinds[1], k_scale=0.05, v_scale=0.04)
+    say("masked decode_write", mask, size, kinds, num_splits)
+    fused = _masked_run(w, mask, size, True, num_splits)
+    ref = _masked_run(w, mask, size, False, num_splits)
+    assert _same(fused[1:], ref[1:]), "pools differ from pa_write_kv's"
+    assert torch.equal(_bytes(fused[0]), _bytes(ref[0])), "output differs from the masked decode's after the write"
