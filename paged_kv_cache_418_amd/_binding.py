@@ -894,7 +894,6 @@ class BlockPool:
 def probe_mfma_peak(blocks: int = 512, iters: int = 20000, reps: int = 3) -> float:
     """Measured bf16 matrix-core rate (TFLOP/s) of v_mfma_f32_32x32x16_bf16 on this GPU (best of reps)."""
     lib = load()
-    _check_pools(query, key_cache, value_cache, fp8=True)
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     best = None
     for _ in range(reps + 1):

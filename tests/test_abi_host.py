@@ -435,3 +435,20 @@ def test_binding_refuses_pools_of_another_dtype():
         pk.pa_decode_write(q.float(), k.float(), k.float(), pool, pool, bt, sl, 0.088, 16)
     with pytest.raises(ValueError, match="GPU tensor"):
         pk.pa_decode_write(q, k, k, pool, pool, bt, sl, 0.088, 16)  # consistent: only the host placement is refused
+
+
+def test_binding_functions_use_only_their_own_arguments():
+    """Every name a binding function passes to the argument checks is one of its own parameters (a check pasted into
+    the wrong function fails only when that function runs, possibly only on a GPU)."""
+    import ast
+    import inspect
+    from paged_kv_cache_418_amd import _binding
+    tree = ast.parse(inspect.getsource(_binding))
+    for node in ast.walk(tree):
+        if not isinstance(node, ast.FunctionDef):
+            continue
+        params = {a.arg for a in node.args.args + node.args.kwonlyargs}
+        for sub in ast.walk(node):
+            if isinstance(sub, ast.Call) and getattr(sub.func, "id", None) in ("_check_pools", "_check_kv_write"):
+                names = {a.id for a in sub.args if isinstance(a, ast.Name)}
+                assert names <= params, (node.name, names - params)
