@@ -19,33 +19,39 @@ struct PrefillShape {
   static constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row (the swizzle period)
   static constexpr int kTileBytes = kKeys * kRowBytes; // one tensor of one tile
   static constexpr int kKSlots = 4;                    // K ring: K(t+3) is copied at step t
-  static constexpr int kVSlots = 3;                    // row-major V ring: V(t+3) copied at step t
-  static constexpr int kVtSlots = 3;                   // V^T ring (64 keys x D, 128-byte rows)
-  static constexpr int kVtRowBytes = kKeys * 2;        // one d row of a V^T tile
-  static constexpr int kTransposes = D / 32;           // 512-byte transposing reads per wave per tile
-  static constexpr int kLdsBytes = (kKSlots + kVSlots + kVtSlots) * kTileBytes;
+  static constexpr int kVSlots = 5;                    // V ring: V(t+3) copied at step t, read at t+3 and t+4
+  static constexpr int kLdsBytes = (kKSlots + kVSlots) * kTileBytes;
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;           // rows one wave-wide 1 KB copy fills
   static constexpr int kCopies = kTileBytes / 1024 / kWaves;      // copies per wave per tensor per tile
   static constexpr int kKSteps = D / 16;               // 32x32x16 MFMAs over d
   static constexpr int kDTiles = D / 32;               // 32-wide d tiles of O^T
   // fp8 pools: the copies fill raw tiles of E4M3 codes (one byte an element).  K operands
-  // are converted as they are read; V is converted into a bf16 row-major tile, which the
-  // transposition then turns into V^T as for bf16 pools.
+  // are converted as they are read; V is converted into a bf16 tile laid out as the bf16
+  // pools' V tiles, which O += V P then reads in the same way.
   static constexpr int kRawRowBytes = D;
   static constexpr int kRawChunks = D / 16;            // 16-byte chunks per raw row (its swizzle period)
   static constexpr int kRawTileBytes = kKeys * kRawRowBytes;
   static constexpr int kRawKSlots = 4;                 // raw K ring: K(t+3) copied at step t
   static constexpr int kRawVSlots = 3;                 // raw V ring: V(t+4) copied at step t, converted at step t+2
-  static constexpr int kVRowSlots8 = 2;                // bf16 V rows: V(t+2) converted at step t, transposed at t+1
+  static constexpr int kVRowSlots8 = 4;                // bf16 V tiles: V(t+2) converted at step t, read at t+2 and t+3
   static constexpr int kRawRowsPerWave = kKeys / kWaves;  // rows of a raw tile each wave copies and converts
   static constexpr int kRawLanes = kRawRowsPerWave * kRawChunks;  // lanes that hold one 16-byte raw chunk
-  static constexpr int kLdsBytesF8 =
-      (kRawKSlots + kRawVSlots) * kRawTileBytes + (kVRowSlots8 + kVtSlots) * kTileBytes;
+  static constexpr int kLdsBytesF8 = (kRawKSlots + kRawVSlots) * kRawTileBytes + kVRowSlots8 * kTileBytes;
   static_assert(kLdsBytesF8 <= kLdsBytes, "the fp8 rings fit the bf16 kernel's LDS");
   static_assert(kRawLanes <= 64, "one raw slab per wave and tensor");
 };
 
 __device__ __forceinline__ bf16x8 u4_to_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Placement of the 16-byte chunks of a V tile row: logical chunk c of key row r sits at
+// c ^ v_swizzle<D>(r % 4).  O += V P reads, per 16-lane group, 4 consecutive key rows x 2
+// chunks (per 32 lanes: 4 rows x 4 chunks); with these four values those chunks land on
+// distinct banks whether the LDS serves 16 lanes over 32 banks or 32 lanes over 64.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r4) {
+  if constexpr (D == 128) return (0xCA60 >> (4 * r4)) & 15;  // 0, 6, 10, 12
+  else return 2 * r4;                                        // 0, 2, 4, 6
+}
 
 __device__ __forceinline__ float max_halves(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -141,7 +147,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // ---- copy role: each wave copies kCopies 1 KB slabs of K and of V per tile.  Slab
   // kCopies*wave + i holds rows kRowsPerCopy*(kCopies*wave + i) ...; lane = (row in slab,
   // physical chunk); the chunk it fetches is the logical chunk stored in that slot,
-  // physical ^ (row % kChunks).  All rows of a wave's slabs lie in one paged block.
+  // physical ^ (row % kChunks) for K, physical ^ v_swizzle(row % 4) for V.  All rows of a
+  // wave's slabs lie in one paged block.
   const int* bt = p.block_tables + (size_t)s * p.bt_stride;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
@@ -161,11 +168,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // into the pool), so the compiler can count it among the loads in flight.
   auto block_of = [&](int tile) { return bt[min(tile * Sh::kKeys + copy_row0, kv_end - 1) >> 4]; };
   // Slab i (0 .. kCopies-1) of this wave's part of one tensor of a tile.
-  auto copy_slab = [&](const uint8_t* base, int tile, int phys, unsigned char* st, int i) {
+  auto copy_slab = [&](bool is_v, int tile, int phys, unsigned char* st, int i) {
+    const uint8_t* const base = is_v ? vbase : kbase;
     phys = min(max(phys, 0), p.num_blocks - 1);
     const int row = copy_row0 + Sh::kRowsPerCopy * i + lane / lanes_per_row;
     const int slot = lane % lanes_per_row;
-    const int chunk = slot ^ (row % Sh::kChunks);
+    const int chunk = slot ^ (is_v ? v_swizzle<D>(row & 3) : row % Sh::kChunks);
     const int key = tile * Sh::kKeys + row;
     const bool live = key < kv_end && (!WINDOW || key >= key_first);
     const int ph = live ? phys : bt_fill;
@@ -174,7 +182,6 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     const uint8_t* src = base + off;
     if constexpr (FRESH) {  // a new row (the filler too): from the input rows
       const int kk = live ? key : fill_key;
-      const bool is_v = base == vbase;
       const uint8_t* nb = reinterpret_cast<const uint8_t*>(is_v ? p.new_v : p.new_k);
       const size_t nrow = (size_t)(is_v ? p.new_v_stride : p.new_k_stride) * 2;
       if (kk >= c) src = nb + (size_t)(q0 + kk - c) * nrow + (size_t)kvh * D * 2 + chunk * 16;
@@ -182,9 +189,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     unsigned char* dst = st + (copy_row0 + Sh::kRowsPerCopy * i) * Sh::kRowBytes;
     __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)src, (void PA_LDS*)dst, 16, 0, 0);
   };
-  auto copy_rows = [&](const uint8_t* base, int tile, int phys, unsigned char* st) {
+  auto copy_rows = [&](bool is_v, int tile, int phys, unsigned char* st) {
 #pragma unroll
-    for (int i = 0; i < Sh::kCopies; ++i) copy_slab(base, tile, phys, st, i);
+    for (int i = 0; i < Sh::kCopies; ++i) copy_slab(is_v, tile, phys, st, i);
   };
   // fp8: this wave's kRawRowsPerWave rows of a raw tile (kRawChunks lanes a row, 16 codes a
   // lane; physical chunk = logical ^ (row % kRawChunks)), one copy instruction
@@ -200,24 +207,21 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     if (lane < Sh::kRawLanes)
       __builtin_amdgcn_global_load_lds((const void PA_GLOBAL*)(base + off), (void PA_LDS*)dst, 16, 0, 0);
   };
-  // LDS: a ring of four K tiles (tile t in slot (t - kt0) % 4), a ring of three row-major
-  // V tiles and a ring of three transposed V tiles (tile t in slot (t - kt0) % 3).
-  // fp8: four raw K tiles (slot (t - kt0) % 4), three raw V tiles (slot (t - kt0) % 3), two
-  // bf16 row-major V tiles (slot (t - kt0) % 2) and the three V^T tiles.
+  // LDS: a ring of four K tiles (tile t in slot (t - kt0) % 4) and a ring of five V tiles
+  // (slot (t - kt0) % 5).  fp8: four raw K tiles (slot (t - kt0) % 4), three raw V tiles
+  // (slot (t - kt0) % 3) and four bf16 V tiles (slot (t - kt0) % 4).
   constexpr int kRawV0 = Sh::kRawKSlots * Sh::kRawTileBytes;        // fp8 layout offsets
   constexpr int kVRow0 = kRawV0 + Sh::kRawVSlots * Sh::kRawTileBytes;
-  constexpr int kVt0 = F8 ? kVRow0 + Sh::kVRowSlots8 * Sh::kTileBytes : (Sh::kKSlots + Sh::kVSlots) * Sh::kTileBytes;
   auto k_stage = [&](int tile) {
     return smem + ((tile - kt0) & 3) * (F8 ? Sh::kRawTileBytes : Sh::kTileBytes);
   };
-  auto v_stage = [&](int tile) {  // the row-major bf16 V tile the transposition reads
-    if constexpr (F8) return smem + kVRow0 + ((tile - kt0) & 1) * Sh::kTileBytes;
-    else return smem + (Sh::kKSlots + (tile - kt0) % 3) * Sh::kTileBytes;
+  auto v_stage = [&](int tile) {  // the bf16 V tile that O += V P reads
+    if constexpr (F8) return smem + kVRow0 + ((tile - kt0) & 3) * Sh::kTileBytes;
+    else return smem + (Sh::kKSlots + (tile - kt0) % Sh::kVSlots) * Sh::kTileBytes;
   };
   auto vraw_stage = [&](int tile) { return smem + kRawV0 + ((tile - kt0) % 3) * Sh::kRawTileBytes; };
   auto k_addr = [&](int tile) { return (uint32_t)(uintptr_t)k_stage(tile); };
   auto v_addr = [&](int tile) { return (uint32_t)(uintptr_t)v_stage(tile); };
-  auto vt_addr = [&](int tile) { return (uint32_t)(uintptr_t)(smem + kVt0 + ((tile - kt0) % 3) * Sh::kTileBytes); };
 
   // block ids of the first four tiles (fp8: five, V runs a tile further ahead), read before Q
   // so the first copies wait only for them
@@ -314,151 +318,69 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     });
   };
 
-  // ---- V^T tiles.  PV needs, per lane, 8 keys of one d in one register quad, while the
-  // pool (and the copied tile) holds rows of d for one key.  Each tile is transposed once
-  // in LDS: wave w turns kTransposes 16(d) x 16(key) blocks of the row-major tile into V^T
-  // rows with ds_read_b64_tr_b16 (in each 16-lane group, output lane i element k is
-  // element i%4 of the 8 bytes addressed by lane 4k + i/4: lane 4k + q addresses key
-  // kb + k at d d0 + 4q, so lane i receives keys kb..kb+3 of d d0 + i) and ds_write_b64.
-  // A V^T row (d) holds the 64 keys in 16-byte chunks 2*ch + h = keys ch*16 + 8*(j/4) +
-  // 4h + j%4, j = 0..7: the order in which the probabilities sit in the S^T registers, so
-  // the operand of chunk ch is one ds_read_b128.  Chunk c of row d is stored at c ^
-  // ((d >> 1) & 7) (rows are half a bank line: reads and writes are conflict-free).
-  constexpr int kTileQuad = Sh::kDTiles;  // V^T operand reads per chunk (one per 32-wide d tile)
-  uint32_t tr_src[Sh::kTransposes], tr_dst[Sh::kTransposes];
+  // ---- V operands.  O^T += V^T P^T needs, per lane (d = 32n + rl, half), the 8 keys whose
+  // probabilities sit in its P register quad -- keys 16*ch + 4*half + 0..3 and 16*ch + 8 +
+  // 4*half + 0..3 of the tile for chunk ch -- at one d, while the tile holds rows of d for
+  // one key.  ds_read_b64_tr_b16 gathers them straight from the row-major tile: in each
+  // 16-lane group g, output lane i element k is element i%4 of the 8 bytes addressed by lane
+  // 4k + i/4, so lane 4k + q addresses key kb + k at d d0 + 4q .. +3 (d0 = 32n + 16*(g%2),
+  // kb = 16*ch + 4*(g/2), plus 8 for the second four keys) and lane i receives keys
+  // kb .. kb+3 of d d0 + i.  Two such reads make one operand.  A lane's address for d tile
+  // n sits in v_off[n]; chunk ch and the second read are immediate offsets.
+  constexpr int kTileQuad = Sh::kDTiles;  // operands per chunk (one per 32-wide d tile)
+  uint32_t v_off[kTileQuad];
   {
     const int g = lane >> 4, i = lane & 15;
+    const int row = 4 * (g >> 1) + (i >> 2);  // row % 4 == i >> 2
 #pragma unroll
-    for (int j = 0; j < Sh::kTransposes; ++j) {
-      const int blk = wave * Sh::kTransposes + j;  // (d block, key chunk) of the tile
-      const int dblk = blk >> 2, ch = blk & 3;
-      const int key = ch * 16 + 4 * g + (i >> 2);  // the key this lane addresses
-      const int byte = (16 * dblk + 4 * (i & 3)) * 2;
-      tr_src[j] = (uint32_t)(key * Sh::kRowBytes + ((((byte >> 4) ^ (key % Sh::kChunks)) << 4) | (byte & 15)));
-      const int d = 16 * dblk + i;  // the row this lane writes: keys ch*16 + 4g .. +3
-      tr_dst[j] = (uint32_t)(d * Sh::kVtRowBytes + ((((2 * ch + (g & 1)) ^ ((d >> 1) & 7))) << 4) + 8 * (g >> 1));
+    for (int n = 0; n < kTileQuad; ++n) {
+      const int chunk = 4 * n + 2 * (g & 1) + ((i & 3) >> 1);
+      v_off[n] = (uint32_t)(row * Sh::kRowBytes + ((chunk ^ v_swizzle<D>(i >> 2)) << 4) + 8 * (i & 1));
     }
   }
-  auto tr_addrs = [&](uint32_t (&a)[Sh::kTransposes], uint32_t base, const uint32_t (&off)[Sh::kTransposes]) {
+  // issues (no wait) the 2*kTileQuad transposing reads of chunk CH of the V tile at vbase:
+  // x[2n] and x[2n+1] are the two halves of d tile n's operand
+  auto v_issue = [&](u32x2 (&x)[2 * kTileQuad], uint32_t vbase_lds, auto ch_c) {
+    constexpr int CH = decltype(ch_c)::value;
+    constexpr int o0 = 16 * CH * Sh::kRowBytes, o1 = (16 * CH + 8) * Sh::kRowBytes;
+    uint32_t a[kTileQuad];
 #pragma unroll
-    for (int j = 0; j < Sh::kTransposes; ++j) a[j] = base + off[j];
-  };
-  // writes the transposed rows (the registers hold landed data)
-  auto tr_write = [&](const u32x2 (&x)[Sh::kTransposes], uint32_t dst) {
-    uint32_t w[Sh::kTransposes];
-    tr_addrs(w, dst, tr_dst);
-    if constexpr (Sh::kTransposes == 4) {
-      asm volatile(
-          "ds_write_b64 %0, %4\n\t"
-          "ds_write_b64 %1, %5\n\t"
-          "ds_write_b64 %2, %6\n\t"
-          "ds_write_b64 %3, %7"
-          :
-          : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3])
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_write_b64 %0, %2\n\t"
-          "ds_write_b64 %1, %3"
-          :
-          : "v"(w[0]), "v"(w[1]), "v"(x[0]), "v"(x[1])
-          : "memory");
-    }
-  };
-  // the whole transposition of this wave's blocks of a tile, reads waited for at once
-  auto transpose = [&](uint32_t src, uint32_t dst) {
-    u32x2 x[Sh::kTransposes];
-    uint32_t a[Sh::kTransposes];
-    tr_addrs(a, src, tr_src);
-    if constexpr (Sh::kTransposes == 4) {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %4\n\t"
-          "ds_read_b64_tr_b16 %1, %5\n\t"
-          "ds_read_b64_tr_b16 %2, %6\n\t"
-          "ds_read_b64_tr_b16 %3, %7\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
-          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %2\n\t"
-          "ds_read_b64_tr_b16 %1, %3\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(x[0]), "=&v"(x[1])
-          : "v"(a[0]), "v"(a[1])
-          : "memory");
-    }
-    tr_write(x, dst);
-  };
-  // lane (d = 32n + rl, h = half) reads chunk 2*ch + h of V^T row d: offset vt_off[ch] + n*32 rows
-  uint32_t vt_off[4];
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch)
-    vt_off[ch] = (uint32_t)(rl * Sh::kVtRowBytes + (((2 * ch + half) ^ ((rl >> 1) & 7)) << 4));
-  // issue (no wait) the V^T operand reads of one chunk; op_wait waits for each of them and
-  // hands the register on.  Issued from asm: the compiler would otherwise wait for every LDS copy in
-  // flight before an LDS read it cannot tell apart from them.
-  auto vt_issue = [&](u32x4 (&x)[kTileQuad], uint32_t base) {
-    constexpr int kRows32 = 32 * Sh::kVtRowBytes;
+    for (int n = 0; n < kTileQuad; ++n) a[n] = vbase_lds + v_off[n];
     if constexpr (kTileQuad == 4) {
       asm volatile(
-          "ds_read_b128 %0, %4\n\t"
-          "ds_read_b128 %1, %4 offset:%5\n\t"
-          "ds_read_b128 %2, %4 offset:%6\n\t"
-          "ds_read_b128 %3, %4 offset:%7"
+          "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %7, %11 offset:%13"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+            "=&v"(x[7])
+          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(o0), "i"(o1)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+          "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+          "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+          "ds_read_b64_tr_b16 %3, %5 offset:%7"
           : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
-          : "v"(base), "i"(kRows32), "i"(2 * kRows32), "i"(3 * kRows32)
+          : "v"(a[0]), "v"(a[1]), "i"(o0), "i"(o1)
           : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b128 %0, %2\n\t"
-          "ds_read_b128 %1, %2 offset:%3"
-          : "=&v"(x[0]), "=&v"(x[1])
-          : "v"(base), "i"(kRows32)
-          : "memory");
-    }
-  };
-  // issues (no wait) this wave's transposing reads of a tile
-  auto tr_issue = [&](u32x2 (&t)[Sh::kTransposes], uint32_t src) {
-    uint32_t a[Sh::kTransposes];
-    tr_addrs(a, src, tr_src);
-    if constexpr (Sh::kTransposes == 4) {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %4\n\t"
-          "ds_read_b64_tr_b16 %1, %5\n\t"
-          "ds_read_b64_tr_b16 %2, %6\n\t"
-          "ds_read_b64_tr_b16 %3, %7"
-          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
-          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %2\n\t"
-          "ds_read_b64_tr_b16 %1, %3"
-          : "=&v"(t[0]), "=&v"(t[1])
-          : "v"(a[0]), "v"(a[1])
-          : "memory");
-    }
-  };
-  // waits for this wave's transposing reads (the last LDS reads it issued)
-  auto tr_wait = [&](u32x2 (&t)[Sh::kTransposes]) {
-    if constexpr (Sh::kTransposes == 4) {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]) : : "memory");
-    } else {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]) : : "memory");
     }
   };
 
-  // fp8: this wave's rows of a raw V tile -> the bf16 row-major tile the transposition reads.
-  // Lane (row cv_row, logical raw chunk cv_cr) converts 16 codes (d = 16*cv_cr .. +15) into bf16
-  // chunks 2*cv_cr and 2*cv_cr+1 of the row, each stored at chunk ^ (row % kChunks).  With
+  // fp8: this wave's rows of a raw V tile -> a bf16 V tile.  Lane (row cv_row, logical raw
+  // chunk cv_cr) converts 16 codes (d = 16*cv_cr .. +15) into bf16 chunks 2*cv_cr and
+  // 2*cv_cr+1 of the row, each stored at chunk ^ v_swizzle(row % 4), as the copies place them.  With
   // fewer rows' chunks than lanes (D = 64) the upper lanes repeat the lower ones' work.
   const int cv_row = Sh::kRawRowsPerWave * wave + (lane % Sh::kRawLanes) / Sh::kRawChunks;
   const int cv_cr = lane % Sh::kRawChunks;
   const uint32_t cv_src = (uint32_t)(cv_row * Sh::kRawRowBytes + ((cv_cr ^ (cv_row % Sh::kRawChunks)) << 4));
-  const uint32_t cv_dst0 = (uint32_t)(cv_row * Sh::kRowBytes + (((2 * cv_cr) ^ (cv_row % Sh::kChunks)) << 4));
-  const uint32_t cv_dst1 = (uint32_t)(cv_row * Sh::kRowBytes + (((2 * cv_cr + 1) ^ (cv_row % Sh::kChunks)) << 4));
+  const uint32_t cv_dst0 = (uint32_t)(cv_row * Sh::kRowBytes + (((2 * cv_cr) ^ v_swizzle<D>(cv_row & 3)) << 4));
+  const uint32_t cv_dst1 = (uint32_t)(cv_row * Sh::kRowBytes + (((2 * cv_cr + 1) ^ v_swizzle<D>(cv_row & 3)) << 4));
   auto vraw_issue = [&](u32x4& x, uint32_t raw_base) {
     asm volatile("ds_read_b128 %0, %1" : "=&v"(x) : "v"(raw_base + cv_src) : "memory");
   };
@@ -542,42 +464,47 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
     lsum += ps;
   };
 
-  // O^T += V^T P^T for one tile, V^T from the slot at byte address vtbase.  The reads of
+  // waits until at most N LDS reads issued after x's and y's are in flight (y issued after
+  // x: both have landed) and hands both registers on
+  auto op_wait2 = [&](auto& x, auto& y, auto n_c) {
+    constexpr int N = decltype(n_c)::value;
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N) : "memory");
+  };
+  // O^T += V^T P^T for one tile, from the V tile at byte address vbase_lds.  The reads of
   // chunk ch+1 are in flight while the MFMAs of chunk ch run; between(ch) is called after
   // they are issued (the copies of the step go there, spread over the matrix-core work
   // instead of stalling the wave at once).
-  auto pv = [&](const u32x4 (&pw)[4], uint32_t vtbase, auto&& between) {
-    u32x4 vb[2][kTileQuad];
-    vt_issue(vb[0], vtbase + vt_off[0]);
+  auto pv = [&](const u32x4 (&pw)[4], uint32_t vbase_lds, auto&& between) {
+    u32x2 vb[2][2 * kTileQuad];
+    v_issue(vb[0], vbase_lds, std::integral_constant<int, 0>{});
     static_for<0, 4>([&](auto ch_c) {
       constexpr int ch = decltype(ch_c)::value;
-      if constexpr (ch + 1 < 4) vt_issue(vb[(ch + 1) & 1], vtbase + vt_off[ch + 1]);
-      constexpr int kLater = ch + 1 < 4 ? kTileQuad : 0;
+      if constexpr (ch + 1 < 4) v_issue(vb[(ch + 1) & 1], vbase_lds, std::integral_constant<int, ch + 1>{});
+      constexpr int kLater = ch + 1 < 4 ? 2 * kTileQuad : 0;
       const bf16x8 pb = u4_to_bf16x8(pw[ch]);
       static_for<0, kTileQuad>([&](auto n_c) {
         constexpr int n = decltype(n_c)::value;
-        op_wait(vb[ch & 1][n], std::integral_constant<int, kLater + kTileQuad - 1 - n>{});
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(vb[ch & 1][n]), pb, acc[n], 0, 0, 0);
+        u32x2& lo = vb[ch & 1][2 * n];
+        u32x2& hi = vb[ch & 1][2 * n + 1];
+        op_wait2(lo, hi, std::integral_constant<int, kLater + 2 * (kTileQuad - 1 - n)>{});
+        const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_to_bf16x8(a), pb, acc[n], 0, 0, 0);
         if constexpr (n == 0) between(ch);  // the step's copy of this chunk, beside the first MFMA
       });
     });
   };
-  // the softmax phase of a step with this wave's share of the transposition V(t+1) -> V^T(t+1):
-  // its reads issued first, its rows written after the exponentials
-  // (fp8: also this wave's share of the conversion of raw V(t+2) into bf16 rows, its read issued
-  // with the transposing reads and its rows written after them)
-  auto softmax_tr = [&](bool comp, f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4], uint32_t tr_from, uint32_t tr_to,
-                        uint32_t raw_from, uint32_t row_to) {
-    u32x2 tx[Sh::kTransposes];
-    u32x4 vr;
-    if constexpr (F8) vraw_issue(vr, raw_from);
-    tr_issue(tx, tr_from);
-    if (comp) softmax(sacc, key0, pw);
-    tr_wait(tx);
-    tr_write(tx, tr_to);
+  // the softmax phase of a step (fp8: with this wave's share of the conversion of raw V(t+2)
+  // into its bf16 tile, the read issued before the exponentials and the rows written after)
+  auto softmax_cv = [&](bool comp, f32x16 (&sacc)[2], int key0, u32x4 (&pw)[4], uint32_t raw_from,
+                        uint32_t row_to) {
     if constexpr (F8) {
-      asm volatile("" : "+v"(vr) : : "memory");  // landed with the transposing reads (lgkmcnt(0) above)
+      u32x4 vr;
+      vraw_issue(vr, raw_from);
+      if (comp) softmax(sacc, key0, pw);
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vr) : : "memory");
       vraw_write(vr, row_to);
+    } else {
+      if (comp) softmax(sacc, key0, pw);
     }
   };
 
@@ -588,24 +515,20 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   // order, so one group's exponentials issue while the other group's MFMAs run:
   //   leading group   (waves 0-3): O += V P(t-1), S(t)  | softmax(t) -> P(t)
   //   following group (waves 4-7): softmax(t) -> P(t)   | O += V P(t), S(t+1)
-  // and every wave transposes its share of V(t+1) into V^T(t+1) in its softmax part (its
-  // transposing reads are in flight during the exponentials, off the matrix-core part).
   // Step t also reads the block id of tile t+4 and starts the copies of K(t+3) and
   // V(t+3) (spread over the matrix-core part).  K slot (t+3)%4 last held K(t-1), read at
-  // step t-1; V slot (t+3)%3 last held V(t), transposed at step t-1; V^T slot (t+1)%3
-  // last held V^T(t-2), read at step t-1.  Before the barrier a wave waits for its V^T
-  // writes and for everything older than this step's copies (vector-memory instructions
-  // retire in order and the copies are the last loads of a step: vmcnt <= 2*kCopies),
-  // which covers K(t+2) and V(t+2), the newest tiles step t+1 reads.  Block ids are read
-  // before the copies of their step, so consuming one never waits on copies in flight.
-  // Tiles past the item's range are copied too (valid rows, never used) so that every
-  // step is alike.
+  // step t-1; V slot (t+3)%5 last held V(t-2), read at step t-1 (the step reads V(t-1) and
+  // V(t)).  Before the barrier a wave waits for its LDS reads and for everything older than
+  // this step's copies (vector-memory instructions retire in order and the copies are the
+  // last loads of a step: vmcnt <= 2*kCopies), which covers K(t+2) and V(t+2), the newest
+  // tiles step t+1 reads.  Block ids are read before the copies of their step, so
+  // consuming one never waits on copies in flight.  Tiles past the item's range are copied
+  // too (valid rows, never used) so that every step is alike.
   // fp8: step t copies raw K(t+3) and raw V(t+4) (block ids of tiles t+4 and t+5 read), and
-  // every wave also converts its rows of raw V(t+2) into bf16 row slot t%2, which last held
-  // V(t), transposed at step t-1; the transposition of step t reads slot (t+1)%2, written at
-  // step t-1.  Raw V slot (t+4)%3 last held V(t+1), converted at step t-1; raw K slot
-  // (t+3)%4 last held K(t-1).  The end-of-step wait covers raw K(t+2) and raw V(t+3), the
-  // newest raw tiles step t+1 reads.
+  // every wave also converts its rows of raw V(t+2), in its softmax part, into bf16 slot
+  // (t+2)%4, which last held V(t-2), read at step t-1.  Raw V slot (t+4)%3 last held V(t+1),
+  // converted at step t-1; raw K slot (t+3)%4 last held K(t-1).  The end-of-step wait covers
+  // raw K(t+2) and raw V(t+3), the newest raw tiles step t+1 reads.
   constexpr int kStepLoads = F8 ? 2 : 2 * Sh::kCopies;  // copy instructions per wave and step
   const int wave_tiles_end = min(kt1, wave_last / Sh::kKeys + 1);  // tiles this wave computes
   // (a sliding window's lower edge is left to the item's key range and to masking: a wave
@@ -615,8 +538,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
   {
     wait_vmcnt<Sh::kKSteps>();  // the block ids have landed; Q may still be in flight
     if constexpr (F8) {
-      // raw K and V of tiles kt0 .. kt0+2; V(kt0) and V(kt0+1) converted, V(kt0) transposed,
-      // and raw V(kt0+3) copied into the slot V(kt0) left, before the first step
+      // raw K and V of tiles kt0 .. kt0+2; V(kt0) and V(kt0+1) converted, and raw V(kt0+3)
+      // copied into the slot V(kt0) left, before the first step
       copy_raw(kbase, kt0, ph0, k_stage(kt0));
       copy_raw(vbase, kt0, ph0, vraw_stage(kt0));
       copy_raw(kbase, kt0 + 1, ph1, k_stage(kt0 + 1));
@@ -629,21 +552,17 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
       vraw_convert((uint32_t)(uintptr_t)vraw_stage(kt0 + 1), v_addr(kt0 + 1));
       wait_vmcnt_lgkm0<2>();
       __builtin_amdgcn_s_barrier();
-      transpose(v_addr(kt0), vt_addr(kt0));
       copy_raw(vbase, kt0 + 3, phys_next, vraw_stage(kt0 + 3));
       wait_vmcnt_lgkm0<1>();  // tile kt0+2 has landed; raw V(kt0+3) may be in flight
       __builtin_amdgcn_s_barrier();
     } else {
-      copy_rows(kbase, kt0, ph0, k_stage(kt0));
-      copy_rows(vbase, kt0, ph0, v_stage(kt0));
-      copy_rows(kbase, kt0 + 1, ph1, k_stage(kt0 + 1));
-      copy_rows(vbase, kt0 + 1, ph1, v_stage(kt0 + 1));
-      copy_rows(kbase, kt0 + 2, ph2, k_stage(kt0 + 2));
-      copy_rows(vbase, kt0 + 2, ph2, v_stage(kt0 + 2));
+      copy_rows(false, kt0, ph0, k_stage(kt0));
+      copy_rows(true, kt0, ph0, v_stage(kt0));
+      copy_rows(false, kt0 + 1, ph1, k_stage(kt0 + 1));
+      copy_rows(true, kt0 + 1, ph1, v_stage(kt0 + 1));
+      copy_rows(false, kt0 + 2, ph2, k_stage(kt0 + 2));
+      copy_rows(true, kt0 + 2, ph2, v_stage(kt0 + 2));
       wait_vmcnt<2 * Sh::kCopies>();  // Q and tiles kt0, kt0+1 have landed
-      __builtin_amdgcn_s_barrier();
-      transpose(v_addr(kt0), vt_addr(kt0));
-      wait_vmcnt_lgkm0<2 * Sh::kCopies>();
       __builtin_amdgcn_s_barrier();
     }
 
@@ -666,9 +585,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
             copy_raw(vbase, tile + 4, phys_v, v_dst);
         } else {
           if (part < Sh::kCopies)
-            copy_slab(kbase, tile + 3, phys, k_dst, part);
+            copy_slab(false, tile + 3, phys, k_dst, part);
           else if (part < 2 * Sh::kCopies)
-            copy_slab(vbase, tile + 3, phys, v_dst, part - Sh::kCopies);
+            copy_slab(true, tile + 3, phys, v_dst, part - Sh::kCopies);
         }
       };
       auto copy_all = [&]() {
@@ -677,24 +596,23 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
       };
       phys_next = phys_new;
       phys_v_next = phys_v_new;
-      // V(t+1) -> V^T(t+1) by every wave; tiles past the range hold valid rows too, so the
-      // transposition is unconditional (fp8: and raw V(t+2) -> bf16 rows, into the slot V(t) left)
-      const uint32_t tr_from = v_addr(tile + 1), tr_to = vt_addr(tile + 1);
+      // fp8: raw V(t+2) -> its bf16 tile by every wave; tiles past the range hold valid rows
+      // too, so the conversion is unconditional
       const uint32_t raw_from = F8 ? (uint32_t)(uintptr_t)vraw_stage(tile + 2) : 0u;
       const uint32_t row_to = F8 ? v_addr(tile + 2) : 0u;
-      if (!leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to, raw_from, row_to);
+      if (!leading) softmax_cv(computes(tile), sc, tile * Sh::kKeys, pw, raw_from, row_to);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
       if (leading) {
         if (tile > kt0 && computes(tile - 1)) {
-          pv(pw, vt_addr(tile - 1), copy_part);
+          pv(pw, v_addr(tile - 1), copy_part);
         } else {
           copy_all();
         }
         if (computes(tile)) scores(sc, k_addr(tile));
       } else {
         if (computes(tile)) {
-          pv(pw, vt_addr(tile), copy_part);
+          pv(pw, v_addr(tile), copy_part);
         } else {
           copy_all();
         }
@@ -702,13 +620,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, unsigned ch
       }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      if (leading) softmax_tr(computes(tile), sc, tile * Sh::kKeys, pw, tr_from, tr_to, raw_from, row_to);
+      if (leading) softmax_cv(computes(tile), sc, tile * Sh::kKeys, pw, raw_from, row_to);
       wait_vmcnt_lgkm0<kStepLoads>();
       __builtin_amdgcn_s_barrier();
     }
-    // the last O += V P of the leading group (the last step transposed V(kt1) into a slot
-    // that nothing reads: tiles past the range hold valid rows)
-    if (leading && computes(kt1 - 1)) pv(pw, vt_addr(kt1 - 1), [](int) {});
+    // the last O += V P of the leading group (the copies of the last step went to other slots)
+    if (leading && computes(kt1 - 1)) pv(pw, v_addr(kt1 - 1), [](int) {});
     wait_vmcnt<0>();  // no copy may still be writing LDS when the work-group ends
   }
 

@@ -15,10 +15,11 @@
 // gathered once for all of them.  Wave w owns rows 32w .. 32w+31, one 32-row
 // matrix-core block.  K/V tiles of 64 keys (4 paged blocks) are copied through
 // the block table straight from HBM into LDS (global_load_lds_dwordx4, no
-// registers on the way), row-major with XOR-swizzled 16-byte chunks, in a ring
-// of four stages filled three tiles ahead:
+// registers on the way), row-major with XOR-swizzled 16-byte chunks, in rings
+// (four K stages, five V stages) filled three tiles ahead:
 //   S^T[key][row] = K Q^T    v_mfma_f32_32x32x16_bf16 (K rows from LDS, Q in registers)
-//   O^T[d][row]  += V^T P^T  v_mfma_f32_32x32x16_bf16 (V^T through ds_read_b64_tr_b16,
+//   O^T[d][row]  += V^T P^T  v_mfma_f32_32x32x16_bf16 (V^T gathered from the row-major
+//                                                      V tile by ds_read_b64_tr_b16,
 //                                                      P straight from the S^T registers)
 // The scores of tile t+1 are issued to the matrix cores before the softmax
 // of tile t.  The running maximum is only moved when a row's
@@ -30,8 +31,8 @@
 //
 // fp8 pools (tutorial 6 of the same page: E4M3 KV with a scale): the tiles are copied as
 // raw codes; K operands are converted to bf16 as they are read, and V is converted into a
-// bf16 row-major tile before its transposition, so the matrix cores see the codes' exact
-// bf16 values (the scales go to the score scale and the output).
+// bf16 row-major tile that O += V P reads as it reads bf16 tiles, so the matrix cores see
+// the codes' exact bf16 values (the scales go to the score scale and the output).
 #include <type_traits>
 
 #include "pa_device.h"
