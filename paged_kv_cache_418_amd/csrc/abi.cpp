@@ -906,8 +906,10 @@ CascadeTilePlan plan_cascade_tiles(int num_seqs, int num_q_heads, int num_kv_hea
   const int prefix_len = prefix_blocks * pa::kBlockSize;
   cp.key_tiles = ceil_div(prefix_len, pa::kPrefillKeys);
   static const double tile_s = env_int("PA_FUSED_TILE_NS", 2200, 100, 1000000) * 1e-9;
-  static const double bw = env_int("PA_FUSED_DECODE_GBPS", 6000, 100, 100000) * 1e9;
-  static const double bw_cu = env_int("PA_FUSED_CU_GBPS", 29, 1, 100000) * 1e9;
+  // the decode shares' rate inside the fused launch: about 30 GB/s per compute unit, and no
+  // more than about 5.8 TB/s in all (the items' own traffic shares HBM with it)
+  static const double bw = env_int("PA_FUSED_DECODE_GBPS", 5800, 100, 100000) * 1e9;
+  static const double bw_cu = env_int("PA_FUSED_CU_GBPS", 30, 1, 100000) * 1e9;
   // an fp8 block is half the bytes for the same work per block: fewer bytes per compute unit
   // (measured on the prefix-shared fp8 step: 18 GB/s per decode compute unit)
   static const double bw_cu8 = env_int("PA_FUSED_CU_GBPS_FP8", 18, 1, 100000) * 1e9;
@@ -1347,8 +1349,10 @@ pa_status_t plan_step(const int32_t* qsl, const int32_t* sl, int num_seqs, int n
       sp.plan.items.size() > (size_t)pa::kMaxPrefillItems)
     return PA_OK;
   static const double tile_s = env_int("PA_FUSED_TILE_NS", 2200, 100, 1000000) * 1e-9;
-  static const double bw = env_int("PA_FUSED_DECODE_GBPS", 6000, 100, 100000) * 1e9;
-  static const double bw_cu = env_int("PA_FUSED_CU_GBPS", 29, 1, 100000) * 1e9;
+  // the decode shares' rate inside the fused launch: about 30 GB/s per compute unit, and no
+  // more than about 5.8 TB/s in all (the items' own traffic shares HBM with it)
+  static const double bw = env_int("PA_FUSED_DECODE_GBPS", 5800, 100, 100000) * 1e9;
+  static const double bw_cu = env_int("PA_FUSED_CU_GBPS", 30, 1, 100000) * 1e9;
   const double item_s = 5e-6;
   const int C = device_cu_count();
   double dec_bytes = 0;
@@ -1374,26 +1378,34 @@ pa_status_t plan_step(const int32_t* qsl, const int32_t* sl, int num_seqs, int n
     return *std::max_element(load.begin(), load.end());
   };
   const double t_seq = dec_bytes / bw + t_pre(sp.plan, C);
-  double best = mode == 2 ? 1e30 : t_seq * 0.95;  // fuse only for a clear gain (mode 2: always)
-  int best_q = 0;
-  VarlenPlan best_plan;
+  const double limit = mode == 2 ? 1e30 : t_seq * 0.95;  // fuse only for a clear gain (mode 2: always)
   const std::string saved = g_last_error;
   static const int forced_q = env_int("PA_FUSED_DECODE_CUS", 0, 0, 1 << 20);  // measurement: fix Q
+  auto plan_for = [&](int q, VarlenPlan& pl) {
+    return plan_varlen(qsl, sl, num_seqs, num_tokens, bt_stride, group, num_kv_heads, pl, window, chunk,
+                       std::max(1, (C - q) / num_kv_heads)) == PA_OK &&
+           pl.items.size() <= (size_t)pa::kMaxPrefillItems;
+  };
+  // modelled time of every Q; then the smallest Q within 1% of the best: once the decode
+  // stream has the compute units it can use, more of them only slow the items down
+  std::vector<std::pair<int, double>> cand;
+  double best = 1e30;
   for (int q = std::max(8, C / 4); q <= C - num_kv_heads; q += 8) {
     if (forced_q > 0 && q != forced_q) continue;
-    const int cus = C - q;
     VarlenPlan pl;
-    if (plan_varlen(qsl, sl, num_seqs, num_tokens, bt_stride, group, num_kv_heads, pl, window, chunk,
-                    std::max(1, cus / num_kv_heads)) != PA_OK ||
-        pl.items.size() > (size_t)pa::kMaxPrefillItems)
-      continue;
-    const double t = std::max(t_dec(q), t_pre(pl, cus));
-    if (t <= best || forced_q > 0) {  // ties: the larger share for the decode stream
-      best = t;
-      best_q = q;
-      best_plan = std::move(pl);
-    }
+    if (!plan_for(q, pl)) continue;
+    const double t = std::max(t_dec(q), t_pre(pl, C - q));
+    cand.emplace_back(q, t);
+    best = std::min(best, t);
   }
+  int best_q = 0;
+  for (const auto& [q, t] : cand)
+    if (forced_q > 0 || (t <= limit && t <= best * 1.01)) {
+      best_q = q;
+      break;
+    }
+  VarlenPlan best_plan;
+  if (best_q > 0 && !plan_for(best_q, best_plan)) best_q = 0;
   g_last_error = saved;
   if (best_q == 0) return PA_OK;
   sp.fused = true;
