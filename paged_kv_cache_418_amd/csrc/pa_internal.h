@@ -129,7 +129,7 @@ struct PrefillParams {
   uint64_t items[kMaxPrefillItems];
 };
 
-// Merge of split row tiles: grid (n_items, num_kv_heads).  Item bits: sequence
+// Merge of split row tiles: grid (n_items x 8 groups of 32 rows, num_kv_heads).  Item bits: sequence
 // (16), row tile (16), first slot (20), number of slots (12).
 struct PrefillMergeParams {
   void* out;
