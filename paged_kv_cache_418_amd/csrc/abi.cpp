@@ -160,11 +160,14 @@ int decode_waves_per_simd(bool fp8) {
   return env ? env : 1;
 }
 
-// Blocks' worth of time a decode piece costs to start (PA_DECODE_PIECE_COST): the share
-// planner counts it for every sequence, so shares that start several pieces hold fewer blocks.
-int decode_piece_cost() {
-  static const int c = env_int("PA_DECODE_PIECE_COST", 3, 0, 64);
-  return c;
+// Blocks' worth of time a decode piece costs to start (PA_DECODE_PIECE_COST overrides): the
+// share planner counts it for every sequence, so shares that start several pieces hold fewer
+// blocks.  An E4M3 block streams in about half a bf16 block's time, so the same start costs
+// more of them: on the Llama-3-8B-shaped batch the fp8 decode launch took 48.5-49.0 us at 3,
+// 47.5-47.6 at 5, 48.1 at 6 and 48.2-48.3 at 8; bf16 pools are best at 3.
+int decode_piece_cost(bool fp8) {
+  static const int env = env_int("PA_DECODE_PIECE_COST", -1, -1, 64);
+  return env >= 0 ? env : fp8 ? 5 : 3;
 }
 
 // Waves per share of a decode launch: a kv head's q heads go 16 at a time to the matrix-core
@@ -305,7 +308,7 @@ pa::DecodeParams make_decode_params(void* out, const void* query, const void* ke
   p.head_groups = (p.group + 15) / 16;  // 1 for a cascade (at most 16 q heads per kv head)
   p.max_seq_len = max_seq_len;
   p.n_splits = n_splits;
-  p.piece_cost = decode_piece_cost();
+  p.piece_cost = decode_piece_cost(kv_kind == pa::kFP8);
   p.window = sliding_window > 0 ? sliding_window : 0;
   p.chunk = local_chunk > 0 ? local_chunk : 0;
   p.scale_log2 = scale * 1.4426950408889634f * (kv_kind == pa::kFP8 ? k_scale : 1.f);
